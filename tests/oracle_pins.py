@@ -1,0 +1,371 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes a loaded oracle library (the real one, or a
+mutant compiled by the planted-mistake test) and raises AssertionError if
+the oracle disagrees with:
+  * torch's own float8 / bf16 conversions (a library routine independent of
+    the oracle's bit-field decoders),
+  * the OCP spot values stored in tests/golden/,
+  * exact rational arithmetic (fractions.Fraction) on tiny inputs,
+  * closed forms, the integer matrix product, and exact invariants of the
+    definition (power-of-two scale doubling, permutation inputs).
+
+What is pinned is the definition of the scaled dot given as async_dot_scaled
+in the TLX API Quick Reference ("Matrix Multiply (MMA)": D = (A*scale_A) @
+(B*scale_B) + D) with one uint8 scale per 32 K-elements (TLX async-compute
+page, "TMEM-backed MX Scales", K extent BLOCK_K // 32).
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+import mxinputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+FMT_NAMES = {"e4m3": 0, "e5m2": 1, "e8m0": 2}
+_TORCH = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2, 2: torch.float8_e8m0fnu}
+
+
+def torch_decode(fmt: int) -> np.ndarray:
+    codes = torch.arange(256, dtype=torch.uint8)
+    return codes.view(_TORCH[fmt]).to(torch.float64).numpy()
+
+
+def same(a, b, signed_zero: bool = False) -> bool:
+    """Equal as floats with NaN equal to NaN; the sign of zero counts only
+    when signed_zero is set (a sum that is exactly zero has no fixed sign)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    both_nan = np.isnan(a) & np.isnan(b)
+    eq = a == b
+    if signed_zero:
+        eq &= np.signbit(a) == np.signbit(b)
+    return bool(np.all(both_nan | eq))
+
+
+def bf16_bits_to_float(bits) -> np.ndarray:
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32)
+
+
+def _parse_value(tok: str) -> float:
+    if tok == "-0":
+        return -0.0
+    if tok.startswith("0x") or tok.startswith("-0x"):
+        return float.fromhex(tok)
+    return float(tok)
+
+
+def golden_spot_values():
+    out = []
+    with open(os.path.join(GOLDEN, "ocp_fp8_spot_values.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            fmt, code, val = line.split()
+            out.append((FMT_NAMES[fmt], int(code, 16), _parse_value(val)))
+    return out
+
+
+# ---------------------------------------------------------------- formats --
+
+def pin_tables_match_torch(lib):
+    for fmt in (0, 1, 2):
+        got = oracle.decode_table(fmt, lib)
+        want = torch_decode(fmt)
+        assert same(got, want, signed_zero=True), \
+            f"format {fmt}: oracle table differs from torch's float8 view"
+
+
+def pin_spot_values(lib):
+    for fmt, code, val in golden_spot_values():
+        got = lib.mxref_decode(fmt, code)
+        assert same(got, val, signed_zero=True), f"format {fmt} code {code:#04x}: {got!r} != {val!r}"
+
+
+def pin_special_counts(lib):
+    e4 = oracle.decode_table(0, lib)
+    e5 = oracle.decode_table(1, lib)
+    e8 = oracle.decode_table(2, lib)
+    assert np.isnan(e4).sum() == 2 and np.isinf(e4).sum() == 0
+    assert np.isnan(e5).sum() == 6 and np.isinf(e5).sum() == 2
+    assert np.isnan(e8).sum() == 1 and np.isinf(e8).sum() == 0
+    fin4, fin5 = e4[np.isfinite(e4)], e5[np.isfinite(e5)]
+    assert fin4.max() == 448.0 and fin4.min() == -448.0
+    assert fin5.max() == 57344.0 and fin5.min() == -57344.0
+    # every finite positive value appears once (no duplicate encodings but +-0)
+    assert len(np.unique(fin4[fin4 > 0])) == 126 and len(np.unique(fin5[fin5 > 0])) == 123
+
+
+def pin_bf16_rne(lib):
+    g = np.random.Generator(np.random.PCG64(4242))
+    x = g.standard_normal(4000).astype(np.float32) * np.float32(3.0)
+    bits = g.integers(0, 2**32, size=4000, dtype=np.uint64).astype(np.uint32)
+    y = bits.view(np.float32)
+    # exact ties: low 16 bits 0x8000, both parities of bit 16
+    ties = (np.arange(64, dtype=np.uint32) * 0x10000 + 0x3f808000).view(np.float32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 3.4028235e38, -3.4028235e38,
+                        1e-45, 1.17549435e-38, 65504.0], dtype=np.float32)
+    allv = np.concatenate([x, y, ties, special])
+    got = oracle.bf16_rne(allv, lib)
+    want = torch.from_numpy(allv).to(torch.bfloat16).view(torch.uint16).numpy()
+    fin = ~np.isnan(allv)
+    assert np.array_equal(got[fin], want[fin]), "bf16 RNE differs from torch's cast"
+    nanout = got[~fin]
+    assert np.all((nanout & 0x7f80) == 0x7f80) and np.all((nanout & 0x007f) != 0)
+
+
+# ------------------------------------------------------------ the product --
+
+def _exact_value(code: int, fmt: int, dec) -> Fraction:
+    return Fraction(float(dec[fmt][code]))
+
+
+def pin_bruteforce_fraction(lib):
+    """Tiny random problems: the oracle's double sum is within Higham's
+    recursive-summation bound of the exact rational sum, its fp32 result is
+    the correct rounding whenever the double sum is exact, and never more
+    than one fp32 ulp away."""
+    dec = {f: torch_decode(f) for f in (0, 1, 2)}
+    cases = [(3, 4, 64, 0, 0, False, 0), (2, 3, 96, 1, 0, False, 0), (4, 2, 40, 0, 1, False, 0),
+             (3, 3, 256, 1, 1, True, 0), (2, 2, 33, 0, 0, True, 1), (1, 1, 1, 1, 1, False, 0),
+             (4, 4, 160, 0, 0, True, 0)]
+    for i, (M, N, K, fa, fb, acc, cdt) in enumerate(cases):
+        p = mxinputs.random_problem(M, N, K, seed=50 + i, fmtA=fa, fmtB=fb, scale_lo=110,
+                                    scale_hi=140, use_acc=acc,
+                                    out_dtype=mxinputs.OUT_BF16 if cdt else mxinputs.OUT_F32)
+        r = oracle.gemm_full(p.A, p.As, fa, p.B, p.Bs, fb, M, N, K, cin=p.Cin, nthreads=2, lib=lib)
+        for m in range(M):
+            for n in range(N):
+                exact = Fraction(0)
+                mag = Fraction(0)
+                for k in range(K):
+                    t = (_exact_value(p.A[m, k], fa, dec) * _exact_value(p.As[m, k // 32], 2, dec)
+                         * _exact_value(p.B[n, k], fb, dec) * _exact_value(p.Bs[n, k // 32], 2, dec))
+                    exact += t
+                    mag += abs(t)
+                if acc:
+                    if cdt == 0:
+                        c = Fraction(float(p.Cin[m, n]))
+                    else:
+                        c = Fraction(float(bf16_bits_to_float(p.Cin[m, n])))
+                    exact += c
+                    mag += abs(c)
+                s = r["sum"][m, n]
+                bound = Fraction(K + 1) * Fraction(2) ** -53 * mag
+                assert abs(Fraction(s) - exact) <= bound, f"case {i} ({m},{n}): sum off"
+                assert float(mag) == r["mag"][m, n] or abs(Fraction(r["mag"][m, n]) - mag) <= bound
+                want32 = np.float32(float(exact))  # double rounding only if exact not a double
+                if Fraction(float(exact)) == exact:
+                    assert r["ref32"][m, n] == want32, f"case {i} ({m},{n}): fp32 rounding"
+                else:
+                    ulp = np.spacing(np.float32(abs(want32)))
+                    assert abs(float(r["ref32"][m, n]) - float(want32)) <= ulp
+
+
+def _pairwise(lib, fa, fb, sa, sb):
+    """M = N = 256, K = 32: A[m,0] = code m, B[0,n] = code n, all else 0."""
+    M = N = 256
+    K = 32
+    A = np.zeros((M, K), np.uint8)
+    B = np.zeros((N, K), np.uint8)
+    A[:, 0] = np.arange(256, dtype=np.uint8)
+    B[:, 0] = np.arange(256, dtype=np.uint8)
+    As = np.full((M, 1), sa, np.uint8)
+    Bs = np.full((N, 1), sb, np.uint8)
+    return oracle.gemm_full(A, As, fa, B, Bs, fb, M, N, K, nthreads=4, lib=lib)
+
+
+def pin_pairwise_products(lib):
+    """Every pair of codes, for every format pair and several scale bytes:
+    C[m,n] is exactly dec(m) * dec(n) * 2^(sa+sb-254)."""
+    dec = {f: torch_decode(f) for f in (0, 1)}
+    for fa in (0, 1):
+        for fb in (0, 1):
+            for sa, sb in ((127, 127), (0, 127), (127, 1), (126, 128), (253, 254), (254, 254),
+                           (1, 0), (100, 140)):
+                r = _pairwise(lib, fa, fb, sa, sb)
+                scale = math.ldexp(1.0, sa - 127) * math.ldexp(1.0, sb - 127)
+                want = np.outer(dec[fa], dec[fb])
+                with np.errstate(invalid="ignore", over="ignore"):
+                    want = want * scale  # a power of two times an exact product
+                    # inf * 0 from the zero padding terms is NaN in the definition too
+                    assert same(r["sum"], want), f"pairwise fa={fa} fb={fb} sa={sa} sb={sb}"
+                    want32 = want.astype(np.float32)   # numpy's IEEE rounding to fp32
+                assert same(r["ref32"], want32), f"pairwise fp32 fa={fa} fb={fb} sa={sa} sb={sb}"
+
+
+def pin_closed_form(lib):
+    """A = B = 1.0 (code 0x38) everywhere with constant scales:
+    C = K * 2^(sa + sb - 254) exactly."""
+    for K, sa, sb, fa, fb in ((32, 127, 127, 0, 0), (96, 130, 120, 0, 0), (1024, 140, 100, 0, 0),
+                              (320, 127, 128, 1, 1), (4096, 5, 250, 0, 1)):
+        M, N = 3, 5
+        c1 = {0: 0x38, 1: 0x3C}
+        A = np.full((M, K), c1[fa], np.uint8)
+        B = np.full((N, K), c1[fb], np.uint8)
+        As = np.full((M, K // 32), sa, np.uint8)
+        Bs = np.full((N, K // 32), sb, np.uint8)
+        r = oracle.gemm_full(A, As, fa, B, Bs, fb, M, N, K, nthreads=1, lib=lib)
+        want = K * math.ldexp(1.0, sa + sb - 254)
+        assert np.all(r["sum"] == want) and np.all(r["ref32"] == np.float32(want)), f"K={K}"
+        assert np.all(r["mag"] == want)
+
+
+def pin_integer_gemm(lib):
+    """Codes restricted to integers (e4m3: -16..16, e5m2: -8..8), scales 1.0:
+    C equals the int64 matrix product exactly."""
+    for fa, fb, seed in ((0, 0, 1), (1, 0, 2), (0, 1, 3), (1, 1, 4)):
+        g = np.random.Generator(np.random.PCG64(seed))
+        M, N, K = 37, 29, 544
+        lim = {0: 16, 1: 8}
+        ia = g.integers(-lim[fa], lim[fa] + 1, size=(M, K))
+        ib = g.integers(-lim[fb], lim[fb] + 1, size=(N, K))
+        A = mxinputs.quantize(ia.astype(np.float32), fa)
+        B = mxinputs.quantize(ib.astype(np.float32), fb)
+        As = np.full((M, K // 32), 127, np.uint8)
+        Bs = np.full((N, K // 32), 127, np.uint8)
+        r = oracle.gemm_full(A, As, fa, B, Bs, fb, M, N, K, nthreads=3, lib=lib)
+        want = ia.astype(np.int64) @ ib.astype(np.int64).T
+        assert np.array_equal(r["sum"], want.astype(np.float64)), f"integer gemm {fa},{fb}"
+        assert np.array_equal(r["ref32"], want.astype(np.float32))
+
+
+def pin_scale_doubling(lib):
+    """Adding 1 to every A-scale byte of row m (or B-scale byte of column n)
+    doubles that row (column) exactly; bumping one block's byte changes only
+    that block's contribution, by exactly its own value."""
+    p = mxinputs.random_problem(9, 7, 256, seed=77)
+    M, N, K = p.M, p.N, p.K
+    base = oracle.gemm_full(p.A, p.As, 0, p.B, p.Bs, 0, M, N, K, lib=lib)
+    As2 = p.As.copy(); As2[4, :] += 1
+    r = oracle.gemm_full(p.A, As2, 0, p.B, p.Bs, 0, M, N, K, lib=lib)
+    assert np.array_equal(r["sum"][4], 2 * base["sum"][4])
+    assert np.array_equal(r["ref32"][4], 2 * base["ref32"][4])
+    mask = np.ones(M, bool); mask[4] = False
+    assert np.array_equal(r["sum"][mask], base["sum"][mask])
+    Bs2 = p.Bs.copy(); Bs2[2, :] += 1
+    r = oracle.gemm_full(p.A, p.As, 0, p.B, Bs2, 0, M, N, K, lib=lib)
+    assert np.array_equal(r["ref32"][:, 2], 2 * base["ref32"][:, 2])
+    # one block: the difference equals that block's partial sum
+    As3 = p.As.copy(); As3[1, 3] += 1
+    r = oracle.gemm_full(p.A, As3, 0, p.B, p.Bs, 0, M, N, K, lib=lib)
+    blk = np.zeros((M, K), np.uint8); blk[:, 96:128] = p.A[:, 96:128]
+    part = oracle.gemm_full(blk, p.As, 0, p.B, p.Bs, 0, M, N, K, lib=lib)
+    assert np.allclose(r["sum"][1] - base["sum"][1], part["sum"][1], rtol=1e-12, atol=0)
+    assert np.array_equal(r["sum"][0], base["sum"][0])
+
+
+def pin_permutation(lib):
+    """A a permutation matrix of 1.0 codes with scale bytes 127: C[m,n] is the
+    scaled B element at K index pi(m); and the same with B a permutation."""
+    dec = {f: torch_decode(f) for f in (0, 1, 2)}
+    g = np.random.Generator(np.random.PCG64(11))
+    M = N = 64
+    K = 128
+    pi = g.permutation(K)[:M]
+    p = mxinputs.random_problem(M, N, K, seed=12, fmtB=1)
+    A = np.zeros((M, K), np.uint8); A[np.arange(M), pi] = 0x38
+    As = np.full((M, K // 32), 127, np.uint8)
+    r = oracle.gemm_full(A, As, 0, p.B, p.Bs, 1, M, N, K, lib=lib)
+    want = dec[1][p.B[:, pi].T] * dec[2][p.Bs[:, pi // 32].T]
+    assert same(r["sum"], want), "A = permutation"
+    sigma = g.permutation(K)[:N]
+    B = np.zeros((N, K), np.uint8); B[np.arange(N), sigma] = 0x38
+    Bs = np.full((N, K // 32), 127, np.uint8)
+    r = oracle.gemm_full(p.A, p.As, 0, B, Bs, 0, M, N, K, lib=lib)
+    want = dec[0][p.A[:, sigma]] * dec[2][p.As[:, sigma // 32]]
+    assert same(r["sum"], want), "B = permutation"
+
+
+def pin_numpy_matmul(lib):
+    """Medium random problems, including a K that is not a multiple of 32 and
+    use_acc with an fp32 and a bf16 C: the oracle agrees with numpy's float64
+    matmul of the decoded, scaled operands (torch decode) within 1e-12 * mag."""
+    for i, (M, N, K, fa, fb, acc, outd) in enumerate((
+            (70, 53, 512, 0, 0, False, 0), (33, 65, 200, 1, 0, True, 0),
+            (48, 17, 96, 0, 1, True, 1), (20, 20, 1000, 1, 1, False, 0))):
+        p = mxinputs.random_problem(M, N, K, seed=300 + i, fmtA=fa, fmtB=fb, use_acc=acc,
+                                    out_dtype=outd)
+        dec = {f: torch_decode(f) for f in (0, 1, 2)}
+        sa = np.repeat(dec[2][p.As], 32, axis=1)[:, :K]
+        sb = np.repeat(dec[2][p.Bs], 32, axis=1)[:, :K]
+        a = dec[fa][p.A] * sa
+        b = dec[fb][p.B] * sb
+        want = a @ b.T
+        mag = np.abs(a) @ np.abs(b).T
+        if acc:
+            if outd == 0:
+                c = p.Cin.astype(np.float64)
+            else:
+                c = bf16_bits_to_float(p.Cin).astype(np.float64)
+            want = want + c
+            mag = mag + np.abs(c)
+        r = oracle.gemm_full(p.A, p.As, fa, p.B, p.Bs, fb, M, N, K, cin=p.Cin, lib=lib)
+        assert np.all(np.abs(r["sum"] - want) <= 1e-12 * mag + 1e-300), f"case {i}"
+        assert np.allclose(r["mag"], mag, rtol=1e-12, atol=0)
+        if outd == 1:
+            want_bf = torch.from_numpy(r["ref32"]).to(torch.bfloat16).view(torch.uint16).numpy()
+            assert np.array_equal(r["refbf16"], want_bf)
+
+
+def pin_nan_propagation(lib):
+    """A NaN code or a NaN scale byte (255) poisons exactly the outputs it
+    reaches; an e5m2 infinity times a nonzero value gives an infinity."""
+    p = mxinputs.random_problem(6, 5, 64, seed=90)
+    A = p.A.copy(); A[2, 17] = 0x7F                     # e4m3 NaN
+    Bs = p.Bs.copy(); Bs[3, 1] = 255                   # NaN scale on column 3
+    r = oracle.gemm_full(A, p.As, 0, p.B, Bs, 0, 6, 5, 64, lib=lib)
+    nan = np.isnan(r["ref32"])
+    want = np.zeros((6, 5), bool); want[2, :] = True; want[:, 3] = True
+    assert np.array_equal(nan, want)
+    A5 = np.full((1, 32), 0x3C, np.uint8); A5[0, 0] = 0x7C  # +inf in e5m2
+    B = np.full((1, 32), 0x38, np.uint8)
+    r = oracle.gemm_full(A5, np.full((1, 1), 127, np.uint8), 1, B,
+                         np.full((1, 1), 127, np.uint8), 0, 1, 1, 32, lib=lib)
+    assert r["ref32"][0, 0] == np.inf
+
+
+def pin_thread_independence(lib):
+    p = mxinputs.random_problem(31, 23, 320, seed=5)
+    outs = [oracle.gemm_full(p.A, p.As, 0, p.B, p.Bs, 0, 31, 23, 320, nthreads=t, lib=lib)
+            for t in (1, 3, 8)]
+    for o in outs[1:]:
+        assert np.array_equal(o["sum"].view(np.int64), outs[0]["sum"].view(np.int64))
+
+
+def pin_scale_tile_extent(lib):
+    """The page's scale tiles: (rows, K//32) bytes, one per 32 K-elements.
+    With scale byte j of row 0 raised by one, only K-elements 32j..32j+31
+    of that row are doubled."""
+    with open(os.path.join(GOLDEN, "scale_tile_shapes.txt")) as f:
+        tiles = [tuple(int(t) for t in ln.split()) for ln in f
+                 if ln.strip() and not ln.startswith("#")]
+    for nrows, cols, kcov in tiles:
+        assert kcov == 32 * cols
+        K, M, N = kcov, nrows, 2
+        for j in range(cols):
+            A = np.zeros((M, K), np.uint8)
+            A[0, 32 * j: 32 * j + 32] = 0x38        # 1.0 inside block j only
+            B = np.full((N, K), 0x38, np.uint8)
+            Bs = np.full((N, cols), 127, np.uint8)
+            As = np.full((M, cols), 127, np.uint8)
+            As[0, j] = 128
+            r = oracle.gemm_full(A, As, 0, B, Bs, 0, M, N, K, lib=lib)
+            assert np.all(r["sum"][0] == 64.0) and np.all(r["sum"][1:] == 0.0)
+            As[0, j] = 127
+            As[0, (j + 1) % cols] = 128
+            r = oracle.gemm_full(A, As, 0, B, Bs, 0, M, N, K, lib=lib)
+            assert np.all(r["sum"][0] == 32.0)
+
+
+ALL_PINS = [pin_tables_match_torch, pin_spot_values, pin_special_counts, pin_bf16_rne,
+            pin_bruteforce_fraction, pin_pairwise_products, pin_closed_form,
+            pin_integer_gemm, pin_scale_doubling, pin_permutation, pin_numpy_matmul,
+            pin_nan_propagation, pin_thread_independence, pin_scale_tile_extent]

@@ -1,0 +1,76 @@
+"""The seeded input generators (shared by the oracle and the HIP path)."""
+import numpy as np
+import torch
+
+import mxinputs as mi
+import oracle
+
+
+def test_quantizer_saturates_and_rounds_to_even():
+    e4 = oracle.decode_table(0)
+    e5 = oracle.decode_table(1)
+    big = np.array([449, 464, 480, 1e9, -1e9, np.inf], np.float32)
+    assert list(mi.quantize(big, 0)) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x7E]
+    assert list(mi.quantize(np.array([60000, 1e30], np.float32), 1)) == [0x7B, 0x7B]
+    # midpoints between neighbouring positive e4m3 values go to the even code
+    pos = np.sort(e4[1:0x7F])
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    codes = mi.quantize(mids, 0)
+    assert np.all(codes % 2 == 0)
+    # every value lands on the nearest representable value
+    g = np.random.Generator(np.random.PCG64(1))
+    x = g.standard_normal(20000).astype(np.float32) * 40
+    for fmt, tab in ((0, e4), (1, e5)):
+        c = mi.quantize(x, fmt)
+        v = tab[c]
+        fin = tab[np.isfinite(tab)]
+        nearest = np.min(np.abs(fin[None, :] - np.clip(x, -mi.FMT_MAX[fmt], mi.FMT_MAX[fmt])[:, None]
+                                .astype(np.float64)), axis=1)
+        assert np.all(np.abs(v - np.clip(x, -mi.FMT_MAX[fmt], mi.FMT_MAX[fmt])) == nearest)
+
+
+def test_generators_are_seeded():
+    a = mi.random_problem(17, 9, 96, seed=3)
+    b = mi.random_problem(17, 9, 96, seed=3)
+    c = mi.random_problem(17, 9, 96, seed=4)
+    assert np.array_equal(a.A, b.A) and np.array_equal(a.Bs, b.Bs)
+    assert not np.array_equal(a.A, c.A)
+    assert a.As.min() >= 120 and a.As.max() <= 134
+
+
+def test_block_exponent_is_minimal():
+    g = np.random.Generator(np.random.PCG64(2))
+    amax = np.abs(g.standard_normal(5000)) * 0.05
+    amax = np.concatenate([amax, [448.0, 896.0, 448.0 * 2**-20, 448.0 * 2**-20 * 1.0000001, 0.0]])
+    e = mi.block_exponent(amax)
+    nz = amax > 0
+    assert np.all(amax[nz] <= 448.0 * np.ldexp(1.0, e[nz]))
+    assert np.all(amax[nz] > 448.0 * np.ldexp(1.0, e[nz] - 1))
+    assert e[-1] == -127
+
+
+def test_mx_block_quantize_recipe():
+    g = np.random.Generator(np.random.PCG64(3))
+    x = (g.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    codes, scales = mi.mx_block_quantize(x)
+    e4 = oracle.decode_table(0)
+    dec = e4[codes].reshape(16, 8, 32) * np.ldexp(1.0, scales.astype(np.int64) - 127)[:, :, None]
+    blocks = x.reshape(16, 8, 32).astype(np.float64)
+    # scale bytes near 127 + ceil(log2(0.02*~2.5/448)) and no saturation
+    assert scales.min() >= 110 and scales.max() <= 118
+    assert np.all(np.abs(codes.reshape(16, 8, 32).astype(np.int64) & 0x7F) <= 0x7E)
+    # each block's largest magnitude uses the top binade of e4m3 (>= 256)
+    top = np.abs(e4[codes]).reshape(16, 8, 32).max(axis=2)
+    assert np.all(top >= 224.0)
+    rel = np.abs(dec - blocks) / np.maximum(np.abs(blocks), 1e-30)
+    big = np.abs(blocks) > 2.0**-6 * np.ldexp(1.0, scales.astype(np.int64) - 127)[:, :, None]
+    assert np.all(rel[big] <= 2.0**-4 + 1e-12)
+
+
+def test_sample_points_cover_edges():
+    r, c = mi.sample_points(1000, 700, 500, seed=1, edge=64)
+    pts = set(zip(r.tolist(), c.tolist()))
+    assert (0, 0) in pts and (999, 699) in pts and (999, 0) in pts and (0, 699) in pts
+    assert all((999, j) in pts for j in range(700))
+    assert all((i, 699) in pts for i in range(1000))
+    assert len(pts) == len(r)

@@ -1,0 +1,55 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies oracle/mxref.c, applies one plausible mistake (a dropped
+term, a wrong sign, a wrong index or block size, a transposed operand, a
+wrong bias, a wrong rounding rule), builds the copy with gcc under a
+temporary directory and runs the pins against it: at least one pin must
+fail.  The oracle itself is never modified.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "mxref.c")
+
+MUTANTS = {
+    "scale_block_16": ("j->te[sa[k / 32]]", "j->te[sa[k / 16]]"),
+    "dropped_b_scale": ("double bv = j->tb[b[k]] * j->te[sb[k / 32]];", "double bv = j->tb[b[k]];"),
+    "wrong_sign": ("s += prod;", "s -= prod;"),
+    "transposed_b_row": ("*b = j->B + n * j->K", "*b = j->B + (n % j->M) * j->K"),
+    "a_scale_indexed_by_n": ("*sa = j->As + m * j->KB", "*sa = j->As + (n % j->M) * j->KB"),
+    "e4m3_bias_8": ("(int)e - 7 - 3", "(int)e - 8 - 3"),
+    "e4m3_no_subnormal": ("v = ldexp((double)m, 1 - 7 - 3);", "v = 0.0;"),
+    "e5m2_inf_as_nan": ("v = (m == 0u) ? INFINITY : NAN;", "v = NAN;"),
+    "e8m0_bias_128": ("return ldexp(1.0, (int)s - 127);", "return ldexp(1.0, (int)s - 128);"),
+    "e8m0_255_finite": ("    if (s == 255u)\n        return NAN;\n    return ldexp", "    return ldexp"),
+    "dropped_cin": ("            s += c;\n", "\n"),
+    "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u;"),
+    "last_k_dropped": ("for (int64_t k = 0; k < j->K; ++k)", "for (int64_t k = 0; k + 1 < j->K; ++k)"),
+    "mag_signed": ("mag += fabs(prod);", "mag += prod;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found once"
+    mpath = tmp_path / "mxref_mut.c"
+    mpath.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmxref_mut.so")
+    oracle.build(str(mpath), so)
+    lib = oracle.load(so)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin catches the planted mistake {name}"
