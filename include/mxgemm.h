@@ -1,0 +1,134 @@
+/*
+ * mxgemm.h -- C ABI of the MI355X (gfx950) microscaled FP8 matrix multiply.
+ *
+ * The operation is the scaled dot listed as async_dot_scaled in the TLX API
+ * Quick Reference ("Matrix Multiply (MMA)" table): D = (A*scale_A) @
+ * (B*scale_B) + D with FP8 operands, accumulating in fp32 (TLX async-compute
+ * page, "TMEM-backed MX Scales": fp32 accumulator, uint8 scale tiles of K
+ * extent BLOCK_K // 32).  Written out:
+ *
+ *   C[m,n] (+)= sum_k dec(A[m,k]) * 2^(As[m,k/32]-127) * dec(B[k,n]) * 2^(Bs[n,k/32]-127)
+ *
+ * with the operand formats named "e4m3" / "e5m2" (TLX API Quick Reference,
+ * Utility table, get_fp8_format_name) and the argument order of the
+ * synchronous form, dot_scaled(lhs, lhs_scale, lhs_format, rhs, rhs_scale,
+ * rhs_format, acc, ..., out_dtype=float32) (TLX async-compute page,
+ * "Scaled dot").
+ *
+ * Encodings (the pages give the names only): e4m3 is OCP E4M3 "FN"
+ * (bias 7, no infinities, S.1111.111 = NaN, max 448); e5m2 is OCP E5M2
+ * (bias 15, IEEE inf/NaN, max 57344); a scale byte s is E8M0, 2^(s-127),
+ * with 255 = NaN.
+ *
+ * Memory layout (all dense, no leading-dimension arguments):
+ *   A        M x K codes, row-major (byte A[m*K + k]).
+ *   B        N x K codes, K contiguous ("K-major"): byte B[n*K + k] = B[k,n].
+ *   A_scale  M x (K/32) bytes, row-major.
+ *   B_scale  N x (K/32) bytes, row-major.
+ *   C        M x N, row-major, fp32 or bf16 (bit pattern in uint16).
+ *
+ * Ownership: the caller owns every buffer; all pointers given to
+ * mxgemm_run are device pointers on the handle's device.  The library
+ * allocates no device memory per call and keeps no state between calls
+ * beyond the handle.
+ *
+ * Errors: every entry point returns an MXGEMM_* status.  On an error nothing
+ * is launched and no output is touched.  Nothing throws across this ABI.
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mxgemm_ctx *mxgemm_t;
+
+/* operand formats (format strings "e4m3" / "e5m2") */
+enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
+
+/* output types of C (out_dtype); bf16 is rounded to nearest even from the
+ * fp32 accumulator */
+enum { MXGEMM_OUT_F32 = 0, MXGEMM_OUT_BF16 = 1 };
+
+/* kernel variants (mxgemm_set_variant) */
+enum {
+    MXGEMM_VARIANT_AUTO = 0,    /* large-tile for M > 64, skinny otherwise */
+    MXGEMM_VARIANT_LARGE = 1,   /* 256x256 tiles, MFMA-bound shapes */
+    MXGEMM_VARIANT_SKINNY = 2   /* small M, streams B once at HBM rate */
+};
+
+enum {
+    MXGEMM_OK = 0,
+    MXGEMM_ERR_NULL = 1,    /* a required pointer is NULL */
+    MXGEMM_ERR_FMT = 2,     /* fmtA / fmtB not e4m3 or e5m2 */
+    MXGEMM_ERR_DTYPE = 3,   /* out_dtype not f32/bf16, or use_acc not 0/1 */
+    MXGEMM_ERR_SHAPE = 4,   /* M, N, K out of range or K % 32 != 0 */
+    MXGEMM_ERR_ALIGN = 5,   /* A, B or C not 16-byte aligned */
+    MXGEMM_ERR_DEVICE = 6,  /* not a gfx950 device, or not the handle's device */
+    MXGEMM_ERR_HIP = 7,     /* the HIP runtime reported an error */
+    MXGEMM_ERR_HANDLE = 8,  /* NULL or destroyed handle */
+    MXGEMM_ERR_ALIAS = 9,   /* C overlaps an input buffer */
+    MXGEMM_ERR_VARIANT = 10 /* unknown variant */
+};
+
+/* Limits of one call. */
+#define MXGEMM_MAX_M ((int64_t)1 << 30)
+#define MXGEMM_MAX_N ((int64_t)1 << 20)
+#define MXGEMM_MAX_K ((int64_t)1 << 21)
+
+/* Library ABI version (this header: 1). */
+int mxgemm_version(void);
+
+/* Create a handle bound to the current HIP device.  Fails with
+ * MXGEMM_ERR_DEVICE if that device is not gfx950, MXGEMM_ERR_NULL if out is
+ * NULL, MXGEMM_ERR_HIP if the runtime fails.  The handle owns only host
+ * memory. */
+int mxgemm_create(mxgemm_t *out);
+
+/* Destroy a handle (NULL is accepted and ignored).  Work already launched
+ * with it is unaffected. */
+int mxgemm_destroy(mxgemm_t h);
+
+/* Select the kernel variant used by later mxgemm_run calls on this handle
+ * (MXGEMM_VARIANT_*); results differ between variants only in fp32
+ * summation order.  Forcing MXGEMM_VARIANT_SKINNY makes mxgemm_run return
+ * MXGEMM_ERR_VARIANT for M > 64.  Not synchronised with mxgemm_run calls
+ * running on the same handle in other threads. */
+int mxgemm_set_variant(mxgemm_t h, int variant);
+
+/* Check the arguments of mxgemm_run without touching the GPU: pointers
+ * non-NULL, formats, out_dtype, use_acc in {0,1}, 1 <= M <= MXGEMM_MAX_M,
+ * 1 <= N <= MXGEMM_MAX_N, 32 <= K <= MXGEMM_MAX_K with K % 32 == 0,
+ * A, B, C 16-byte aligned, and C not overlapping A, B or the scales
+ * (byte ranges A[M*K], B[N*K], A_scale[M*K/32], B_scale[N*K/32],
+ * C[M*N*sizeof(out)]).  Scales need no alignment. */
+int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA,
+                         const void *B, const uint8_t *B_scale, int fmtB,
+                         const void *C, int64_t M, int64_t N, int64_t K,
+                         int use_acc, int out_dtype);
+
+/* C (+)= (A * 2^(A_scale-127)) @ (B * 2^(B_scale-127)), asynchronously on
+ * `stream` (0 = the null stream).  With use_acc = 0, C is overwritten and
+ * its previous contents are never read; with use_acc = 1 the previous C
+ * (fp32, or bf16 widened to fp32) is added to the fp32 accumulator before
+ * the single rounding to out_dtype.  Buffers must stay valid until the
+ * stream reaches this point; the caller synchronises.  Thread-safe: a
+ * handle may be used from several host threads on different streams. */
+int mxgemm_run(mxgemm_t h,
+               const void *A, const uint8_t *A_scale, int fmtA,
+               const void *B, const uint8_t *B_scale, int fmtB,
+               void *C, int64_t M, int64_t N, int64_t K,
+               int use_acc, int out_dtype, hipStream_t stream);
+
+/* Static text for a status code ("unknown status" for others). */
+const char *mxgemm_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

@@ -1,0 +1,168 @@
+"""MI355X (gfx950) microscaled FP8 matrix multiply -- Python binding.
+
+Thin ctypes binding of ``libmxgemm.so`` (C ABI in include/mxgemm.h), with
+the same entry-point names.  It only marshals arguments: every step of the
+multiply runs in the library's HIP kernels.  PyTorch supplies device memory
+and streams; it is imported before the library is loaded so that both use
+the one HIP runtime already in the process.
+
+If the library has not been built this module raises on use; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the process's HIP runtime first)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxgemm.so")
+
+MXGEMM_FMT_E4M3 = 0
+MXGEMM_FMT_E5M2 = 1
+MXGEMM_OUT_F32 = 0
+MXGEMM_OUT_BF16 = 1
+MXGEMM_VARIANT_AUTO = 0
+MXGEMM_VARIANT_LARGE = 1
+MXGEMM_VARIANT_SKINNY = 2
+
+STATUS = {0: "MXGEMM_OK", 1: "MXGEMM_ERR_NULL", 2: "MXGEMM_ERR_FMT", 3: "MXGEMM_ERR_DTYPE",
+          4: "MXGEMM_ERR_SHAPE", 5: "MXGEMM_ERR_ALIGN", 6: "MXGEMM_ERR_DEVICE",
+          7: "MXGEMM_ERR_HIP", 8: "MXGEMM_ERR_HANDLE", 9: "MXGEMM_ERR_ALIAS",
+          10: "MXGEMM_ERR_VARIANT"}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
+
+# name -> (restype, argtypes), in the order of include/mxgemm.h
+_vp, _i32, _i64, _u8p = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+SIGNATURES = {
+    "mxgemm_version": (_i32, []),
+    "mxgemm_create": (_i32, [ctypes.POINTER(ctypes.c_void_p)]),
+    "mxgemm_destroy": (_i32, [_vp]),
+    "mxgemm_set_variant": (_i32, [_vp, _i32]),
+    "mxgemm_validate_args": (_i32, [_vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64,
+                                    _i32, _i32]),
+    "mxgemm_run": (_i32, [_vp, _vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64, _i32,
+                          _i32, _vp]),
+    "mxgemm_status_string": (ctypes.c_char_p, [_i32]),
+}
+
+_lib = None
+
+
+class MxgemmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({status_string(code)})")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmxgemm.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().mxgemm_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise MxgemmError(code, where)
+
+
+def mxgemm_version() -> int:
+    return load_library().mxgemm_version()
+
+
+def mxgemm_create() -> int:
+    h = ctypes.c_void_p()
+    _check(load_library().mxgemm_create(ctypes.byref(h)), "mxgemm_create")
+    return h.value
+
+
+def mxgemm_destroy(h: int) -> None:
+    _check(load_library().mxgemm_destroy(h), "mxgemm_destroy")
+
+
+def mxgemm_set_variant(h: int, variant: int) -> None:
+    _check(load_library().mxgemm_set_variant(h, int(variant)), "mxgemm_set_variant")
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def mxgemm_validate_args(A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc,
+                         out_dtype) -> int:
+    """Returns the status code (0 = valid); pure host check."""
+    return load_library().mxgemm_validate_args(
+        _ptr(A), _ptr(A_scale), int(fmtA), _ptr(B), _ptr(B_scale), int(fmtB), _ptr(C),
+        int(M), int(N), int(K), int(use_acc), int(out_dtype))
+
+
+def mxgemm_run(h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc, out_dtype,
+               stream=None) -> None:
+    """C (+)= (A*2^(As-127)) @ (B*2^(Bs-127)) on `stream` (default: torch's
+    current stream).  Tensors are passed by device pointer; shapes and dtypes
+    are the caller's responsibility, as in the C ABI."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(load_library().mxgemm_run(
+        h, _ptr(A), _ptr(A_scale), int(fmtA), _ptr(B), _ptr(B_scale), int(fmtB), _ptr(C),
+        int(M), int(N), int(K), int(use_acc), int(out_dtype), stream), "mxgemm_run")
+
+
+class Gemm:
+    """Owns one handle; call(...) checks tensor shapes and runs."""
+
+    def __init__(self):
+        self.h = mxgemm_create()
+
+    def close(self):
+        if self.h:
+            mxgemm_destroy(self.h)
+            self.h = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_variant(self, variant: int):
+        mxgemm_set_variant(self.h, variant)
+
+    def __call__(self, A, A_scale, fmtA, B, B_scale, fmtB, C, use_acc=False,
+                 out_dtype=MXGEMM_OUT_F32, stream=None):
+        M, K = A.shape
+        N = B.shape[0]
+        if B.shape[1] != K or A_scale.shape != (M, K // 32) or B_scale.shape != (N, K // 32):
+            raise ValueError("operand shapes do not match (A MxK, B NxK, scales K/32)")
+        want = torch.float32 if out_dtype == MXGEMM_OUT_F32 else torch.bfloat16
+        if C.shape != (M, N) or C.dtype != want:
+            raise ValueError(f"C must be ({M}, {N}) {want}")
+        for t in (A, A_scale, B, B_scale, C):
+            if not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError("all operands must be contiguous device tensors")
+        mxgemm_run(self.h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, int(bool(use_acc)),
+                   out_dtype, stream)
+        return C

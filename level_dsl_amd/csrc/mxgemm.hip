@@ -1,0 +1,191 @@
+// mxgemm.hip -- host side of the C ABI declared in include/mxgemm.h.
+//
+// Argument checking, variant selection and the launch on the caller's
+// stream.  Everything the multiply computes runs in the gfx950 kernels
+// (mxgemm_large.h, mxgemm_skinny.h); this file does no arithmetic on the
+// operands.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "mxgemm.h"
+#include "mxgemm_large.h"
+#include "mxgemm_skinny.h"
+
+struct mxgemm_ctx {
+    uint32_t magic;
+    int device;
+    int variant;
+};
+
+namespace {
+
+constexpr uint32_t kMagic = 0x4d584732u;  // "MXG2"
+constexpr uint32_t kDead = 0xdeadbeefu;
+
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+template <int FA, int FB>
+hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
+{
+    const int blocks = a.tiles_m * a.tiles_n;
+    hipLaunchKernelGGL((mxg::large::kernel<FA, FB>), dim3(blocks), dim3(mxg::large::THREADS), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+template <int FA, int FB>
+hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
+{
+    const int blocks = a.tiles_m * a.tiles_n;
+    hipLaunchKernelGGL((mxg::skinny::kernel<FA, FB>), dim3(blocks), dim3(mxg::skinny::THREADS),
+                       0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace
+
+extern "C" {
+
+int mxgemm_version(void) { return 1; }
+
+const char *mxgemm_status_string(int code)
+{
+    switch (code) {
+    case MXGEMM_OK: return "ok";
+    case MXGEMM_ERR_NULL: return "a required pointer is NULL";
+    case MXGEMM_ERR_FMT: return "operand format must be e4m3 (0) or e5m2 (1)";
+    case MXGEMM_ERR_DTYPE: return "out_dtype must be f32 (0) or bf16 (1) and use_acc 0 or 1";
+    case MXGEMM_ERR_SHAPE: return "M, N, K out of range or K not a multiple of 32";
+    case MXGEMM_ERR_ALIGN: return "A, B and C must be 16-byte aligned";
+    case MXGEMM_ERR_DEVICE: return "device is not gfx950 or not the handle's device";
+    case MXGEMM_ERR_HIP: return "HIP runtime error";
+    case MXGEMM_ERR_HANDLE: return "invalid handle";
+    case MXGEMM_ERR_ALIAS: return "C overlaps an input";
+    case MXGEMM_ERR_VARIANT: return "unknown kernel variant";
+    default: return "unknown status";
+    }
+}
+
+int mxgemm_create(mxgemm_t *out)
+{
+    if (!out) return MXGEMM_ERR_NULL;
+    *out = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXGEMM_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MXGEMM_ERR_DEVICE;
+    mxgemm_ctx *h = new (std::nothrow) mxgemm_ctx;
+    if (!h) return MXGEMM_ERR_HIP;
+    h->magic = kMagic;
+    h->device = dev;
+    h->variant = MXGEMM_VARIANT_AUTO;
+    *out = h;
+    return MXGEMM_OK;
+}
+
+int mxgemm_destroy(mxgemm_t h)
+{
+    if (!h) return MXGEMM_OK;
+    if (h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    h->magic = kDead;
+    delete h;
+    return MXGEMM_OK;
+}
+
+int mxgemm_set_variant(mxgemm_t h, int variant)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    if (variant < MXGEMM_VARIANT_AUTO || variant > MXGEMM_VARIANT_SKINNY)
+        return MXGEMM_ERR_VARIANT;
+    h->variant = variant;
+    return MXGEMM_OK;
+}
+
+int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const void *B,
+                         const uint8_t *B_scale, int fmtB, const void *C, int64_t M, int64_t N,
+                         int64_t K, int use_acc, int out_dtype)
+{
+    if (!A || !A_scale || !B || !B_scale || !C) return MXGEMM_ERR_NULL;
+    if ((fmtA != MXGEMM_FMT_E4M3 && fmtA != MXGEMM_FMT_E5M2) ||
+        (fmtB != MXGEMM_FMT_E4M3 && fmtB != MXGEMM_FMT_E5M2))
+        return MXGEMM_ERR_FMT;
+    if ((out_dtype != MXGEMM_OUT_F32 && out_dtype != MXGEMM_OUT_BF16) ||
+        (use_acc != 0 && use_acc != 1))
+        return MXGEMM_ERR_DTYPE;
+    if (M < 1 || N < 1 || K < 32 || M > MXGEMM_MAX_M || N > MXGEMM_MAX_N || K > MXGEMM_MAX_K ||
+        (K % 32) != 0)
+        return MXGEMM_ERR_SHAPE;
+    if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15u) return MXGEMM_ERR_ALIGN;
+    const uint64_t csize = (uint64_t)M * (uint64_t)N * (out_dtype == MXGEMM_OUT_F32 ? 4u : 2u);
+    if (overlaps(C, csize, A, (uint64_t)M * K) || overlaps(C, csize, B, (uint64_t)N * K) ||
+        overlaps(C, csize, A_scale, (uint64_t)M * (K / 32)) ||
+        overlaps(C, csize, B_scale, (uint64_t)N * (K / 32)))
+        return MXGEMM_ERR_ALIAS;
+    return MXGEMM_OK;
+}
+
+int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const void *B,
+               const uint8_t *B_scale, int fmtB, void *C, int64_t M, int64_t N, int64_t K,
+               int use_acc, int out_dtype, hipStream_t stream)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    const int rc = mxgemm_validate_args(A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc,
+                                        out_dtype);
+    if (rc != MXGEMM_OK) return rc;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
+    if (dev != h->device) return MXGEMM_ERR_DEVICE;
+
+    mxg::GemmArgs a;
+    a.A = (const uint8_t *)A;
+    a.As = A_scale;
+    a.B = (const uint8_t *)B;
+    a.Bs = B_scale;
+    a.C = C;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.KB = (int)(K / 32);
+    a.use_acc = use_acc;
+    a.out_bf16 = out_dtype == MXGEMM_OUT_BF16;
+    a.scale_dword = (a.KB % 4 == 0) && ((((uintptr_t)A_scale) | ((uintptr_t)B_scale)) & 3u) == 0;
+    a.c_vec = (N % 4) == 0;
+
+    int variant = h->variant;
+    if (variant == MXGEMM_VARIANT_AUTO)
+        variant = M <= mxg::skinny::MAX_M ? MXGEMM_VARIANT_SKINNY : MXGEMM_VARIANT_LARGE;
+
+    hipError_t e;
+    const int f = fmtA * 2 + fmtB;
+    if (variant == MXGEMM_VARIANT_SKINNY && M > mxg::skinny::MAX_M) return MXGEMM_ERR_VARIANT;
+    if (variant == MXGEMM_VARIANT_SKINNY) {
+        a.tiles_m = 1;
+        a.tiles_n = (int)((N + mxg::skinny::BN - 1) / mxg::skinny::BN);
+        switch (f) {
+        case 0: e = launch_skinny<0, 0>(a, stream); break;
+        case 1: e = launch_skinny<0, 1>(a, stream); break;
+        case 2: e = launch_skinny<1, 0>(a, stream); break;
+        default: e = launch_skinny<1, 1>(a, stream); break;
+        }
+    } else {
+        a.tiles_m = (int)((M + mxg::large::BM - 1) / mxg::large::BM);
+        a.tiles_n = (int)((N + mxg::large::BN - 1) / mxg::large::BN);
+        switch (f) {
+        case 0: e = launch_large<0, 0>(a, stream); break;
+        case 1: e = launch_large<0, 1>(a, stream); break;
+        case 2: e = launch_large<1, 0>(a, stream); break;
+        default: e = launch_large<1, 1>(a, stream); break;
+        }
+    }
+    return e == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
+}
+
+} // extern "C"

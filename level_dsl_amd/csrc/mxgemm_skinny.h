@@ -1,0 +1,172 @@
+// mxgemm_skinny.h -- small-M (M <= 64) MX-FP8 GEMM kernel for gfx950.
+//
+// With M <= 64 the multiply is bound by reading B once from HBM (about 120
+// flop per byte at M = 64, far below the chip's MFMA-to-HBM balance), so
+// the kernel is organised around streaming B:
+//   * one workgroup per 112 columns of C (N = 28672 gives exactly 256
+//     workgroups, one per CU); the four waves split K, wave w taking the
+//     128-byte K stages w, w+4, w+8, ...;
+//   * operands go straight from global memory into registers in the layout
+//     of the 16x16x128 scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): lane
+//     l holds the 32 bytes of K block l/16 of row l%16, and the scale byte of
+//     that block, so no LDS staging is needed; the next stage's loads are in
+//     flight while the current stage's MFMAs run;
+//   * A (at most 64 x K bytes) is re-read by every workgroup and stays in L2;
+//   * at the end the four per-wave partial tiles are summed in a fixed order
+//     through LDS (deterministic), use_acc adds the old C, and C is written
+//     with coalesced 16-byte (fp32) or 8-byte (bf16) buffer stores.
+#pragma once
+
+#include "mxgemm_common.h"
+
+namespace mxg {
+namespace skinny {
+
+constexpr int MAX_M = 64;
+constexpr int BN = 112;
+constexpr int BK = 128;
+constexpr int THREADS = 256;
+constexpr int WAVES = THREADS / 64;
+constexpr int SUB_M = MAX_M / 16, SUB_N = BN / 16;
+
+template <int FX, int FY>
+__device__ __forceinline__ v4f mfma16(v8i x, v8i y, v4f c, uint32_t sx, uint32_t sy)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, 0, (int)sx, 0,
+                                                           (int)sy);
+}
+
+struct Stage {
+    v8i b[SUB_N];
+    v8i a[SUB_M];
+    uint32_t sb[SUB_N];
+    uint32_t sa[SUB_M];
+};
+
+template <int FA, int FB>
+__global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
+{
+    __shared__ __attribute__((aligned(16))) float red[WAVES][MAX_M][BN];
+
+    const int n0 = blockIdx.x * BN;
+    const int rows_b = min(BN, p.N - n0);
+    const int M = p.M, N = p.N, K = p.K, KB = p.KB;
+
+    const rsrc_t rA = make_rsrc(p.A, (uint32_t)M * K);
+    const rsrc_t rB = make_rsrc(p.B + (size_t)n0 * K, (uint32_t)rows_b * K);
+    const rsrc_t rAs = make_rsrc(p.As, (uint32_t)M * KB);
+    const rsrc_t rBs = make_rsrc(p.Bs + (size_t)n0 * KB, (uint32_t)rows_b * KB);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+
+    uint32_t boff[SUB_N], aoff[SUB_M], bsoff[SUB_N], asoff[SUB_M];
+#pragma unroll
+    for (int j = 0; j < SUB_N; ++j) {
+        boff[j] = (uint32_t)(16 * j + r16) * K + kq * 32;
+        bsoff[j] = (uint32_t)(16 * j + r16) * KB + kq;
+    }
+#pragma unroll
+    for (int i = 0; i < SUB_M; ++i) {
+        aoff[i] = (uint32_t)(16 * i + r16) * K + kq * 32;
+        asoff[i] = (uint32_t)(16 * i + r16) * KB + kq;
+    }
+
+    auto load_stage = [&](int kt, Stage &s) {
+        const int k0 = kt * BK;
+        const bool kin = k0 + kq * 32 < K;
+        const int kb0 = kt * (BK / 32);
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) {
+            const uint32_t o = kin ? boff[j] + k0 : kOob;
+            v4i lo = load16(rB, o), hi = load16(rB, kin ? o + 16 : kOob);
+            s.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            s.sb[j] = load1(rBs, kin ? bsoff[j] + kb0 : kOob);
+        }
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i) {
+            const uint32_t o = kin ? aoff[i] + k0 : kOob;
+            v4i lo = load16(rA, o), hi = load16(rA, kin ? o + 16 : kOob);
+            s.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            s.sa[i] = load1(rAs, kin ? asoff[i] + kb0 : kOob);
+        }
+    };
+
+    v4f acc[SUB_M][SUB_N];
+#pragma unroll
+    for (int i = 0; i < SUB_M; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) acc[i][j] = v4f{};
+
+    const int nk = (K + BK - 1) / BK;
+    Stage cur, nxt;
+    if (wave < nk) load_stage(wave, cur);
+    for (int kt = wave; kt < nk; kt += WAVES) {
+        const bool more = kt + WAVES < nk;
+        if (more) load_stage(kt + WAVES, nxt);
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j)
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i)
+                acc[i][j] = mfma16<FB, FA>(cur.b[j], cur.a[i], acc[i][j], cur.sb[j], cur.sa[i]);
+        if (more) cur = nxt;
+    }
+
+    // acc[i][j] register r of lane l: m = 16 i + l % 16, n = 16 j + 4 (l / 16) + r.
+#pragma unroll
+    for (int i = 0; i < SUB_M; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j)
+            *reinterpret_cast<v4f *>(&red[wave][16 * i + r16][16 * j + 4 * kq]) = acc[i][j];
+    __syncthreads();
+
+    const int esz = p.out_bf16 ? 2 : 4;
+    const rsrc_t rC = make_rsrc((uint8_t *)p.C, (uint32_t)M * N * esz);
+    constexpr int Q = MAX_M * BN / 4;  // float4 groups in the tile
+    for (int q = tid; q < Q; q += THREADS) {
+        const int m = q / (BN / 4), nl = (q % (BN / 4)) * 4;
+        if (m >= M) continue;
+        v4f v = *reinterpret_cast<const v4f *>(&red[0][m][nl]);
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const v4f *>(&red[w][m][nl]);
+        const int n = n0 + nl;
+        const uint32_t e0 = (uint32_t)m * N + n;
+        if (p.c_vec) {
+            const uint32_t off = n < N ? e0 * esz : kOob;
+            if (!p.out_bf16) {
+                if (p.use_acc) v += __builtin_bit_cast(v4f, load16(rC, off));
+                store16(rC, off, v);
+            } else {
+                if (p.use_acc) {
+                    v2i old = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rC, off, 0, 0));
+                    v[0] += bf16_to_f32((uint32_t)old[0] & 0xffffu);
+                    v[1] += bf16_to_f32((uint32_t)old[0] >> 16);
+                    v[2] += bf16_to_f32((uint32_t)old[1] & 0xffffu);
+                    v[3] += bf16_to_f32((uint32_t)old[1] >> 16);
+                }
+                v2i o = {(int)(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16)),
+                         (int)(bf16_bits(v[2]) | (bf16_bits(v[3]) << 16))};
+                store8(rC, off, o);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t off = (n + e) < N ? (e0 + e) * esz : kOob;
+                float x = v[e];
+                if (!p.out_bf16) {
+                    if (p.use_acc) x += __builtin_bit_cast(float, load4(rC, off));
+                    store4(rC, off, __builtin_bit_cast(uint32_t, x));
+                } else {
+                    if (p.use_acc)
+                        x += bf16_to_f32(
+                            (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rC, off, 0, 0));
+                    store2(rC, off, (uint16_t)bf16_bits(x));
+                }
+            }
+        }
+    }
+}
+
+} // namespace skinny
+} // namespace mxg

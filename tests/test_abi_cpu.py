@@ -1,0 +1,89 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/mxgemm.h declares, and its host-side argument checks return the
+documented status codes.  No GPU call is made here."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import level_dsl_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mxgemm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert names == sorted(L.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (mxgemm_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings_and_version():
+    assert L.mxgemm_version() == 1
+    for code in range(0, 11):
+        s = L.status_string(code)
+        assert s and s != "unknown status"
+    assert L.status_string(99) == "unknown status"
+
+
+A, AS, B, BS, C = 0x10000, 0x20001, 0x30000, 0x40003, 0x1000000
+
+
+def v(**kw):
+    args = dict(A=A, A_scale=AS, fmtA=0, B=B, B_scale=BS, fmtB=0, C=C, M=64, N=64, K=128,
+                use_acc=0, out_dtype=0)
+    args.update(kw)
+    return L.mxgemm_validate_args(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, "MXGEMM_OK"),
+    ({"A": 0}, "MXGEMM_ERR_NULL"), ({"B_scale": 0}, "MXGEMM_ERR_NULL"), ({"C": 0}, "MXGEMM_ERR_NULL"),
+    ({"fmtA": 2}, "MXGEMM_ERR_FMT"), ({"fmtB": -1}, "MXGEMM_ERR_FMT"),
+    ({"out_dtype": 2}, "MXGEMM_ERR_DTYPE"), ({"use_acc": 2}, "MXGEMM_ERR_DTYPE"),
+    ({"M": 0}, "MXGEMM_ERR_SHAPE"), ({"N": -3}, "MXGEMM_ERR_SHAPE"), ({"K": 0}, "MXGEMM_ERR_SHAPE"),
+    ({"K": 48}, "MXGEMM_ERR_SHAPE"), ({"K": 16}, "MXGEMM_ERR_SHAPE"),
+    ({"N": (1 << 20) + 1}, "MXGEMM_ERR_SHAPE"), ({"K": (1 << 21) + 32}, "MXGEMM_ERR_SHAPE"),
+    ({"A": A + 8}, "MXGEMM_ERR_ALIGN"), ({"C": C + 4}, "MXGEMM_ERR_ALIGN"),
+    ({"B": B + 1}, "MXGEMM_ERR_ALIGN"),
+    ({"C": A + 16}, "MXGEMM_ERR_ALIAS"), ({"C": 0x40000 - 64 * 64 * 4 + 16}, "MXGEMM_ERR_ALIAS"),
+    ({"M": 1, "N": 1, "K": 32}, "MXGEMM_OK"), ({"out_dtype": 1, "use_acc": 1}, "MXGEMM_OK"),
+])
+def test_validate_args(kw, code):
+    assert v(**kw) == L.STATUS_CODE[code]
+
+
+def test_run_rejects_bad_handle_without_gpu_work():
+    lib = L.load_library()
+    assert lib.mxgemm_run(None, A, AS, 0, B, BS, 0, C, 64, 64, 128, 0, 0, None) == \
+        L.STATUS_CODE["MXGEMM_ERR_HANDLE"]
+    assert lib.mxgemm_destroy(None) == 0
+    assert lib.mxgemm_set_variant(None, 0) == L.STATUS_CODE["MXGEMM_ERR_HANDLE"]
+    assert lib.mxgemm_create(None) == L.STATUS_CODE["MXGEMM_ERR_NULL"]
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The binding and the HIP sources never reach the oracle or a CPU path."""
+    pkg = os.path.join(ROOT, "level_dsl_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("no oracle", ""), f
+                assert "mxref" not in text, f

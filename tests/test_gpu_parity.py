@@ -1,0 +1,220 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Exact cases (bitwise): permutation and pairwise-product probes, the
+integer matrix product and the scale-doubling invariant.  Random cases:
+the agreement rule in gpu_helpers (1e-5 * sum|ab|, plus one bf16 ulp for
+bf16 output), on full outputs at sizes the oracle finishes in seconds
+(several tiles plus ragged tails) and on 65,536 sampled outputs plus the
+edge tiles at the five named workload sizes, in the launch configuration
+the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import level_dsl_amd as L
+import mxinputs as mi
+import oracle
+from gpu_helpers import compare, log, oracle_full, oracle_points, run, to_dev, alloc_c, c_numpy
+
+pytestmark = pytest.mark.gpu
+
+LARGE, SKINNY, AUTO = L.MXGEMM_VARIANT_LARGE, L.MXGEMM_VARIANT_SKINNY, L.MXGEMM_VARIANT_AUTO
+
+
+@pytest.fixture(scope="module")
+def gemm():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    g = L.Gemm()
+    yield g
+    g.close()
+
+
+def _variants_for(M):
+    return [LARGE, SKINNY] if M <= 64 else [LARGE]
+
+
+# ------------------------------------------------------------ exact probes --
+
+@pytest.mark.parametrize("variant", [LARGE, SKINNY], ids=["large", "skinny"])
+@pytest.mark.parametrize("which", ["A", "B"])
+def test_permutation_probe_exact(gemm, variant, which):
+    """One 1.0 per row of A (or of B): every output is a single scaled
+    element of the other operand, so the result is exact; a wrong fragment,
+    lane or scale mapping shows up as a wrong source element."""
+    M = 64 if variant == SKINNY else 320
+    N, K = 288, 512
+    g = np.random.Generator(np.random.PCG64(21))
+    p = mi.random_problem(M, N, K, seed=31, fmtA=0, fmtB=1, scale_lo=100, scale_hi=150)
+    if which == "A":
+        pi = np.array([g.integers(0, K) for _ in range(M)])
+        p.A[:] = 0
+        p.A[np.arange(M), pi] = 0x38
+    else:
+        sg = np.array([g.integers(0, K) for _ in range(N)])
+        p.B[:] = 0
+        p.B[np.arange(N), sg] = 0x38
+    log(f"permutation probe {which} variant={variant} M={M} N={N} K={K}")
+    got = run(gemm, p, variant)
+    ref = oracle_full(p)
+    assert np.array_equal(got, ref["ref32"]), f"{np.sum(got != ref['ref32'])} mismatches"
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("sa,sb", [(127, 127), (1, 254), (140, 100)])
+def test_pairwise_products_exact(gemm, fa, fb, sa, sb):
+    """A[m,0] = code m, B[0,n] = code n (finite codes only), all else zero:
+    C[m,n] = dec(m) dec(n) 2^(sa+sb-254) exactly, for every pair."""
+    M = N = 256
+    K = 32
+    tab = {f: oracle.decode_table(f) for f in (0, 1)}
+    A = np.zeros((M, K), np.uint8)
+    B = np.zeros((N, K), np.uint8)
+    ca = np.arange(256, dtype=np.uint8)
+    ca[~np.isfinite(tab[fa])] = 0
+    cb = np.arange(256, dtype=np.uint8)
+    cb[~np.isfinite(tab[fb])] = 0
+    A[:, 0] = ca
+    B[:, 0] = cb
+    p = mi.Problem(M, N, K, fa, fb, A, np.full((M, 1), sa, np.uint8), B,
+                   np.full((N, 1), sb, np.uint8), mi.OUT_F32, False)
+    log(f"pairwise fa={fa} fb={fb} sa={sa} sb={sb}")
+    got = run(gemm, p, LARGE)
+    ref = oracle_full(p)
+    # products that are fp32-normal are exact; record the rest separately
+    r = ref["ref32"]
+    normal = np.abs(r) >= np.float32(2.0**-126)
+    assert np.array_equal(got[normal], r[normal]), f"{np.sum(got[normal] != r[normal])} mismatches"
+    zero = r == 0
+    assert np.all(got[zero] == 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 544), (64, 200, 1024), (1, 5, 32)])
+def test_integer_gemm_bitexact(gemm, M, N, K):
+    """Integer-valued codes with unit scales: every partial sum is an integer
+    below 2^24, so the GPU result is the exact integer product, bit for bit."""
+    g = np.random.Generator(np.random.PCG64(M * 7 + N))
+    ia = g.integers(-16, 17, size=(M, K))
+    ib = g.integers(-8, 9, size=(N, K))
+    A = mi.quantize(ia.astype(np.float32), 0)
+    B = mi.quantize(ib.astype(np.float32), 1)
+    p = mi.Problem(M, N, K, 0, 1, A, np.full((M, K // 32), 127, np.uint8), B,
+                   np.full((N, K // 32), 127, np.uint8), mi.OUT_F32, False)
+    want = (ia @ ib.T).astype(np.float32)
+    for v in _variants_for(M):
+        log(f"integer gemm M={M} N={N} K={K} variant={v}")
+        got = run(gemm, p, v)
+        assert np.array_equal(got, want), f"variant {v}: {np.sum(got != want)} mismatches"
+
+
+@pytest.mark.parametrize("M", [200, 48])
+def test_scale_doubling_bitexact(gemm, M):
+    """Raising every scale byte of A row m by one doubles row m exactly and
+    leaves the other rows bit-identical (same kernel, same order)."""
+    N, K = 136, 640
+    p = mi.random_problem(M, N, K, seed=41)
+    for v in _variants_for(M):
+        log(f"scale doubling M={M} variant={v}")
+        base = run(gemm, p, v)
+        q = mi.Problem(**{**p.__dict__})
+        q.As = p.As.copy()
+        q.As[M // 2, :] += 1
+        q.Bs = p.Bs.copy()
+        q.Bs[N - 1, :] += 1
+        got = run(gemm, q, v)
+        rows = np.ones(M, bool)
+        rows[M // 2] = False
+        cols = np.ones(N, bool)
+        cols[N - 1] = False
+        assert np.array_equal(got[M // 2, :-1], 2 * base[M // 2, :-1])
+        assert np.array_equal(got[:, N - 1][rows], 2 * base[:, N - 1][rows])
+        assert got[M // 2, N - 1] == 4 * base[M // 2, N - 1]
+        assert np.array_equal(got[np.ix_(rows, cols)], base[np.ix_(rows, cols)])
+
+
+# --------------------------------------------------- random, full outputs --
+
+RANDOM_CASES = [
+    # M, N, K, fmtA, fmtB, out, use_acc
+    (256, 256, 256, 0, 0, mi.OUT_F32, False),
+    (517, 389, 1056, 0, 0, mi.OUT_F32, False),   # ragged M/N, N % 4 != 0, K % 128 != 0
+    (300, 512, 640, 1, 0, mi.OUT_BF16, False),
+    (1, 1, 32, 0, 0, mi.OUT_F32, False),
+    (7, 9, 64, 1, 1, mi.OUT_F32, False),
+    (130, 260, 384, 0, 1, mi.OUT_F32, True),
+    (257, 255, 512, 1, 1, mi.OUT_BF16, True),
+    (512, 768, 2048, 0, 0, mi.OUT_BF16, False),
+    (64, 448, 1024, 0, 0, mi.OUT_F32, False),
+    (1, 113, 96, 0, 0, mi.OUT_F32, False),
+    (33, 300, 2048, 1, 0, mi.OUT_BF16, True),
+    (64, 1000, 4128, 0, 0, mi.OUT_F32, False),
+    (17, 1234, 160, 1, 0, mi.OUT_F32, True),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: "x".join(map(str, c[:3])) +
+                         f"_f{c[3]}{c[4]}_o{c[5]}_acc{int(c[6])}")
+def test_random_full(gemm, case):
+    M, N, K, fa, fb, out, acc = case
+    p = mi.random_problem(M, N, K, seed=M * 131 + N * 7 + K, fmtA=fa, fmtB=fb, out_dtype=out,
+                          use_acc=acc)
+    ref = oracle_full(p)
+    for v in _variants_for(M) + [AUTO]:
+        log(f"random full {case} variant={v}")
+        got = run(gemm, p, v, guard=64)
+        compare(got, ref, out, f"{case} variant {v}")
+
+
+def test_deterministic(gemm):
+    p = mi.random_problem(333, 444, 1536, seed=9, out_dtype=mi.OUT_BF16)
+    for v in (LARGE,):
+        log(f"determinism variant={v}")
+        a = run(gemm, p, v)
+        b = run(gemm, p, v)
+        assert np.array_equal(a, b)
+    q = mi.random_problem(40, 700, 1536, seed=10)
+    log("determinism skinny")
+    assert np.array_equal(run(gemm, q, SKINNY), run(gemm, q, SKINNY))
+
+
+# ------------------------------------------------ the five named workloads --
+
+def _workload_check(gemm, wid, full: bool):
+    p = mi.workload(wid)
+    log(f"workload {wid} ({p.name}) generated")
+    dev = to_dev(p)
+    buf, c = alloc_c(p)
+    gemm.set_variant(AUTO)
+    log(f"workload {wid} run")
+    gemm(*dev[:2], p.fmtA, *dev[2:], p.fmtB, c, use_acc=p.use_acc, out_dtype=p.out_dtype)
+    torch.cuda.synchronize()
+    log(f"workload {wid} done on GPU")
+    if full:
+        got = c_numpy(c, p.out_dtype)
+        ref = oracle_full(p)
+        compare(got, ref, p.out_dtype, p.name)
+        return
+    rows, cols = mi.sample_points(p.M, p.N, 65536, seed=wid)
+    ref = oracle_points(p, rows, cols)
+    got = c_numpy(c, p.out_dtype)[rows, cols]
+    compare(got, ref, p.out_dtype, p.name)
+
+
+def test_workload_256cube_full(gemm):
+    _workload_check(gemm, 0, full=True)
+
+
+def test_workload_4096cube_sampled(gemm):
+    _workload_check(gemm, 1, full=False)
+
+
+def test_workload_8192cube_bf16_sampled(gemm):
+    _workload_check(gemm, 2, full=False)
+
+
+def test_workload_skinny_m64_sampled(gemm):
+    _workload_check(gemm, 3, full=False)
+
+
+def test_workload_16384cube_acc_sampled(gemm):
+    _workload_check(gemm, 4, full=False)
