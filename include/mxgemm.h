@@ -54,11 +54,25 @@ enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
  * fp32 accumulator */
 enum { MXGEMM_OUT_F32 = 0, MXGEMM_OUT_BF16 = 1 };
 
-/* kernel variants (mxgemm_set_variant) */
+/* kernel variants (mxgemm_set_variant).
+ *
+ * Exact variants (AUTO, LARGE, SKINNY) decode every code with its block
+ * scale to bf16 (exact for scaled magnitudes inside the bf16 normal range)
+ * and multiply on the bf16 MFMA, whose sums keep fp32 precision: results
+ * agree with the exact sum to |err| <= 1e-5 * sum_k |a_k b_k|.
+ *
+ * Native variants feed the codes and scales to the gfx950 scaled MFMA
+ * (v_mfma_scale_f32_*_f8f6f4) at twice the bf16 rate.  That instruction
+ * sums each aligned group of 8 products in a fixed-point window reaching
+ * 13 bits below the group's largest product and truncates the rest, so its
+ * error is bounded only by about 2^-10 of each group's largest |product|
+ * (measured: up to ~3e-5 * sum|ab| on N(0,1) data). */
 enum {
-    MXGEMM_VARIANT_AUTO = 0,    /* large-tile for M > 64, skinny otherwise */
-    MXGEMM_VARIANT_LARGE = 1,   /* 256x256 tiles, MFMA-bound shapes */
-    MXGEMM_VARIANT_SKINNY = 2   /* small M, streams B once at HBM rate */
+    MXGEMM_VARIANT_AUTO = 0,          /* exact; skinny for M <= 64, else large */
+    MXGEMM_VARIANT_LARGE = 1,         /* exact, 256x256 tiles (MFMA-bound shapes) */
+    MXGEMM_VARIANT_SKINNY = 2,        /* exact, M <= 64, streams B once (HBM-bound) */
+    MXGEMM_VARIANT_LARGE_NATIVE = 3,  /* native scaled-MFMA accumulation, 256x256 tiles */
+    MXGEMM_VARIANT_SKINNY_NATIVE = 4  /* native scaled-MFMA accumulation, M <= 64 */
 };
 
 enum {
@@ -94,8 +108,8 @@ int mxgemm_create(mxgemm_t *out);
 int mxgemm_destroy(mxgemm_t h);
 
 /* Select the kernel variant used by later mxgemm_run calls on this handle
- * (MXGEMM_VARIANT_*); results differ between variants only in fp32
- * summation order.  Forcing MXGEMM_VARIANT_SKINNY makes mxgemm_run return
+ * (MXGEMM_VARIANT_*).  Exact variants differ from each other only in fp32
+ * summation order.  Forcing a skinny variant makes mxgemm_run return
  * MXGEMM_ERR_VARIANT for M > 64.  Not synchronised with mxgemm_run calls
  * running on the same handle in other threads. */
 int mxgemm_set_variant(mxgemm_t h, int variant);

@@ -26,6 +26,8 @@ MXGEMM_OUT_BF16 = 1
 MXGEMM_VARIANT_AUTO = 0
 MXGEMM_VARIANT_LARGE = 1
 MXGEMM_VARIANT_SKINNY = 2
+MXGEMM_VARIANT_LARGE_NATIVE = 3
+MXGEMM_VARIANT_SKINNY_NATIVE = 4
 
 STATUS = {0: "MXGEMM_OK", 1: "MXGEMM_ERR_NULL", 2: "MXGEMM_ERR_FMT", 3: "MXGEMM_ERR_DTYPE",
           4: "MXGEMM_ERR_SHAPE", 5: "MXGEMM_ERR_ALIGN", 6: "MXGEMM_ERR_DEVICE",

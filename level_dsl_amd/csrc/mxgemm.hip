@@ -31,22 +31,41 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
     return x < y + nb && y < x + na;
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool NATIVE>
 hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
 {
     const int blocks = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((mxg::large::kernel<FA, FB>), dim3(blocks), dim3(mxg::large::THREADS), 0,
-                       s, a);
+    hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE>), dim3(blocks),
+                       dim3(mxg::large::THREADS), 0, s, a);
     return hipGetLastError();
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool NATIVE>
 hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
 {
     const int blocks = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((mxg::skinny::kernel<FA, FB>), dim3(blocks), dim3(mxg::skinny::THREADS),
-                       0, s, a);
+    hipLaunchKernelGGL((mxg::skinny::kernel<FA, FB, NATIVE>), dim3(blocks),
+                       dim3(mxg::skinny::THREADS), 0, s, a);
     return hipGetLastError();
+}
+
+template <bool NATIVE>
+hipError_t dispatch(bool skinny, int f, const mxg::GemmArgs &a, hipStream_t s)
+{
+    if (skinny) {
+        switch (f) {
+        case 0: return launch_skinny<0, 0, NATIVE>(a, s);
+        case 1: return launch_skinny<0, 1, NATIVE>(a, s);
+        case 2: return launch_skinny<1, 0, NATIVE>(a, s);
+        default: return launch_skinny<1, 1, NATIVE>(a, s);
+        }
+    }
+    switch (f) {
+    case 0: return launch_large<0, 0, NATIVE>(a, s);
+    case 1: return launch_large<0, 1, NATIVE>(a, s);
+    case 2: return launch_large<1, 0, NATIVE>(a, s);
+    default: return launch_large<1, 1, NATIVE>(a, s);
+    }
 }
 
 } // namespace
@@ -103,7 +122,7 @@ int mxgemm_destroy(mxgemm_t h)
 int mxgemm_set_variant(mxgemm_t h, int variant)
 {
     if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
-    if (variant < MXGEMM_VARIANT_AUTO || variant > MXGEMM_VARIANT_SKINNY)
+    if (variant < MXGEMM_VARIANT_AUTO || variant > MXGEMM_VARIANT_SKINNY_NATIVE)
         return MXGEMM_ERR_VARIANT;
     h->variant = variant;
     return MXGEMM_OK;
@@ -160,31 +179,24 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     a.c_vec = (N % 4) == 0;
 
     int variant = h->variant;
+    const bool native = variant == MXGEMM_VARIANT_LARGE_NATIVE ||
+                        variant == MXGEMM_VARIANT_SKINNY_NATIVE;
+    bool skinny;
     if (variant == MXGEMM_VARIANT_AUTO)
-        variant = M <= mxg::skinny::MAX_M ? MXGEMM_VARIANT_SKINNY : MXGEMM_VARIANT_LARGE;
-
-    hipError_t e;
-    const int f = fmtA * 2 + fmtB;
-    if (variant == MXGEMM_VARIANT_SKINNY && M > mxg::skinny::MAX_M) return MXGEMM_ERR_VARIANT;
-    if (variant == MXGEMM_VARIANT_SKINNY) {
+        skinny = M <= mxg::skinny::MAX_M;
+    else
+        skinny = variant == MXGEMM_VARIANT_SKINNY || variant == MXGEMM_VARIANT_SKINNY_NATIVE;
+    if (skinny && M > mxg::skinny::MAX_M) return MXGEMM_ERR_VARIANT;
+    if (skinny) {
         a.tiles_m = 1;
         a.tiles_n = (int)((N + mxg::skinny::BN - 1) / mxg::skinny::BN);
-        switch (f) {
-        case 0: e = launch_skinny<0, 0>(a, stream); break;
-        case 1: e = launch_skinny<0, 1>(a, stream); break;
-        case 2: e = launch_skinny<1, 0>(a, stream); break;
-        default: e = launch_skinny<1, 1>(a, stream); break;
-        }
     } else {
         a.tiles_m = (int)((M + mxg::large::BM - 1) / mxg::large::BM);
         a.tiles_n = (int)((N + mxg::large::BN - 1) / mxg::large::BN);
-        switch (f) {
-        case 0: e = launch_large<0, 0>(a, stream); break;
-        case 1: e = launch_large<0, 1>(a, stream); break;
-        case 2: e = launch_large<1, 0>(a, stream); break;
-        default: e = launch_large<1, 1>(a, stream); break;
-        }
     }
+    const int f = fmtA * 2 + fmtB;
+    const hipError_t e = native ? dispatch<true>(skinny, f, a, stream)
+                                : dispatch<false>(skinny, f, a, stream);
     return e == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
 }
 

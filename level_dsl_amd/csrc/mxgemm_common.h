@@ -19,6 +19,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // Word 3 of a gfx9-family raw buffer descriptor (32-bit data format, no
 // swizzle, no stride).
@@ -83,14 +85,67 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
 }
 
 // One 32x32x64 scaled MFMA: D = (X * 2^(sx-127)) @ (Y * 2^(sy-127)) + C where
-// X supplies the 32 output rows and Y the 32 output columns; each lane holds
-// 32 consecutive K bytes of one row of X (lane % 32) in K half (lane / 32),
-// and byte 0 of sx / sy is the scale of that row's 32-element K block.
-template <int FX, int FY>
+// X supplies the 32 output rows and Y the 32 output columns.  Operand layout
+// of gfx950 (measured on the device with one-hot inputs): lane l holds row
+// l % 32; with h = l / 32, its register bytes 0..15 carry K 16h..16h+15 and
+// bytes 16..31 carry K 32+16h..32+16h+15; lane half h supplies the scale of
+// the row's K block h (K 32h..32h+31), taken from byte OP of sx / sy.
+// Accumulator register r of lane l is D[8 (r/4) + 4 (l/32) + r%4][l % 32].
+template <int FX, int FY, int OP>
 __device__ __forceinline__ v16f mfma_scaled(v8i x, v8i y, v16f c, uint32_t sx, uint32_t sy)
 {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, 0, (int)sx, 0,
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, OP, (int)sx, OP,
                                                            (int)sy);
+}
+
+// e8m0 scale byte s -> the fp32 value 2^(s-127): byte 0 is the fp32
+// subnormal 2^-127, byte 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s)
+{
+    const uint32_t bits = s == 0u ? 0x00400000u : (s == 255u ? 0x7fc00000u : s << 23);
+    return __builtin_bit_cast(float, bits);
+}
+
+// Two fp8 codes (bytes 2*hi, 2*hi+1 of w) -> two bf16 equal to the codes' values
+// times `scale`, rounded to nearest even (v_cvt_scalef32_pk_bf16_fp8 / _bf8).
+// For every code and every power-of-two scale 2^-127..2^127 this was checked
+// on the device to equal round-to-nearest-even of the exact product; it is
+// exact whenever that product is a bf16 number.
+template <int F, bool HI>
+__device__ __forceinline__ v2bf cvt2(uint32_t w, float scale)
+{
+    if constexpr (F == 0)
+        return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
+    else
+        return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, HI);
+}
+
+// 16 fp8 codes (one 16-byte chunk, byte order) scaled -> 16 bf16 as two
+// 8-element MFMA operands (bytes 0..7 and 8..15).
+template <int F>
+__device__ __forceinline__ void decode16(v4i x, float scale, v8bf &lo, v8bf &hi)
+{
+    const v2bf a0 = cvt2<F, false>((uint32_t)x[0], scale), a1 = cvt2<F, true>((uint32_t)x[0], scale);
+    const v2bf b0 = cvt2<F, false>((uint32_t)x[1], scale), b1 = cvt2<F, true>((uint32_t)x[1], scale);
+    const v2bf c0 = cvt2<F, false>((uint32_t)x[2], scale), c1 = cvt2<F, true>((uint32_t)x[2], scale);
+    const v2bf d0 = cvt2<F, false>((uint32_t)x[3], scale), d1 = cvt2<F, true>((uint32_t)x[3], scale);
+    lo = v8bf{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+    hi = v8bf{c0[0], c0[1], c1[0], c1[1], d0[0], d0[1], d1[0], d1[1]};
+}
+
+// bf16 MFMAs: products of bf16 operands are exact and, as measured on the
+// device, summed without the narrow per-group alignment of the fp8 MFMAs, so
+// an fp8 x fp8 x 2^s x 2^t product sum decoded to bf16 is accumulated at fp32
+// precision.  32x32x16: accumulator layout as in mfma_scaled; 16x16x32:
+// register r of lane l is D[4 (l/16) + r][l % 16].
+__device__ __forceinline__ v16f mfma_bf16_32(v8bf x, v8bf y, v16f c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma_bf16_16(v8bf x, v8bf y, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
 }
 
 } // namespace mxg

@@ -8,9 +8,9 @@
 //   * global -> registers: raw 16-byte buffer loads of the next A and B
 //     tiles (256 rows x 128 bytes each) plus, straight into registers, the
 //     scale dwords each lane needs for the next stage;
-//   * LDS -> registers: ds_read_b128 of the current stage's fragments, in
-//     the scaled-MFMA operand layout (32 consecutive K bytes of one row per
-//     lane);
+//   * LDS -> registers: two ds_read_b128 per operand fragment, in the
+//     scaled-MFMA operand layout (lane half h of row r takes 16-byte chunks
+//     h and h+2 of each 64-byte K step);
 //   * 32 scaled MFMAs per wave per stage, issued K-major, then N, then M,
 //     so that consecutive MFMAs update independent accumulators (the issue
 //     order of amd_scheduled_mfma on the TLX async-compute page, "Explicit
@@ -77,7 +77,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = w / gs;
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool NATIVE>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE_BYTES];  // [stage][A/B]
@@ -130,9 +130,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     };
 
     // ---- scales: one dword (4 blocks = one stage) per lane per subtile ---
-    // lane (row lrow, K half khalf) needs block 2*kk + khalf of the stage for
-    // MFMA k-step kk; lanes of the upper half shift their dword by one byte so
-    // that byte 0 (kk = 0) and byte 2 (kk = 1) are theirs.
+    // lane half khalf of a row supplies block 2*kk + khalf of the stage to
+    // MFMA k-step kk; lanes of the upper half shift their dword down one byte
+    // so that the instruction's byte select is 0 for kk = 0 and 2 for kk = 1.
     uint32_t sa[SUB_M], sb[SUB_N];
     auto sload = [&](int k0) {
         const int kb0 = k0 >> 5;
@@ -187,9 +187,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         const int st = kt & 1;
         uint32_t csa[SUB_M], csb[SUB_N];
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) csa[i] = khalf ? sa[i] >> 8 : sa[i];
+        for (int i = 0; i < SUB_M; ++i) csa[i] = (NATIVE && khalf) ? sa[i] >> 8 : sa[i];
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) csb[j] = khalf ? sb[j] >> 8 : sb[j];
+        for (int j = 0; j < SUB_N; ++j) csb[j] = (NATIVE && khalf) ? sb[j] >> 8 : sb[j];
 
         const bool more = kt + 1 < nk;
         if (more) {
@@ -197,30 +197,60 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             sload((kt + 1) * BK);
         }
 
+        if constexpr (NATIVE) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c0 = kk * 4 + khalf * 2;
-            const uint32_t o0 = ((c0 ^ sw) << 4), o1 = (((c0 + 1) ^ sw) << 4);
-            v8i fa[SUB_M], fb[SUB_N];
+            for (int kk = 0; kk < 2; ++kk) {
+                const int c0 = kk * 4 + khalf;  // K 64kk+16h .. +15; chunk c0 + 2: K +32
+                const uint32_t o0 = ((c0 ^ sw) << 4), o1 = (((c0 + 2) ^ sw) << 4);
+                v8i fa[SUB_M], fb[SUB_N];
 #pragma unroll
-            for (int i = 0; i < SUB_M; ++i) {
-                v4i lo = *reinterpret_cast<const v4i *>(&lds[st][0][fa_off[i] + o0]);
-                v4i hi = *reinterpret_cast<const v4i *>(&lds[st][0][fa_off[i] + o1]);
-                fa[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                for (int i = 0; i < SUB_M; ++i) {
+                    v4i lo = *reinterpret_cast<const v4i *>(&lds[st][0][fa_off[i] + o0]);
+                    v4i hi = *reinterpret_cast<const v4i *>(&lds[st][0][fa_off[i] + o1]);
+                    fa[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+#pragma unroll
+                for (int j = 0; j < SUB_N; ++j) {
+                    v4i lo = *reinterpret_cast<const v4i *>(&lds[st][1][fb_off[j] + o0]);
+                    v4i hi = *reinterpret_cast<const v4i *>(&lds[st][1][fb_off[j] + o1]);
+                    fb[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+#pragma unroll
+                for (int j = 0; j < SUB_N; ++j)
+#pragma unroll
+                    for (int i = 0; i < SUB_M; ++i) {
+                        if (kk == 0)
+                            acc[i][j] = mfma_scaled<FB, FA, 0>(fb[j], fa[i], acc[i][j], csb[j], csa[i]);
+                        else
+                            acc[i][j] = mfma_scaled<FB, FA, 2>(fb[j], fa[i], acc[i][j], csb[j], csa[i]);
+                    }
             }
+        } else {
+            // Exact path: K block p (32 bytes) of the stage; lane half h takes
+            // its 16-byte chunk 2p + h, decodes it with the row's block-p scale
+            // into 16 bf16 and feeds two 32x32x16 bf16 MFMAs.
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) {
-                v4i lo = *reinterpret_cast<const v4i *>(&lds[st][1][fb_off[j] + o0]);
-                v4i hi = *reinterpret_cast<const v4i *>(&lds[st][1][fb_off[j] + o1]);
-                fb[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            for (int pb = 0; pb < BK / 32; ++pb) {
+                const uint32_t o = (((2 * pb + khalf) ^ sw) << 4);
+                v8bf fa[SUB_M][2], fb[SUB_N][2];
+#pragma unroll
+                for (int i = 0; i < SUB_M; ++i) {
+                    const v4i x = *reinterpret_cast<const v4i *>(&lds[st][0][fa_off[i] + o]);
+                    decode16<FA>(x, e8m0_to_f32((csa[i] >> (8 * pb)) & 0xffu), fa[i][0], fa[i][1]);
+                }
+#pragma unroll
+                for (int j = 0; j < SUB_N; ++j) {
+                    const v4i x = *reinterpret_cast<const v4i *>(&lds[st][1][fb_off[j] + o]);
+                    decode16<FB>(x, e8m0_to_f32((csb[j] >> (8 * pb)) & 0xffu), fb[j][0], fb[j][1]);
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int j = 0; j < SUB_N; ++j)
+#pragma unroll
+                        for (int i = 0; i < SUB_M; ++i)
+                            acc[i][j] = mfma_bf16_32(fb[j][hh], fa[i][hh], acc[i][j]);
             }
-            const int sh = 16 * kk;
-#pragma unroll
-            for (int j = 0; j < SUB_N; ++j)
-#pragma unroll
-                for (int i = 0; i < SUB_M; ++i)
-                    acc[i][j] = mfma_scaled<FB, FA>(fb[j], fa[i], acc[i][j], csb[j] >> sh,
-                                                    csa[i] >> sh);
         }
 
         if (more) lstore(st ^ 1);

@@ -6,11 +6,15 @@
 //   * one workgroup per 112 columns of C (N = 28672 gives exactly 256
 //     workgroups, one per CU); the four waves split K, wave w taking the
 //     128-byte K stages w, w+4, w+8, ...;
-//   * operands go straight from global memory into registers in the layout
-//     of the 16x16x128 scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): lane
-//     l holds the 32 bytes of K block l/16 of row l%16, and the scale byte of
-//     that block, so no LDS staging is needed; the next stage's loads are in
-//     flight while the current stage's MFMAs run;
+//   * operands go straight from global memory into registers, so no LDS
+//     staging is needed, and the next stage's loads are in flight while the
+//     current stage's MFMAs run.  Lane l works on row l % 16 and K block
+//     g = l / 16 of each 128-byte stage.  Exact mode (default): the lane
+//     loads its row's whole block g, decodes it with the block's scale into
+//     32 bf16 and feeds four 16x16x32 bf16 MFMAs.  Native mode: the lane
+//     loads K 16g..16g+15 and 64+16g..64+16g+15 (the operand layout of
+//     v_mfma_scale_f32_16x16x128_f8f6f4, as measured on the device) and
+//     supplies the scale of block g to that instruction;
 //   * A (at most 64 x K bytes) is re-read by every workgroup and stays in L2;
 //   * at the end the four per-wave partial tiles are summed in a fixed order
 //     through LDS (deterministic), use_acc adds the old C, and C is written
@@ -43,7 +47,7 @@ struct Stage {
     uint32_t sa[SUB_M];
 };
 
-template <int FA, int FB>
+template <int FA, int FB, bool NATIVE>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
     __shared__ __attribute__((aligned(16))) float red[WAVES][MAX_M][BN];
@@ -62,34 +66,38 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int r16 = lane & 15, kq = lane >> 4;
 
     uint32_t boff[SUB_N], aoff[SUB_M], bsoff[SUB_N], asoff[SUB_M];
+    // Native: chunks K 16g.. and 64+16g.. of the stage.  Exact: the lane's
+    // whole 32-byte block g of the stage (chunks 32g.. and 32g+16..).
+    constexpr int LO = NATIVE ? 16 : 32, HI = NATIVE ? 64 : 16;
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) {
-        boff[j] = (uint32_t)(16 * j + r16) * K + kq * 32;
+        boff[j] = (uint32_t)(16 * j + r16) * K + kq * LO;
         bsoff[j] = (uint32_t)(16 * j + r16) * KB + kq;
     }
 #pragma unroll
     for (int i = 0; i < SUB_M; ++i) {
-        aoff[i] = (uint32_t)(16 * i + r16) * K + kq * 32;
+        aoff[i] = (uint32_t)(16 * i + r16) * K + kq * LO;
         asoff[i] = (uint32_t)(16 * i + r16) * KB + kq;
     }
 
     auto load_stage = [&](int kt, Stage &s) {
         const int k0 = kt * BK;
-        const bool kin = k0 + kq * 32 < K;
+        const bool lo_in = k0 + kq * LO < K, hi_in = k0 + kq * LO + HI < K;
+        const bool s_in = k0 + kq * 32 < K;  // this lane's scale block
         const int kb0 = kt * (BK / 32);
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) {
-            const uint32_t o = kin ? boff[j] + k0 : kOob;
-            v4i lo = load16(rB, o), hi = load16(rB, kin ? o + 16 : kOob);
+            v4i lo = load16(rB, lo_in ? boff[j] + k0 : kOob);
+            v4i hi = load16(rB, hi_in ? boff[j] + k0 + HI : kOob);
             s.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            s.sb[j] = load1(rBs, kin ? bsoff[j] + kb0 : kOob);
+            s.sb[j] = load1(rBs, s_in ? bsoff[j] + kb0 : kOob);
         }
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) {
-            const uint32_t o = kin ? aoff[i] + k0 : kOob;
-            v4i lo = load16(rA, o), hi = load16(rA, kin ? o + 16 : kOob);
+            v4i lo = load16(rA, lo_in ? aoff[i] + k0 : kOob);
+            v4i hi = load16(rA, hi_in ? aoff[i] + k0 + HI : kOob);
             s.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            s.sa[i] = load1(rAs, kin ? asoff[i] + kb0 : kOob);
+            s.sa[i] = load1(rAs, s_in ? asoff[i] + kb0 : kOob);
         }
     };
 
@@ -105,11 +113,36 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     for (int kt = wave; kt < nk; kt += WAVES) {
         const bool more = kt + WAVES < nk;
         if (more) load_stage(kt + WAVES, nxt);
+        if constexpr (NATIVE) {
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j)
+            for (int j = 0; j < SUB_N; ++j)
 #pragma unroll
-            for (int i = 0; i < SUB_M; ++i)
-                acc[i][j] = mfma16<FB, FA>(cur.b[j], cur.a[i], acc[i][j], cur.sb[j], cur.sa[i]);
+                for (int i = 0; i < SUB_M; ++i)
+                    acc[i][j] = mfma16<FB, FA>(cur.b[j], cur.a[i], acc[i][j], cur.sb[j], cur.sa[i]);
+        } else {
+            // decode each lane's 32 codes with its block scale into 4 x 8 bf16,
+            // then four 16x16x32 bf16 MFMAs per (i, j)
+            v8bf fa[SUB_M][4], fb[SUB_N][4];
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i) {
+                const float sc = e8m0_to_f32(cur.sa[i]);
+                decode16<FA>(v4i{cur.a[i][0], cur.a[i][1], cur.a[i][2], cur.a[i][3]}, sc, fa[i][0], fa[i][1]);
+                decode16<FA>(v4i{cur.a[i][4], cur.a[i][5], cur.a[i][6], cur.a[i][7]}, sc, fa[i][2], fa[i][3]);
+            }
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) {
+                const float sc = e8m0_to_f32(cur.sb[j]);
+                decode16<FB>(v4i{cur.b[j][0], cur.b[j][1], cur.b[j][2], cur.b[j][3]}, sc, fb[j][0], fb[j][1]);
+                decode16<FB>(v4i{cur.b[j][4], cur.b[j][5], cur.b[j][6], cur.b[j][7]}, sc, fb[j][2], fb[j][3]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < SUB_N; ++j)
+#pragma unroll
+                    for (int i = 0; i < SUB_M; ++i)
+                        acc[i][j] = mfma_bf16_16(fb[j][q], fa[i][q], acc[i][j]);
+        }
         if (more) cur = nxt;
     }
 

@@ -41,8 +41,8 @@ def alloc_c(p: mi.Problem, guard: int = 0):
     buf = torch.empty(total, dtype=dt, device="cuda:0")
     buf.fill_(float("nan"))
     if guard:
-        buf[:guard] = 1234.5
-        buf[-guard:] = -4321.5
+        buf[:guard] = 1.5
+        buf[-guard:] = -2.25
     c = buf[guard:guard + p.M * p.N].view(p.M, p.N)
     if p.use_acc:
         if p.out_dtype == mi.OUT_F32:
@@ -62,7 +62,7 @@ def run(gemm, p: mi.Problem, variant=None, guard: int = 0, dev_inputs=None):
     if guard:
         g0 = buf[:guard].float().cpu().numpy()
         g1 = buf[-guard:].float().cpu().numpy()
-        assert np.all(g0 == 1234.5) and np.all(g1 == -4321.5), "store outside C"
+        assert np.all(g0 == 1.5) and np.all(g1 == -2.25), "store outside C"
     return c_numpy(c, p.out_dtype)
 
 

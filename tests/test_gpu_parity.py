@@ -20,6 +20,10 @@ from gpu_helpers import compare, log, oracle_full, oracle_points, run, to_dev, a
 pytestmark = pytest.mark.gpu
 
 LARGE, SKINNY, AUTO = L.MXGEMM_VARIANT_LARGE, L.MXGEMM_VARIANT_SKINNY, L.MXGEMM_VARIANT_AUTO
+LARGE_NATIVE, SKINNY_NATIVE = L.MXGEMM_VARIANT_LARGE_NATIVE, L.MXGEMM_VARIANT_SKINNY_NATIVE
+ALL_VARIANTS = [LARGE, SKINNY, LARGE_NATIVE, SKINNY_NATIVE]
+VNAME = {AUTO: "auto", LARGE: "large", SKINNY: "skinny", LARGE_NATIVE: "large_native",
+         SKINNY_NATIVE: "skinny_native"}
 
 
 @pytest.fixture(scope="module")
@@ -30,19 +34,26 @@ def gemm():
     g.close()
 
 
-def _variants_for(M):
-    return [LARGE, SKINNY] if M <= 64 else [LARGE]
+def _variants_for(M, native=False):
+    v = [LARGE, SKINNY] if M <= 64 else [LARGE]
+    if native:
+        v += [LARGE_NATIVE, SKINNY_NATIVE] if M <= 64 else [LARGE_NATIVE]
+    return v
+
+
+def _is_skinny(v):
+    return v in (SKINNY, SKINNY_NATIVE)
 
 
 # ------------------------------------------------------------ exact probes --
 
-@pytest.mark.parametrize("variant", [LARGE, SKINNY], ids=["large", "skinny"])
+@pytest.mark.parametrize("variant", ALL_VARIANTS, ids=lambda v: VNAME[v])
 @pytest.mark.parametrize("which", ["A", "B"])
 def test_permutation_probe_exact(gemm, variant, which):
     """One 1.0 per row of A (or of B): every output is a single scaled
     element of the other operand, so the result is exact; a wrong fragment,
     lane or scale mapping shows up as a wrong source element."""
-    M = 64 if variant == SKINNY else 320
+    M = 64 if _is_skinny(variant) else 320
     N, K = 288, 512
     g = np.random.Generator(np.random.PCG64(21))
     p = mi.random_problem(M, N, K, seed=31, fmtA=0, fmtB=1, scale_lo=100, scale_hi=150)
@@ -60,11 +71,19 @@ def test_permutation_probe_exact(gemm, variant, which):
     assert np.array_equal(got, ref["ref32"]), f"{np.sum(got != ref['ref32'])} mismatches"
 
 
+@pytest.mark.parametrize("variant", [LARGE, LARGE_NATIVE], ids=lambda v: VNAME[v])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (0, 1), (1, 0), (1, 1)])
-@pytest.mark.parametrize("sa,sb", [(127, 127), (1, 254), (140, 100)])
-def test_pairwise_products_exact(gemm, fa, fb, sa, sb):
+@pytest.mark.parametrize("sa,sb", [(127, 127), (10, 239), (140, 100), (1, 254)])
+def test_pairwise_products_exact(gemm, variant, fa, fb, sa, sb):
     """A[m,0] = code m, B[0,n] = code n (finite codes only), all else zero:
-    C[m,n] = dec(m) dec(n) 2^(sa+sb-254) exactly, for every pair."""
+    C[m,n] = dec(m) dec(n) 2^(sa+sb-254) exactly, for every pair.  The exact
+    variants decode to bf16 with the scale applied, which is exact for scale
+    bytes 3..246 (e4m3) and 10..239 (e5m2); outside that range (1, 254) only
+    the native variant is graded."""
+    rng_ = {0: (3, 246), 1: (10, 239)}
+    in_range = rng_[fa][0] <= sa <= rng_[fa][1] and rng_[fb][0] <= sb <= rng_[fb][1]
+    if variant == LARGE and not in_range:
+        pytest.skip("scale byte outside the exact variants' bf16 range")
     M = N = 256
     K = 32
     tab = {f: oracle.decode_table(f) for f in (0, 1)}
@@ -78,8 +97,8 @@ def test_pairwise_products_exact(gemm, fa, fb, sa, sb):
     B[:, 0] = cb
     p = mi.Problem(M, N, K, fa, fb, A, np.full((M, 1), sa, np.uint8), B,
                    np.full((N, 1), sb, np.uint8), mi.OUT_F32, False)
-    log(f"pairwise fa={fa} fb={fb} sa={sa} sb={sb}")
-    got = run(gemm, p, LARGE)
+    log(f"pairwise fa={fa} fb={fb} sa={sa} sb={sb} variant={VNAME[variant]}")
+    got = run(gemm, p, variant)
     ref = oracle_full(p)
     # products that are fp32-normal are exact; record the rest separately
     r = ref["ref32"]
@@ -101,7 +120,7 @@ def test_integer_gemm_bitexact(gemm, M, N, K):
     p = mi.Problem(M, N, K, 0, 1, A, np.full((M, K // 32), 127, np.uint8), B,
                    np.full((N, K // 32), 127, np.uint8), mi.OUT_F32, False)
     want = (ia @ ib.T).astype(np.float32)
-    for v in _variants_for(M):
+    for v in _variants_for(M, native=True):
         log(f"integer gemm M={M} N={N} K={K} variant={v}")
         got = run(gemm, p, v)
         assert np.array_equal(got, want), f"variant {v}: {np.sum(got != want)} mismatches"
@@ -113,7 +132,7 @@ def test_scale_doubling_bitexact(gemm, M):
     leaves the other rows bit-identical (same kernel, same order)."""
     N, K = 136, 640
     p = mi.random_problem(M, N, K, seed=41)
-    for v in _variants_for(M):
+    for v in _variants_for(M, native=True):
         log(f"scale doubling M={M} variant={v}")
         base = run(gemm, p, v)
         q = mi.Problem(**{**p.__dict__})
@@ -167,14 +186,54 @@ def test_random_full(gemm, case):
 
 def test_deterministic(gemm):
     p = mi.random_problem(333, 444, 1536, seed=9, out_dtype=mi.OUT_BF16)
-    for v in (LARGE,):
+    for v in (LARGE, LARGE_NATIVE):
         log(f"determinism variant={v}")
         a = run(gemm, p, v)
         b = run(gemm, p, v)
         assert np.array_equal(a, b)
     q = mi.random_problem(40, 700, 1536, seed=10)
-    log("determinism skinny")
-    assert np.array_equal(run(gemm, q, SKINNY), run(gemm, q, SKINNY))
+    for v in (SKINNY, SKINNY_NATIVE):
+        log(f"determinism {VNAME[v]}")
+        assert np.array_equal(run(gemm, q, v), run(gemm, q, v))
+
+
+NATIVE_CASES = [(256, 256, 256, 0, 0, mi.OUT_F32, False), (517, 389, 1056, 1, 0, mi.OUT_F32, True),
+                (64, 448, 1024, 0, 1, mi.OUT_BF16, False), (33, 300, 2048, 1, 1, mi.OUT_F32, True)]
+
+
+@pytest.mark.parametrize("case", NATIVE_CASES, ids=lambda c: "x".join(map(str, c[:3])))
+def test_native_within_group_window_bound(gemm, case):
+    """The native variants sum each aligned group of 8 products in a window
+    reaching 13 bits below the group's largest product (measured on the
+    device).  Bound checked here: |err| <= 1e-5 * sum|ab| + 8 * sum_g
+    2^(E_g - 13), E_g = floor(log2 max_{k in g} |a_k b_k|)."""
+    M, N, K, fa, fb, out, acc = case
+    p = mi.random_problem(M, N, K, seed=M + N + K, fmtA=fa, fmtB=fb, out_dtype=out, use_acc=acc)
+    ref = oracle_full(p)
+    ta, tb, te = oracle.decode_table(fa), oracle.decode_table(fb), oracle.decode_table(2)
+    a = ta[p.A] * np.repeat(te[p.As], 32, axis=1)[:, :K]
+    b = tb[p.B] * np.repeat(te[p.Bs], 32, axis=1)[:, :K]
+    gmax = np.zeros((M, N))
+    for g0 in range(0, K, 8):
+        prod = np.abs(a[:, None, g0:g0 + 8] * b[None, :, g0:g0 + 8]).max(axis=2)
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(prod))
+        gmax += np.where(prod > 0, np.ldexp(1.0, np.where(prod > 0, e, 0).astype(np.int64) - 13), 0)
+    ref = dict(ref)
+    extra = 8 * gmax
+    for v in ([LARGE_NATIVE, SKINNY_NATIVE] if M <= 64 else [LARGE_NATIVE]):
+        log(f"native bound {case} variant={VNAME[v]}")
+        got = run(gemm, p, v)
+        if out == mi.OUT_F32:
+            g = got.astype(np.float64)
+            r = ref["ref32"].astype(np.float64)
+            tol = 1e-5 * ref["mag"] + extra
+        else:
+            from gpu_helpers import bf16_to_f32, bf16_ulp
+            g = bf16_to_f32(got).astype(np.float64)
+            r = bf16_to_f32(ref["refbf16"]).astype(np.float64)
+            tol = 1e-5 * ref["mag"] + extra + np.maximum(bf16_ulp(r), bf16_ulp(g))
+        assert np.all(np.abs(g - r) <= tol), f"{np.sum(np.abs(g - r) > tol)} outside the bound"
 
 
 # ------------------------------------------------ the five named workloads --
