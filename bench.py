@@ -1,0 +1,238 @@
+"""Benchmark of the MX-FP8 GEMM on one MI355X.
+
+One step = one mxgemm_run over the 8192 x 8192 x 8192 workload (e4m3 A and
+B with e8m0 scales, bf16 output), the whole hot path.  The JSON line's
+`value` is TFLOP/s (2*M*N*K per step) over exactly `--steps` timed steps,
+bracketed by a device synchronisation on both sides, with all inputs
+already resident in HBM.  Inputs rotate over several device copies so that
+no step finds the previous step's operands in L2 or in the 256 MiB
+Infinity Cache.
+
+Also reported on the same line:
+  * skinny: the M=64, N=28672, K=8192 workload in GB/s of algorithmic bytes
+    (A, scales and B read once, C written once), B rotated over 3 copies;
+  * native: the same 8192^3 workload on the native scaled-MFMA variant;
+  * roofline: algorithmic work per launch / mean launch duration from HIP
+    events recorded around every timed launch on the launch stream;
+  * cpu_baseline: the CPU oracle timed on a bounded sample of outputs of
+    the 8192^3 workload on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X published dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+METRIC = "MXFP8 GEMM TFLOP/s at 8192\u00b3 (% of dense MXFP8 peak); GB/s (% HBM) at M=64"
+KERNEL_SOURCES = ["level_dsl_amd/csrc/mxgemm.hip", "level_dsl_amd/csrc/mxgemm_common.h",
+                  "level_dsl_amd/csrc/mxgemm_large.h", "level_dsl_amd/csrc/mxgemm_skinny.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def traffic_from_profiles(kernel_key: str):
+    """HBM bytes per launch from a committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    e = d.get("kernels", {}).get(kernel_key)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def time_launches(run_step, steps: int, warmup: int, stream):
+    import torch
+    for i in range(warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        run_step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
+    return wall, float(np.mean(per)), float(np.median(per)), float(np.min(per))
+
+
+def upload(p, copies: int, rotate_a: bool = True):
+    import torch
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    A, As, B, Bs = t(p.A), t(p.As), t(p.B), t(p.Bs)
+    sets = [(A, As, B, Bs)]
+    for _ in range(copies - 1):
+        sets.append((A.clone() if rotate_a else A, As.clone() if rotate_a else As,
+                     B.clone(), Bs.clone()))
+    return sets
+
+
+def bench_gemm(gemm, p, variant, steps, warmup, copies):
+    import torch
+    import level_dsl_amd as L
+    sets = upload(p, copies, rotate_a=p.M > 64)
+    dt = torch.float32 if p.out_dtype == 0 else torch.bfloat16
+    C = [torch.empty((p.M, p.N), dtype=dt, device="cuda:0") for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+    gemm.set_variant(variant)
+    h = gemm.h
+
+    def step(i):
+        A, As, B, Bs = sets[i % copies]
+        L.mxgemm_run(h, A, As, p.fmtA, B, Bs, p.fmtB, C[i % copies], p.M, p.N, p.K,
+                     int(p.use_acc), p.out_dtype, stream.cuda_stream)
+
+    wall, mean_s, med_s, min_s = time_launches(step, steps, warmup, stream)
+    del sets, C
+    torch.cuda.empty_cache()
+    return wall, mean_s, med_s, min_s
+
+
+def cpu_baseline(p, target_s: float = 12.0):
+    import mxinputs as mi
+    import oracle
+    threads = oracle.default_threads()
+    rows, cols = mi.sample_points(p.M, p.N, 256, seed=99, edge=1)
+    t0 = time.perf_counter()
+    oracle.gemm_points(p.A, p.As, p.fmtA, p.B, p.Bs, p.fmtB, p.M, p.N, p.K, rows, cols,
+                       nthreads=threads)
+    t_cal = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(max(rows.size * target_s / t_cal, 256), 60_000_000))
+    g = np.random.Generator(np.random.PCG64(2024))
+    r = g.integers(0, p.M, size=n, dtype=np.int64)
+    c = g.integers(0, p.N, size=n, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm_points(p.A, p.As, p.fmtA, p.B, p.Bs, p.fmtB, p.M, p.N, p.K, r, c,
+                       nthreads=threads)
+    t = time.perf_counter() - t0
+    return {"value": round(2.0 * p.K * n / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} random outputs of the {p.M}x{p.N}x{p.K} workload "
+                      f"({2 * p.K} flop each), {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the GEMM "
+              "would shard by C columns with no exchange, which is not built here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import level_dsl_amd as L
+    import mxinputs as mi
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    L.load_library()
+    gemm = L.Gemm()
+    out = {}
+
+    # ---- headline: 8192^3, bf16 out, exact variant ----------------------------
+    p = mi.workload(2)
+    log(f"bench: {p.name} generated")
+    flops = mi.algorithmic_flops(p.M, p.N, p.K)
+    steps, warmup = args.steps, args.warmup
+    wall, mean_s, med_s, min_s = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE, steps, warmup, 3)
+    value = flops * steps / wall / 1e12
+    achieved = flops / mean_s / 1e12
+    log(f"bench: large exact {value:.1f} TFLOP/s whole-job, {achieved:.1f} per launch "
+        f"(mean {mean_s * 1e6:.1f} us)")
+    traffic = traffic_from_profiles("large_exact")
+    out.update({
+        "metric": METRIC,
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "A": "e4m3", "B": "e4m3",
+                   "scales": "e8m0 per 32 K", "mfma": "bf16 32x32x16 after exact scaled decode",
+                   "accumulate": "f32", "out": "bf16 (RNE)", "input_rotation": 3},
+        "pct_of_mxfp8_peak": round(100 * value / PEAK_TFLOPS["fp8"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": traffic, "kernel": "mxg::large::kernel<0,0,false>",
+                     "launch_mean_us": round(mean_s * 1e6, 2),
+                     "launch_median_us": round(med_s * 1e6, 2)},
+    })
+
+    # ---- native scaled-MFMA variant on the same workload ----------------------
+    wall_n, mean_n, med_n, _ = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE_NATIVE, steps, warmup, 3)
+    out["native_scaled_mfma"] = {
+        "value": round(flops * steps / wall_n / 1e12, 2), "unit": "TFLOP/s",
+        "achieved_per_launch": round(flops / mean_n / 1e12, 2), "peak": PEAK_TFLOPS["fp8"],
+        "frac": round(flops / mean_n / 1e12 / PEAK_TFLOPS["fp8"], 4),
+        "launch_mean_us": round(mean_n * 1e6, 2),
+        "note": "v_mfma_scale_f32_32x32x64_f8f6f4; not within 1e-5*sum|ab| (8-product "
+                "groups truncated 13 bits below their largest product)"}
+    log(f"bench: native {out['native_scaled_mfma']['value']} TFLOP/s")
+
+    cpu_src = p
+    # ---- skinny: M=64, N=28672, K=8192, fp32 out --------------------------------
+    ps = mi.workload(3)
+    log(f"bench: {ps.name} generated")
+    sbytes = mi.algorithmic_bytes(ps.M, ps.N, ps.K, ps.out_dtype)
+    sk_steps = max(steps, 30)
+    wall_s, mean_ss, med_ss, _ = bench_gemm(gemm, ps, L.MXGEMM_VARIANT_SKINNY, sk_steps, warmup, 3)
+    out["skinny_m64"] = {
+        "workload": ps.name, "value": round(sbytes * sk_steps / wall_s / 1e9, 1), "unit": "GB/s",
+        "pct_of_hbm_peak": round(100 * sbytes * sk_steps / wall_s / 1e9 / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(sbytes / mean_ss / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(sbytes / mean_ss / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles("skinny_exact"),
+                     "kernel": "mxg::skinny::kernel<0,0,false>",
+                     "launch_mean_us": round(mean_ss * 1e6, 2)},
+        "algorithmic_bytes": sbytes, "steps": sk_steps, "b_rotation": 3}
+    log(f"bench: skinny {out['skinny_m64']['value']} GB/s")
+    del ps
+    gemm.close()
+
+    if not args.no_cpu:
+        log("bench: CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(cpu_src)
+    else:
+        out["cpu_baseline"] = None
+    out["kernel_hash"] = kernel_hash()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,6 +30,22 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOob = 0x80000000u;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Arguments shared by every kernel (validated on the host).
+struct GemmArgs {
+    const uint8_t *A;
+    const uint8_t *As;
+    const uint8_t *B;
+    const uint8_t *Bs;
+    void *C;
+    int M, N, K, KB;       // KB = K / 32
+    int tiles_m, tiles_n;
+    int use_acc;           // 0 / 1
+    int out_bf16;          // 0 fp32, 1 bf16
+    int scale_dword;       // 1: KB % 4 == 0 and scale bases 4-byte aligned
+    int c_vec;             // 1: N % 4 == 0 (aligned vector stores of C)
+};
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -50,6 +66,34 @@ __device__ __forceinline__ uint32_t load4(rsrc_t r, uint32_t off)
 __device__ __forceinline__ uint32_t load1(rsrc_t r, uint32_t off)
 {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// 16 bytes per lane straight into LDS: lane i of the wave writes
+// lds_base + 16 i .. + 15 (buffer_load_dwordx4 ... lds; lds_base must be
+// the same for the whole wave).  Out-of-range lanes write zeros.
+__device__ __forceinline__ void load16_lds(rsrc_t r, void *lds_base, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, off, 0, 0, 0);
+}
+
+// Wait until every vector-memory operation of this wave has completed,
+// including loads that write LDS directly, which the compiler does not
+// track (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Scale bytes kb0 .. kb0+3 of scale row r as one little-endian dword; bytes
+// past KB read as zero.  `dword` selects one aligned 4-byte load (KB % 4 == 0
+// and a 4-byte aligned base), else four byte loads.
+__device__ __forceinline__ uint32_t load_scale4(rsrc_t rs, uint32_t r, int KB, int kb0, int dword)
+{
+    if (dword) return __builtin_amdgcn_raw_buffer_load_b32(rs, r * KB + kb0, 0, 0);
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+                 rs, kb0 + b < KB ? r * KB + kb0 + b : kOob, 0, 0)
+             << (8 * b);
+    return v;
 }
 
 __device__ __forceinline__ void store16(rsrc_t r, uint32_t off, v4f v)
@@ -82,6 +126,50 @@ __device__ __forceinline__ uint32_t bf16_bits(float f)
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
 {
     return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Epilogue store of 4 consecutive columns n..n+3 of one row of C, element
+// index e0 = row * N + n relative to the descriptor rC.  use_acc adds the
+// previous C (fp32, or bf16 widened) before the single rounding to the
+// output type.  With c_vec (N % 4 == 0) one 16-byte (fp32) or 8-byte (bf16)
+// store; otherwise per-element stores with columns >= N masked.  Rows past
+// the descriptor's range are dropped by the hardware.
+__device__ __forceinline__ void store_c4(rsrc_t rC, uint32_t e0, int n, int N, v4f v, int out_bf16,
+                                         int use_acc, int c_vec)
+{
+    const int esz = out_bf16 ? 2 : 4;
+    if (c_vec) {
+        const uint32_t off = n < N ? e0 * esz : kOob;
+        if (!out_bf16) {
+            if (use_acc) v += __builtin_bit_cast(v4f, load16(rC, off));
+            store16(rC, off, v);
+        } else {
+            if (use_acc) {
+                v2i old = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rC, off, 0, 0));
+                v[0] += bf16_to_f32((uint32_t)old[0] & 0xffffu);
+                v[1] += bf16_to_f32((uint32_t)old[0] >> 16);
+                v[2] += bf16_to_f32((uint32_t)old[1] & 0xffffu);
+                v[3] += bf16_to_f32((uint32_t)old[1] >> 16);
+            }
+            v2i o = {(int)(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16)),
+                     (int)(bf16_bits(v[2]) | (bf16_bits(v[3]) << 16))};
+            store8(rC, off, o);
+        }
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t off = (n + e) < N ? (e0 + e) * esz : kOob;
+        float x = v[e];
+        if (!out_bf16) {
+            if (use_acc) x += __builtin_bit_cast(float, load4(rC, off));
+            store4(rC, off, __builtin_bit_cast(uint32_t, x));
+        } else {
+            if (use_acc)
+                x += bf16_to_f32((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rC, off, 0, 0));
+            store2(rC, off, (uint16_t)bf16_bits(x));
+        }
+    }
 }
 
 // One 32x32x64 scaled MFMA: D = (X * 2^(sx-127)) @ (Y * 2^(sy-127)) + C where

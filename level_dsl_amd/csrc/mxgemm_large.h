@@ -1,26 +1,34 @@
 // mxgemm_large.h -- 256x256-tile MX-FP8 GEMM kernel for gfx950 (MFMA-bound shapes).
 //
-// One workgroup of four waves computes a 256 (M) x 256 (N) tile of C; each
-// wave owns a 128 x 128 quarter held as 4 x 4 accumulators of the 32x32
-// scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), i.e. 256 fp32 per lane.
+// One workgroup of eight waves computes a 256 (M) x 256 (N) tile of C.  Each
+// SIMD runs two of the waves, so while one issues MFMAs the other decodes,
+// reads LDS or waits on memory; each wave owns a 128 (M) x 64 (N) block held
+// as 4 x 2 accumulators of a 32x32 MFMA (128 fp32 per lane).
 //
-// K loop (BK = 128 bytes of K per stage, two LDS stages):
-//   * global -> registers: raw 16-byte buffer loads of the next A and B
-//     tiles (256 rows x 128 bytes each) plus, straight into registers, the
-//     scale dwords each lane needs for the next stage;
-//   * LDS -> registers: two ds_read_b128 per operand fragment, in the
-//     scaled-MFMA operand layout (lane half h of row r takes 16-byte chunks
-//     h and h+2 of each 64-byte K step);
-//   * 32 scaled MFMAs per wave per stage, issued K-major, then N, then M,
-//     so that consecutive MFMAs update independent accumulators (the issue
-//     order of amd_scheduled_mfma on the TLX async-compute page, "Explicit
-//     MFMA scheduling");
-//   * the prefetched registers are written to the other LDS stage, then
-//     one workgroup barrier.
-// LDS rows are 128 bytes; 16-byte chunk c of row r is stored at chunk
-// position c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so that the lanes
-// of one ds_read_b128 pass (consecutive rows, same chunk) and of one
-// ds_write_b128 pass hit distinct banks.
+// K loop (BK = 128 bytes of K per stage, two LDS stages of 2 x 32 KiB):
+//   * global -> LDS: 16-byte raw buffer loads that write LDS directly
+//     (buffer_load_dwordx4 ... lds); each wave instruction fills one
+//     contiguous 1 KiB LDS segment (8 tile rows), lane i writing bytes
+//     16i..16i+15; the swizzle is applied by choosing which global chunk each
+//     lane fetches.  K and row tails read as zero through the descriptor's
+//     range check.  The next stage's loads are issued before the current
+//     stage's MFMAs and waited for (vmcnt(0)) just before the stage barrier;
+//   * scale dwords (4 blocks = one stage) go straight to registers, one per
+//     lane per 32-row fragment, also one stage ahead;
+//   * LDS -> registers: ds_read_b128 fragments, then the multiply:
+//       exact mode (default): lane half h of a row takes 16-byte chunk
+//       2p + h of K block p, decodes the 16 codes with the row's block-p
+//       scale into 16 bf16 (v_cvt_scalef32_pk_bf16_fp8/bf8) and feeds two
+//       32x32x16 bf16 MFMAs;
+//       native mode: lane half h takes chunks 4kk+h and 4kk+2+h for the
+//       kk-th 64-byte step and one v_mfma_scale_f32_32x32x64_f8f6f4 consumes
+//       them with the scale bytes selected by op_sel;
+//     MFMAs are issued K-major, then N, then M, so consecutive MFMAs update
+//     independent accumulators (the issue order of amd_scheduled_mfma on the
+//     TLX async-compute page, "Explicit MFMA scheduling").
+// LDS rows are 128 bytes; 16-byte chunk c of row r sits at chunk position
+// c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the lanes of one
+// ds_read_b128 pass (consecutive rows, same chunk) hit distinct banks.
 //
 // Roles in the MFMA: the B tile supplies the instruction's rows and the A
 // tile its columns, so each lane's accumulator registers hold 4 consecutive
@@ -32,29 +40,15 @@
 #include "mxgemm_common.h"
 
 namespace mxg {
-
-struct GemmArgs {
-    const uint8_t *A;
-    const uint8_t *As;
-    const uint8_t *B;
-    const uint8_t *Bs;
-    void *C;
-    int M, N, K, KB;       // KB = K / 32
-    int tiles_m, tiles_n;
-    int use_acc;           // 0 / 1
-    int out_bf16;          // 0 fp32, 1 bf16
-    int scale_dword;       // 1: KB % 4 == 0 and scale bases 4-byte aligned
-    int c_vec;             // 1: N % 4 == 0 (aligned vector stores of C)
-};
-
 namespace large {
 
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int THREADS = 256;
-constexpr int WAVE_M = 128, WAVE_N = 128;     // per-wave tile
+constexpr int WAVES = 8, THREADS = 64 * WAVES;
+constexpr int WAVE_M = 128, WAVE_N = 64;      // per-wave tile
 constexpr int SUB_M = WAVE_M / 32, SUB_N = WAVE_N / 32;
 constexpr int TILE_BYTES = BM * BK;           // one operand, one stage (32 KiB)
-constexpr int LOADS_PER_THREAD = TILE_BYTES / 16 / THREADS;  // 8 per operand
+constexpr int SEG = 1024;                     // bytes one wave load instruction fills
+constexpr int SEGS_PER_WAVE = TILE_BYTES / SEG / WAVES;  // 4 per operand per stage
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -80,7 +74,7 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
 template <int FA, int FB, bool NATIVE>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][TILE_BYTES];  // [stage][A/B]
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][TILE_BYTES];  // [stage][A/B]
 
     int tm, tn;
     tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
@@ -94,75 +88,49 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const rsrc_t rBs = make_rsrc(p.Bs + (size_t)n0 * KB, (uint32_t)rows_b * KB);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
     const int lrow = lane & 31, khalf = lane >> 5;
 
-    // ---- global -> register loads of one stage --------------------------
-    // chunk c = tid + 256*i: tile row c / 8, 16-byte chunk c % 8 of the row.
-    uint32_t goff[LOADS_PER_THREAD];
-    uint32_t lds_w[LOADS_PER_THREAD];
+    // ---- global -> LDS, one stage ---------------------------------------
+    // segment s = SEGS_PER_WAVE*wave + j holds tile rows 8s..8s+7; lane i
+    // writes row 8s + i/8 at chunk position i%8, i.e. global chunk
+    // (i%8) ^ swz(row) = (i%8) ^ (i/8) ^ (s & 1).
+    uint32_t goff[SEGS_PER_WAVE], gk[SEGS_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_THREAD; ++i) {
-        const int c = tid + THREADS * i;
-        const int r = c >> 3, ch = c & 7;
-        goff[i] = (uint32_t)r * K + ch * 16;
-        lds_w[i] = r * BK + ((ch ^ swz(r)) << 4);
+    for (int j = 0; j < SEGS_PER_WAVE; ++j) {
+        const int s = SEGS_PER_WAVE * wave + j;
+        const int r = 8 * s + (lane >> 3);
+        const int c = (lane & 7) ^ (lane >> 3) ^ (s & 1);
+        gk[j] = 16 * c;
+        goff[j] = (uint32_t)r * K + 16 * c;
     }
-    const int ch_lane = (tid & 7) * 16;  // K byte of this thread's chunk within a stage
-
-    v4i ga[LOADS_PER_THREAD], gb[LOADS_PER_THREAD];
-    auto gload = [&](int k0) {
-        const bool kin = k0 + ch_lane < K;
+    auto gload = [&](int st, int k0) {
 #pragma unroll
-        for (int i = 0; i < LOADS_PER_THREAD; ++i) {
-            const uint32_t off = kin ? goff[i] + k0 : kOob;
-            ga[i] = load16(rA, off);
-            gb[i] = load16(rB, off);
-        }
-    };
-    auto lstore = [&](int st) {
-#pragma unroll
-        for (int i = 0; i < LOADS_PER_THREAD; ++i) {
-            *reinterpret_cast<v4i *>(&lds[st][0][lds_w[i]]) = ga[i];
-            *reinterpret_cast<v4i *>(&lds[st][1][lds_w[i]]) = gb[i];
+        for (int j = 0; j < SEGS_PER_WAVE; ++j) {
+            const int s = SEGS_PER_WAVE * wave + j;
+            const uint32_t off = (int)(k0 + gk[j]) < K ? goff[j] + k0 : kOob;
+            load16_lds(rA, &lds[st][0][s * SEG], off);
+            load16_lds(rB, &lds[st][1][s * SEG], off);
         }
     };
 
-    // ---- scales: one dword (4 blocks = one stage) per lane per subtile ---
-    // lane half khalf of a row supplies block 2*kk + khalf of the stage to
-    // MFMA k-step kk; lanes of the upper half shift their dword down one byte
-    // so that the instruction's byte select is 0 for kk = 0 and 2 for kk = 1.
+    // ---- scales: one dword (4 blocks = one stage) per lane per fragment --
     uint32_t sa[SUB_M], sb[SUB_N];
     auto sload = [&](int k0) {
         const int kb0 = k0 >> 5;
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) {
-            const int r = wm * WAVE_M + i * 32 + lrow;
-            sa[i] = 0;
-            if (p.scale_dword) {
-                sa[i] = load4(rAs, (uint32_t)r * KB + kb0);
-            } else {
+        for (int i = 0; i < SUB_M; ++i)
+            sa[i] = load_scale4(rAs, (uint32_t)(wm * WAVE_M + i * 32 + lrow), KB, kb0,
+                                p.scale_dword);
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    sa[i] |= load1(rAs, kb0 + b < KB ? (uint32_t)r * KB + kb0 + b : kOob) << (8 * b);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < SUB_N; ++j) {
-            const int r = wn * WAVE_N + j * 32 + lrow;
-            sb[j] = 0;
-            if (p.scale_dword) {
-                sb[j] = load4(rBs, (uint32_t)r * KB + kb0);
-            } else {
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    sb[j] |= load1(rBs, kb0 + b < KB ? (uint32_t)r * KB + kb0 + b : kOob) << (8 * b);
-            }
-        }
+        for (int j = 0; j < SUB_N; ++j)
+            sb[j] = load_scale4(rBs, (uint32_t)(wn * WAVE_N + j * 32 + lrow), KB, kb0,
+                                p.scale_dword);
     };
 
-    // ---- fragment reads -------------------------------------------------
+    // ---- fragment addresses --------------------------------------------
     const int sw = swz(lrow);
     uint32_t fa_off[SUB_M], fb_off[SUB_N];
 #pragma unroll
@@ -178,9 +146,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     const int nk = (K + BK - 1) / BK;
 
-    gload(0);
+    gload(0, 0);
     sload(0);
-    lstore(0);
+    wait_vmem();
     __syncthreads();
 
     for (int kt = 0; kt < nk; ++kt) {
@@ -193,10 +161,11 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
         const bool more = kt + 1 < nk;
         if (more) {
-            gload((kt + 1) * BK);
+            gload(st ^ 1, (kt + 1) * BK);
             sload((kt + 1) * BK);
         }
 
+        const uint8_t *la = lds[st][0], *lb = lds[st][1];
         if constexpr (NATIVE) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -205,14 +174,14 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                 v8i fa[SUB_M], fb[SUB_N];
 #pragma unroll
                 for (int i = 0; i < SUB_M; ++i) {
-                    v4i lo = *reinterpret_cast<const v4i *>(&lds[st][0][fa_off[i] + o0]);
-                    v4i hi = *reinterpret_cast<const v4i *>(&lds[st][0][fa_off[i] + o1]);
+                    v4i lo = *reinterpret_cast<const v4i *>(la + fa_off[i] + o0);
+                    v4i hi = *reinterpret_cast<const v4i *>(la + fa_off[i] + o1);
                     fa[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 }
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) {
-                    v4i lo = *reinterpret_cast<const v4i *>(&lds[st][1][fb_off[j] + o0]);
-                    v4i hi = *reinterpret_cast<const v4i *>(&lds[st][1][fb_off[j] + o1]);
+                    v4i lo = *reinterpret_cast<const v4i *>(lb + fb_off[j] + o0);
+                    v4i hi = *reinterpret_cast<const v4i *>(lb + fb_off[j] + o1);
                     fb[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 }
 #pragma unroll
@@ -226,21 +195,18 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                     }
             }
         } else {
-            // Exact path: K block p (32 bytes) of the stage; lane half h takes
-            // its 16-byte chunk 2p + h, decodes it with the row's block-p scale
-            // into 16 bf16 and feeds two 32x32x16 bf16 MFMAs.
 #pragma unroll
             for (int pb = 0; pb < BK / 32; ++pb) {
                 const uint32_t o = (((2 * pb + khalf) ^ sw) << 4);
                 v8bf fa[SUB_M][2], fb[SUB_N][2];
 #pragma unroll
                 for (int i = 0; i < SUB_M; ++i) {
-                    const v4i x = *reinterpret_cast<const v4i *>(&lds[st][0][fa_off[i] + o]);
+                    const v4i x = *reinterpret_cast<const v4i *>(la + fa_off[i] + o);
                     decode16<FA>(x, e8m0_to_f32((csa[i] >> (8 * pb)) & 0xffu), fa[i][0], fa[i][1]);
                 }
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) {
-                    const v4i x = *reinterpret_cast<const v4i *>(&lds[st][1][fb_off[j] + o]);
+                    const v4i x = *reinterpret_cast<const v4i *>(lb + fb_off[j] + o);
                     decode16<FB>(x, e8m0_to_f32((csb[j] >> (8 * pb)) & 0xffu), fb[j][0], fb[j][1]);
                 }
 #pragma unroll
@@ -253,7 +219,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             }
         }
 
-        if (more) lstore(st ^ 1);
+        if (more) wait_vmem();
         __syncthreads();
     }
 
@@ -275,40 +241,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                 const uint32_t e0 = (uint32_t)m * N + n;                        // element index
                 v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3]};
-                if (p.c_vec) {
-                    const uint32_t off = n < N ? e0 * esz : kOob;
-                    if (!p.out_bf16) {
-                        if (p.use_acc) v += __builtin_bit_cast(v4f, load16(rC, off));
-                        store16(rC, off, v);
-                    } else {
-                        if (p.use_acc) {
-                            v2i old = __builtin_bit_cast(
-                                v2i, __builtin_amdgcn_raw_buffer_load_b64(rC, off, 0, 0));
-                            v[0] += bf16_to_f32((uint32_t)old[0] & 0xffffu);
-                            v[1] += bf16_to_f32((uint32_t)old[0] >> 16);
-                            v[2] += bf16_to_f32((uint32_t)old[1] & 0xffffu);
-                            v[3] += bf16_to_f32((uint32_t)old[1] >> 16);
-                        }
-                        v2i o = {(int)(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16)),
-                                 (int)(bf16_bits(v[2]) | (bf16_bits(v[3]) << 16))};
-                        store8(rC, off, o);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t off = (n + e) < N ? (e0 + e) * esz : kOob;
-                        float x = v[e];
-                        if (!p.out_bf16) {
-                            if (p.use_acc) x += __builtin_bit_cast(float, load4(rC, off));
-                            store4(rC, off, __builtin_bit_cast(uint32_t, x));
-                        } else {
-                            if (p.use_acc)
-                                x += bf16_to_f32((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                    rC, off, 0, 0));
-                            store2(rC, off, (uint16_t)bf16_bits(x));
-                        }
-                    }
-                }
+                store_c4(rC, e0, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
             }
         }
     }

@@ -154,8 +154,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             *reinterpret_cast<v4f *>(&red[wave][16 * i + r16][16 * j + 4 * kq]) = acc[i][j];
     __syncthreads();
 
-    const int esz = p.out_bf16 ? 2 : 4;
-    const rsrc_t rC = make_rsrc((uint8_t *)p.C, (uint32_t)M * N * esz);
+    const rsrc_t rC = make_rsrc((uint8_t *)p.C, (uint32_t)M * N * (p.out_bf16 ? 2 : 4));
     constexpr int Q = MAX_M * BN / 4;  // float4 groups in the tile
     for (int q = tid; q < Q; q += THREADS) {
         const int m = q / (BN / 4), nl = (q % (BN / 4)) * 4;
@@ -164,40 +163,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const v4f *>(&red[w][m][nl]);
         const int n = n0 + nl;
-        const uint32_t e0 = (uint32_t)m * N + n;
-        if (p.c_vec) {
-            const uint32_t off = n < N ? e0 * esz : kOob;
-            if (!p.out_bf16) {
-                if (p.use_acc) v += __builtin_bit_cast(v4f, load16(rC, off));
-                store16(rC, off, v);
-            } else {
-                if (p.use_acc) {
-                    v2i old = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rC, off, 0, 0));
-                    v[0] += bf16_to_f32((uint32_t)old[0] & 0xffffu);
-                    v[1] += bf16_to_f32((uint32_t)old[0] >> 16);
-                    v[2] += bf16_to_f32((uint32_t)old[1] & 0xffffu);
-                    v[3] += bf16_to_f32((uint32_t)old[1] >> 16);
-                }
-                v2i o = {(int)(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16)),
-                         (int)(bf16_bits(v[2]) | (bf16_bits(v[3]) << 16))};
-                store8(rC, off, o);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t off = (n + e) < N ? (e0 + e) * esz : kOob;
-                float x = v[e];
-                if (!p.out_bf16) {
-                    if (p.use_acc) x += __builtin_bit_cast(float, load4(rC, off));
-                    store4(rC, off, __builtin_bit_cast(uint32_t, x));
-                } else {
-                    if (p.use_acc)
-                        x += bf16_to_f32(
-                            (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rC, off, 0, 0));
-                    store2(rC, off, (uint16_t)bf16_bits(x));
-                }
-            }
-        }
+        store_c4(rC, (uint32_t)m * N + n, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
     }
 }
 
