@@ -35,8 +35,17 @@ template <int FA, int FB, bool NATIVE>
 hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
 {
     const int blocks = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE>), dim3(blocks),
-                       dim3(mxg::large::THREADS), 0, s, a);
+    // 16-byte scale windows need K % 512 == 0 and 16-byte aligned scale rows;
+    // the native variant has no registers to spare for them
+    if constexpr (!NATIVE) {
+        if (a.scale_dword == 2) {
+            hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, true>), dim3(blocks),
+                               dim3(mxg::large::THREADS), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+        hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, false>), dim3(blocks),
+                           dim3(mxg::large::THREADS), 0, s, a);
     return hipGetLastError();
 }
 
@@ -175,7 +184,9 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     a.KB = (int)(K / 32);
     a.use_acc = use_acc;
     a.out_bf16 = out_dtype == MXGEMM_OUT_BF16;
-    a.scale_dword = (a.KB % 4 == 0) && ((((uintptr_t)A_scale) | ((uintptr_t)B_scale)) & 3u) == 0;
+    const uintptr_t salign = ((uintptr_t)A_scale) | ((uintptr_t)B_scale);
+    a.scale_dword = (a.KB % 16 == 0 && (salign & 15u) == 0) ? 2
+                    : (a.KB % 4 == 0 && (salign & 3u) == 0) ? 1 : 0;
     a.c_vec = (N % 4) == 0;
 
     int variant = h->variant;

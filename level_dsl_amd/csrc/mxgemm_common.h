@@ -12,7 +12,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Lambdas in the kernels carry this so that the K loop is one straight-line
+// body (an outlined call would move the accumulators through scratch).
+#define MXG_INLINE __attribute__((always_inline))
+
 namespace mxg {
+
+template <int V>
+struct int_c {
+    static constexpr int value = V;
+};
+// Calls f(int_c<0>{}), ..., f(int_c<N-1>{}) (compile-time loop index).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(int_c<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -43,7 +61,8 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int use_acc;           // 0 / 1
     int out_bf16;          // 0 fp32, 1 bf16
-    int scale_dword;       // 1: KB % 4 == 0 and scale bases 4-byte aligned
+    int scale_dword;       // 2: KB % 16 == 0 and scale bases 16-byte aligned;
+                           // 1: KB % 4 == 0 and 4-byte aligned; 0: neither
     int c_vec;             // 1: N % 4 == 0 (aligned vector stores of C)
 };
 
@@ -192,6 +211,15 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s)
 {
     const uint32_t bits = s == 0u ? 0x00400000u : (s == 255u ? 0x7fc00000u : s << 23);
     return __builtin_bit_cast(float, bits);
+}
+
+// Byte `b` of the scale dword d as the fp32 2^(s-127), valid for s in
+// 1..254 (one shift): the exact variants' bf16 decode is only exact for
+// scale bytes well inside that range, so the endpoints need no fix-up there.
+template <int b>
+__device__ __forceinline__ float scale_f32(uint32_t d)
+{
+    return __builtin_bit_cast(float, ((d >> (8 * b)) & 0xffu) << 23);
 }
 
 // Two fp8 codes (bytes 2*hi, 2*hi+1 of w) -> two bf16 equal to the codes' values

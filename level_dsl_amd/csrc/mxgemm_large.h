@@ -1,21 +1,32 @@
 // mxgemm_large.h -- 256x256-tile MX-FP8 GEMM kernel for gfx950 (MFMA-bound shapes).
 //
-// One workgroup of eight waves computes a 256 (M) x 256 (N) tile of C.  Each
-// SIMD runs two of the waves, so while one issues MFMAs the other decodes,
-// reads LDS or waits on memory; each wave owns a 128 (M) x 64 (N) block held
-// as 4 x 2 accumulators of a 32x32 MFMA (128 fp32 per lane).
+// One workgroup of four waves (one per SIMD) computes a 256 (M) x 256 (N)
+// tile of C; each wave owns a 128 x 128 quarter held as 4 x 4 accumulators
+// of a 32x32 MFMA (256 fp32 per lane, in the accumulator registers), which
+// leaves the 256 ordinary VGPRs for a software pipeline.
 //
-// K loop (BK = 128 bytes of K per stage, two LDS stages of 2 x 32 KiB):
+// Data flow per stage of BK = 128 bytes of K (two LDS stages of 2 x 32 KiB):
 //   * global -> LDS: 16-byte raw buffer loads that write LDS directly
-//     (buffer_load_dwordx4 ... lds); each wave instruction fills one
+//     (buffer_load_dwordx4 ... lds); one wave instruction fills one
 //     contiguous 1 KiB LDS segment (8 tile rows), lane i writing bytes
 //     16i..16i+15; the swizzle is applied by choosing which global chunk each
 //     lane fetches.  K and row tails read as zero through the descriptor's
-//     range check.  The next stage's loads are issued before the current
-//     stage's MFMAs and waited for (vmcnt(0)) just before the stage barrier;
-//   * scale dwords (4 blocks = one stage) go straight to registers, one per
-//     lane per 32-row fragment, also one stage ahead;
-//   * LDS -> registers: ds_read_b128 fragments, then the multiply:
+//     range check.  Loads for stage kt+2 are issued right after the barrier
+//     that retires stage kt's buffer, one stage before they are needed.
+//   * scales: with K % 512 == 0, each lane fetches 16 scale bytes of each of
+//     its 8 fragment rows at a time (four stages' worth, one dwordx4 load per
+//     row, prefetched a window ahead); otherwise one dword (or four bytes) per
+//     row per stage, prefetched one stage ahead.
+//   * blocks: a stage is split into blocks (exact mode: the four 32-byte K
+//     blocks; native mode: the two 64-byte MFMA K steps).  While the MFMAs of
+//     block g run, the fragments of block g+1 are read from LDS (ds_read_b128)
+//     and, in exact mode, decoded to bf16 -- the intra-wave interleave of
+//     memory and MFMA work described for gfx950 on the TLX warp-
+//     specialization page ("Warp pipeline", intra-wave scheduling).  The
+//     stage barrier sits where the last fragment of a stage has been read,
+//     so the next stage's first block is read while the last block's MFMAs
+//     still run.
+//   * the multiply:
 //       exact mode (default): lane half h of a row takes 16-byte chunk
 //       2p + h of K block p, decodes the 16 codes with the row's block-p
 //       scale into 16 bf16 (v_cvt_scalef32_pk_bf16_fp8/bf8) and feeds two
@@ -39,16 +50,19 @@
 
 #include "mxgemm_common.h"
 
+#include <type_traits>
+
 namespace mxg {
 namespace large {
 
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int WAVES = 8, THREADS = 64 * WAVES;
-constexpr int WAVE_M = 128, WAVE_N = 64;      // per-wave tile
+constexpr int WAVES = 4, THREADS = 64 * WAVES;
+constexpr int WAVE_M = 128, WAVE_N = 128;     // per-wave tile
 constexpr int SUB_M = WAVE_M / 32, SUB_N = WAVE_N / 32;
 constexpr int TILE_BYTES = BM * BK;           // one operand, one stage (32 KiB)
 constexpr int SEG = 1024;                     // bytes one wave load instruction fills
-constexpr int SEGS_PER_WAVE = TILE_BYTES / SEG / WAVES;  // 4 per operand per stage
+constexpr int SEGS_PER_WAVE = TILE_BYTES / SEG / WAVES;  // 8 per operand per stage
+constexpr int WINDOW = 4;                     // stages per 16-byte scale window
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -71,9 +85,36 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &
     tn = w / gs;
 }
 
-template <int FA, int FB, bool NATIVE>
+// Fragments of one block: exact mode keeps 16 bf16 (two MFMA operands) per
+// fragment, native mode the 32 raw codes.
+template <bool NATIVE>
+struct Frags;
+template <>
+struct Frags<false> {
+    v8bf a[SUB_M][2], b[SUB_N][2];
+};
+template <>
+struct Frags<true> {
+    v8i a[SUB_M], b[SUB_N];
+};
+template <bool NATIVE>
+struct Raw;
+template <>
+struct Raw<false> {
+    v4i a[SUB_M], b[SUB_N];
+};
+template <>
+struct Raw<true> {};  // native fragments are read straight into the operand registers
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002, SG_SALU = 0x004, SG_MFMA = 0x008, SG_VMEM_RD = 0x020,
+              SG_DS_RD = 0x100;
+
+template <int FA, int FB, bool NATIVE, bool SCALE16>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
+    constexpr int BLOCKS = NATIVE ? 2 : 4;               // blocks per stage
+    constexpr int MF = NATIVE ? SUB_M * SUB_N : 2 * SUB_M * SUB_N;  // MFMAs per block
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][TILE_BYTES];  // [stage][A/B]
 
     int tm, tn;
@@ -92,51 +133,100 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int lrow = lane & 31, khalf = lane >> 5;
+    const int nk = (K + BK - 1) / BK;
 
     // ---- global -> LDS, one stage ---------------------------------------
     // segment s = SEGS_PER_WAVE*wave + j holds tile rows 8s..8s+7; lane i
     // writes row 8s + i/8 at chunk position i%8, i.e. global chunk
-    // (i%8) ^ swz(row) = (i%8) ^ (i/8) ^ (s & 1).
-    uint32_t goff[SEGS_PER_WAVE], gk[SEGS_PER_WAVE];
-#pragma unroll
-    for (int j = 0; j < SEGS_PER_WAVE; ++j) {
-        const int s = SEGS_PER_WAVE * wave + j;
-        const int r = 8 * s + (lane >> 3);
-        const int c = (lane & 7) ^ (lane >> 3) ^ (s & 1);
-        gk[j] = 16 * c;
-        goff[j] = (uint32_t)r * K + 16 * c;
-    }
-    auto gload = [&](int st, int k0) {
+    // (i%8) ^ swz(row) = (i%8) ^ (i/8) ^ (s & 1).  Stages past the end of K
+    // read as zero (every offset is out of range), so the call needs no guard.
+    const int gc0 = (lane & 7) ^ (lane >> 3);  // chunk for even segments; odd: gc0 ^ 1
+    const uint32_t grow = (uint32_t)(8 * SEGS_PER_WAVE * wave + (lane >> 3)) * K;
+    auto gload = [&](int st, int k0) MXG_INLINE {
 #pragma unroll
         for (int j = 0; j < SEGS_PER_WAVE; ++j) {
             const int s = SEGS_PER_WAVE * wave + j;
-            const uint32_t off = (int)(k0 + gk[j]) < K ? goff[j] + k0 : kOob;
+            const int c = gc0 ^ (j & 1);
+            const uint32_t off = k0 + 16 * c < K ? grow + (uint32_t)(8 * j) * K + 16 * c + k0 : kOob;
             load16_lds(rA, &lds[st][0][s * SEG], off);
             load16_lds(rB, &lds[st][1][s * SEG], off);
         }
     };
 
-    // ---- scales: one dword (4 blocks = one stage) per lane per fragment --
-    uint32_t sa[SUB_M], sb[SUB_N];
-    auto sload = [&](int k0) {
-        const int kb0 = k0 >> 5;
+    // ---- scales ---------------------------------------------------------
+    // Fragment rows of this lane: A rows wm*128 + 32i + lrow, B rows
+    // wn*128 + 32j + lrow.  SCALE16: 16 bytes (4 stages) per row and load;
+    // otherwise one dword (or four bytes) per row and stage.
+    const uint32_t sra = (uint32_t)(wm * WAVE_M + lrow), srb = (uint32_t)(wn * WAVE_N + lrow);
+    auto scale16 = [&](int kt, v4i *xa, v4i *xb) MXG_INLINE {  // window starting at stage kt
+        const int kb0 = kt * (BK / 32);
+        const bool in = kb0 < KB;
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i)
-            sa[i] = load_scale4(rAs, (uint32_t)(wm * WAVE_M + i * 32 + lrow), KB, kb0,
-                                p.scale_dword);
+        for (int i = 0; i < SUB_M; ++i) xa[i] = load16(rAs, in ? (sra + 32 * i) * KB + kb0 : kOob);
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j)
-            sb[j] = load_scale4(rBs, (uint32_t)(wn * WAVE_N + j * 32 + lrow), KB, kb0,
-                                p.scale_dword);
+        for (int j = 0; j < SUB_N; ++j) xb[j] = load16(rBs, in ? (srb + 32 * j) * KB + kb0 : kOob);
+    };
+    auto scale4 = [&](int kt, uint32_t *xa, uint32_t *xb) MXG_INLINE {  // stage kt
+        const int kb0 = kt * (BK / 32);
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i) xa[i] = load_scale4(rAs, sra + 32 * i, KB, kb0, p.scale_dword);
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) xb[j] = load_scale4(rBs, srb + 32 * j, KB, kb0, p.scale_dword);
+    };
+    // native mode: the upper lane half supplies the odd K blocks
+    auto native_shift = [&](uint32_t *xa, uint32_t *xb) MXG_INLINE {
+        if (NATIVE && khalf) {
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i) xa[i] >>= 8;
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) xb[j] >>= 8;
+        }
     };
 
-    // ---- fragment addresses --------------------------------------------
+    // ---- fragments --------------------------------------------------------
     const int sw = swz(lrow);
-    uint32_t fa_off[SUB_M], fb_off[SUB_N];
+    const uint32_t fa_off = (wm * WAVE_M + lrow) * BK, fb_off = (wn * WAVE_N + lrow) * BK;
+    // read block `blk` of LDS stage `st` (exact: into raw; native: straight
+    // into the MFMA operands f)
+    auto read_block = [&](int st, int blk, Raw<NATIVE> &r, Frags<NATIVE> &f) MXG_INLINE {
+        const uint8_t *la = lds[st][0] + fa_off, *lb = lds[st][1] + fb_off;
+        if constexpr (NATIVE) {
+            const int c0 = blk * 4 + khalf;  // K 64blk+16h .. +15; chunk c0 + 2: K +32
+            const uint32_t o0 = ((c0 ^ sw) << 4), o1 = (((c0 + 2) ^ sw) << 4);
 #pragma unroll
-    for (int i = 0; i < SUB_M; ++i) fa_off[i] = (wm * WAVE_M + i * 32 + lrow) * BK;
+            for (int i = 0; i < SUB_M; ++i) {
+                const v4i lo = *reinterpret_cast<const v4i *>(la + i * 32 * BK + o0);
+                const v4i hi = *reinterpret_cast<const v4i *>(la + i * 32 * BK + o1);
+                f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
 #pragma unroll
-    for (int j = 0; j < SUB_N; ++j) fb_off[j] = (wn * WAVE_N + j * 32 + lrow) * BK;
+            for (int j = 0; j < SUB_N; ++j) {
+                const v4i lo = *reinterpret_cast<const v4i *>(lb + j * 32 * BK + o0);
+                const v4i hi = *reinterpret_cast<const v4i *>(lb + j * 32 * BK + o1);
+                f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        } else {
+            const uint32_t o = (((2 * blk + khalf) ^ sw) << 4);
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i) r.a[i] = *reinterpret_cast<const v4i *>(la + i * 32 * BK + o);
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) r.b[j] = *reinterpret_cast<const v4i *>(lb + j * 32 * BK + o);
+        }
+    };
+    // exact mode: decode raw block `blk` (scale dwords sa/sb of its stage)
+    // into the bf16 MFMA operands; native mode: nothing to do
+    auto prep_block = [&](auto BLK, const Raw<NATIVE> &r, const uint32_t *sa_, const uint32_t *sb_,
+                          Frags<NATIVE> &f) MXG_INLINE {
+        constexpr int blk = decltype(BLK)::value;
+        if constexpr (!NATIVE) {
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i)
+                decode16<FA>(r.a[i], scale_f32<blk>(sa_[i]), f.a[i][0], f.a[i][1]);
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j)
+                decode16<FB>(r.b[j], scale_f32<blk>(sb_[j]), f.b[j][0], f.b[j][1]);
+        }
+    };
 
     v16f acc[SUB_M][SUB_N];
 #pragma unroll
@@ -144,83 +234,150 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) acc[i][j] = v16f{};
 
-    const int nk = (K + BK - 1) / BK;
+    // MFMAs t = T0 .. T0+CNT-1 of a block, in K-major, N, M order
+    auto mfma_range = [&](auto BLK, auto T0, auto CNT, const Frags<NATIVE> &f, const uint32_t *sa_,
+                          const uint32_t *sb_) MXG_INLINE {
+        constexpr int blk = decltype(BLK)::value;
+        constexpr int t0 = decltype(T0)::value, cnt = decltype(CNT)::value;
+        static_for<cnt>([&](auto TT) MXG_INLINE {
+            constexpr int t = t0 + decltype(TT)::value;
+            if constexpr (NATIVE) {
+                constexpr int j = t / SUB_M, i = t % SUB_M;
+                acc[i][j] = mfma_scaled<FB, FA, 2 * blk>(f.b[j], f.a[i], acc[i][j], sb_[j], sa_[i]);
+            } else {
+                constexpr int hh = t / (SUB_M * SUB_N), j = (t / SUB_M) % SUB_N, i = t % SUB_M;
+                acc[i][j] = mfma_bf16_32(f.b[j][hh], f.a[i][hh], acc[i][j]);
+            }
+        });
+    };
 
+    // Interleave for a block: the next block's LDS reads first, a few MFMAs
+    // to cover their latency, then one MFMA per three VALU (decode) slots.
+    auto sched_block = [&]() MXG_INLINE {
+        if constexpr (NATIVE) {
+            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 4, 0);
+            static_for<MF>([&](auto) MXG_INLINE {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+            });
+        } else {
+            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, SUB_M + SUB_N, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+            static_for<MF - 4>([&](auto) MXG_INLINE {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+            });
+        }
+    };
+
+    Raw<NATIVE> raw;
+    Frags<NATIVE> f0, f1;
+    uint32_t csa[SUB_M], csb[SUB_N];  // scale dwords of the stage being decoded
+    v4i wa[SUB_M], wb[SUB_N], na[SUB_M], nb[SUB_N];  // SCALE16 windows (current, next)
+    uint32_t sa1[SUB_M], sb1[SUB_N];  // !SCALE16: next stage's scale dwords
+
+    // One stage.  SS: the stage's position in its 4-stage window (SCALE16),
+    // CROSS: whether the last block continues into stage kt+1.
+    auto stage = [&](int kt, auto SS, auto CROSS) MXG_INLINE {
+        constexpr int ss = decltype(SS)::value;
+        constexpr bool cross = decltype(CROSS)::value;
+        const int st = kt & 1;
+        if constexpr (SCALE16) {
+            if constexpr (ss == 0) scale16(kt + WINDOW, na, nb);  // next window, 4 stages ahead
+        } else {
+            scale4(kt + 1, sa1, sb1);                             // next stage
+        }
+        uint32_t ksa[SUB_M], ksb[SUB_N];  // this stage's scale dwords (native MFMAs need them)
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i) ksa[i] = csa[i];
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) ksb[j] = csb[j];
+        static_for<BLOCKS>([&](auto BLK) MXG_INLINE {
+            constexpr int blk = decltype(BLK)::value;
+            Frags<NATIVE> &cur = (blk & 1) ? f1 : f0;
+            Frags<NATIVE> &nxt = (blk & 1) ? f0 : f1;
+            if constexpr (blk + 1 < BLOCKS) {
+                read_block(st, blk + 1, raw, nxt);
+                mfma_range(BLK, int_c<0>{}, int_c<MF>{}, cur, ksa, ksb);
+                prep_block(int_c<blk + 1>{}, raw, csa, csb, nxt);
+                sched_block();
+                __builtin_amdgcn_sched_barrier(0);
+            } else if constexpr (cross) {
+                // MFMAs that keep the matrix pipe busy across the barrier
+                mfma_range(BLK, int_c<0>{}, int_c<MF / 4>{}, cur, ksa, ksb);
+                // every wave has read all of stage kt's buffer; stage kt+1 has
+                // landed once this wave's loads are done and all waves pass
+                wait_vmem();
+                __syncthreads();
+                read_block(st ^ 1, 0, raw, nxt);
+                gload(st, (kt + 2) * BK);
+                // scale dwords of stage kt+1
+                if constexpr (SCALE16) {
+                    if constexpr (ss == WINDOW - 1) {
+#pragma unroll
+                        for (int i = 0; i < SUB_M; ++i) wa[i] = na[i];
+#pragma unroll
+                        for (int j = 0; j < SUB_N; ++j) wb[j] = nb[j];
+                    }
+                    constexpr int nx = (ss + 1) % WINDOW;
+#pragma unroll
+                    for (int i = 0; i < SUB_M; ++i) csa[i] = (uint32_t)wa[i][nx];
+#pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) csb[j] = (uint32_t)wb[j][nx];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < SUB_M; ++i) csa[i] = sa1[i];
+#pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) csb[j] = sb1[j];
+                }
+                native_shift(csa, csb);
+                mfma_range(BLK, int_c<MF / 4>{}, int_c<MF - MF / 4>{}, cur, ksa, ksb);
+                prep_block(int_c<0>{}, raw, csa, csb, nxt);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                mfma_range(BLK, int_c<0>{}, int_c<MF>{}, cur, ksa, ksb);
+            }
+        });
+    };
+
+    // ---- prologue ---------------------------------------------------------
     gload(0, 0);
-    sload(0);
+    if constexpr (SCALE16) {
+        scale16(0, wa, wb);
+    } else {
+        scale4(0, sa1, sb1);
+    }
     wait_vmem();
     __syncthreads();
+    gload(1, BK);
+    if constexpr (SCALE16) {
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i) csa[i] = (uint32_t)wa[i][0];
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) csb[j] = (uint32_t)wb[j][0];
+    } else {
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i) csa[i] = sa1[i];
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) csb[j] = sb1[j];
+    }
+    native_shift(csa, csb);
+    read_block(0, 0, raw, f0);
+    prep_block(int_c<0>{}, raw, csa, csb, f0);
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt & 1;
-        uint32_t csa[SUB_M], csb[SUB_N];
-#pragma unroll
-        for (int i = 0; i < SUB_M; ++i) csa[i] = (NATIVE && khalf) ? sa[i] >> 8 : sa[i];
-#pragma unroll
-        for (int j = 0; j < SUB_N; ++j) csb[j] = (NATIVE && khalf) ? sb[j] >> 8 : sb[j];
-
-        const bool more = kt + 1 < nk;
-        if (more) {
-            gload(st ^ 1, (kt + 1) * BK);
-            sload((kt + 1) * BK);
-        }
-
-        const uint8_t *la = lds[st][0], *lb = lds[st][1];
-        if constexpr (NATIVE) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int c0 = kk * 4 + khalf;  // K 64kk+16h .. +15; chunk c0 + 2: K +32
-                const uint32_t o0 = ((c0 ^ sw) << 4), o1 = (((c0 + 2) ^ sw) << 4);
-                v8i fa[SUB_M], fb[SUB_N];
-#pragma unroll
-                for (int i = 0; i < SUB_M; ++i) {
-                    v4i lo = *reinterpret_cast<const v4i *>(la + fa_off[i] + o0);
-                    v4i hi = *reinterpret_cast<const v4i *>(la + fa_off[i] + o1);
-                    fa[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
-#pragma unroll
-                for (int j = 0; j < SUB_N; ++j) {
-                    v4i lo = *reinterpret_cast<const v4i *>(lb + fb_off[j] + o0);
-                    v4i hi = *reinterpret_cast<const v4i *>(lb + fb_off[j] + o1);
-                    fb[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
-#pragma unroll
-                for (int j = 0; j < SUB_N; ++j)
-#pragma unroll
-                    for (int i = 0; i < SUB_M; ++i) {
-                        if (kk == 0)
-                            acc[i][j] = mfma_scaled<FB, FA, 0>(fb[j], fa[i], acc[i][j], csb[j], csa[i]);
-                        else
-                            acc[i][j] = mfma_scaled<FB, FA, 2>(fb[j], fa[i], acc[i][j], csb[j], csa[i]);
-                    }
-            }
-        } else {
-#pragma unroll
-            for (int pb = 0; pb < BK / 32; ++pb) {
-                const uint32_t o = (((2 * pb + khalf) ^ sw) << 4);
-                v8bf fa[SUB_M][2], fb[SUB_N][2];
-#pragma unroll
-                for (int i = 0; i < SUB_M; ++i) {
-                    const v4i x = *reinterpret_cast<const v4i *>(la + fa_off[i] + o);
-                    decode16<FA>(x, e8m0_to_f32((csa[i] >> (8 * pb)) & 0xffu), fa[i][0], fa[i][1]);
-                }
-#pragma unroll
-                for (int j = 0; j < SUB_N; ++j) {
-                    const v4i x = *reinterpret_cast<const v4i *>(lb + fb_off[j] + o);
-                    decode16<FB>(x, e8m0_to_f32((csb[j] >> (8 * pb)) & 0xffu), fb[j][0], fb[j][1]);
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int j = 0; j < SUB_N; ++j)
-#pragma unroll
-                        for (int i = 0; i < SUB_M; ++i)
-                            acc[i][j] = mfma_bf16_32(fb[j][hh], fa[i][hh], acc[i][j]);
-            }
-        }
-
-        if (more) wait_vmem();
-        __syncthreads();
+    // ---- main loop --------------------------------------------------------
+    if constexpr (SCALE16) {
+        // nk is a multiple of the window; the last window's last stage ends
+        const int nw = nk / WINDOW;
+        for (int w = 0; w + 1 < nw; ++w)
+            static_for<WINDOW>([&](auto SS) MXG_INLINE { stage(WINDOW * w + decltype(SS)::value, SS, std::true_type{}); });
+        static_for<WINDOW - 1>([&](auto SS) MXG_INLINE {
+            stage(WINDOW * (nw - 1) + decltype(SS)::value, SS, std::true_type{});
+        });
+        stage(nk - 1, int_c<WINDOW - 1>{}, std::false_type{});
+    } else {
+        for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, int_c<0>{}, std::true_type{});
+        stage(nk - 1, int_c<0>{}, std::false_type{});
     }
 
     // ---- epilogue ---------------------------------------------------------

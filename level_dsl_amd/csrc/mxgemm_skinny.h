@@ -125,13 +125,13 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             v8bf fa[SUB_M][4], fb[SUB_N][4];
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) {
-                const float sc = e8m0_to_f32(cur.sa[i]);
+                const float sc = scale_f32<0>(cur.sa[i]);
                 decode16<FA>(v4i{cur.a[i][0], cur.a[i][1], cur.a[i][2], cur.a[i][3]}, sc, fa[i][0], fa[i][1]);
                 decode16<FA>(v4i{cur.a[i][4], cur.a[i][5], cur.a[i][6], cur.a[i][7]}, sc, fa[i][2], fa[i][3]);
             }
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j) {
-                const float sc = e8m0_to_f32(cur.sb[j]);
+                const float sc = scale_f32<0>(cur.sb[j]);
                 decode16<FB>(v4i{cur.b[j][0], cur.b[j][1], cur.b[j][2], cur.b[j][3]}, sc, fb[j][0], fb[j][1]);
                 decode16<FB>(v4i{cur.b[j][4], cur.b[j][5], cur.b[j][6], cur.b[j][7]}, sc, fb[j][2], fb[j][3]);
             }
