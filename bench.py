@@ -37,7 +37,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X published dense MFMA pe
 PEAK_HBM_GBS = 8000.0
 METRIC = "MXFP8 GEMM TFLOP/s at 8192\u00b3 (% of dense MXFP8 peak); GB/s (% HBM) at M=64"
 KERNEL_SOURCES = ["level_dsl_amd/csrc/mxgemm.hip", "level_dsl_amd/csrc/mxgemm_common.h",
-                  "level_dsl_amd/csrc/mxgemm_large.h", "level_dsl_amd/csrc/mxgemm_skinny.h"]
+                  "level_dsl_amd/csrc/mxgemm_large.h", "level_dsl_amd/csrc/mxgemm_skinny.h",
+                  "level_dsl_amd/csrc/mxgemm_stream.h"]
 
 
 def kernel_hash() -> str:
@@ -218,7 +219,7 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(sbytes / mean_ss / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": traffic_from_profiles("skinny_exact"),
-                     "kernel": "mxg::skinny::kernel<0,0,false>",
+                     "kernel": "mxg::stream::kernel<0,0,true>",
                      "launch_mean_us": round(mean_ss * 1e6, 2)},
         "algorithmic_bytes": sbytes, "steps": sk_steps, "b_rotation": 3}
     log(f"bench: skinny {out['skinny_m64']['value']} GB/s")

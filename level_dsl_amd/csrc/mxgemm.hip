@@ -13,6 +13,10 @@
 #include "mxgemm.h"
 #include "mxgemm_large.h"
 #include "mxgemm_skinny.h"
+#include "mxgemm_stream.h"
+
+static_assert(mxg::stream::BN == mxg::skinny::BN && mxg::stream::MAX_M == mxg::skinny::MAX_M,
+              "both small-M kernels tile N and bound M alike");
 
 struct mxgemm_ctx {
     uint32_t magic;
@@ -58,9 +62,29 @@ hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int FA, int FB>
+hipError_t launch_stream(const mxg::GemmArgs &a, hipStream_t s)
+{
+    if (a.scale_dword)
+        hipLaunchKernelGGL((mxg::stream::kernel<FA, FB, true>), dim3(a.tiles_n),
+                           dim3(mxg::stream::THREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL((mxg::stream::kernel<FA, FB, false>), dim3(a.tiles_n),
+                           dim3(mxg::stream::THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
 template <bool NATIVE>
 hipError_t dispatch(bool skinny, int f, const mxg::GemmArgs &a, hipStream_t s)
 {
+    if (skinny && !NATIVE) {
+        switch (f) {
+        case 0: return launch_stream<0, 0>(a, s);
+        case 1: return launch_stream<0, 1>(a, s);
+        case 2: return launch_stream<1, 0>(a, s);
+        default: return launch_stream<1, 1>(a, s);
+        }
+    }
     if (skinny) {
         switch (f) {
         case 0: return launch_skinny<0, 0, NATIVE>(a, s);

@@ -251,6 +251,32 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         });
     };
 
+    // Interleave for the block that crosses into the next stage (after its
+    // barrier): the next stage's first LDS reads, then the 2*SEGS_PER_WAVE
+    // direct-to-LDS loads of stage kt+2 spread over the remaining MFMAs,
+    // then the decode.
+    auto sched_cross = [&]() MXG_INLINE {
+        constexpr int rest = MF - MF / 4;  // MFMAs after the barrier
+        constexpr int nld = 2 * SEGS_PER_WAVE;
+        __builtin_amdgcn_sched_group_barrier(SG_DS_RD, NATIVE ? 4 : SUB_M + SUB_N, 0);
+        static_for<(nld < rest ? nld : rest)>([&](auto) MXG_INLINE {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_SALU, 2, 0);
+        });
+        if constexpr (!NATIVE) {
+            static_for<(rest > nld ? rest - nld : 0)>([&](auto) MXG_INLINE {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+            });
+        } else {
+            static_for<(rest > nld ? rest - nld : 0)>([&](auto) MXG_INLINE {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+            });
+        }
+    };
+
     // Interleave for a block: the next block's LDS reads first, a few MFMAs
     // to cover their latency, then one MFMA per three VALU (decode) slots.
     auto sched_block = [&]() MXG_INLINE {
@@ -333,6 +359,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                 native_shift(csa, csb);
                 mfma_range(BLK, int_c<MF / 4>{}, int_c<MF - MF / 4>{}, cur, ksa, ksb);
                 prep_block(int_c<0>{}, raw, csa, csb, nxt);
+                sched_cross();
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 mfma_range(BLK, int_c<0>{}, int_c<MF>{}, cur, ksa, ksb);

@@ -1,0 +1,262 @@
+// mxgemm_stream.h -- small-M (M <= 64) MX-FP8 GEMM, exact mode, for gfx950.
+//
+// With M <= 64 the multiply is bound by reading B once from HBM (about 120
+// flop per byte at M = 64, far below the chip's MFMA-to-HBM balance).  The
+// kernel streams B with as little else in its way as possible, using two
+// producer waves and seven consumer waves per workgroup (the producer /
+// consumer split of warp specialization on the TLX warp-specialization page,
+// with one workgroup barrier per stage standing in for the full/empty
+// barrier pair of the pipelined GEMM pattern in the TLX API Quick Reference):
+//
+//   * a workgroup owns 112 columns of C (N = 28672 gives exactly 256
+//     workgroups, one per CU) and all of K, in stages of 128 bytes of K;
+//     workgroup n starts at stage n (mod the stage count) and wraps around,
+//     so that the workgroups do not all read their B rows at the same K
+//     offset (with a power-of-two row pitch those addresses crowd onto a few
+//     memory channels);
+//   * consumer wave w (0..6) owns columns 16w..16w+15: lane l holds B row
+//     16w + l%16 and, with g = l/16, loads K 16g..16g+15 and 64+16g..64+16g+15
+//     of each stage straight into registers (each load instruction reads 64
+//     contiguous bytes of 16 rows), seven stages ahead in an eight-slot
+//     register ring (about 100 KiB of B in flight per CU, enough to cover the
+//     loaded HBM latency); it decodes its codes with their block scales to bf16
+//     (v_cvt_scalef32_pk_bf16_fp8/bf8) and runs sixteen 16x16x32 bf16 MFMAs
+//     per stage against A;
+//   * two producer waves fetch the A tile (at most 64 rows x 128 bytes per
+//     stage, from L2) seven stages ahead with direct-to-LDS loads into an
+//     eight-slot fp8 ring, decodes it once for the whole workgroup into bf16
+//     with its scales folded in, and writes it to a two-slot LDS ring; a
+//     barrier per stage publishes the slot;
+//   * the scale dwords of A and of this workgroup's B rows for 64 stages at a
+//     time are loaded by all waves into LDS at the start of each 64-stage
+//     chunk (for K <= 8192, once), instead of a scattered load per row and
+//     stage;
+//   * every output element is summed by one lane over all of K in a fixed
+//     order (deterministic); C is written with 16-byte (fp32) or 8-byte
+//     (bf16) buffer stores.
+#pragma once
+
+#include "mxgemm_common.h"
+
+namespace mxg {
+namespace stream {
+
+constexpr int MAX_M = 64;
+constexpr int BN = 112;
+constexpr int BK = 128;
+constexpr int CONSUMERS = 7;
+constexpr int PRODUCERS = 2;             // each decodes 32 rows of A per stage
+constexpr int WAVES = CONSUMERS + PRODUCERS;
+constexpr int PROWS = MAX_M / PRODUCERS;
+constexpr int THREADS = 64 * WAVES;
+constexpr int RING = 8;                  // consumer register ring: the current stage + 7 ahead
+constexpr int ADEPTH = 8;                // producer's fp8 A ring in LDS: the current stage + 7 ahead
+constexpr int A8 = MAX_M * BK;           // bytes of one fp8 A stage (8 KiB)
+constexpr int AROW = 2 * BK;             // bytes of one decoded (bf16) A row per stage
+constexpr int A_SLOT = MAX_M * AROW;     // 16 KiB
+constexpr int SCH = 64;                  // stages whose scale dwords sit in LDS at a time
+constexpr int SROWS = MAX_M + BN;        // scale rows: A rows 0..63, then the B rows
+
+// workgroup barrier that orders LDS only (outstanding global loads stay in flight)
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// bf16 A rows in LDS: 16 chunks of 16 bytes, chunk c of row r at position
+// c ^ (r & 15), so the 16 lanes of a fragment read (16 consecutive rows, one
+// chunk) hit distinct banks.
+__device__ __forceinline__ uint32_t a_addr(int r, int c) { return r * AROW + ((c ^ (r & 15)) << 4); }
+
+// Scale dword of row r for stage kt (4 bytes, one per 32-element block):
+// SDW selects one aligned dword load, else four byte loads; a dead stage or
+// row reads zeros through an out-of-range offset.
+template <bool SDW>
+__device__ __forceinline__ uint32_t scale_dword(rsrc_t rs, uint32_t r, int KB, int kb0, bool live)
+{
+    if constexpr (SDW) {
+        return __builtin_amdgcn_raw_buffer_load_b32(rs, live ? r * KB + kb0 : kOob, 0, 0);
+    } else {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+                     rs, live && kb0 + b < KB ? r * KB + kb0 + b : kOob, 0, 0)
+                 << (8 * b);
+        return v;
+    }
+}
+
+// s_waitcnt vmcnt(n) (other counters untouched); n < 64
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0f70);
+}
+
+template <int FA, int FB, bool SDW>
+__global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t a8_lds[ADEPTH][A8];   // raw A, row-major
+    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][A_SLOT];       // decoded A (bf16)
+    __shared__ __attribute__((aligned(16))) uint32_t s_lds[SROWS][SCH];     // scale dwords
+
+    const int n0 = blockIdx.x * BN;
+    const int rows_b = min(BN, p.N - n0);
+    const int M = p.M, N = p.N, K = p.K, KB = p.KB;
+    const int nk = (K + BK - 1) / BK;
+    static_assert(RING == ADEPTH && SCH % RING == 0, "producer and consumers run the same iterations");
+    const int nu = (nk + RING - 1) / RING * RING;  // iterations, padded to whole rings
+    const int s0 = (int)(blockIdx.x % (unsigned)nk);
+    auto kt_of = [&](int u) MXG_INLINE { const int s = u + s0; return s < nk ? s : s - nk; };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const rsrc_t rAs = make_rsrc(p.As, (uint32_t)M * KB);
+    const rsrc_t rBs = make_rsrc(p.Bs + (size_t)n0 * KB, (uint32_t)rows_b * KB);
+    // All waves: the scale dwords of iterations u0 .. u0+SCH-1 into s_lds
+    // (row r < 64: A row r; else B row r - 64 of this workgroup), column u - u0.
+    // (all loads are issued before the first LDS write, so the chunk costs one
+    // round trip)
+    auto load_scales = [&](int u0) MXG_INLINE {
+        constexpr int PER = (SROWS * SCH + THREADS - 1) / THREADS;
+        uint32_t v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = min(tid + THREADS * i, SROWS * SCH - 1);
+            const int r = e / SCH, uu = e % SCH, u = u0 + uu;
+            const bool live = u < nk;
+            const int kb0 = (live ? kt_of(u) : 0) * (BK / 32);
+            // rows 0..63 are A rows, the rest B rows: pick the descriptor
+            const bool is_a = r < MAX_M;
+            v[i] = scale_dword<SDW>(is_a ? rAs : rBs, (uint32_t)(is_a ? r : r - MAX_M), KB, kb0,
+                                    live);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + THREADS * i;
+            if (e < SROWS * SCH) s_lds[e / SCH][e % SCH] = v[i];
+        }
+    };
+
+    if (wave >= CONSUMERS) {
+        // ----------------------------------------------------------- producers
+        const rsrc_t rA = make_rsrc(p.A, (uint32_t)M * K);
+        // fp8 A of stage u, direct to LDS: producer pw handles rows
+        // PROWS*pw .. +PROWS-1; its instruction j fills rows PROWS*pw + 8j..+7
+        // (lane l: row ... + l/8, 16-byte chunk l%8)
+        const int pw = wave - CONSUMERS;
+        const int c = lane & 7, r0 = PROWS * pw + (lane >> 3);
+        constexpr int NJ = PROWS / 8;
+        auto fetch = [&](int u) MXG_INLINE {
+            const int k0 = (u < nk ? kt_of(u) : 0) * BK;
+            const bool cin = u < nk && k0 + 16 * c < K;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t r = 8 * j + r0;
+                load16_lds(rA, &a8_lds[u % ADEPTH][1024 * (NJ * pw + j)],
+                           cin ? r * K + k0 + 16 * c : kOob);
+            }
+        };
+        // decode stage u (landed in a8_lds) with its A scales into a_lds[u & 1]
+        auto publish = [&](int u) MXG_INLINE {
+            const uint8_t *src = a8_lds[u % ADEPTH] + 1024 * NJ * pw;
+            uint8_t *dst = a_lds[u & 1];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int r = 8 * j + r0;
+                const v4i x = *reinterpret_cast<const v4i *>(src + 1024 * j + 16 * lane);
+                const uint32_t sd = s_lds[r][u % SCH];
+                const float sc = __builtin_bit_cast(float, ((sd >> (8 * (c >> 1))) & 0xffu) << 23);
+                v8bf lo, hi;
+                decode16<FA>(x, sc, lo, hi);
+                *reinterpret_cast<v8bf *>(dst + a_addr(r, 2 * c)) = lo;
+                *reinterpret_cast<v8bf *>(dst + a_addr(r, 2 * c + 1)) = hi;
+            }
+        };
+        for (int u0 = 0; u0 < nu; u0 += SCH) {
+            load_scales(u0);
+            if (u0 == 0)
+                for (int u = 0; u < ADEPTH - 1; ++u) fetch(u);
+            lds_barrier();  // scales of this chunk in place
+            for (int u1 = u0; u1 < min(u0 + SCH, nu); u1 += ADEPTH) {
+                static_for<ADEPTH>([&](auto P) MXG_INLINE {
+                    const int u = u1 + decltype(P)::value;
+                    fetch(u + ADEPTH - 1);
+                    wait_vmcnt<NJ * (ADEPTH - 1)>();  // stage u has landed
+                    publish(u);
+                    lds_barrier();
+                });
+            }
+            lds_barrier();  // every wave is done with this chunk's scales
+        }
+        return;
+    }
+
+    // ------------------------------------------------------------- consumers
+    const int w = wave;
+    const int r16 = lane & 15, g = lane >> 4;
+    const rsrc_t rB = make_rsrc(p.B + (size_t)n0 * K, (uint32_t)rows_b * K);
+    const uint32_t brow = (uint32_t)(16 * w + r16) * K + 16 * g;
+    v4i blo[RING], bhi[RING];
+    auto fetch = [&](int u, auto SLOT) MXG_INLINE {
+        constexpr int sl = decltype(SLOT)::value;
+        const int k0 = (u < nk ? kt_of(u) : 0) * BK;
+        const bool live = u < nk;
+        blo[sl] = load16(rB, live && k0 + 16 * g < K ? brow + k0 : kOob);
+        bhi[sl] = load16(rB, live && k0 + 64 + 16 * g < K ? brow + k0 + 64 : kOob);
+    };
+    v4f acc[MAX_M / 16];
+#pragma unroll
+    for (int i = 0; i < MAX_M / 16; ++i) acc[i] = v4f{};
+
+    static_for<RING - 1>([&](auto P) MXG_INLINE { fetch(decltype(P)::value, P); });
+    for (int u0 = 0; u0 < nu; u0 += SCH) {
+        load_scales(u0);
+        lds_barrier();  // scales of this chunk in place
+        for (int u1 = u0; u1 < min(u0 + SCH, nu); u1 += RING) {
+            static_for<RING>([&](auto P) MXG_INLINE {
+                constexpr int pp = decltype(P)::value;
+                const int u = u1 + pp;
+                fetch(u + RING - 1, int_c<(pp + RING - 1) % RING>{});
+                lds_barrier();
+                // B: K 16g.. (block g/2) and 64+16g.. (block 2+g/2) of this stage
+                const uint32_t sd = s_lds[MAX_M + 16 * w + r16][u % SCH];
+                const float slo = __builtin_bit_cast(float, ((sd >> (8 * (g >> 1))) & 0xffu) << 23);
+                const float shi = __builtin_bit_cast(float, ((sd >> (8 * (2 + (g >> 1)))) & 0xffu) << 23);
+                v8bf bq[4];
+                decode16<FB>(blo[pp], slo, bq[0], bq[1]);
+                decode16<FB>(bhi[pp], shi, bq[2], bq[3]);
+                // A operand (i, q): row 16i + l%16, K 16g + 8(q%2) + 64(q/2), i.e.
+                // bf16 chunk 2g + q%2 + 8(q/2) of the row
+                const uint8_t *al = a_lds[u & 1];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int i = 0; i < MAX_M / 16; ++i) {
+                        const v8bf a = *reinterpret_cast<const v8bf *>(
+                            al + a_addr(16 * i + r16, 2 * g + (q & 1) + 8 * (q >> 1)));
+                        acc[i] = mfma_bf16_16(bq[q], a, acc[i]);
+                    }
+            });
+        }
+        lds_barrier();  // every wave is done with this chunk's scales
+    }
+
+    // acc[i] register r of lane l: m = 16 i + l % 16, n = 16 w + 4 (l / 16) + r.
+    const rsrc_t rC = make_rsrc((uint8_t *)p.C, (uint32_t)M * N * (p.out_bf16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < MAX_M / 16; ++i) {
+        const int m = 16 * i + r16;
+        const int n = n0 + 16 * w + 4 * g;
+        store_c4(rC, (uint32_t)m * N + n, n, N, acc[i], p.out_bf16, p.use_acc, p.c_vec);
+    }
+}
+
+} // namespace stream
+} // namespace mxg
