@@ -12,12 +12,21 @@ Also reported on the same line:
   * skinny: the M=64, N=28672, K=8192 workload in GB/s of algorithmic bytes
     (A, scales and B read once, C written once), B rotated over 3 copies;
   * native: the same 8192^3 workload on the native scaled-MFMA variant;
-  * roofline: algorithmic work per launch / mean launch duration from HIP
-    events recorded around every timed launch on the launch stream;
+  * roofline: algorithmic work per launch / mean launch duration, from one
+    pair of HIP events recorded on the launch stream around the timed
+    launches;
   * cpu_baseline: the CPU oracle timed on a bounded sample of outputs of
     the 8192^3 workload on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+
+Counter passes (HBM traffic per launch):
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o p -- python bench.py --traffic
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o p -- python bench.py --traffic
+  python bench.py --traffic-report D1/p_counter_collection.csv D2/p_counter_collection.csv
+--traffic launches a plain negating copy of COPY_BYTES (read once, written once)
+and three launches each of the two timed kernels; --traffic-report scales the
+counters by what they read for that copy and writes profiles/hbm_traffic.json.
 """
 from __future__ import annotations
 
@@ -70,22 +79,24 @@ def traffic_from_profiles(kernel_key: str):
 
 
 def time_launches(run_step, steps: int, warmup: int, stream):
+    """W untimed steps, then exactly `steps` back-to-back launches between a
+    device synchronisation on each side.  Returns the wall time of the timed
+    region and the mean launch duration from one pair of HIP events recorded
+    on the launch stream around it."""
     import torch
     for i in range(warmup):
         run_step(i)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
-        starts[i].record(stream)
         run_step(i)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
-    return wall, float(np.mean(per)), float(np.median(per)), float(np.min(per))
+    return wall, start.elapsed_time(end) * 1e-3 / steps
 
 
 def upload(p, copies: int, rotate_a: bool = True):
@@ -115,17 +126,104 @@ def bench_gemm(gemm, p, variant, steps, warmup, copies):
         L.mxgemm_run(h, A, As, p.fmtA, B, Bs, p.fmtB, C[i % copies], p.M, p.N, p.K,
                      int(p.use_acc), p.out_dtype, stream.cuda_stream)
 
-    wall, mean_s, med_s, min_s = time_launches(step, steps, warmup, stream)
+    wall, mean_s = time_launches(step, steps, warmup, stream)
     del sets, C
     torch.cuda.empty_cache()
-    return wall, mean_s, med_s, min_s
+    return wall, mean_s
+
+
+COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
+# key: (kernel name as rocprofv3 prints it, workload id, variant, C bytes per element)
+TRAFFIC_KERNELS = {"large_exact": ("void mxg::large::kernel<0, 0, false, true>", 2,
+                                   "MXGEMM_VARIANT_LARGE", 2),
+                   "skinny_exact": ("void mxg::stream::kernel<0, 0, true>", 3,
+                                    "MXGEMM_VARIANT_SKINNY", 4)}
+
+
+def traffic_launches():
+    """Launch the calibration copy and each timed kernel three times (run under
+    rocprofv3 --pmc)."""
+    import torch
+    import level_dsl_amd as L
+    import mxinputs as mi
+    L.load_library()
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    gemm = L.Gemm()
+    for key, (_, wid, var, _) in TRAFFIC_KERNELS.items():
+        p = mi.workload(wid)
+        log(f"traffic: {key} on {p.name}")
+        bench_gemm(gemm, p, getattr(L, var), 3, 0, 3)
+    gemm.close()
+    torch.cuda.synchronize()
+    log("traffic: done")
+
+
+def traffic_report(fetch_csv: str, write_csv: str):
+    """Per-launch HBM bytes of each timed kernel from the two counter passes,
+    scaled by the counters' reading for the calibration copy."""
+    import csv
+    import collections
+    import mxinputs as mi
+
+    def per_dispatch(path, counter):
+        tot = collections.defaultdict(float)
+        name = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            tot[d] += float(r["Counter_Value"])
+            name[d] = r["Kernel_Name"]
+        return tot, name
+
+    out = {"kernel_hash": kernel_hash(), "copy_bytes": COPY_BYTES, "kernels": {}}
+    scale = {}
+    vals = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        tot, name = per_dispatch(path, counter)
+        copy = [tot[d] for d in sorted(tot) if "neg" in name[d]]
+        if not copy:
+            raise SystemExit(f"no calibration copy dispatch in {path}")
+        kib = float(np.median(copy))
+        scale[counter] = COPY_BYTES / (kib * 1024.0)
+        out[f"copy_{counter}_kib"] = kib
+        for key, (kname, _, _, _) in TRAFFIC_KERNELS.items():
+            ks = [tot[d] for d in sorted(tot) if name[d].startswith(kname)]
+            if ks:
+                vals.setdefault(key, {})[counter] = float(np.mean(ks)) * 1024.0 * scale[counter]
+    for counter in scale:
+        out[f"scale_{counter}"] = scale[counter]
+    for key, (kname, wid, _, cbytes) in TRAFFIC_KERNELS.items():
+        v = vals.get(key, {})
+        if "FETCH_SIZE" not in v or "WRITE_SIZE" not in v:
+            continue
+        p = mi.WORKLOADS[wid]
+        alg = mi.algorithmic_bytes(p["M"], p["N"], p["K"],
+                                   mi.OUT_BF16 if cbytes == 2 else mi.OUT_F32)
+        out["kernels"][key] = {"kernel": kname, "workload": p["name"],
+                               "fetch_bytes": round(v["FETCH_SIZE"]),
+                               "write_bytes": round(v["WRITE_SIZE"]),
+                               "bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
+                               "algorithmic_bytes": alg,
+                               "ratio_to_algorithmic":
+                                   round((v["FETCH_SIZE"] + v["WRITE_SIZE"]) / alg, 3)}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(p, target_s: float = 12.0):
     import mxinputs as mi
     import oracle
     threads = oracle.default_threads()
-    rows, cols = mi.sample_points(p.M, p.N, 256, seed=99, edge=1)
+    rows, cols = mi.sample_points(p.M, p.N, 8192, seed=99, edge=1)
     t0 = time.perf_counter()
     oracle.gemm_points(p.A, p.As, p.fmtA, p.B, p.Bs, p.fmtB, p.M, p.N, p.K, rows, cols,
                        nthreads=threads)
@@ -150,12 +248,22 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--traffic", action="store_true",
+                    help="only launch the counter-pass workload (under rocprofv3 --pmc)")
+    ap.add_argument("--traffic-report", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two counter passes")
     args = ap.parse_args()
+    if args.traffic_report:
+        traffic_report(*args.traffic_report)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the GEMM "
               "would shard by C columns with no exchange, which is not built here.",
               file=sys.stderr)
         sys.exit(2)
+    if args.traffic:
+        traffic_launches()
+        return
 
     import torch
     import level_dsl_amd as L
@@ -171,7 +279,7 @@ def main():
     log(f"bench: {p.name} generated")
     flops = mi.algorithmic_flops(p.M, p.N, p.K)
     steps, warmup = args.steps, args.warmup
-    wall, mean_s, med_s, min_s = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE, steps, warmup, 3)
+    wall, mean_s = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE, steps, warmup, 3)
     value = flops * steps / wall / 1e12
     achieved = flops / mean_s / 1e12
     log(f"bench: large exact {value:.1f} TFLOP/s whole-job, {achieved:.1f} per launch "
@@ -189,13 +297,12 @@ def main():
         "pct_of_mxfp8_peak": round(100 * value / PEAK_TFLOPS["fp8"], 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": traffic, "kernel": "mxg::large::kernel<0,0,false>",
-                     "launch_mean_us": round(mean_s * 1e6, 2),
-                     "launch_median_us": round(med_s * 1e6, 2)},
+                     "traffic": traffic, "kernel": "mxg::large::kernel<0,0,false,true>",
+                     "launch_mean_us": round(mean_s * 1e6, 2)},
     })
 
     # ---- native scaled-MFMA variant on the same workload ----------------------
-    wall_n, mean_n, med_n, _ = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE_NATIVE, steps, warmup, 3)
+    wall_n, mean_n = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE_NATIVE, steps, warmup, 3)
     out["native_scaled_mfma"] = {
         "value": round(flops * steps / wall_n / 1e12, 2), "unit": "TFLOP/s",
         "achieved_per_launch": round(flops / mean_n / 1e12, 2), "peak": PEAK_TFLOPS["fp8"],
@@ -211,7 +318,7 @@ def main():
     log(f"bench: {ps.name} generated")
     sbytes = mi.algorithmic_bytes(ps.M, ps.N, ps.K, ps.out_dtype)
     sk_steps = max(steps, 30)
-    wall_s, mean_ss, med_ss, _ = bench_gemm(gemm, ps, L.MXGEMM_VARIANT_SKINNY, sk_steps, warmup, 3)
+    wall_s, mean_ss = bench_gemm(gemm, ps, L.MXGEMM_VARIANT_SKINNY, sk_steps, warmup, 3)
     out["skinny_m64"] = {
         "workload": ps.name, "value": round(sbytes * sk_steps / wall_s / 1e9, 1), "unit": "GB/s",
         "pct_of_hbm_peak": round(100 * sbytes * sk_steps / wall_s / 1e9 / PEAK_HBM_GBS, 2),
