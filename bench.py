@@ -51,10 +51,16 @@ KERNEL_SOURCES = ["level_dsl_amd/csrc/mxgemm.hip", "level_dsl_amd/csrc/mxgemm_co
 
 
 def kernel_hash() -> str:
+    """Hash of the kernel and launch sources with comments and blank space
+    removed (a comment edit does not invalidate stored counter readings)."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -93,6 +93,7 @@ enum {
 #define MXGEMM_MAX_M ((int64_t)1 << 30)
 #define MXGEMM_MAX_N ((int64_t)1 << 20)
 #define MXGEMM_MAX_K ((int64_t)1 << 21)
+#define MXGEMM_MAX_MN ((int64_t)1 << 36) /* M * N: C up to 256 GiB of fp32 */
 
 /* Library ABI version (this header: 1). */
 int mxgemm_version(void);
@@ -116,7 +117,8 @@ int mxgemm_set_variant(mxgemm_t h, int variant);
 
 /* Check the arguments of mxgemm_run without touching the GPU: pointers
  * non-NULL, formats, out_dtype, use_acc in {0,1}, 1 <= M <= MXGEMM_MAX_M,
- * 1 <= N <= MXGEMM_MAX_N, 32 <= K <= MXGEMM_MAX_K with K % 32 == 0,
+ * 1 <= N <= MXGEMM_MAX_N, M * N <= MXGEMM_MAX_MN, 32 <= K <= MXGEMM_MAX_K
+ * with K % 32 == 0,
  * A, B, C 16-byte aligned, and C not overlapping A, B or the scales
  * (byte ranges A[M*K], B[N*K], A_scale[M*K/32], B_scale[N*K/32],
  * C[M*N*sizeof(out)]).  Scales need no alignment. */

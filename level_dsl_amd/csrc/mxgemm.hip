@@ -173,7 +173,7 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const 
         (use_acc != 0 && use_acc != 1))
         return MXGEMM_ERR_DTYPE;
     if (M < 1 || N < 1 || K < 32 || M > MXGEMM_MAX_M || N > MXGEMM_MAX_N || K > MXGEMM_MAX_K ||
-        (K % 32) != 0)
+        (K % 32) != 0 || M * N > MXGEMM_MAX_MN)
         return MXGEMM_ERR_SHAPE;
     if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15u) return MXGEMM_ERR_ALIGN;
     const uint64_t csize = (uint64_t)M * (uint64_t)N * (out_dtype == MXGEMM_OUT_F32 ? 4u : 2u);

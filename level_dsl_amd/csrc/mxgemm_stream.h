@@ -22,11 +22,11 @@
 //     loaded HBM latency); it decodes its codes with their block scales to bf16
 //     (v_cvt_scalef32_pk_bf16_fp8/bf8) and runs sixteen 16x16x32 bf16 MFMAs
 //     per stage against A;
-//   * two producer waves fetch the A tile (at most 64 rows x 128 bytes per
-//     stage, from L2) seven stages ahead with direct-to-LDS loads into an
-//     eight-slot fp8 ring, decodes it once for the whole workgroup into bf16
-//     with its scales folded in, and writes it to a two-slot LDS ring; a
-//     barrier per stage publishes the slot;
+//   * two producer waves (32 rows each) fetch the A tile (at most 64 rows x
+//     128 bytes per stage, from L2) seven stages ahead with direct-to-LDS
+//     loads into an eight-slot fp8 ring, decode it once for the whole
+//     workgroup into bf16 with its scales folded in, and write it to a
+//     two-slot LDS ring; a barrier per stage publishes the slot;
 //   * the scale dwords of A and of this workgroup's B rows for 64 stages at a
 //     time are loaded by all waves into LDS at the start of each 64-stage
 //     chunk (for K <= 8192, once), instead of a scattered load per row and

@@ -60,6 +60,7 @@ def v(**kw):
     ({"M": 0}, "MXGEMM_ERR_SHAPE"), ({"N": -3}, "MXGEMM_ERR_SHAPE"), ({"K": 0}, "MXGEMM_ERR_SHAPE"),
     ({"K": 48}, "MXGEMM_ERR_SHAPE"), ({"K": 16}, "MXGEMM_ERR_SHAPE"),
     ({"N": (1 << 20) + 1}, "MXGEMM_ERR_SHAPE"), ({"K": (1 << 21) + 32}, "MXGEMM_ERR_SHAPE"),
+    ({"M": (1 << 30) + 1}, "MXGEMM_ERR_SHAPE"), ({"M": 1 << 20, "N": 1 << 17}, "MXGEMM_ERR_SHAPE"),
     ({"A": A + 8}, "MXGEMM_ERR_ALIGN"), ({"C": C + 4}, "MXGEMM_ERR_ALIGN"),
     ({"B": B + 1}, "MXGEMM_ERR_ALIGN"),
     ({"C": A + 16}, "MXGEMM_ERR_ALIAS"), ({"C": 0x40000 - 64 * 64 * 4 + 16}, "MXGEMM_ERR_ALIAS"),
