@@ -11,8 +11,9 @@
 //     contiguous 1 KiB LDS segment (8 tile rows), lane i writing bytes
 //     16i..16i+15; the swizzle is applied by choosing which global chunk each
 //     lane fetches.  K and row tails read as zero through the descriptor's
-//     range check.  Loads for stage kt+2 are issued right after the barrier
-//     that retires stage kt's buffer, one stage before they are needed.
+//     range check.  Stage kt+2's A tile is loaded right after the barrier
+//     that retires stage kt's buffer and its B tile one block later, about
+//     one stage before they are needed.
 //   * scales: with K % 512 == 0, each lane fetches 16 scale bytes of each of
 //     its 8 fragment rows at a time (four stages' worth, one dwordx4 load per
 //     row, prefetched a window ahead); otherwise one dword (or four bytes) per
@@ -136,20 +137,26 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int nk = (K + BK - 1) / BK;
 
     // ---- global -> LDS, one stage ---------------------------------------
+    // A stage's two operands are loaded at different points of the K loop
+    // (A right after the barrier that frees the buffer, B one block later),
+    // so that a wave never issues all of its loads in one burst: a burst of
+    // 64 loads per CU backs up the address path and stalls the in-order MFMA
+    // stream behind it.
     // segment s = SEGS_PER_WAVE*wave + j holds tile rows 8s..8s+7; lane i
     // writes row 8s + i/8 at chunk position i%8, i.e. global chunk
     // (i%8) ^ swz(row) = (i%8) ^ (i/8) ^ (s & 1).  Stages past the end of K
     // read as zero (every offset is out of range), so the call needs no guard.
     const int gc0 = (lane & 7) ^ (lane >> 3);  // chunk for even segments; odd: gc0 ^ 1
     const uint32_t grow = (uint32_t)(8 * SEGS_PER_WAVE * wave + (lane >> 3)) * K;
-    auto gload = [&](int st, int k0) MXG_INLINE {
+    // operand OP (0: A, 1: B) of the stage starting at K offset k0 into LDS stage st
+    auto gload = [&](int st, int k0, auto OP) MXG_INLINE {
+        constexpr int op = decltype(OP)::value;
 #pragma unroll
         for (int j = 0; j < SEGS_PER_WAVE; ++j) {
             const int s = SEGS_PER_WAVE * wave + j;
             const int c = gc0 ^ (j & 1);
             const uint32_t off = k0 + 16 * c < K ? grow + (uint32_t)(8 * j) * K + 16 * c + k0 : kOob;
-            load16_lds(rA, &lds[st][0][s * SEG], off);
-            load16_lds(rB, &lds[st][1][s * SEG], off);
+            load16_lds(op == 0 ? rA : rB, &lds[st][op][s * SEG], off);
         }
     };
 
@@ -252,12 +259,12 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     };
 
     // Interleave for the block that crosses into the next stage (after its
-    // barrier): the next stage's first LDS reads, then the 2*SEGS_PER_WAVE
-    // direct-to-LDS loads of stage kt+2 spread over the remaining MFMAs,
-    // then the decode.
+    // barrier): the next stage's first LDS reads, then the SEGS_PER_WAVE
+    // direct-to-LDS loads of stage kt+2's A tile spread over the remaining
+    // MFMAs, then the decode.
     auto sched_cross = [&]() MXG_INLINE {
         constexpr int rest = MF - MF / 4;  // MFMAs after the barrier
-        constexpr int nld = 2 * SEGS_PER_WAVE;
+        constexpr int nld = SEGS_PER_WAVE;
         __builtin_amdgcn_sched_group_barrier(SG_DS_RD, NATIVE ? 4 : SUB_M + SUB_N, 0);
         static_for<(nld < rest ? nld : rest)>([&](auto) MXG_INLINE {
             __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
@@ -296,6 +303,29 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         }
     };
 
+    // Block 0 of a stage also issues the SEGS_PER_WAVE loads of the next
+    // stage's B tile, one per MFMA after the LDS reads' head start.
+    auto sched_block_ld = [&]() MXG_INLINE {
+        __builtin_amdgcn_sched_group_barrier(SG_DS_RD, NATIVE ? 4 : SUB_M + SUB_N, 0);
+        if constexpr (!NATIVE) __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+        static_for<SEGS_PER_WAVE>([&](auto) MXG_INLINE {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_SALU, 2, 0);
+            if constexpr (NATIVE)
+                __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+            else
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        });
+        static_for<MF - (NATIVE ? 0 : 4) - SEGS_PER_WAVE>([&](auto) MXG_INLINE {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            if constexpr (NATIVE)
+                __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+            else
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        });
+    };
+
     Raw<NATIVE> raw;
     Frags<NATIVE> f0, f1;
     uint32_t csa[SUB_M], csb[SUB_N];  // scale dwords of the stage being decoded
@@ -324,9 +354,14 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             Frags<NATIVE> &nxt = (blk & 1) ? f0 : f1;
             if constexpr (blk + 1 < BLOCKS) {
                 read_block(st, blk + 1, raw, nxt);
+                // B tile of stage kt+1 (its buffer was freed at the last barrier)
+                if constexpr (blk == 0) gload(st ^ 1, (kt + 1) * BK, int_c<1>{});
                 mfma_range(BLK, int_c<0>{}, int_c<MF>{}, cur, ksa, ksb);
                 prep_block(int_c<blk + 1>{}, raw, csa, csb, nxt);
-                sched_block();
+                if constexpr (blk == 0)
+                    sched_block_ld();
+                else
+                    sched_block();
                 __builtin_amdgcn_sched_barrier(0);
             } else if constexpr (cross) {
                 // MFMAs that keep the matrix pipe busy across the barrier
@@ -336,7 +371,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                 wait_vmem();
                 __syncthreads();
                 read_block(st ^ 1, 0, raw, nxt);
-                gload(st, (kt + 2) * BK);
+                gload(st, (kt + 2) * BK, int_c<0>{});  // A tile of stage kt+2
                 // scale dwords of stage kt+1
                 if constexpr (SCALE16) {
                     if constexpr (ss == WINDOW - 1) {
@@ -368,7 +403,8 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     };
 
     // ---- prologue ---------------------------------------------------------
-    gload(0, 0);
+    gload(0, 0, int_c<0>{});
+    gload(0, 0, int_c<1>{});
     if constexpr (SCALE16) {
         scale16(0, wa, wb);
     } else {
@@ -376,7 +412,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     }
     wait_vmem();
     __syncthreads();
-    gload(1, BK);
+    gload(1, BK, int_c<0>{});  // stage 1's B tile follows in stage 0's first block
     if constexpr (SCALE16) {
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) csa[i] = (uint32_t)wa[i][0];

@@ -57,12 +57,19 @@ constexpr int A_SLOT = MAX_M * AROW;     // 16 KiB
 constexpr int SCH = 64;                  // stages whose scale dwords sit in LDS at a time
 constexpr int SROWS = MAX_M + BN;        // scale rows: A rows 0..63, then the B rows
 
-// workgroup barrier that orders LDS only (outstanding global loads stay in flight)
+// Workgroup barrier that orders LDS only: this wave's LDS reads and writes
+// complete (lgkmcnt(0)), then s_barrier; the signal fences keep the compiler
+// from moving LDS accesses across it.  Outstanding global loads stay in
+// flight, including the producers' loads that write LDS directly: an LDS
+// memory fence would wait for those too (vmcnt(0)) and drain the producers'
+// prefetch every stage.  Each producer wave reads back only the rows its own
+// direct loads wrote, after waiting for them with vmcnt.
 __device__ __forceinline__ void lds_barrier()
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // bf16 A rows in LDS: 16 chunks of 16 bytes, chunk c of row r at position
