@@ -55,6 +55,8 @@ constexpr int A8 = MAX_M * BK;           // bytes of one fp8 A stage (8 KiB)
 constexpr int AROW = 2 * BK;             // bytes of one decoded (bf16) A row per stage
 constexpr int A_SLOT = MAX_M * AROW;     // 16 KiB
 constexpr int SCH = 64;                  // stages whose scale dwords sit in LDS at a time
+constexpr int SPITCH = SCH + 1;          // LDS row pitch of the scale table (dwords): rows of one
+                                         // column fall in different banks
 constexpr int SROWS = MAX_M + BN;        // scale rows: A rows 0..63, then the B rows
 
 // Workgroup barrier that orders LDS only: this wave's LDS reads and writes
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t a8_lds[ADEPTH][A8];   // raw A, row-major
     __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][A_SLOT];       // decoded A (bf16)
-    __shared__ __attribute__((aligned(16))) uint32_t s_lds[SROWS][SCH];     // scale dwords
+    __shared__ __attribute__((aligned(16))) uint32_t s_lds[SROWS][SPITCH];  // scale dwords
 
     const int n0 = blockIdx.x * BN;
     const int rows_b = min(BN, p.N - n0);
