@@ -277,3 +277,59 @@ def test_workload_skinny_m64_sampled(gemm):
 
 def test_workload_16384cube_acc_sampled(gemm):
     _workload_check(gemm, 4, full=False)
+
+
+# ------------------------------------------------------------- edge cases --
+
+EDGE_CASES = [
+    # M, N, K, fmtA, fmtB, out, use_acc
+    (37, 250, 20576, 0, 0, mi.OUT_F32, False),   # 161 K stages: three scale chunks, a ragged last stage
+    (64, 224, 16384, 1, 1, mi.OUT_BF16, True),   # two full scale chunks, e5m2 x e5m2, bf16 accumulate
+    (96, 130, 9248, 0, 1, mi.OUT_F32, False),    # K % 128 == 32: per-byte scale path of the large kernel
+    (2, 3, 1 << 21, 0, 0, mi.OUT_F32, False),    # the largest K (16384 stages)
+    (3, 1 << 20, 64, 0, 0, mi.OUT_F32, False),   # the largest N (9363 small-M workgroups)
+    (70000, 40, 64, 1, 0, mi.OUT_BF16, False),   # many row tiles, ragged last tile
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: "x".join(map(str, c[:3])))
+def test_edge_full(gemm, case):
+    M, N, K, fa, fb, out, acc = case
+    p = mi.random_problem(M, N, K, seed=(M * 7 + N * 3 + K) % 100003, fmtA=fa, fmtB=fb,
+                          out_dtype=out, use_acc=acc)
+    ref = oracle_full(p)
+    dev = to_dev(p)
+    for v in _variants_for(M):
+        log(f"edge {case} variant={VNAME[v]}")
+        got = run(gemm, p, v, guard=64, dev_inputs=dev)
+        compare(got, ref, out, f"edge {case} variant {VNAME[v]}")
+
+
+def test_invalid_call_launches_nothing(gemm):
+    """Every rejected call returns its status and leaves C untouched."""
+    p = mi.random_problem(64, 64, 128, seed=5)
+    A, As, B, Bs = to_dev(p)
+    buf, c = alloc_c(p)  # NaN-filled
+    h = gemm.h
+    bad = [
+        (dict(M=0), "MXGEMM_ERR_SHAPE"), (dict(K=48), "MXGEMM_ERR_SHAPE"),
+        (dict(fmtA=3), "MXGEMM_ERR_FMT"), (dict(out_dtype=7), "MXGEMM_ERR_DTYPE"),
+        (dict(C=c.data_ptr() + 4), "MXGEMM_ERR_ALIGN"), (dict(C=A.data_ptr()), "MXGEMM_ERR_ALIAS"),
+    ]
+    for kw, status in bad:
+        args = dict(A=A, A_scale=As, fmtA=0, B=B, B_scale=Bs, fmtB=0, C=c, M=64, N=64, K=128,
+                    use_acc=0, out_dtype=0)
+        args.update(kw)
+        with pytest.raises(L.MxgemmError) as e:
+            L.mxgemm_run(h, **args)
+        assert e.value.code == L.STATUS_CODE[status], kw
+    q = mi.random_problem(65, 8, 32, seed=6)
+    qA, qAs, qB, qBs = to_dev(q)
+    qbuf, qc = alloc_c(q)
+    gemm.set_variant(SKINNY)
+    with pytest.raises(L.MxgemmError) as e:  # a forced small-M variant with M > 64
+        L.mxgemm_run(h, qA, qAs, 0, qB, qBs, 0, qc, 65, 8, 32, 0, 0)
+    assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_VARIANT"]
+    gemm.set_variant(AUTO)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(buf).all()) and bool(torch.isnan(qbuf).all()), "a rejected call wrote C"
