@@ -2,7 +2,7 @@
 //
 // With M <= 64 the multiply is bound by reading B once from HBM (about 120
 // flop per byte at M = 64, far below the chip's MFMA-to-HBM balance).  The
-// kernel streams B with as little else in its way as possible, using two
+// kernel streams B with as little else in its way as possible, using four
 // producer waves and seven consumer waves per workgroup (the producer /
 // consumer split of warp specialization on the TLX warp-specialization page,
 // with one workgroup barrier per stage standing in for the full/empty
@@ -22,7 +22,8 @@
 //     loaded HBM latency); it decodes its codes with their block scales to bf16
 //     (v_cvt_scalef32_pk_bf16_fp8/bf8) and runs sixteen 16x16x32 bf16 MFMAs
 //     per stage against A;
-//   * two producer waves (32 rows each) fetch the A tile (at most 64 rows x
+//   * four producer waves (16 rows each, so that every SIMD carries a
+//     similar share of the decode) fetch the A tile (at most 64 rows x
 //     128 bytes per stage, from L2) seven stages ahead with direct-to-LDS
 //     loads into an eight-slot fp8 ring, decode it once for the whole
 //     workgroup into bf16 with its scales folded in, and write it to a
@@ -45,7 +46,7 @@ constexpr int MAX_M = 64;
 constexpr int BN = 112;
 constexpr int BK = 128;
 constexpr int CONSUMERS = 7;
-constexpr int PRODUCERS = 2;             // each decodes 32 rows of A per stage
+constexpr int PRODUCERS = 4;             // each decodes 16 rows of A per stage
 constexpr int WAVES = CONSUMERS + PRODUCERS;
 constexpr int PROWS = MAX_M / PRODUCERS;
 constexpr int THREADS = 64 * WAVES;
