@@ -53,6 +53,8 @@ def _bind(lib):
                                       i64, i64, i64, vp, vp, i64,
                                       vp, vp, vp, vp, i32]
     lib.mxref_gemm_points.restype = i32
+    lib.mxref_quantize.argtypes = [vp, i32, i64, i64, i32, vp, vp]
+    lib.mxref_quantize.restype = i32
     return lib
 
 
@@ -149,3 +151,28 @@ def gemm_full(A, As, fmtA, B, Bs, fmtB, M, N, K, cin=None, nthreads=None, lib=No
     r = gemm_points(A, As, fmtA, B, Bs, fmtB, M, N, K, mm.ravel(), nn.ravel(),
                     cin=cin, nthreads=nthreads, lib=lib)
     return {k: v.reshape(M, N) for k, v in r.items()}
+
+
+def quantize(X, fmt, lib=None):
+    """MX block quantization of an (R, K) matrix: X float32, or uint16 bf16
+    bit patterns.  Returns (codes (R, K) uint8, scales (R, ceil(K/32)) uint8).
+    Raises ValueError for non-finite input (the recipe covers finite values)."""
+    lib = lib or load()
+    X = np.ascontiguousarray(X)
+    if X.ndim != 2:
+        raise ValueError("X must be 2-D")
+    if X.dtype == np.float32:
+        x_dtype = 0
+    elif X.dtype == np.uint16:
+        x_dtype = 1
+    else:
+        raise TypeError("X must be float32 or uint16 (bf16 bits)")
+    R, K = X.shape
+    codes = np.empty((R, K), np.uint8)
+    scales = np.empty((R, (K + 31) // 32), np.uint8)
+    rc = lib.mxref_quantize(_ptr(X), x_dtype, int(R), int(K), int(fmt), _ptr(codes), _ptr(scales))
+    if rc == -2:
+        raise ValueError("non-finite input")
+    if rc != 0:
+        raise ValueError(f"mxref_quantize rejected its arguments (rc={rc})")
+    return codes, scales

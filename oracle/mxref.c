@@ -249,3 +249,96 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *As, int fmtA,
     }
     return 0;
 }
+
+/* ---- MX block quantization ------------------------------------------------ */
+/*
+ * The step that produces the multiply's operands: each row of X is cut into
+ * blocks of 32 consecutive K-elements (the last block may be shorter), and
+ * every block gets one e8m0 scale byte and 32 codes (the uint8 scale tile
+ * whose K extent is BLOCK_K // 32, TLX async-compute page, "TMEM-backed MX
+ * Scales").  The pages do not say how the scale is chosen; the reading taken
+ * here is the recipe that makes the block's largest magnitude fit the
+ * format: with MAX the format's largest finite value (448 for e4m3, 57344
+ * for e5m2),
+ *   e     = the smallest integer with max|x| <= MAX * 2^e
+ *           (an all-zero block takes the smallest scale),
+ *   scale = e + 127, clamped to 0..254,
+ *   code  = x * 2^(127 - scale) rounded to the nearest value of the format,
+ *           ties to the code whose mantissa field is even (round to nearest
+ *           even), saturating at +-MAX; the sign is kept (-0 gives 0x80).
+ * Written from that definition: the exponent by exact comparisons with
+ * ldexp, the rounding by exhaustive search over the format's codes.
+ */
+static double fmt_max(int fmt) { return fmt == MXREF_FMT_E4M3 ? 448.0 : 57344.0; }
+
+/* Nearest code of `fmt` to v, ties to an even mantissa field (the lowest
+ * bit of the code), largest finite magnitude if |v| exceeds it. */
+static uint8_t nearest_code(int fmt, double v)
+{
+    const double *t = table(fmt);
+    const double a = fabs(v);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < 128; ++c) {
+        if (!isfinite(t[c]))
+            continue;
+        const double d = fabs(t[c] - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+/* Smallest integer e with amax <= MAX * 2^e, for finite amax > 0. */
+static int block_exponent(int fmt, double amax)
+{
+    const double mx = fmt_max(fmt);
+    int e = (int)floor(log2(amax / mx));
+    while (amax > ldexp(mx, e))
+        ++e;
+    while (amax <= ldexp(mx, e - 1))
+        --e;
+    return e;
+}
+
+/*
+ * Quantize the R x K matrix X (row-major; x_dtype 0: fp32, 1: bf16 bit
+ * patterns) to codes (R x K) and scales (R x ceil(K/32)) of format fmt
+ * (0 e4m3, 1 e5m2).  Returns 0; -1 on bad arguments; -2 if X holds a NaN or
+ * an infinity (the recipe is defined for finite inputs only).
+ */
+int mxref_quantize(const void *X, int x_dtype, int64_t R, int64_t K, int fmt, uint8_t *codes,
+                   uint8_t *scales)
+{
+    if (!X || !codes || !scales || R < 1 || K < 1 || (x_dtype != 0 && x_dtype != 1) ||
+        (fmt != MXREF_FMT_E4M3 && fmt != MXREF_FMT_E5M2))
+        return -1;
+    const int64_t KB = (K + 31) / 32;
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < KB; ++b) {
+            const int64_t k0 = 32 * b, k1 = k0 + 32 < K ? k0 + 32 : K;
+            double x[32];
+            double amax = 0.0;
+            for (int64_t k = k0; k < k1; ++k) {
+                const int64_t i = r * K + k;
+                x[k - k0] = x_dtype == 0 ? (double)((const float *)X)[i]
+                                         : bf16_to_double(((const uint16_t *)X)[i]);
+                if (!isfinite(x[k - k0]))
+                    return -2;
+                if (fabs(x[k - k0]) > amax)
+                    amax = fabs(x[k - k0]);
+            }
+            int s = 0;
+            if (amax > 0.0) {
+                s = block_exponent(fmt, amax) + 127;
+                s = s < 0 ? 0 : (s > 254 ? 254 : s);
+            }
+            scales[r * KB + b] = (uint8_t)s;
+            for (int64_t k = k0; k < k1; ++k)
+                codes[r * K + k] = nearest_code(fmt, ldexp(x[k - k0], 127 - s));
+        }
+    }
+    return 0;
+}

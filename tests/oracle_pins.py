@@ -13,7 +13,11 @@ the oracle disagrees with:
 What is pinned is the definition of the scaled dot given as async_dot_scaled
 in the TLX API Quick Reference ("Matrix Multiply (MMA)": D = (A*scale_A) @
 (B*scale_B) + D) with one uint8 scale per 32 K-elements (TLX async-compute
-page, "TMEM-backed MX Scales", K extent BLOCK_K // 32).
+page, "TMEM-backed MX Scales", K extent BLOCK_K // 32), and the block
+quantization that produces such operands (the ``pin_quant_*`` functions:
+torch's round-to-nearest-even float8 casts, the block exponent's defining
+inequality evaluated directly, power-of-two invariance, and the input
+generator's own torch-based quantizer).
 """
 from __future__ import annotations
 
@@ -365,7 +369,127 @@ def pin_scale_tile_extent(lib):
             assert np.all(r["sum"][0] == 32.0)
 
 
+# ------------------------------------------------------- block quantization --
+
+QMAX = {0: 448.0, 1: 57344.0}
+
+
+def _quant_probe_values(fmt: int, n: int, seed: int) -> np.ndarray:
+    """Values with |v| <= MAX: log-uniform magnitudes down into the
+    subnormal range, exact midpoints between neighbouring codes (ties), the
+    fp32 neighbours of those midpoints, zeros of both signs."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    mx = QMAX[fmt]
+    mag = np.exp2(g.uniform(-22.0, np.log2(mx), n)).astype(np.float32)
+    sgn = np.where(g.random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+    tab = torch_decode(fmt)[:128]
+    fin = np.sort(tab[np.isfinite(tab)])
+    mids = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)       # exact in fp32
+    up = np.nextafter(mids, np.float32(np.inf)).astype(np.float32)
+    dn = np.nextafter(mids, np.float32(0)).astype(np.float32)
+    extra = np.concatenate([mids, -mids, up, -up, dn, -dn, fin.astype(np.float32),
+                            -fin.astype(np.float32), np.float32([0.0, -0.0])])
+    return np.concatenate([mag * sgn, extra]).astype(np.float32)
+
+
+def pin_quant_rne_vs_torch(lib):
+    """Blocks whose largest magnitude is exactly MAX get scale 127 (2^0), so
+    each code must be torch's RNE float8 cast of the value itself."""
+    for fmt in (0, 1):
+        v = _quant_probe_values(fmt, 20000, seed=11 + fmt)
+        nb = (v.size + 30) // 31
+        v = np.concatenate([v, np.zeros(nb * 31 - v.size, np.float32)])
+        X = np.empty((nb, 32), np.float32)
+        X[:, 0] = np.where(np.arange(nb) % 2 == 0, QMAX[fmt], -QMAX[fmt])
+        X[:, 1:] = v.reshape(nb, 31)
+        codes, scales = oracle.quantize(X, fmt, lib=lib)
+        assert np.all(scales == 127), "scale of a block whose max is MAX"
+        want = torch.from_numpy(X).to(_TORCH[fmt]).view(torch.uint8).numpy()
+        assert np.array_equal(codes, want), f"{np.sum(codes != want)} codes differ from torch ({fmt})"
+
+
+def pin_quant_block_exponent(lib):
+    """scale byte b satisfies the definition: amax <= MAX*2^(b-127), and b is
+    0 or amax > MAX*2^(b-128) (the smallest such e), over the whole fp32
+    range including subnormals; an all-zero block has b = 0."""
+    g = np.random.Generator(np.random.PCG64(21))
+    for fmt in (0, 1):
+        rows = 4000
+        amax = np.exp2(g.uniform(-148.0, 127.9, rows)).astype(np.float32)
+        amax[:8] = np.float32([0.0, 2.0**-149, QMAX[fmt], np.nextafter(np.float32(QMAX[fmt]), 0),
+                               np.nextafter(np.float32(QMAX[fmt]), np.float32(1e9)), 1.0,
+                               3.4e38, 2.0**-126])
+        X = (g.uniform(-1, 1, (rows, 32)).astype(np.float32) * amax[:, None]).astype(np.float32)
+        X[np.arange(rows), g.integers(0, 32, rows)] = amax * np.where(g.random(rows) < 0.5, -1, 1)
+        codes, scales = oracle.quantize(X, fmt, lib=lib)
+        am = np.abs(X.astype(np.float64)).max(axis=1)
+        for r in range(rows):
+            b = int(scales[r, 0])
+            if am[r] == 0.0:
+                assert b == 0
+                continue
+            assert am[r] <= math.ldexp(QMAX[fmt], b - 127), (fmt, am[r], b)
+            assert b == 0 or am[r] > math.ldexp(QMAX[fmt], b - 128), (fmt, am[r], b)
+
+
+def pin_quant_scale_invariance(lib):
+    """X * 2^j (exact in fp32, no clamping) gives the same codes and every
+    scale byte raised by j."""
+    g = np.random.Generator(np.random.PCG64(31))
+    X = (g.standard_normal((64, 256)) * np.exp2(g.integers(-6, 7, (64, 1)))).astype(np.float32)
+    for fmt in (0, 1):
+        c0, s0 = oracle.quantize(X, fmt, lib=lib)
+        for j in (-9, 1, 13):
+            c1, s1 = oracle.quantize((X * np.float32(2.0**j)).astype(np.float32), fmt, lib=lib)
+            assert np.array_equal(c1, c0) and np.array_equal(s1.astype(int), s0.astype(int) + j)
+
+
+def pin_quant_matches_generator(lib):
+    """The input generator's quantizer (clamp + torch cast) on the skinny
+    workload's recipe agrees with the oracle."""
+    g = np.random.Generator(np.random.PCG64(41))
+    for fmt in (0, 1):
+        raw = (g.standard_normal((48, 1024)) * 0.02).astype(np.float32)
+        want_c, want_s = mxinputs.mx_block_quantize(raw, fmt)
+        codes, scales = oracle.quantize(raw, fmt, lib=lib)
+        assert np.array_equal(scales, want_s) and np.array_equal(codes, want_c)
+
+
+def pin_quant_bf16_input(lib):
+    """bf16 input quantizes exactly as its fp32 widening."""
+    g = np.random.Generator(np.random.PCG64(51))
+    X = (g.standard_normal((16, 160)) * 3.0).astype(np.float32)
+    bits = torch.from_numpy(X).to(torch.bfloat16).view(torch.uint16).numpy()
+    wide = (bits.astype(np.uint32) << 16).view(np.float32)
+    for fmt in (0, 1):
+        a = oracle.quantize(bits, fmt, lib=lib)
+        b = oracle.quantize(wide, fmt, lib=lib)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def pin_quant_ragged_and_nonfinite(lib):
+    """A last block shorter than 32 is quantized on its own; a NaN or an
+    infinity is rejected."""
+    g = np.random.Generator(np.random.PCG64(61))
+    X = g.standard_normal((5, 72)).astype(np.float32)
+    X[:, 64:] *= np.float32(100.0)
+    codes, scales = oracle.quantize(X, 0, lib=lib)
+    tail_c, tail_s = oracle.quantize(np.ascontiguousarray(X[:, 64:]), 0, lib=lib)
+    assert scales.shape == (5, 3)
+    assert np.array_equal(codes[:, 64:], tail_c) and np.array_equal(scales[:, 2:], tail_s)
+    for bad in (np.nan, np.inf):
+        Y = X.copy()
+        Y[2, 5] = bad
+        try:
+            oracle.quantize(Y, 0, lib=lib)
+        except ValueError:
+            continue
+        raise AssertionError("non-finite input accepted")
+
+
 ALL_PINS = [pin_tables_match_torch, pin_spot_values, pin_special_counts, pin_bf16_rne,
             pin_bruteforce_fraction, pin_pairwise_products, pin_closed_form,
             pin_integer_gemm, pin_scale_doubling, pin_permutation, pin_numpy_matmul,
-            pin_nan_propagation, pin_thread_independence, pin_scale_tile_extent]
+            pin_nan_propagation, pin_thread_independence, pin_scale_tile_extent,
+            pin_quant_rne_vs_torch, pin_quant_block_exponent, pin_quant_scale_invariance,
+            pin_quant_matches_generator, pin_quant_bf16_input, pin_quant_ragged_and_nonfinite]

@@ -32,6 +32,12 @@ MUTANTS = {
     "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u;"),
     "last_k_dropped": ("for (int64_t k = 0; k < j->K; ++k)", "for (int64_t k = 0; k + 1 < j->K; ++k)"),
     "mag_signed": ("mag += fabs(prod);", "mag += prod;"),
+    "quant_ties_to_odd": ("(d == bd && (c & 1) == 0)", "(d == bd && (c & 1) == 1)"),
+    "quant_exponent_plus_one": ("s = block_exponent(fmt, amax) + 127;", "s = block_exponent(fmt, amax) + 128;"),
+    "quant_sign_dropped": ("(signbit(v) ? 0x80 : 0)", "0"),
+    "quant_scale_inverted": ("ldexp(x[k - k0], 127 - s)", "ldexp(x[k - k0], s - 127)"),
+    "quant_e4m3_max_480": ("return fmt == MXREF_FMT_E4M3 ? 448.0", "return fmt == MXREF_FMT_E4M3 ? 480.0"),
+    "quant_zero_block_scale": ("int s = 0;\n            if (amax > 0.0) {", "int s = 127;\n            if (amax > 0.0) {"),
 }
 
 
