@@ -54,6 +54,9 @@ enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
  * fp32 accumulator */
 enum { MXGEMM_OUT_F32 = 0, MXGEMM_OUT_BF16 = 1 };
 
+/* input types of mxgemm_quantize */
+enum { MXGEMM_X_F32 = 0, MXGEMM_X_BF16 = 1 };
+
 /* kernel variants (mxgemm_set_variant).
  *
  * Exact variants (AUTO, LARGE, SKINNY) decode every code with its block
@@ -94,6 +97,7 @@ enum {
 #define MXGEMM_MAX_N ((int64_t)1 << 20)
 #define MXGEMM_MAX_K ((int64_t)1 << 21)
 #define MXGEMM_MAX_MN ((int64_t)1 << 36) /* M * N: C up to 256 GiB of fp32 */
+#define MXGEMM_MAX_QELEMS ((int64_t)1 << 38) /* R * K of one mxgemm_quantize call */
 
 /* Library ABI version (this header: 1). */
 int mxgemm_version(void);
@@ -139,6 +143,34 @@ int mxgemm_run(mxgemm_t h,
                const void *B, const uint8_t *B_scale, int fmtB,
                void *C, int64_t M, int64_t N, int64_t K,
                int use_acc, int out_dtype, hipStream_t stream);
+
+/* MX block quantization: the step that produces the multiply's operands.
+ * X is R x K, row-major, fp32 or bf16 (x_dtype MXGEMM_X_*); each row is cut
+ * into blocks of 32 consecutive elements, one e8m0 scale byte per block
+ * (the uint8 scale tile of K extent BLOCK_K // 32, TLX async-compute page,
+ * "TMEM-backed MX Scales"), laid out like the operands of mxgemm_run:
+ *   codes   R x K bytes, row-major (an A operand, or B stored K-contiguous);
+ *   scales  R x (K/32) bytes, row-major.
+ * The scale rule (a reading; the pages do not fix it): with MAX = 448
+ * (e4m3) or 57344 (e5m2), e is the smallest integer with
+ * max|x| <= MAX * 2^e over the block (an all-zero block takes the smallest
+ * scale), the scale byte is e + 127 clamped to 0..254, and each code is
+ * x * 2^(127 - scale byte) rounded to the nearest value of the format, ties
+ * to even, -0 kept as 0x80.  Inputs must be finite; for a block holding a NaN
+ * or an infinity the output is unspecified.
+ *
+ * Checks (pure host): pointers non-NULL, fmt e4m3/e5m2, x_dtype, 1 <= R <=
+ * MXGEMM_MAX_M, 32 <= K <= MXGEMM_MAX_K with K % 32 == 0, R * K <=
+ * MXGEMM_MAX_QELEMS, X and codes 16-byte aligned, and X, codes and scales
+ * pairwise disjoint.  Same status codes as mxgemm_validate_args. */
+int mxgemm_validate_quantize(const void *X, int x_dtype, int64_t R, int64_t K, int fmt,
+                             const uint8_t *codes, const uint8_t *scales);
+
+/* Quantize as above, asynchronously on `stream`; all pointers are device
+ * pointers on the handle's device, owned by the caller.  Nothing is
+ * allocated.  On an error nothing is launched. */
+int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K, int fmt,
+                    uint8_t *codes, uint8_t *scales, hipStream_t stream);
 
 /* Static text for a status code ("unknown status" for others). */
 const char *mxgemm_status_string(int code);

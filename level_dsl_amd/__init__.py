@@ -23,6 +23,8 @@ MXGEMM_FMT_E4M3 = 0
 MXGEMM_FMT_E5M2 = 1
 MXGEMM_OUT_F32 = 0
 MXGEMM_OUT_BF16 = 1
+MXGEMM_X_F32 = 0
+MXGEMM_X_BF16 = 1
 MXGEMM_VARIANT_AUTO = 0
 MXGEMM_VARIANT_LARGE = 1
 MXGEMM_VARIANT_SKINNY = 2
@@ -46,6 +48,8 @@ SIGNATURES = {
                                     _i32, _i32]),
     "mxgemm_run": (_i32, [_vp, _vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64, _i32,
                           _i32, _vp]),
+    "mxgemm_validate_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _u8p, _u8p]),
+    "mxgemm_quantize": (_i32, [_vp, _vp, _i32, _i64, _i64, _i32, _u8p, _u8p, _vp]),
     "mxgemm_status_string": (ctypes.c_char_p, [_i32]),
 }
 
@@ -133,6 +137,24 @@ def mxgemm_run(h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc, out_d
         int(M), int(N), int(K), int(use_acc), int(out_dtype), stream), "mxgemm_run")
 
 
+def mxgemm_validate_quantize(X, x_dtype, R, K, fmt, codes, scales) -> int:
+    """Returns the status code (0 = valid); pure host check."""
+    return load_library().mxgemm_validate_quantize(
+        _ptr(X), int(x_dtype), int(R), int(K), int(fmt), _ptr(codes), _ptr(scales))
+
+
+def mxgemm_quantize(h, X, x_dtype, R, K, fmt, codes, scales, stream=None) -> None:
+    """MX block quantization of the R x K matrix X into codes (R x K) and
+    scales (R x K/32) on `stream` (default: torch's current stream)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(load_library().mxgemm_quantize(
+        h, _ptr(X), int(x_dtype), int(R), int(K), int(fmt), _ptr(codes), _ptr(scales), stream),
+        "mxgemm_quantize")
+
+
 class Gemm:
     """Owns one handle; call(...) checks tensor shapes and runs."""
 
@@ -168,3 +190,25 @@ class Gemm:
         mxgemm_run(self.h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, int(bool(use_acc)),
                    out_dtype, stream)
         return C
+
+    def quantize(self, X, fmt, codes=None, scales=None, stream=None):
+        """MX block quantization of a contiguous (R, K) fp32 or bf16 device
+        tensor; returns (codes (R, K) uint8, scales (R, K/32) uint8)."""
+        if X.dim() != 2 or not X.is_contiguous() or X.device.type != "cuda":
+            raise ValueError("X must be a contiguous 2-D device tensor")
+        if X.dtype == torch.float32:
+            xd = MXGEMM_X_F32
+        elif X.dtype == torch.bfloat16:
+            xd = MXGEMM_X_BF16
+        else:
+            raise ValueError("X must be float32 or bfloat16")
+        R, K = X.shape
+        if codes is None:
+            codes = torch.empty((R, K), dtype=torch.uint8, device=X.device)
+        if scales is None:
+            scales = torch.empty((R, K // 32), dtype=torch.uint8, device=X.device)
+        if codes.shape != (R, K) or scales.shape != (R, K // 32) or \
+                codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+            raise ValueError("codes must be (R, K) and scales (R, K/32), uint8")
+        mxgemm_quantize(self.h, X, xd, R, K, fmt, codes, scales, stream)
+        return codes, scales

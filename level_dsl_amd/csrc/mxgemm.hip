@@ -14,6 +14,7 @@
 #include "mxgemm_large.h"
 #include "mxgemm_skinny.h"
 #include "mxgemm_stream.h"
+#include "mxquant.h"
 
 static_assert(mxg::stream::BN == mxg::skinny::BN && mxg::stream::MAX_M == mxg::skinny::MAX_M,
               "both small-M kernels tile N and bound M alike");
@@ -233,6 +234,53 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     const hipError_t e = native ? dispatch<true>(skinny, f, a, stream)
                                 : dispatch<false>(skinny, f, a, stream);
     return e == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
+}
+
+int mxgemm_validate_quantize(const void *X, int x_dtype, int64_t R, int64_t K, int fmt,
+                             const uint8_t *codes, const uint8_t *scales)
+{
+    if (!X || !codes || !scales) return MXGEMM_ERR_NULL;
+    if (fmt != MXGEMM_FMT_E4M3 && fmt != MXGEMM_FMT_E5M2) return MXGEMM_ERR_FMT;
+    if (x_dtype != MXGEMM_X_F32 && x_dtype != MXGEMM_X_BF16) return MXGEMM_ERR_DTYPE;
+    if (R < 1 || K < 32 || R > MXGEMM_MAX_M || K > MXGEMM_MAX_K || (K % 32) != 0 ||
+        R * K > MXGEMM_MAX_QELEMS)
+        return MXGEMM_ERR_SHAPE;
+    if (((uintptr_t)X | (uintptr_t)codes) & 15u) return MXGEMM_ERR_ALIGN;
+    const uint64_t n = (uint64_t)R * (uint64_t)K;
+    const uint64_t xbytes = n * (x_dtype == MXGEMM_X_F32 ? 4u : 2u);
+    if (overlaps(X, xbytes, codes, n) || overlaps(X, xbytes, scales, n / 32) ||
+        overlaps(codes, n, scales, n / 32))
+        return MXGEMM_ERR_ALIAS;
+    return MXGEMM_OK;
+}
+
+int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K, int fmt,
+                    uint8_t *codes, uint8_t *scales, hipStream_t stream)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    const int rc = mxgemm_validate_quantize(X, x_dtype, R, K, fmt, codes, scales);
+    if (rc != MXGEMM_OK) return rc;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
+    if (dev != h->device) return MXGEMM_ERR_DEVICE;
+
+    mxg::quant::QuantArgs a;
+    a.X = (const uint8_t *)X;
+    a.codes = codes;
+    a.scales = scales;
+    a.n = (uint64_t)R * (uint64_t)K;
+    const uint64_t esz = x_dtype == MXGEMM_X_F32 ? 4 : 2;
+    const uint64_t per_block = (uint64_t)(mxg::quant::THREADS / 64) * mxg::quant::WAVE_BYTES / esz;
+    const dim3 grid((unsigned)((a.n + per_block - 1) / per_block));
+    const dim3 block(mxg::quant::THREADS);
+    const int sel = fmt * 2 + (x_dtype == MXGEMM_X_BF16 ? 1 : 0);
+    switch (sel) {
+    case 0: hipLaunchKernelGGL((mxg::quant::kernel<0, 0>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((mxg::quant::kernel<0, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((mxg::quant::kernel<1, 0>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((mxg::quant::kernel<1, 1>), grid, block, 0, stream, a); break;
+    }
+    return hipGetLastError() == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
 }
 
 } // extern "C"

@@ -1,0 +1,116 @@
+// mxquant.h -- MX block quantization for gfx950: fp32 or bf16 values to fp8
+// codes (e4m3 / e5m2) with one e8m0 scale byte per 32 consecutive elements
+// of a row (the operand layout of the scaled multiply: a uint8 scale tile
+// whose K extent is BLOCK_K // 32, TLX async-compute page, "TMEM-backed MX
+// Scales").  Per block: the scale is the smallest power of two 2^e with
+// max|x| <= MAX * 2^e (MAX = 448 for e4m3, 57344 for e5m2; an all-zero
+// block takes the smallest scale), stored as e + 127 clamped to 0..254, and
+// each code is x * 2^-e rounded to nearest even.
+//
+// The work is a flat stream (K % 32 == 0, so blocks never straddle rows):
+//   * a wave owns 4 x 64 consecutive 16-byte chunks of X; lane l loads
+//     chunks l, 64 + l, 128 + l, 192 + l (every load instruction reads 1 KiB
+//     of contiguous memory), so a block is 8 lanes of fp32 or 4 lanes of
+//     bf16;
+//   * the block maximum is an integer max over the magnitude bits (IEEE
+//     order for finite values), reduced across the block's lanes with
+//     cross-lane shuffles; the scale byte is read off its exponent and
+//     mantissa fields: max|x| = 1.f * 2^(E-127) <= 0.875 * 2^(e+9) for e4m3
+//     gives e + 127 = E - 8 + (f > 0.75), for e5m2 E - 15 + (f > 0.75);
+//   * x * 2^(127 - scale) is exact (a power-of-two product whose magnitude
+//     is at most MAX), and v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 round it to
+//     nearest even, two values per instruction;
+//   * codes leave as one 4-byte (fp32 input) or 8-byte (bf16 input) store
+//     per lane and chunk, 256 or 512 contiguous bytes per instruction; the
+//     first lane of each block stores its scale byte.
+// Descriptors are rebased per wave, so every offset stays far below 2^32 and
+// the tail of the stream is masked by the descriptors' range checks.
+#pragma once
+
+#include "mxgemm_common.h"
+
+namespace mxg {
+namespace quant {
+
+constexpr int THREADS = 256;
+constexpr int CHUNKS = 4;                 // 16-byte chunks per lane
+constexpr int WAVE_BYTES = CHUNKS * 64 * 16;  // input bytes per wave
+
+struct QuantArgs {
+    const uint8_t *X;
+    uint8_t *codes;
+    uint8_t *scales;
+    uint64_t n;  // elements (R * K, a multiple of 32)
+};
+
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt_pair(float a, float b, uint32_t old, bool hi)
+{
+    if constexpr (FMT == 0)
+        return (uint32_t)(hi ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true)
+                             : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false));
+    else
+        return (uint32_t)(hi ? __builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, true)
+                             : __builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, false));
+}
+
+template <int FMT, int XBF16>
+__global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
+{
+    constexpr int EPL = XBF16 ? 8 : 4;    // elements per 16-byte chunk
+    constexpr int LPB = 32 / EPL;         // lanes per block
+    constexpr int ESZ = XBF16 ? 2 : 4;
+    constexpr int WAVE_ELEMS = WAVE_BYTES / ESZ;
+    constexpr uint32_t OFF = FMT == 0 ? 8 : 15;  // scale byte = E - OFF + (f > 0.75)
+
+    const int lane = threadIdx.x & 63;
+    const uint64_t e0 = ((uint64_t)blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6)) * WAVE_ELEMS;
+    if (e0 >= p.n) return;  // whole wave past the end
+    const uint64_t left = p.n - e0;
+    const uint32_t ne = left < (uint64_t)WAVE_ELEMS ? (uint32_t)left : (uint32_t)WAVE_ELEMS;
+    const rsrc_t rX = make_rsrc(p.X + e0 * ESZ, ne * ESZ);
+    const rsrc_t rQ = make_rsrc(p.codes + e0, ne);
+    const rsrc_t rS = make_rsrc(p.scales + e0 / 32, ne / 32);
+
+    v4i x[CHUNKS];
+#pragma unroll
+    for (int j = 0; j < CHUNKS; ++j) x[j] = load16(rX, (uint32_t)(64 * j + lane) * 16);
+
+#pragma unroll
+    for (int j = 0; j < CHUNKS; ++j) {
+        // the chunk's elements as fp32, and their largest magnitude (bits)
+        float f[EPL];
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            uint32_t b;
+            if constexpr (XBF16)
+                b = ((uint32_t)x[j][i / 2] >> (16 * (i & 1))) << 16;
+            else
+                b = (uint32_t)x[j][i];
+            f[i] = __builtin_bit_cast(float, b);
+            m = max(m, b & 0x7fffffffu);
+        }
+#pragma unroll
+        for (int d = 1; d < LPB; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+        const int E = (int)(m >> 23);
+        int s = E - (int)OFF + ((m & 0x7fffffu) > 0x600000u ? 1 : 0);
+        s = s < 0 ? 0 : (s > 254 ? 254 : s);
+        const int sh = 127 - s;
+        uint32_t w[EPL / 4];
+#pragma unroll
+        for (int q = 0; q < EPL / 4; ++q) {
+            uint32_t v = cvt_pair<FMT>(__builtin_ldexpf(f[4 * q], sh), __builtin_ldexpf(f[4 * q + 1], sh), 0u, false);
+            w[q] = cvt_pair<FMT>(__builtin_ldexpf(f[4 * q + 2], sh), __builtin_ldexpf(f[4 * q + 3], sh), v, true);
+        }
+        const uint32_t c = (uint32_t)(64 * j + lane);  // chunk index within the wave
+        if constexpr (XBF16)
+            store8(rQ, c * 8, v2i{(int)w[0], (int)w[1]});
+        else
+            store4(rQ, c * 4, w[0]);
+        if (lane % LPB == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)s, rS, c / LPB, 0, 0);
+    }
+}
+
+} // namespace quant
+} // namespace mxg

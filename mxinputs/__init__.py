@@ -127,6 +127,15 @@ WORKLOADS = {
 }
 
 
+def skinny_b_raw() -> np.ndarray:
+    """The fp32 draws behind the skinny workload's B: (N, K) = (28672, 8192)
+    samples of N(0, 0.02^2), before MX block quantization."""
+    w = WORKLOADS[3]
+    braw = rng(3, T_B).standard_normal(size=(w["N"], w["K"]), dtype=np.float32)
+    braw *= np.float32(0.02)
+    return braw
+
+
 def workload(wid: int) -> Problem:
     """Build one of the five named workloads (see the module docstring)."""
     w = WORKLOADS[wid]
@@ -144,8 +153,7 @@ def workload(wid: int) -> Problem:
     if wid == 3:
         A = normal_codes(rng(wid, T_A), (M, K), 1.0, FMT_E4M3)
         As = uniform_scales(rng(wid, T_AS), (M, kb), 125, 129)
-        braw = rng(wid, T_B).standard_normal(size=(N, K), dtype=np.float32)
-        braw *= np.float32(0.02)
+        braw = skinny_b_raw()
         B, Bs = mx_block_quantize(braw, FMT_E4M3)
         del braw
         return Problem(M, N, K, FMT_E4M3, FMT_E4M3, A, As, B, Bs, OUT_F32, False, None, w["name"])

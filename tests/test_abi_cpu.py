@@ -88,3 +88,30 @@ def test_product_path_has_no_oracle_or_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("no oracle", ""), f
                 assert "mxref" not in text, f
+
+
+def vq(**kw):
+    args = dict(X=0x100000, x_dtype=0, R=64, K=128, fmt=0, codes=0x200000, scales=0x300001)
+    args.update(kw)
+    return L.mxgemm_validate_quantize(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, "MXGEMM_OK"), ({"x_dtype": 1}, "MXGEMM_OK"), ({"fmt": 1, "R": 1, "K": 32}, "MXGEMM_OK"),
+    ({"X": 0}, "MXGEMM_ERR_NULL"), ({"codes": 0}, "MXGEMM_ERR_NULL"), ({"scales": 0}, "MXGEMM_ERR_NULL"),
+    ({"fmt": 2}, "MXGEMM_ERR_FMT"), ({"x_dtype": 2}, "MXGEMM_ERR_DTYPE"),
+    ({"R": 0}, "MXGEMM_ERR_SHAPE"), ({"K": 16}, "MXGEMM_ERR_SHAPE"), ({"K": 48}, "MXGEMM_ERR_SHAPE"),
+    ({"K": (1 << 21) + 32}, "MXGEMM_ERR_SHAPE"), ({"R": 1 << 20, "K": 1 << 19}, "MXGEMM_ERR_SHAPE"),
+    ({"X": 0x100008}, "MXGEMM_ERR_ALIGN"), ({"codes": 0x200004}, "MXGEMM_ERR_ALIGN"),
+    ({"codes": 0x100000 + 64 * 128 * 4 - 16}, "MXGEMM_ERR_ALIAS"),
+    ({"scales": 0x200000 + 64 * 128 - 1}, "MXGEMM_ERR_ALIAS"),
+    ({"scales": 0x100000 + 64 * 128 * 2, "x_dtype": 1}, "MXGEMM_OK"),
+])
+def test_validate_quantize(kw, code):
+    assert vq(**kw) == L.STATUS_CODE[code]
+
+
+def test_quantize_rejects_bad_handle_without_gpu_work():
+    with pytest.raises(L.MxgemmError) as e:
+        L.mxgemm_quantize(None, 0x100000, 0, 64, 128, 0, 0x200000, 0x300000, stream=0)
+    assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_HANDLE"]
