@@ -12,6 +12,10 @@ Also reported on the same line:
   * skinny: the M=64, N=28672, K=8192 workload in GB/s of algorithmic bytes
     (A, scales and B read once, C written once), B rotated over 3 copies;
   * native: the same 8192^3 workload on the native scaled-MFMA variant;
+  * mx_quantize: MX block quantization of the skinny workload's fp32 weight
+    (28672 x 8192 -> e4m3 codes + e8m0 scales) in GB/s of algorithmic bytes
+    (X read once, codes and scales written once), inputs rotated over 3
+    copies;
   * roofline: algorithmic work per launch / mean launch duration, from one
     pair of HIP events recorded on the launch stream around the timed
     launches;
@@ -47,7 +51,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "MXFP8 GEMM TFLOP/s at 8192\u00b3 (% of dense MXFP8 peak); GB/s (% HBM) at M=64"
 KERNEL_SOURCES = ["level_dsl_amd/csrc/mxgemm.hip", "level_dsl_amd/csrc/mxgemm_common.h",
                   "level_dsl_amd/csrc/mxgemm_large.h", "level_dsl_amd/csrc/mxgemm_skinny.h",
-                  "level_dsl_amd/csrc/mxgemm_stream.h"]
+                  "level_dsl_amd/csrc/mxgemm_stream.h", "level_dsl_amd/csrc/mxquant.h"]
 
 
 def kernel_hash() -> str:
@@ -71,6 +75,15 @@ def log(msg):
 def traffic_from_profiles(kernel_key: str):
     """HBM bytes per launch from a committed counter summary, if it was
     taken on the current kernel sources (else None)."""
+    v = vals.get("mx_quantize", {})
+    if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+        alg = quant_bytes(*QUANT_SHAPE)
+        out["kernels"]["mx_quantize"] = {
+            "kernel": QUANT_KERNEL, "workload": "mxquant_skinny_weight_28672x8192_f32_e4m3",
+            "fetch_bytes": round(v["FETCH_SIZE"]), "write_bytes": round(v["WRITE_SIZE"]),
+            "bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
+            "algorithmic_bytes": alg,
+            "ratio_to_algorithmic": round((v["FETCH_SIZE"] + v["WRITE_SIZE"]) / alg, 3)}
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -144,6 +157,33 @@ TRAFFIC_KERNELS = {"large_exact": ("void mxg::large::kernel<0, 0, false, true>",
                                    "MXGEMM_VARIANT_LARGE", 2),
                    "skinny_exact": ("void mxg::stream::kernel<0, 0, true>", 3,
                                     "MXGEMM_VARIANT_SKINNY", 4)}
+QUANT_KERNEL = "void mxg::quant::kernel<0, 0>"
+QUANT_SHAPE = (28672, 8192)  # the skinny workload's weight, N x K
+
+
+def quant_bytes(R, K, esz=4):
+    return R * K * esz + R * K + R * K // 32
+
+
+def bench_quantize(gemm, X, steps, warmup, copies):
+    """Time mxgemm_quantize of the (R, K) fp32 host array X, rotated over
+    `copies` device copies.  Returns (wall, mean launch seconds)."""
+    import torch
+    dev = torch.device("cuda:0")
+    R, K = X.shape
+    xs = [torch.from_numpy(X).to(dev)]
+    xs += [xs[0].clone() for _ in range(copies - 1)]
+    cs = [torch.empty((R, K), dtype=torch.uint8, device=dev) for _ in range(copies)]
+    ss = [torch.empty((R, K // 32), dtype=torch.uint8, device=dev) for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        gemm.quantize(xs[i % copies], 0, cs[i % copies], ss[i % copies], stream.cuda_stream)
+
+    wall, mean_s = time_launches(step, steps, warmup, stream)
+    del xs, cs, ss
+    torch.cuda.empty_cache()
+    return wall, mean_s
 
 
 def traffic_launches():
@@ -164,6 +204,8 @@ def traffic_launches():
         p = mi.workload(wid)
         log(f"traffic: {key} on {p.name}")
         bench_gemm(gemm, p, getattr(L, var), 3, 0, 3)
+    log("traffic: mx_quantize")
+    bench_quantize(gemm, mi.skinny_b_raw(), 3, 0, 3)
     gemm.close()
     torch.cuda.synchronize()
     log("traffic: done")
@@ -198,7 +240,9 @@ def traffic_report(fetch_csv: str, write_csv: str):
         kib = float(np.median(copy))
         scale[counter] = COPY_BYTES / (kib * 1024.0)
         out[f"copy_{counter}_kib"] = kib
-        for key, (kname, _, _, _) in TRAFFIC_KERNELS.items():
+        names = {k: v[0] for k, v in TRAFFIC_KERNELS.items()}
+        names["mx_quantize"] = QUANT_KERNEL
+        for key, kname in names.items():
             ks = [tot[d] for d in sorted(tot) if name[d].startswith(kname)]
             if ks:
                 vals.setdefault(key, {})[counter] = float(np.mean(ks)) * 1024.0 * scale[counter]
@@ -218,6 +262,15 @@ def traffic_report(fetch_csv: str, write_csv: str):
                                "algorithmic_bytes": alg,
                                "ratio_to_algorithmic":
                                    round((v["FETCH_SIZE"] + v["WRITE_SIZE"]) / alg, 3)}
+    v = vals.get("mx_quantize", {})
+    if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+        alg = quant_bytes(*QUANT_SHAPE)
+        out["kernels"]["mx_quantize"] = {
+            "kernel": QUANT_KERNEL, "workload": "mxquant_skinny_weight_28672x8192_f32_e4m3",
+            "fetch_bytes": round(v["FETCH_SIZE"]), "write_bytes": round(v["WRITE_SIZE"]),
+            "bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
+            "algorithmic_bytes": alg,
+            "ratio_to_algorithmic": round((v["FETCH_SIZE"] + v["WRITE_SIZE"]) / alg, 3)}
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -337,6 +390,26 @@ def main():
         "algorithmic_bytes": sbytes, "steps": sk_steps, "b_rotation": 3}
     log(f"bench: skinny {out['skinny_m64']['value']} GB/s")
     del ps
+
+    # ---- MX block quantization of the skinny weight ------------------------------
+    R, K = QUANT_SHAPE
+    qbytes = quant_bytes(R, K)
+    raw = mi.skinny_b_raw()
+    q_steps = max(steps, 30)
+    wall_q, mean_q = bench_quantize(gemm, raw, q_steps, warmup, 3)
+    del raw
+    out["mx_quantize"] = {
+        "workload": "mxquant_skinny_weight_28672x8192_f32_e4m3", "value":
+            round(qbytes * q_steps / wall_q / 1e9, 1), "unit": "GB/s",
+        "pct_of_hbm_peak": round(100 * qbytes * q_steps / wall_q / 1e9 / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(qbytes / mean_q / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(qbytes / mean_q / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles("mx_quantize"),
+                     "kernel": "mxg::quant::kernel<0,0>",
+                     "launch_mean_us": round(mean_q * 1e6, 2)},
+        "algorithmic_bytes": qbytes, "steps": q_steps, "x_rotation": 3}
+    log(f"bench: mx_quantize {out['mx_quantize']['value']} GB/s")
     gemm.close()
 
     if not args.no_cpu:
