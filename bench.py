@@ -75,15 +75,6 @@ def log(msg):
 def traffic_from_profiles(kernel_key: str):
     """HBM bytes per launch from a committed counter summary, if it was
     taken on the current kernel sources (else None)."""
-    v = vals.get("mx_quantize", {})
-    if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
-        alg = quant_bytes(*QUANT_SHAPE)
-        out["kernels"]["mx_quantize"] = {
-            "kernel": QUANT_KERNEL, "workload": "mxquant_skinny_weight_28672x8192_f32_e4m3",
-            "fetch_bytes": round(v["FETCH_SIZE"]), "write_bytes": round(v["WRITE_SIZE"]),
-            "bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
-            "algorithmic_bytes": alg,
-            "ratio_to_algorithmic": round((v["FETCH_SIZE"] + v["WRITE_SIZE"]) / alg, 3)}
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -211,7 +202,7 @@ def traffic_launches():
     log("traffic: done")
 
 
-def traffic_report(fetch_csv: str, write_csv: str):
+def traffic_report(fetch_csv: str, write_csv: str, out_path: str = None):
     """Per-launch HBM bytes of each timed kernel from the two counter passes,
     scaled by the counters' reading for the calibration copy."""
     import csv
@@ -271,7 +262,7 @@ def traffic_report(fetch_csv: str, write_csv: str):
             "bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
             "algorithmic_bytes": alg,
             "ratio_to_algorithmic": round((v["FETCH_SIZE"] + v["WRITE_SIZE"]) / alg, 3)}
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
