@@ -333,3 +333,31 @@ def test_invalid_call_launches_nothing(gemm):
     gemm.set_variant(AUTO)
     torch.cuda.synchronize()
     assert bool(torch.isnan(buf).all()) and bool(torch.isnan(qbuf).all()), "a rejected call wrote C"
+
+
+# ------------------------------------------------ non-finite codes, scales --
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 1), (1, 0)])
+def test_nonfinite_pattern(gemm, fa, fb):
+    """NaN and infinity codes and NaN scale bytes (255) are outside every
+    workload; the exact variants still put NaN and +-inf exactly where the
+    oracle's IEEE arithmetic does (the decode turns them into bf16 NaN/inf,
+    which the bf16 MFMA propagates), and the finite outputs of the same
+    problem meet the usual tolerance."""
+    p = mi.random_problem(70, 72, 256, seed=77 + fa * 2 + fb, fmtA=fa, fmtB=fb)
+    nan_a = 0x7F if fa == 0 else 0x7E
+    p.A[3, 5] = nan_a                 # NaN code in row 3
+    p.As[10, 2] = 255                 # NaN scale for row 10, block 2
+    if fb == 1:
+        p.B[7, 40] = 0x7C             # +inf in column 7
+        p.B[8, 41] = 0xFC             # -inf in column 8
+    ref = oracle_full(p)
+    for v in _variants_for(p.M):
+        got = run(gemm, p, v)
+        r = ref["ref32"]
+        assert np.array_equal(np.isnan(got), np.isnan(r)), \
+            f"NaN pattern differs ({VNAME[v]}): {np.isnan(got).sum()} vs {np.isnan(r).sum()}"
+        fin = np.isfinite(r)
+        inf = np.isinf(r)
+        assert np.array_equal(got[inf], r[inf]), f"infinities differ ({VNAME[v]})"
+        compare(got[fin], {k: a[fin] for k, a in ref.items()}, mi.OUT_F32, f"finite part {VNAME[v]}")
