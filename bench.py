@@ -307,7 +307,7 @@ def main():
         traffic_report(*args.traffic_report)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the GEMM "
+        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}); the GEMM "
               "would shard by C columns with no exchange, which is not built here.",
               file=sys.stderr)
         sys.exit(2)
