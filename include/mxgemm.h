@@ -27,10 +27,11 @@
  *   B_scale  N x (K/32) bytes, row-major.
  *   C        M x N, row-major, fp32 or bf16 (bit pattern in uint16).
  *
- * Ownership: the caller owns every buffer; all pointers given to
- * mxgemm_run are device pointers on the handle's device.  The library
- * allocates no device memory per call and keeps no state between calls
- * beyond the handle.
+ * Ownership: the caller owns every buffer, including the optional split-K
+ * workspace (mxgemm_set_workspace); all pointers given to mxgemm_run are
+ * device pointers on the handle's device.  The library allocates no device
+ * memory and keeps no state between calls beyond the handle and the
+ * workspace's arrival counters, which every call leaves at zero.
  *
  * Errors: every entry point returns an MXGEMM_* status.  On an error nothing
  * is launched and no output is touched.  Nothing throws across this ABI.
@@ -89,7 +90,8 @@ enum {
     MXGEMM_ERR_HIP = 7,     /* the HIP runtime reported an error */
     MXGEMM_ERR_HANDLE = 8,  /* NULL or destroyed handle */
     MXGEMM_ERR_ALIAS = 9,   /* C overlaps an input buffer */
-    MXGEMM_ERR_VARIANT = 10 /* unknown variant */
+    MXGEMM_ERR_VARIANT = 10, /* unknown variant */
+    MXGEMM_ERR_WORKSPACE = 11 /* workspace missing for a forced split, too small or misaligned */
 };
 
 /* Limits of one call. */
@@ -98,6 +100,10 @@ enum {
 #define MXGEMM_MAX_K ((int64_t)1 << 21)
 #define MXGEMM_MAX_MN ((int64_t)1 << 36) /* M * N: C up to 256 GiB of fp32 */
 #define MXGEMM_MAX_QELEMS ((int64_t)1 << 38) /* R * K of one mxgemm_quantize call */
+
+/* Bytes of the split-K workspace: 4 KiB of arrival counters, then room for
+ * 256 fp32 partial tiles of 64 x 112. */
+#define MXGEMM_WORKSPACE_BYTES ((size_t)4096 + (size_t)256 * 64 * 112 * 4)
 
 /* Library ABI version (this header: 1). */
 int mxgemm_version(void);
@@ -119,6 +125,29 @@ int mxgemm_destroy(mxgemm_t h);
  * running on the same handle in other threads. */
 int mxgemm_set_variant(mxgemm_t h, int variant);
 
+/* Attach a caller-owned device buffer of at least MXGEMM_WORKSPACE_BYTES
+ * (256-byte aligned) to the handle, or detach it with ws = NULL.  With a
+ * workspace attached, exact small-M calls (M <= 64) whose N gives fewer
+ * than 129 column tiles of 112 split K over several workgroups.  The TLX
+ * global-memory page offers an atomic buffer add (tlx.buffer_atomic_add) for
+ * such partial sums; here instead every split writes an fp32 partial tile to
+ * the workspace and the last split of each tile to finish adds the partials
+ * in split order, so results are deterministic (and within the exact
+ * variants' bound).
+ * Attaching zeroes the counter area with a kernel on `stream`; later calls
+ * must be ordered after it.  Calls that use one workspace must not overlap
+ * on the GPU (order them on one stream, or give each stream its own handle
+ * and workspace).  MXGEMM_ERR_WORKSPACE for a short or misaligned buffer. */
+int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream);
+
+/* Number of K splits for exact small-M calls: 0 (default) chooses it from
+ * the shape, 1 never splits, S >= 2 forces S splits, reduced to at most the
+ * number of 128-byte K stages and to 256 / column tiles (so tiles_n * S <=
+ * 256).  A forced S >= 2 that survives this makes mxgemm_run return
+ * MXGEMM_ERR_WORKSPACE when no workspace is attached.  MXGEMM_ERR_SHAPE for
+ * S < 0. */
+int mxgemm_set_splits(mxgemm_t h, int splits);
+
 /* Check the arguments of mxgemm_run without touching the GPU: pointers
  * non-NULL, formats, out_dtype, use_acc in {0,1}, 1 <= M <= MXGEMM_MAX_M,
  * 1 <= N <= MXGEMM_MAX_N, M * N <= MXGEMM_MAX_MN, 32 <= K <= MXGEMM_MAX_K
@@ -137,7 +166,8 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA,
  * (fp32, or bf16 widened to fp32) is added to the fp32 accumulator before
  * the single rounding to out_dtype.  Buffers must stay valid until the
  * stream reaches this point; the caller synchronises.  Thread-safe: a
- * handle may be used from several host threads on different streams. */
+ * handle without a workspace may be used from several host threads on
+ * different streams (see mxgemm_set_workspace for one with). */
 int mxgemm_run(mxgemm_t h,
                const void *A, const uint8_t *A_scale, int fmtA,
                const void *B, const uint8_t *B_scale, int fmtB,

@@ -30,11 +30,12 @@ MXGEMM_VARIANT_LARGE = 1
 MXGEMM_VARIANT_SKINNY = 2
 MXGEMM_VARIANT_LARGE_NATIVE = 3
 MXGEMM_VARIANT_SKINNY_NATIVE = 4
+MXGEMM_WORKSPACE_BYTES = 4096 + 256 * 64 * 112 * 4
 
 STATUS = {0: "MXGEMM_OK", 1: "MXGEMM_ERR_NULL", 2: "MXGEMM_ERR_FMT", 3: "MXGEMM_ERR_DTYPE",
           4: "MXGEMM_ERR_SHAPE", 5: "MXGEMM_ERR_ALIGN", 6: "MXGEMM_ERR_DEVICE",
           7: "MXGEMM_ERR_HIP", 8: "MXGEMM_ERR_HANDLE", 9: "MXGEMM_ERR_ALIAS",
-          10: "MXGEMM_ERR_VARIANT"}
+          10: "MXGEMM_ERR_VARIANT", 11: "MXGEMM_ERR_WORKSPACE"}
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 # name -> (restype, argtypes), in the order of include/mxgemm.h
@@ -44,6 +45,8 @@ SIGNATURES = {
     "mxgemm_create": (_i32, [ctypes.POINTER(ctypes.c_void_p)]),
     "mxgemm_destroy": (_i32, [_vp]),
     "mxgemm_set_variant": (_i32, [_vp, _i32]),
+    "mxgemm_set_workspace": (_i32, [_vp, _vp, ctypes.c_size_t, _vp]),
+    "mxgemm_set_splits": (_i32, [_vp, _i32]),
     "mxgemm_validate_args": (_i32, [_vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64,
                                     _i32, _i32]),
     "mxgemm_run": (_i32, [_vp, _vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64, _i32,
@@ -105,6 +108,26 @@ def mxgemm_destroy(h: int) -> None:
 
 def mxgemm_set_variant(h: int, variant: int) -> None:
     _check(load_library().mxgemm_set_variant(h, int(variant)), "mxgemm_set_variant")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def mxgemm_set_workspace(h, ws, nbytes: int, stream=None) -> None:
+    """Attach a device buffer of at least MXGEMM_WORKSPACE_BYTES (256-byte
+    aligned) for split-K, or detach with ws=None; zeroes its counters on
+    `stream`."""
+    _check(load_library().mxgemm_set_workspace(h, _ptr(ws), int(nbytes),
+                                               _stream(stream) if ws is not None else None),
+           "mxgemm_set_workspace")
+
+
+def mxgemm_set_splits(h, splits: int) -> None:
+    """K splits of exact small-M calls: 0 automatic, 1 never, S >= 2 forced."""
+    _check(load_library().mxgemm_set_splits(h, int(splits)), "mxgemm_set_splits")
 
 
 def _ptr(x) -> int:
@@ -174,6 +197,22 @@ class Gemm:
 
     def set_variant(self, variant: int):
         mxgemm_set_variant(self.h, variant)
+
+    def enable_split_k(self, device="cuda:0", stream=None):
+        """Give the handle its own split-K workspace (a torch allocation that
+        this object keeps alive); calls through this handle must then be
+        ordered on one stream."""
+        if getattr(self, "workspace", None) is None:
+            self.workspace = torch.empty(MXGEMM_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+            mxgemm_set_workspace(self.h, self.workspace, MXGEMM_WORKSPACE_BYTES, stream)
+
+    def disable_split_k(self):
+        if getattr(self, "workspace", None) is not None:
+            mxgemm_set_workspace(self.h, None, 0)
+            self.workspace = None
+
+    def set_splits(self, splits: int):
+        mxgemm_set_splits(self.h, splits)
 
     def __call__(self, A, A_scale, fmtA, B, B_scale, fmtB, C, use_acc=False,
                  out_dtype=MXGEMM_OUT_F32, stream=None):

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <new>
 
@@ -23,6 +24,8 @@ struct mxgemm_ctx {
     uint32_t magic;
     int device;
     int variant;
+    int splits;      // 0 automatic, 1 never, S >= 2 forced
+    uint8_t *ws;     // caller's split-K workspace, or NULL
 };
 
 namespace {
@@ -63,16 +66,63 @@ hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int FA, int FB, int MT>
+hipError_t launch_stream_mt(const mxg::GemmArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.tiles_n * a.splits), block(mxg::stream::threads_for<MT>());
+    if (a.scale_dword)
+        hipLaunchKernelGGL((mxg::stream::kernel<FA, FB, true, MT>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((mxg::stream::kernel<FA, FB, false, MT>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <int FA, int FB>
 hipError_t launch_stream(const mxg::GemmArgs &a, hipStream_t s)
 {
-    if (a.scale_dword)
-        hipLaunchKernelGGL((mxg::stream::kernel<FA, FB, true>), dim3(a.tiles_n),
-                           dim3(mxg::stream::THREADS), 0, s, a);
-    else
-        hipLaunchKernelGGL((mxg::stream::kernel<FA, FB, false>), dim3(a.tiles_n),
-                           dim3(mxg::stream::THREADS), 0, s, a);
-    return hipGetLastError();
+    switch ((a.M + 15) / 16) {
+    case 1: return launch_stream_mt<FA, FB, 1>(a, s);
+    case 2: return launch_stream_mt<FA, FB, 2>(a, s);
+    case 3: return launch_stream_mt<FA, FB, 3>(a, s);
+    default: return launch_stream_mt<FA, FB, 4>(a, s);
+    }
+}
+
+__global__ void zero_words(uint32_t *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+constexpr size_t kCounterBytes = 4096;
+static_assert(MXGEMM_WORKSPACE_BYTES ==
+                  kCounterBytes + (size_t)mxg::stream::MAX_SPLITS_TILES * mxg::stream::MAX_M *
+                                      mxg::stream::BN * sizeof(float),
+              "workspace layout");
+static_assert((256 / 2) * mxg::stream::CONSUMERS * sizeof(uint32_t) <= kCounterBytes,
+              "one counter per consumer wave of every split tile");
+
+// K splits of an exact small-M call: none unless asked for or the column
+// tiles leave more than half of the 256 CUs idle; then the largest power of
+// two that keeps every split at least 8 K stages (1 KiB) long, tiles_n * S
+// within one workgroup per CU, and S <= 8 (measured: more splits cost more in
+// the reduction than they gain in streaming).  With K a multiple of 1 KiB * S
+// every split is a whole number of the kernel's 8-stage rings.
+int choose_splits(int forced, int tiles_n, int nk)
+{
+    constexpr int kTarget = mxg::stream::MAX_SPLITS_TILES, kMinStages = 8, kMaxAuto = 8;
+    int s;
+    if (forced >= 1) {
+        s = forced;
+    } else if (tiles_n > kTarget / 2) {
+        s = 1;
+    } else {
+        const int cap = std::min(kMaxAuto, std::min(kTarget / tiles_n, nk / kMinStages));
+        s = 1;
+        while (2 * s <= cap) s *= 2;
+    }
+    s = std::min(s, std::min(nk, kTarget / tiles_n));
+    return std::max(s, 1);
 }
 
 template <bool NATIVE>
@@ -122,6 +172,7 @@ const char *mxgemm_status_string(int code)
     case MXGEMM_ERR_HANDLE: return "invalid handle";
     case MXGEMM_ERR_ALIAS: return "C overlaps an input";
     case MXGEMM_ERR_VARIANT: return "unknown kernel variant";
+    case MXGEMM_ERR_WORKSPACE: return "split-K workspace missing, too small or misaligned";
     default: return "unknown status";
     }
 }
@@ -140,6 +191,8 @@ int mxgemm_create(mxgemm_t *out)
     h->magic = kMagic;
     h->device = dev;
     h->variant = MXGEMM_VARIANT_AUTO;
+    h->splits = 0;
+    h->ws = nullptr;
     *out = h;
     return MXGEMM_OK;
 }
@@ -159,6 +212,33 @@ int mxgemm_set_variant(mxgemm_t h, int variant)
     if (variant < MXGEMM_VARIANT_AUTO || variant > MXGEMM_VARIANT_SKINNY_NATIVE)
         return MXGEMM_ERR_VARIANT;
     h->variant = variant;
+    return MXGEMM_OK;
+}
+
+int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    if (!ws) {
+        h->ws = nullptr;
+        return MXGEMM_OK;
+    }
+    if (bytes < MXGEMM_WORKSPACE_BYTES || ((uintptr_t)ws & 255u)) return MXGEMM_ERR_WORKSPACE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
+    if (dev != h->device) return MXGEMM_ERR_DEVICE;
+    constexpr int words = (int)(kCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       (uint32_t *)ws, words);
+    if (hipGetLastError() != hipSuccess) return MXGEMM_ERR_HIP;
+    h->ws = (uint8_t *)ws;
+    return MXGEMM_OK;
+}
+
+int mxgemm_set_splits(mxgemm_t h, int splits)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    if (splits < 0) return MXGEMM_ERR_SHAPE;
+    h->splits = splits;
     return MXGEMM_OK;
 }
 
@@ -223,9 +303,24 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     else
         skinny = variant == MXGEMM_VARIANT_SKINNY || variant == MXGEMM_VARIANT_SKINNY_NATIVE;
     if (skinny && M > mxg::skinny::MAX_M) return MXGEMM_ERR_VARIANT;
+    a.splits = 1;
+    a.ws = nullptr;
+    a.cnt = nullptr;
     if (skinny) {
         a.tiles_m = 1;
         a.tiles_n = (int)((N + mxg::skinny::BN - 1) / mxg::skinny::BN);
+        if (!native) {
+            const int nk = (int)((K + mxg::stream::BK - 1) / mxg::stream::BK);
+            a.splits = choose_splits(h->splits, a.tiles_n, nk);
+            if (a.splits > 1 && !h->ws) {
+                if (h->splits >= 2) return MXGEMM_ERR_WORKSPACE;
+                a.splits = 1;
+            }
+            if (a.splits > 1) {
+                a.cnt = (uint32_t *)h->ws;
+                a.ws = (float *)(h->ws + kCounterBytes);
+            }
+        }
     } else {
         a.tiles_m = (int)((M + mxg::large::BM - 1) / mxg::large::BM);
         a.tiles_n = (int)((N + mxg::large::BN - 1) / mxg::large::BN);

@@ -64,6 +64,9 @@ struct GemmArgs {
     int scale_dword;       // 2: KB % 16 == 0 and scale bases 16-byte aligned;
                            // 1: KB % 4 == 0 and 4-byte aligned; 0: neither
     int c_vec;             // 1: N % 4 == 0 (aligned vector stores of C)
+    int splits;            // small-M exact path: K splits per column tile (1: none)
+    float *ws;             // split-K partial tiles (splits > 1)
+    uint32_t *cnt;         // split-K arrival counters, zero between calls
 };
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)

@@ -22,19 +22,26 @@
 //     loaded HBM latency); it decodes its codes with their block scales to bf16
 //     (v_cvt_scalef32_pk_bf16_fp8/bf8) and runs sixteen 16x16x32 bf16 MFMAs
 //     per stage against A;
-//   * four producer waves (16 rows each, so that every SIMD carries a
-//     similar share of the decode) fetch the A tile (at most 64 rows x
-//     128 bytes per stage, from L2) seven stages ahead with direct-to-LDS
-//     loads into an eight-slot fp8 ring, decode it once for the whole
-//     workgroup into bf16 with its scales folded in, and write it to a
-//     two-slot LDS ring; a barrier per stage publishes the slot;
+//   * one producer wave per 16-row tile of M (MT = ceil(M/16) of them, so
+//     that at M = 64 every SIMD carries a similar share of the decode) fetch
+//     the A tile (at most 64 rows x 128 bytes per stage, from L2) seven
+//     stages ahead with direct-to-LDS loads into an eight-slot fp8 ring,
+//     decode it once for the whole workgroup into bf16 with its scales
+//     folded in, and write it to a two-slot LDS ring; a barrier per stage
+//     publishes the slot.  The consumers run MT row tiles of MFMAs, so a
+//     decode-size M pays for its own rows only;
 //   * the scale dwords of A and of this workgroup's B rows for 64 stages at a
 //     time are loaded by all waves into LDS at the start of each 64-stage
 //     chunk (for K <= 8192, once), instead of a scattered load per row and
 //     stage;
 //   * every output element is summed by one lane over all of K in a fixed
 //     order (deterministic); C is written with 16-byte (fp32) or 8-byte
-//     (bf16) buffer stores.
+//     (bf16) buffer stores;
+//   * split K (when N leaves most CUs idle): workgroup (tile, split) streams
+//     a contiguous range of K stages and leaves an fp32 partial tile in a
+//     caller-owned workspace; the last split of each consumer wave's 16
+//     columns to arrive (an arrival counter) adds the partials in split
+//     order and writes C, so the result is still deterministic.
 #pragma once
 
 #include "mxgemm_common.h"
@@ -46,10 +53,11 @@ constexpr int MAX_M = 64;
 constexpr int BN = 112;
 constexpr int BK = 128;
 constexpr int CONSUMERS = 7;
-constexpr int PRODUCERS = 4;             // each decodes 16 rows of A per stage
-constexpr int WAVES = CONSUMERS + PRODUCERS;
-constexpr int PROWS = MAX_M / PRODUCERS;
-constexpr int THREADS = 64 * WAVES;
+constexpr int PROWS = 16;                // rows of A each producer wave decodes per stage
+constexpr int MAX_SPLITS_TILES = 256;    // split-K: at most this many (tile, split) workgroups
+// one producer wave per 16-row M tile: MT = ceil(M / 16) tiles, 1..4
+template <int MT>
+constexpr int threads_for() { return 64 * (CONSUMERS + MT); }
 constexpr int RING = 8;                  // consumer register ring: the current stage + 7 ahead
 constexpr int ADEPTH = 8;                // producer's fp8 A ring in LDS: the current stage + 7 ahead
 constexpr int A8 = MAX_M * BK;           // bytes of one fp8 A stage (8 KiB)
@@ -107,21 +115,33 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0f70);
 }
 
-template <int FA, int FB, bool SDW>
-__global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
+template <int FA, int FB, bool SDW, int MT>
+__global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
 {
+    static_assert(MT >= 1 && MT * 16 <= MAX_M, "M tiles");
+    constexpr int THREADS = threads_for<MT>();
     __shared__ __attribute__((aligned(1024))) uint8_t a8_lds[ADEPTH][A8];   // raw A, row-major
     __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][A_SLOT];       // decoded A (bf16)
     __shared__ __attribute__((aligned(16))) uint32_t s_lds[SROWS][SPITCH];  // scale dwords
 
-    const int n0 = blockIdx.x * BN;
+    // workgroup -> (column tile, K split): split sp takes stages
+    // [sp * nk / splits, (sp + 1) * nk / splits)
+    const int tile = (int)(blockIdx.x % (unsigned)p.tiles_n);
+    const int sp = (int)(blockIdx.x / (unsigned)p.tiles_n);
+    const int n0 = tile * BN;
     const int rows_b = min(BN, p.N - n0);
     const int M = p.M, N = p.N, K = p.K, KB = p.KB;
-    const int nk = (K + BK - 1) / BK;
+    const int nk_all = (K + BK - 1) / BK;
+    const int kbeg = (int)((int64_t)sp * nk_all / p.splits);
+    const int nk = (int)((int64_t)(sp + 1) * nk_all / p.splits) - kbeg;  // this split's stages, >= 1
     static_assert(RING == ADEPTH && SCH % RING == 0, "producer and consumers run the same iterations");
-    const int nu = (nk + RING - 1) / RING * RING;  // iterations, padded to whole rings
-    const int s0 = (int)(blockIdx.x % (unsigned)nk);
-    auto kt_of = [&](int u) MXG_INLINE { const int s = u + s0; return s < nk ? s : s - nk; };
+    // iterations, padded to whole rings; a padding iteration loads nothing
+    // (its offsets fail the range check) and adds products of zeros.  Testing
+    // each stage instead costs more (measured: 15% at M <= 16), and a tested
+    // copy of the last ring alone makes the kernel spill.
+    const int nu = (nk + RING - 1) / RING * RING;
+    const int s0 = tile % nk;
+    auto kt_of = [&](int u) MXG_INLINE { const int s = u + s0; return kbeg + (s < nk ? s : s - nk); };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -157,8 +177,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     if (wave >= CONSUMERS) {
         // ----------------------------------------------------------- producers
         const rsrc_t rA = make_rsrc(p.A, (uint32_t)M * K);
-        // fp8 A of stage u, direct to LDS: producer pw handles rows
-        // PROWS*pw .. +PROWS-1; its instruction j fills rows PROWS*pw + 8j..+7
+        // fp8 A of stage u, direct to LDS: producer pw (one per M tile)
+        // handles rows PROWS*pw .. +PROWS-1; its instruction j fills rows
+        // PROWS*pw + 8j..+7
         // (lane l: row ... + l/8, 16-byte chunk l%8)
         const int pw = wave - CONSUMERS;
         const int c = lane & 7, r0 = PROWS * pw + (lane >> 3);
@@ -221,9 +242,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         blo[sl] = load16(rB, live && k0 + 16 * g < K ? brow + k0 : kOob);
         bhi[sl] = load16(rB, live && k0 + 64 + 16 * g < K ? brow + k0 + 64 : kOob);
     };
-    v4f acc[MAX_M / 16];
+    v4f acc[MT];
 #pragma unroll
-    for (int i = 0; i < MAX_M / 16; ++i) acc[i] = v4f{};
+    for (int i = 0; i < MT; ++i) acc[i] = v4f{};
 
     static_for<RING - 1>([&](auto P) MXG_INLINE { fetch(decltype(P)::value, P); });
     for (int u0 = 0; u0 < nu; u0 += SCH) {
@@ -248,7 +269,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int i = 0; i < MAX_M / 16; ++i) {
+                    for (int i = 0; i < MT; ++i) {
                         const v8bf a = *reinterpret_cast<const v8bf *>(
                             al + a_addr(16 * i + r16, 2 * g + (q & 1) + 8 * (q >> 1)));
                         acc[i] = mfma_bf16_16(bq[q], a, acc[i]);
@@ -260,10 +281,71 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     // acc[i] register r of lane l: m = 16 i + l % 16, n = 16 w + 4 (l / 16) + r.
     const rsrc_t rC = make_rsrc((uint8_t *)p.C, (uint32_t)M * N * (p.out_bf16 ? 2 : 4));
+    const int n = n0 + 16 * w + 4 * g;
+    if (p.splits > 1) {
+        // Split K: every split leaves its fp32 partial tile in the workspace
+        // ([split][tile][64 rows][112 columns]); per consumer wave (16
+        // columns of the tile) a counter counts the splits that are done, and
+        // the wave that completes the count adds the partials in split order
+        // 0, 1, ..., so the result does not depend on which split finishes
+        // last.  That wave also resets the counter for the next call.
+        // Partials are written and read with device-scope coherent (sc1)
+        // buffer accesses, the encoding of agent-scope atomic loads and
+        // stores, so they bypass the per-XCD L2s' non-coherent copies: the
+        // wait for this wave's stores to complete is the whole release, and
+        // no L2 writeback or invalidate is needed (a full agent-scope fence
+        // writes back the whole L2 and costs tens of microseconds here).
+        constexpr int TILE_F = MAX_M * BN;
+        constexpr int SC1 = 16;  // cache-policy bit of the buffer intrinsics
+        const rsrc_t rW = make_rsrc(p.ws, (uint32_t)(p.splits * p.tiles_n * TILE_F * 4));
+        const uint32_t lane_off = (uint32_t)(tile * TILE_F + r16 * BN + 16 * w + 4 * g) * 4;
+        const uint32_t split_pitch = (uint32_t)(p.tiles_n * TILE_F) * 4;
 #pragma unroll
-    for (int i = 0; i < MAX_M / 16; ++i) {
+        for (int i = 0; i < MT; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i]), rW,
+                                                   lane_off + sp * split_pitch + i * 16 * BN * 4,
+                                                   0, SC1);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partial has reached the coherent level
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        uint32_t *cnt = p.cnt + tile * CONSUMERS + w;
+        uint32_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = (uint32_t)__shfl((int)old, 0, 64);
+        if (old != (uint32_t)(p.splits - 1)) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the partials of up to QB splits are in flight at once (a split
+        // past the last reads zeros through the range check and is not
+        // added); they are summed in split order
+        constexpr int QB = 8;
+        for (int q0 = 0; q0 < p.splits; q0 += QB) {
+            v4f part[QB][MT];
+#pragma unroll
+            for (int qq = 0; qq < QB; ++qq)
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    part[qq][i] = __builtin_bit_cast(
+                        v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                 rW,
+                                 q0 + qq < p.splits
+                                     ? lane_off + (q0 + qq) * split_pitch + i * 16 * BN * 4
+                                     : kOob,
+                                 0, SC1));
+#pragma unroll
+            for (int qq = 0; qq < QB; ++qq)
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    if (q0 + qq == 0)
+                        acc[i] = part[qq][i];
+                    else if (q0 + qq < p.splits)
+                        acc[i] += part[qq][i];
+                }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
         const int m = 16 * i + r16;
-        const int n = n0 + 16 * w + 4 * g;
         store_c4(rC, (uint32_t)m * N + n, n, N, acc[i], p.out_bf16, p.use_acc, p.c_vec);
     }
 }

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert L.mxgemm_version() == 1
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = L.status_string(code)
         assert s and s != "unknown status"
     assert L.status_string(99) == "unknown status"
@@ -115,3 +115,20 @@ def test_quantize_rejects_bad_handle_without_gpu_work():
     with pytest.raises(L.MxgemmError) as e:
         L.mxgemm_quantize(None, 0x100000, 0, 64, 128, 0, 0x200000, 0x300000, stream=0)
     assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_HANDLE"]
+
+
+def test_split_k_entry_points_reject_bad_handle_without_gpu_work():
+    for call in (lambda: L.mxgemm_set_workspace(None, 0x100000, L.MXGEMM_WORKSPACE_BYTES, 0),
+                 lambda: L.mxgemm_set_workspace(None, None, 0),
+                 lambda: L.mxgemm_set_splits(None, 2)):
+        with pytest.raises(L.MxgemmError) as e:
+            call()
+        assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_HANDLE"]
+
+
+def test_workspace_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MXGEMM_WORKSPACE_BYTES \(\(size_t\)(\d+) \+ \(size_t\)(\d+) \* (\d+) \* (\d+) \* (\d+)\)", text)
+    assert m, "MXGEMM_WORKSPACE_BYTES not found"
+    a, b, c, d, e = map(int, m.groups())
+    assert a + b * c * d * e == L.MXGEMM_WORKSPACE_BYTES

@@ -1,0 +1,183 @@
+"""GPU parity of the small-M exact path's decode-size tiling and split-K.
+
+* M below 64 runs ceil(M/16) row tiles of 16 (and as many decoding waves);
+  every M from 1 to 64 that changes the tile count, or sits on either side
+  of a tile boundary, is compared with the oracle on full outputs.
+* Split-K (a caller-owned workspace attached to the handle): forced split
+  counts, ragged K, both formats, use_acc and bf16 output, against the
+  oracle; the fixed-order reduction gives bitwise-equal results on repeated
+  calls; the arrival counters are back at zero after every call, so calls
+  of different shapes in a row stay correct; the automatic choice at one
+  GPU's share of the M=64 decode workload (N = 3584) against sampled
+  oracle outputs; and the error paths.
+"""
+import numpy as np
+import pytest
+import torch
+
+import level_dsl_amd as L
+import mxinputs as mi
+from gpu_helpers import alloc_c, c_numpy, compare, log, oracle_full, oracle_points, run, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SKINNY = L.MXGEMM_VARIANT_SKINNY
+
+
+@pytest.fixture(scope="module")
+def gemm():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    g = L.Gemm()
+    yield g
+    g.close()
+
+
+@pytest.fixture(scope="module")
+def gemm_ws():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    g = L.Gemm()
+    g.enable_split_k()
+    yield g
+    g.close()
+
+
+@pytest.mark.parametrize("M", [1, 2, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64])
+def test_decode_size_m_full(gemm, M):
+    N, K = 250, 1056  # three column tiles (the last ragged), 8.25 K stages
+    p = mi.random_problem(M, N, K, seed=500 + M, fmtA=M % 2, fmtB=(M // 2) % 2)
+    log(f"decode-size M={M} N={N} K={K} fmt={p.fmtA}{p.fmtB}")
+    got = run(gemm, p, SKINNY, guard=64)
+    compare(got, oracle_full(p), p.out_dtype, f"M={M}")
+
+
+SPLIT_CASES = [
+    # M, N, K, splits, fmtA, fmtB, use_acc, out
+    (64, 250, 8192, 8, 0, 0, False, mi.OUT_F32),
+    (17, 112, 4128, 5, 0, 1, True, mi.OUT_BF16),     # 33 stages, the last partial
+    (1, 3, 1024, 8, 1, 0, False, mi.OUT_F32),        # one stage per split
+    (33, 500, 2080, 3, 1, 1, True, mi.OUT_F32),
+    (48, 130, 640, 64, 0, 0, False, mi.OUT_BF16),    # asks for 64, runs 5 (one per stage)
+    (64, 14336, 512, 2, 0, 0, False, mi.OUT_F32),    # 128 tiles x 2 splits: the workspace's limit
+]
+
+
+@pytest.mark.parametrize("M,N,K,S,fa,fb,acc,out", SPLIT_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}_s{c[3]}" for c in SPLIT_CASES])
+def test_split_k_forced(gemm_ws, M, N, K, S, fa, fb, acc, out):
+    p = mi.random_problem(M, N, K, seed=600 + S, fmtA=fa, fmtB=fb, out_dtype=out, use_acc=acc)
+    log(f"split-K forced S={S} M={M} N={N} K={K} fmt={fa}{fb} use_acc={acc} out={out}")
+    gemm_ws.set_splits(S)
+    try:
+        got = run(gemm_ws, p, SKINNY, guard=64)
+    finally:
+        gemm_ws.set_splits(0)
+    if M * N <= 64 * 500:
+        compare(got, oracle_full(p), out, f"S={S}")
+    else:
+        rows, cols = mi.sample_points(M, N, 8192, seed=S, edge=64)
+        compare(got[rows, cols], oracle_points(p, rows, cols), out, f"S={S} sampled")
+
+
+def test_split_k_bitwise_repeatable(gemm_ws):
+    """The partials are added in split order whatever order the splits
+    finish in: repeated calls give identical bits."""
+    p = mi.random_problem(64, 336, 8192, seed=611)
+    dev = to_dev(p)
+    gemm_ws.set_splits(8)
+    try:
+        outs = [run(gemm_ws, p, SKINNY, dev_inputs=dev) for _ in range(4)]
+    finally:
+        gemm_ws.set_splits(0)
+    log("split-K repeatability: 4 calls, S=8, 64x336x8192")
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    compare(outs[0], oracle_full(p), p.out_dtype, "S=8")
+
+
+def test_split_k_counters_reset_across_calls(gemm_ws):
+    """Calls of different shapes and split counts in a row, without any
+    host-side reset in between: each is right, so every call leaves the
+    arrival counters at zero."""
+    cases = [(64, 224, 2048, 4), (5, 700, 1024, 3), (64, 224, 2048, 7), (16, 10, 4096, 8),
+             (64, 224, 2048, 2)]
+    for i, (M, N, K, S) in enumerate(cases):
+        p = mi.random_problem(M, N, K, seed=620 + i)
+        log(f"counter reset case {i}: S={S} M={M} N={N} K={K}")
+        gemm_ws.set_splits(S)
+        try:
+            got = run(gemm_ws, p, SKINNY, guard=16)
+        finally:
+            gemm_ws.set_splits(0)
+        compare(got, oracle_full(p), p.out_dtype, f"case {i}")
+
+
+def test_split_k_auto_sharded_decode(gemm_ws):
+    """One GPU's share of the M=64, N=28672, K=8192 decode workload when its
+    columns are split over 8 GPUs: N = 3584 gives 32 column tiles, so the
+    automatic choice splits K 8 ways (256 workgroups)."""
+    M, N, K = 64, 3584, 8192
+    p = mi.random_problem(M, N, K, seed=630)
+    log(f"auto split at M={M} N={N} K={K}")
+    got = run(gemm_ws, p, L.MXGEMM_VARIANT_AUTO, guard=64)
+    rows, cols = mi.sample_points(M, N, 16384, seed=630, edge=64)
+    compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "auto split")
+    # the same call without a workspace (unsplit) agrees within the rule
+    g = L.Gemm()
+    try:
+        plain = run(g, p, L.MXGEMM_VARIANT_AUTO)
+    finally:
+        g.close()
+    compare(plain[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "unsplit")
+
+
+def test_forced_split_without_workspace_is_an_error(gemm):
+    p = mi.random_problem(64, 200, 2048, seed=640)
+    A, As, B, Bs = to_dev(p)
+    buf, c = alloc_c(p)
+    gemm.set_splits(4)
+    try:
+        with pytest.raises(L.MxgemmError) as e:
+            L.mxgemm_run(gemm.h, A, As, p.fmtA, B, Bs, p.fmtB, c, p.M, p.N, p.K, 0, 0)
+        assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_WORKSPACE"]
+    finally:
+        gemm.set_splits(0)
+    torch.cuda.synchronize()
+    assert torch.isnan(c).all(), "C touched by a rejected call"
+
+
+def test_set_workspace_rejects_short_or_misaligned():
+    g = L.Gemm()
+    try:
+        ws = torch.empty(L.MXGEMM_WORKSPACE_BYTES + 256, dtype=torch.uint8, device="cuda:0")
+        for ptr, n in ((ws.data_ptr(), L.MXGEMM_WORKSPACE_BYTES - 1),
+                       (ws.data_ptr() + 16, L.MXGEMM_WORKSPACE_BYTES)):
+            with pytest.raises(L.MxgemmError) as e:
+                L.mxgemm_set_workspace(g.h, ptr, n)
+            assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_WORKSPACE"]
+        with pytest.raises(L.MxgemmError) as e:
+            L.mxgemm_set_splits(g.h, -1)
+        assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_SHAPE"]
+    finally:
+        g.close()
+
+
+def test_split_k_alternating_problems_never_see_stale_partials(gemm_ws):
+    """Two problems of the same shape alternate on one workspace, ten calls
+    each: a partial left over from the other problem (a store not yet
+    visible, or a stale cached copy) would change the bits of a result, so
+    every call must reproduce the first result of its problem exactly."""
+    M, N, K = 64, 3584, 8192
+    probs = [mi.random_problem(M, N, K, seed=650 + j) for j in range(2)]
+    devs = [to_dev(p) for p in probs]
+    first = [None, None]
+    for it in range(20):
+        j = it % 2
+        got = run(gemm_ws, probs[j], L.MXGEMM_VARIANT_AUTO, dev_inputs=devs[j])
+        if first[j] is None:
+            first[j] = got
+            rows, cols = mi.sample_points(M, N, 4096, seed=650 + j, edge=32)
+            compare(got[rows, cols], oracle_points(probs[j], rows, cols), probs[j].out_dtype,
+                    f"problem {j}")
+        else:
+            assert np.array_equal(got.view(np.uint32), first[j].view(np.uint32)), f"call {it}"
+    log("alternating split-K calls: 20 calls reproduced their first results")
