@@ -146,7 +146,7 @@ COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
 # key: (kernel name as rocprofv3 prints it, workload id, variant, C bytes per element)
 TRAFFIC_KERNELS = {"large_exact": ("void mxg::large::kernel<0, 0, false, true>", 2,
                                    "MXGEMM_VARIANT_LARGE", 2),
-                   "skinny_exact": ("void mxg::stream::kernel<0, 0, true>", 3,
+                   "skinny_exact": ("void mxg::stream::kernel<0, 0, true, 4>", 3,
                                     "MXGEMM_VARIANT_SKINNY", 4)}
 QUANT_KERNEL = "void mxg::quant::kernel<0, 0>"
 QUANT_SHAPE = (28672, 8192)  # the skinny workload's weight, N x K
@@ -376,7 +376,7 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(sbytes / mean_ss / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": traffic_from_profiles("skinny_exact"),
-                     "kernel": "mxg::stream::kernel<0,0,true>",
+                     "kernel": "mxg::stream::kernel<0,0,true,4>",
                      "launch_mean_us": round(mean_ss * 1e6, 2)},
         "algorithmic_bytes": sbytes, "steps": sk_steps, "b_rotation": 3}
     log(f"bench: skinny {out['skinny_m64']['value']} GB/s")
