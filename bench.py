@@ -144,7 +144,7 @@ def bench_gemm(gemm, p, variant, steps, warmup, copies):
 
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
 # key: (kernel name as rocprofv3 prints it, workload id, variant, C bytes per element)
-TRAFFIC_KERNELS = {"large_exact": ("void mxg::large::kernel<0, 0, false, true>", 2,
+TRAFFIC_KERNELS = {"large_exact": ("void mxg::large::kernel<0, 0, false, true, false>", 2,
                                    "MXGEMM_VARIANT_LARGE", 2),
                    "skinny_exact": ("void mxg::stream::kernel<0, 0, true, 4>", 3,
                                     "MXGEMM_VARIANT_SKINNY", 4)}
@@ -347,7 +347,7 @@ def main():
         "pct_of_mxfp8_peak": round(100 * value / PEAK_TFLOPS["fp8"], 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": traffic, "kernel": "mxg::large::kernel<0,0,false,true>",
+                     "traffic": traffic, "kernel": "mxg::large::kernel<0,0,false,true,false>",
                      "launch_mean_us": round(mean_s * 1e6, 2)},
     })
 

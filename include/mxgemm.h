@@ -101,9 +101,13 @@ enum {
 #define MXGEMM_MAX_MN ((int64_t)1 << 36) /* M * N: C up to 256 GiB of fp32 */
 #define MXGEMM_MAX_QELEMS ((int64_t)1 << 38) /* R * K of one mxgemm_quantize call */
 
-/* Bytes of the split-K workspace: 4 KiB of arrival counters, then room for
- * 256 fp32 partial tiles of 64 x 112. */
+/* Bytes of a split-K workspace: 4 KiB of arrival counters, then partial
+ * tiles.  MXGEMM_WORKSPACE_BYTES (the minimum) holds 256 fp32 partials of
+ * 64 x 112, enough for every small-M split; the 256 x 256 tiles of larger M
+ * take 256 KiB each, and MXGEMM_WORKSPACE_BYTES_LARGE holds 256 of them, so
+ * that no large-M split count is cut short by the workspace. */
 #define MXGEMM_WORKSPACE_BYTES ((size_t)4096 + (size_t)256 * 64 * 112 * 4)
+#define MXGEMM_WORKSPACE_BYTES_LARGE ((size_t)4096 + (size_t)256 * 256 * 256 * 4)
 
 /* Library ABI version (this header: 1). */
 int mxgemm_version(void);
@@ -127,8 +131,11 @@ int mxgemm_set_variant(mxgemm_t h, int variant);
 
 /* Attach a caller-owned device buffer of at least MXGEMM_WORKSPACE_BYTES
  * (256-byte aligned) to the handle, or detach it with ws = NULL.  With a
- * workspace attached, exact small-M calls (M <= 64) whose N gives fewer
- * than 129 column tiles of 112 split K over several workgroups.  The TLX
+ * workspace attached, calls that leave most of the 256 CUs idle split K
+ * over several workgroups: exact small-M calls (M <= 64) whose N gives at
+ * most 128 column tiles of 112, and M > 64 calls with at most 128 output
+ * tiles of 256 x 256 (as many splits as the workspace holds partials for,
+ * `bytes` counting; MXGEMM_WORKSPACE_BYTES_LARGE never limits them).  The TLX
  * global-memory page offers an atomic buffer add (tlx.buffer_atomic_add) for
  * such partial sums; here instead every split writes an fp32 partial tile to
  * the workspace and the last split of each tile to finish adds the partials
@@ -140,12 +147,14 @@ int mxgemm_set_variant(mxgemm_t h, int variant);
  * and workspace).  MXGEMM_ERR_WORKSPACE for a short or misaligned buffer. */
 int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream);
 
-/* Number of K splits for exact small-M calls: 0 (default) chooses it from
- * the shape, 1 never splits, S >= 2 forces S splits, reduced to at most the
- * number of 128-byte K stages and to 256 / column tiles (so tiles_n * S <=
- * 256).  A forced S >= 2 that survives this makes mxgemm_run return
- * MXGEMM_ERR_WORKSPACE when no workspace is attached.  MXGEMM_ERR_SHAPE for
- * S < 0. */
+/* Number of K splits: 0 (default) chooses it from the shape, 1 never
+ * splits, S >= 2 forces S splits, reduced to at most the number of 128-byte
+ * K stages (of 4-stage groups where the large kernel reads 16-byte scale
+ * windows, i.e. K % 512 == 0), to 256 / output tiles, and to the partials
+ * the workspace holds.  Applies to the exact small-M kernel and to both
+ * large-kernel variants, not to the native small-M kernel.  A forced S >= 2
+ * that survives this makes mxgemm_run return MXGEMM_ERR_WORKSPACE when no
+ * workspace is attached.  MXGEMM_ERR_SHAPE for S < 0. */
 int mxgemm_set_splits(mxgemm_t h, int splits);
 
 /* Check the arguments of mxgemm_run without touching the GPU: pointers

@@ -31,6 +31,7 @@ MXGEMM_VARIANT_SKINNY = 2
 MXGEMM_VARIANT_LARGE_NATIVE = 3
 MXGEMM_VARIANT_SKINNY_NATIVE = 4
 MXGEMM_WORKSPACE_BYTES = 4096 + 256 * 64 * 112 * 4
+MXGEMM_WORKSPACE_BYTES_LARGE = 4096 + 256 * 256 * 256 * 4
 
 STATUS = {0: "MXGEMM_OK", 1: "MXGEMM_ERR_NULL", 2: "MXGEMM_ERR_FMT", 3: "MXGEMM_ERR_DTYPE",
           4: "MXGEMM_ERR_SHAPE", 5: "MXGEMM_ERR_ALIGN", 6: "MXGEMM_ERR_DEVICE",
@@ -198,13 +199,13 @@ class Gemm:
     def set_variant(self, variant: int):
         mxgemm_set_variant(self.h, variant)
 
-    def enable_split_k(self, device="cuda:0", stream=None):
+    def enable_split_k(self, device="cuda:0", stream=None, nbytes=MXGEMM_WORKSPACE_BYTES_LARGE):
         """Give the handle its own split-K workspace (a torch allocation that
         this object keeps alive); calls through this handle must then be
-        ordered on one stream."""
+        ordered on one stream.  The default size never limits a split."""
         if getattr(self, "workspace", None) is None:
-            self.workspace = torch.empty(MXGEMM_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
-            mxgemm_set_workspace(self.h, self.workspace, MXGEMM_WORKSPACE_BYTES, stream)
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            mxgemm_set_workspace(self.h, self.workspace, nbytes, stream)
 
     def disable_split_k(self):
         if getattr(self, "workspace", None) is not None:

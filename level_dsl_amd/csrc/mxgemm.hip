@@ -26,6 +26,7 @@ struct mxgemm_ctx {
     int variant;
     int splits;      // 0 automatic, 1 never, S >= 2 forced
     uint8_t *ws;     // caller's split-K workspace, or NULL
+    size_t ws_bytes;
 };
 
 namespace {
@@ -39,22 +40,31 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
     return x < y + nb && y < x + na;
 }
 
-template <int FA, int FB, bool NATIVE>
-hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
+template <int FA, int FB, bool NATIVE, bool SPLIT>
+hipError_t launch_large_s(const mxg::GemmArgs &a, hipStream_t s)
 {
-    const int blocks = a.tiles_m * a.tiles_n;
+    const int blocks = a.tiles_m * a.tiles_n * a.splits;
     // 16-byte scale windows need K % 512 == 0 and 16-byte aligned scale rows;
     // the native variant has no registers to spare for them
     if constexpr (!NATIVE) {
         if (a.scale_dword == 2) {
-            hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, true>), dim3(blocks),
+            hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, true, SPLIT>), dim3(blocks),
                                dim3(mxg::large::THREADS), 0, s, a);
             return hipGetLastError();
         }
     }
-        hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, false>), dim3(blocks),
-                           dim3(mxg::large::THREADS), 0, s, a);
+    hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, false, SPLIT>), dim3(blocks),
+                       dim3(mxg::large::THREADS), 0, s, a);
     return hipGetLastError();
+}
+
+// Split launches use their own instantiation, so that the split epilogue
+// adds nothing to the register budget of the unsplit kernel.
+template <int FA, int FB, bool NATIVE>
+hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
+{
+    return a.splits > 1 ? launch_large_s<FA, FB, NATIVE, true>(a, s)
+                        : launch_large_s<FA, FB, NATIVE, false>(a, s);
 }
 
 template <int FA, int FB, bool NATIVE>
@@ -101,6 +111,12 @@ static_assert(MXGEMM_WORKSPACE_BYTES ==
               "workspace layout");
 static_assert((256 / 2) * mxg::stream::CONSUMERS * sizeof(uint32_t) <= kCounterBytes,
               "one counter per consumer wave of every split tile");
+static_assert((256 / 2) * mxg::large::WAVES * sizeof(uint32_t) <= kCounterBytes,
+              "one counter per wave of every split tile");
+constexpr size_t kLargePartial = (size_t)mxg::large::BM * mxg::large::BN * sizeof(float);
+static_assert(MXGEMM_WORKSPACE_BYTES_LARGE ==
+                  kCounterBytes + (size_t)mxg::stream::MAX_SPLITS_TILES * kLargePartial,
+              "large workspace layout");
 
 // K splits of an exact small-M call: none unless asked for or the column
 // tiles leave more than half of the 256 CUs idle; then the largest power of
@@ -122,6 +138,34 @@ int choose_splits(int forced, int tiles_n, int nk)
         while (2 * s <= cap) s *= 2;
     }
     s = std::min(s, std::min(nk, kTarget / tiles_n));
+    return std::max(s, 1);
+}
+
+// K splits of a large-kernel call, in the same way over its split units
+// (4-stage scale windows when it reads 16-byte scale windows, else stages),
+// further limited by how many 256 KiB partial tiles the workspace holds.
+int choose_splits_large(int forced, int tiles, int units, int unit_stages, size_t ws_bytes)
+{
+    constexpr int kTarget = mxg::stream::MAX_SPLITS_TILES, kMinStages = 8, kMaxAuto = 8;
+    const int fit = ws_bytes > kCounterBytes
+                        ? (int)std::min<size_t>((ws_bytes - kCounterBytes) / ((size_t)tiles * kLargePartial),
+                                                (size_t)kTarget)
+                        : 0;
+    int s;
+    if (forced >= 1) {
+        s = forced;
+    } else if (tiles > kTarget / 2) {
+        s = 1;
+    } else {
+        const int per = (kMinStages + unit_stages - 1) / unit_stages;  // units per split, at least
+        const int cap = std::min(kMaxAuto, std::min(kTarget / tiles, units / per));
+        s = 1;
+        while (2 * s <= cap) s *= 2;
+    }
+    s = std::min(s, std::min(units, kTarget / tiles));
+    // with a workspace attached, never more splits than it holds partials for
+    // (ws_bytes == 0: none attached; the caller turns a forced split into an error)
+    if (ws_bytes) s = std::min(s, fit);
     return std::max(s, 1);
 }
 
@@ -193,6 +237,7 @@ int mxgemm_create(mxgemm_t *out)
     h->variant = MXGEMM_VARIANT_AUTO;
     h->splits = 0;
     h->ws = nullptr;
+    h->ws_bytes = 0;
     *out = h;
     return MXGEMM_OK;
 }
@@ -220,6 +265,7 @@ int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream)
     if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
     if (!ws) {
         h->ws = nullptr;
+        h->ws_bytes = 0;
         return MXGEMM_OK;
     }
     if (bytes < MXGEMM_WORKSPACE_BYTES || ((uintptr_t)ws & 255u)) return MXGEMM_ERR_WORKSPACE;
@@ -231,6 +277,7 @@ int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream)
                        (uint32_t *)ws, words);
     if (hipGetLastError() != hipSuccess) return MXGEMM_ERR_HIP;
     h->ws = (uint8_t *)ws;
+    h->ws_bytes = bytes;
     return MXGEMM_OK;
 }
 
@@ -324,6 +371,21 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     } else {
         a.tiles_m = (int)((M + mxg::large::BM - 1) / mxg::large::BM);
         a.tiles_n = (int)((N + mxg::large::BN - 1) / mxg::large::BN);
+        const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+        if (tiles <= mxg::stream::MAX_SPLITS_TILES / 2) {
+            const int nk = (int)((K + mxg::large::BK - 1) / mxg::large::BK);
+            const bool scale16 = !native && a.scale_dword == 2;  // the kernel's SCALE16
+            const int unit = scale16 ? mxg::large::WINDOW : 1;
+            a.splits = choose_splits_large(h->splits, (int)tiles, nk / unit, unit, h->ws_bytes);
+            if (a.splits > 1 && !h->ws) {
+                if (h->splits >= 2) return MXGEMM_ERR_WORKSPACE;
+                a.splits = 1;
+            }
+            if (a.splits > 1) {
+                a.cnt = (uint32_t *)h->ws;
+                a.ws = (float *)(h->ws + kCounterBytes);
+            }
+        }
     }
     const int f = fmtA * 2 + fmtB;
     const hipError_t e = native ? dispatch<true>(skinny, f, a, stream)

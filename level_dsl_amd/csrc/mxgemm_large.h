@@ -111,15 +111,20 @@ struct Raw<true> {};  // native fragments are read straight into the operand reg
 constexpr int SG_VALU = 0x002, SG_SALU = 0x004, SG_MFMA = 0x008, SG_VMEM_RD = 0x020,
               SG_DS_RD = 0x100;
 
-template <int FA, int FB, bool NATIVE, bool SCALE16>
+template <int FA, int FB, bool NATIVE, bool SCALE16, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
     constexpr int BLOCKS = NATIVE ? 2 : 4;               // blocks per stage
     constexpr int MF = NATIVE ? SUB_M * SUB_N : 2 * SUB_M * SUB_N;  // MFMAs per block
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][TILE_BYTES];  // [stage][A/B]
 
+    // workgroup -> (tile, K split); split sp runs stages [ks0, ks0 + nk) of
+    // the nk_all stages (whole 4-stage scale windows when SCALE16)
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int tile = SPLIT ? (int)(blockIdx.x % (unsigned)ntiles) : (int)blockIdx.x;
+    const int sp = SPLIT ? (int)(blockIdx.x / (unsigned)ntiles) : 0;
     int tm, tn;
-    tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    tile_of(tile, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
     const int K = p.K, KB = p.KB;
@@ -134,7 +139,11 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int lrow = lane & 31, khalf = lane >> 5;
-    const int nk = (K + BK - 1) / BK;
+    const int nk_all = (K + BK - 1) / BK;
+    constexpr int SPLIT_UNIT = SCALE16 ? WINDOW : 1;  // stages a split boundary is a multiple of
+    const int nu_all = nk_all / SPLIT_UNIT;           // SCALE16 needs K % 512 == 0: no remainder
+    const int ks0 = SPLIT ? (int)((int64_t)sp * nu_all / p.splits) * SPLIT_UNIT : 0;
+    const int nk = SPLIT ? (int)((int64_t)(sp + 1) * nu_all / p.splits) * SPLIT_UNIT - ks0 : nk_all;
 
     // ---- global -> LDS, one stage ---------------------------------------
     // A stage's two operands are loaded at different points of the K loop
@@ -148,9 +157,10 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // read as zero (every offset is out of range), so the call needs no guard.
     const int gc0 = (lane & 7) ^ (lane >> 3);  // chunk for even segments; odd: gc0 ^ 1
     const uint32_t grow = (uint32_t)(8 * SEGS_PER_WAVE * wave + (lane >> 3)) * K;
-    // operand OP (0: A, 1: B) of the stage starting at K offset k0 into LDS stage st
-    auto gload = [&](int st, int k0, auto OP) MXG_INLINE {
+    // operand OP (0: A, 1: B) of the stage starting at local K offset kl into LDS stage st
+    auto gload = [&](int st, int kl, auto OP) MXG_INLINE {
         constexpr int op = decltype(OP)::value;
+        const int k0 = kl + ks0 * BK;
 #pragma unroll
         for (int j = 0; j < SEGS_PER_WAVE; ++j) {
             const int s = SEGS_PER_WAVE * wave + j;
@@ -165,16 +175,16 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // wn*128 + 32j + lrow.  SCALE16: 16 bytes (4 stages) per row and load;
     // otherwise one dword (or four bytes) per row and stage.
     const uint32_t sra = (uint32_t)(wm * WAVE_M + lrow), srb = (uint32_t)(wn * WAVE_N + lrow);
-    auto scale16 = [&](int kt, v4i *xa, v4i *xb) MXG_INLINE {  // window starting at stage kt
-        const int kb0 = kt * (BK / 32);
+    auto scale16 = [&](int kt, v4i *xa, v4i *xb) MXG_INLINE {  // window starting at local stage kt
+        const int kb0 = (ks0 + kt) * (BK / 32);
         const bool in = kb0 < KB;
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) xa[i] = load16(rAs, in ? (sra + 32 * i) * KB + kb0 : kOob);
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) xb[j] = load16(rBs, in ? (srb + 32 * j) * KB + kb0 : kOob);
     };
-    auto scale4 = [&](int kt, uint32_t *xa, uint32_t *xb) MXG_INLINE {  // stage kt
-        const int kb0 = kt * (BK / 32);
+    auto scale4 = [&](int kt, uint32_t *xa, uint32_t *xb) MXG_INLINE {  // local stage kt
+        const int kb0 = (ks0 + kt) * (BK / 32);
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) xa[i] = load_scale4(rAs, sra + 32 * i, KB, kb0, p.scale_dword);
 #pragma unroll
@@ -446,22 +456,90 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // ---- epilogue ---------------------------------------------------------
     // acc[i][j] register r of lane l: m = 32 i + (l % 32),
     // n = 32 j + 8 (r / 4) + 4 (l / 32) + (r % 4), relative to the wave tile.
+    // Group x = 4 (SUB_N i + j) + g of a lane is registers 4g..4g+3 of acc[i][j].
     const int esz = p.out_bf16 ? 2 : 4;
     const rsrc_t rC = make_rsrc((uint8_t *)p.C + ((size_t)m0 * p.N) * esz,
                                 (uint32_t)rows_a * p.N * esz);
     const int N = p.N;
+    auto store_group = [&](int i, int j, int g, v4f v) MXG_INLINE {
+        const int m = wm * WAVE_M + i * 32 + lrow;                      // tile-local row
+        const int n = n0 + wn * WAVE_N + j * 32 + 8 * g + 4 * khalf;  // global column
+        store_c4(rC, (uint32_t)m * N + n, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
+    };
+    constexpr int GROUPS = SUB_M * SUB_N * 4;  // 16-byte groups per lane
+
+    if constexpr (SPLIT) {
+        // Split K (p.splits > 1): every split stores its wave's fp32 partial
+        // (the 64 groups of each lane, 1 KiB per store instruction) with
+        // device-coherent (sc1) buffer stores; per (tile, wave) an arrival
+        // counter counts the splits that are done, and the wave that
+        // completes the count adds all partials in split order 0, 1, ...
+        // (deterministic), PER groups at a time, writes them to C and resets
+        // the counter.  The sc1 accesses bypass the per-XCD L2s'
+        // non-coherent copies, so waiting for the stores to complete is the
+        // whole release (no L2 writeback).
+        constexpr int SC1 = 16;
+        constexpr uint32_t WAVE_PART = GROUPS * 64 * 16;  // one wave's partial, bytes
+        // the lane index again (mbcnt), so that nothing lane-dependent has to
+        // stay live across the main loop for this path
+        const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        const rsrc_t rW = make_rsrc(p.ws, (uint32_t)p.splits * ntiles * WAVES * WAVE_PART);
+        const uint32_t lane_off = (uint32_t)(tile * WAVES + wave) * WAVE_PART + lane * 16;
+        const uint32_t split_pitch = (uint32_t)ntiles * WAVES * WAVE_PART;
+        static_for<GROUPS>([&](auto X) MXG_INLINE {
+            constexpr int x = decltype(X)::value, i = x / (SUB_N * 4), j = (x / 4) % SUB_N,
+                          g = x % 4;
+            const v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rW,
+                                                   lane_off + sp * split_pitch + x * 1024, 0, SC1);
+        });
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partial has reached the coherent level
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        uint32_t *cnt = p.cnt + tile * WAVES + wave;
+        uint32_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = (uint32_t)__shfl((int)old, 0, 64);
+        if (old != (uint32_t)(p.splits - 1)) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        constexpr int PER = 8;  // groups summed at a time (loads in flight per split)
+        static_for<GROUPS / PER>([&](auto Bt) MXG_INLINE {
+            constexpr int b = decltype(Bt)::value;
+            v4f sum[PER];
+            for (int q = 0; q < p.splits; ++q) {
+                v4f part[PER];
+                static_for<PER>([&](auto Y) MXG_INLINE {
+                    constexpr int y = decltype(Y)::value;
+                    part[y] = __builtin_bit_cast(
+                        v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                 rW, lane_off + q * split_pitch + (b * PER + y) * 1024, 0, SC1));
+                });
 #pragma unroll
-    for (int i = 0; i < SUB_M; ++i) {
-        const int m = wm * WAVE_M + i * 32 + lrow;  // tile-local row
+                for (int y = 0; y < PER; ++y) sum[y] = q == 0 ? part[y] : sum[y] + part[y];
+            }
+            static_for<PER>([&](auto Y) MXG_INLINE {
+                constexpr int x = b * PER + decltype(Y)::value;
+                store_group(x / (SUB_N * 4), (x / 4) % SUB_N, x % 4, sum[decltype(Y)::value]);
+            });
+        });
+
+    } else {
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) {
+        for (int i = 0; i < SUB_M; ++i) {
+            const int m = wm * WAVE_M + i * 32 + lrow;  // tile-local row
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WAVE_N + j * 32 + 8 * g + 4 * khalf;  // global column
-                const uint32_t e0 = (uint32_t)m * N + n;                        // element index
-                v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                         acc[i][j][4 * g + 3]};
-                store_c4(rC, e0, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
+            for (int j = 0; j < SUB_N; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * WAVE_N + j * 32 + 8 * g + 4 * khalf;  // global column
+                    const uint32_t e0 = (uint32_t)m * N + n;                        // element index
+                    v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                             acc[i][j][4 * g + 3]};
+                    store_c4(rC, e0, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
+                }
             }
         }
     }

@@ -132,3 +132,11 @@ def test_workspace_size_matches_header():
     assert m, "MXGEMM_WORKSPACE_BYTES not found"
     a, b, c, d, e = map(int, m.groups())
     assert a + b * c * d * e == L.MXGEMM_WORKSPACE_BYTES
+
+
+def test_large_workspace_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MXGEMM_WORKSPACE_BYTES_LARGE \(\(size_t\)(\d+) \+ \(size_t\)(\d+) \* (\d+) \* (\d+) \* (\d+)\)", text)
+    assert m, "MXGEMM_WORKSPACE_BYTES_LARGE not found"
+    a, b, c, d, e = map(int, m.groups())
+    assert a + b * c * d * e == L.MXGEMM_WORKSPACE_BYTES_LARGE

@@ -10,6 +10,12 @@
   of different shapes in a row stay correct; the automatic choice at one
   GPU's share of the M=64 decode workload (N = 3584) against sampled
   oracle outputs; and the error paths.
+* Split-K of the 256 x 256-tile kernel (M > 64): forced split counts over
+  4-stage scale windows (K % 512 == 0) and over single stages (other K),
+  both variants (the native one against its own bound), use_acc and bf16;
+  the automatic choice at medium M and at few output tiles; bitwise
+  repeatability; and a workspace too small for the asked-for split, which
+  must cut the split count, not overrun the buffer.
 """
 import numpy as np
 import pytest
@@ -17,11 +23,13 @@ import torch
 
 import level_dsl_amd as L
 import mxinputs as mi
-from gpu_helpers import alloc_c, c_numpy, compare, log, oracle_full, oracle_points, run, to_dev
+from gpu_helpers import (alloc_c, c_numpy, compare, compare_native, log, native_group_extra,
+                         oracle_full, oracle_points, run, to_dev)
 
 pytestmark = pytest.mark.gpu
 
 SKINNY = L.MXGEMM_VARIANT_SKINNY
+LARGE, LARGE_NATIVE = L.MXGEMM_VARIANT_LARGE, L.MXGEMM_VARIANT_LARGE_NATIVE
 
 
 @pytest.fixture(scope="module")
@@ -181,3 +189,83 @@ def test_split_k_alternating_problems_never_see_stale_partials(gemm_ws):
         else:
             assert np.array_equal(got.view(np.uint32), first[j].view(np.uint32)), f"call {it}"
     log("alternating split-K calls: 20 calls reproduced their first results")
+
+
+
+LARGE_SPLIT_CASES = [
+    # M, N, K, splits, fmtA, fmtB, use_acc, out
+    (300, 260, 4096, 4, 0, 0, False, mi.OUT_F32),     # 4 tiles; 8 windows -> 2 each
+    (257, 300, 2048, 3, 0, 1, True, mi.OUT_BF16),     # 4 windows over 3 splits (1, 1, 2)
+    (129, 513, 1056, 3, 1, 0, False, mi.OUT_F32),     # K % 512 != 0: 9 stages, 3 each
+    (80, 256, 640, 8, 1, 1, True, mi.OUT_F32),        # scale rows of 20 bytes: 5 stages, 5 splits
+    (512, 512, 8192, 64, 0, 0, False, mi.OUT_BF16),   # asks for 64: 16 windows -> 16 splits
+]
+
+
+@pytest.mark.parametrize("M,N,K,S,fa,fb,acc,out", LARGE_SPLIT_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}_s{c[3]}" for c in LARGE_SPLIT_CASES])
+def test_large_split_k_forced(gemm_ws, M, N, K, S, fa, fb, acc, out):
+    p = mi.random_problem(M, N, K, seed=700 + S + M, fmtA=fa, fmtB=fb, out_dtype=out, use_acc=acc)
+    ref = oracle_full(p)
+    dev = to_dev(p)
+    gemm_ws.set_splits(S)
+    try:
+        log(f"large split-K forced S={S} M={M} N={N} K={K} fmt={fa}{fb} use_acc={acc} out={out}")
+        got = run(gemm_ws, p, LARGE, guard=64, dev_inputs=dev)
+        compare(got, ref, out, f"large S={S}")
+        log(f"large native split-K forced S={S} M={M} N={N} K={K}")
+        got = run(gemm_ws, p, LARGE_NATIVE, guard=64, dev_inputs=dev)
+        compare_native(got, ref, out, native_group_extra(p), f"large native S={S}")
+    finally:
+        gemm_ws.set_splits(0)
+        gemm_ws.set_variant(L.MXGEMM_VARIANT_AUTO)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 28672, 8192), (1024, 1024, 8192), (200, 3000, 4096)])
+def test_large_split_k_auto(gemm_ws, M, N, K):
+    """Automatic split at medium M (one row of tiles) and at few output
+    tiles, against sampled oracle outputs; the unsplit result agrees too."""
+    p = mi.random_problem(M, N, K, seed=720 + M)
+    dev = to_dev(p)
+    rows, cols = mi.sample_points(M, N, 8192, seed=720 + M, edge=64)
+    ref = oracle_points(p, rows, cols)
+    log(f"large auto split M={M} N={N} K={K}")
+    got = run(gemm_ws, p, L.MXGEMM_VARIANT_AUTO, guard=64, dev_inputs=dev)
+    compare(got[rows, cols], ref, p.out_dtype, "auto split")
+    again = run(gemm_ws, p, L.MXGEMM_VARIANT_AUTO, dev_inputs=dev)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "not repeatable"
+    g = L.Gemm()
+    try:
+        plain = run(g, p, L.MXGEMM_VARIANT_AUTO, dev_inputs=dev)
+    finally:
+        g.close()
+    compare(plain[rows, cols], ref, p.out_dtype, "unsplit")
+
+
+def test_large_split_k_small_workspace_is_respected():
+    """A minimum-size workspace (room for 28 partial tiles of 256 x 256)
+    with 16 output tiles and 8 splits asked for: the split count must drop
+    to what fits (here 1), the bytes past the workspace stay untouched and
+    the result is right."""
+    M, N, K = 1024, 1024, 4096
+    p = mi.random_problem(M, N, K, seed=740)
+    guard = 1 << 20
+    buf = torch.full((L.MXGEMM_WORKSPACE_BYTES + guard,), 0x5A, dtype=torch.uint8, device="cuda:0")
+    g = L.Gemm()
+    try:
+        L.mxgemm_set_workspace(g.h, buf, L.MXGEMM_WORKSPACE_BYTES)
+        g.set_splits(8)
+        log("large split with a minimum-size workspace")
+        got = run(g, p, LARGE, guard=64)
+        torch.cuda.synchronize()
+        assert bool((buf[L.MXGEMM_WORKSPACE_BYTES:] == 0x5A).all()), "write past the workspace"
+        rows, cols = mi.sample_points(M, N, 4096, seed=740, edge=32)
+        compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "small workspace")
+        # 4 tiles fit 7 partials each: a split of 4 is honoured and correct
+        q = mi.random_problem(400, 400, 4096, seed=741)
+        g.set_splits(4)
+        got = run(g, q, LARGE, guard=64)
+        compare(got, oracle_full(q), q.out_dtype, "small workspace, 4 tiles x 4 splits")
+        assert bool((buf[L.MXGEMM_WORKSPACE_BYTES:] == 0x5A).all()), "write past the workspace"
+    finally:
+        g.close()
