@@ -22,7 +22,8 @@ tensor_id 0 = A, 1 = B, 2 = A_scale, 3 = B_scale, 4 = C_in.
 
 Layouts: A (M, K) row-major codes; B (N, K) codes with K contiguous
 (B_mem[n*K + k] = B[k, n]); A_scale (M, K/32) and B_scale (N, K/32)
-row-major bytes; C (M, N) row-major.
+row-major bytes; C (M, N) row-major.  An e2m1 operand (format 4) holds two
+codes per byte along K, the even k in the low nibble: (rows, K/2) bytes.
 """
 from __future__ import annotations
 
@@ -36,11 +37,14 @@ import torch
 SEED_ROOT = 0x4D58
 FMT_E4M3 = 0
 FMT_E5M2 = 1
+FMT_E2M1 = 4
 OUT_F32 = 0
 OUT_BF16 = 1
 
 # largest finite value of each format (OCP e4m3fn / e5m2)
-FMT_MAX = {FMT_E4M3: 448.0, FMT_E5M2: 57344.0}
+FMT_MAX = {FMT_E4M3: 448.0, FMT_E5M2: 57344.0, FMT_E2M1: 6.0}
+# e2m1 magnitudes in code order (codes 0..7; bit 3 is the sign)
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
 _TORCH_FP8 = {FMT_E4M3: torch.float8_e4m3fn, FMT_E5M2: torch.float8_e5m2}
 
 T_A, T_B, T_AS, T_BS, T_CIN = 0, 1, 2, 3, 4
@@ -51,8 +55,40 @@ def rng(workload: int, tensor_id: int) -> np.random.Generator:
         np.random.SeedSequence([SEED_ROOT, int(workload), int(tensor_id)])))
 
 
+def _quantize_e2m1(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> e2m1 codes 0..15 (unpacked): clamp to +-6, round to the
+    nearest grid value, ties to the even code (mantissa bit 0); the sign is
+    kept (-0 and tiny negatives give code 8)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    a = np.minimum(a, 6.0)
+    mid = (_E2M1_GRID[:-1] + _E2M1_GRID[1:]) / 2
+    idx = np.searchsorted(mid, a, side="left")            # first midpoint >= a
+    tie = (idx < mid.size) & (a == mid[np.minimum(idx, mid.size - 1)])
+    idx = np.where(tie & (idx % 2 == 1), idx + 1, idx)    # a tie goes to the even code
+    sign = np.signbit(np.asarray(x, dtype=np.float32)).astype(np.uint8)
+    return (idx.astype(np.uint8) | (sign << 3)).astype(np.uint8)
+
+
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """(rows, K) codes 0..15 -> (rows, K/2) bytes, the even k in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % 2 == 0
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_e2m1(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    out[..., 0::2] = p & 15
+    out[..., 1::2] = p >> 4
+    return out
+
+
 def quantize(x: np.ndarray, fmt: int) -> np.ndarray:
-    """fp32 values -> uint8 codes: clamp to +-max, then round to nearest even."""
+    """fp32 values -> uint8 codes: clamp to +-max, then round to nearest even.
+    e2m1 codes come back packed two per byte along the last axis."""
+    if fmt == FMT_E2M1:
+        return pack_e2m1(_quantize_e2m1(x))
     lim = np.float32(FMT_MAX[fmt])
     x = np.clip(np.asarray(x, dtype=np.float32), -lim, lim)
     t = torch.from_numpy(np.ascontiguousarray(x)).to(_TORCH_FP8[fmt])
@@ -108,9 +144,9 @@ class Problem:
     K: int
     fmtA: int
     fmtB: int
-    A: np.ndarray        # (M, K) uint8
+    A: np.ndarray        # (M, K) uint8; e2m1: (M, K/2), two codes per byte
     As: np.ndarray       # (M, ceil(K/32)) uint8
-    B: np.ndarray        # (N, K) uint8, K contiguous
+    B: np.ndarray        # (N, K) uint8, K contiguous; e2m1: (N, K/2)
     Bs: np.ndarray       # (N, ceil(K/32)) uint8
     out_dtype: int
     use_acc: bool

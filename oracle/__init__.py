@@ -78,8 +78,17 @@ def default_threads() -> int:
         return max(1, os.cpu_count() or 1)
 
 
+FMT_E2M1 = 4
+
+
+def packed_width(K: int, fmt: int) -> int:
+    """Bytes per operand row: K codes, or ceil(K/2) for e2m1 (two per byte)."""
+    return (K + 1) // 2 if fmt == FMT_E2M1 else K
+
+
 def decode_table(fmt: int, lib=None) -> np.ndarray:
-    """All 256 decoded values of a format (0 e4m3, 1 e5m2, 2 e8m0)."""
+    """All 256 decoded values of a format (0 e4m3, 1 e5m2, 2 e8m0, 4 e2m1,
+    whose codes above 15 decode to NaN)."""
     lib = lib or load()
     return np.array([lib.mxref_decode(fmt, c) for c in range(256)], dtype=np.float64)
 
@@ -99,7 +108,9 @@ def gemm_points(A, As, fmtA, B, Bs, fmtB, M, N, K, rows, cols,
                 cin=None, nthreads=None, lib=None):
     """Oracle outputs at points (rows[p], cols[p]).
 
-    A: (M, K) uint8 codes; B: (N, K) uint8 codes (K contiguous);
+    A: (M, K) uint8 codes; B: (N, K) uint8 codes (K contiguous); an e2m1
+    operand (fmt 4) is (rows, ceil(K/2)) bytes, two codes per byte, the even
+    k in the low nibble;
     As: (M, ceil(K/32)) and Bs: (N, ceil(K/32)) uint8 e8m0 bytes.
     cin: None (use_acc off), or the incoming (M, N) C as float32, or as
     uint16 bf16 bit patterns.
@@ -108,8 +119,8 @@ def gemm_points(A, As, fmtA, B, Bs, fmtB, M, N, K, rows, cols,
     """
     lib = lib or load()
     kb = (K + 31) // 32
-    A = np.ascontiguousarray(A, dtype=np.uint8).reshape(M, K)
-    B = np.ascontiguousarray(B, dtype=np.uint8).reshape(N, K)
+    A = np.ascontiguousarray(A, dtype=np.uint8).reshape(M, packed_width(K, fmtA))
+    B = np.ascontiguousarray(B, dtype=np.uint8).reshape(N, packed_width(K, fmtB))
     As = np.ascontiguousarray(As, dtype=np.uint8).reshape(M, kb)
     Bs = np.ascontiguousarray(Bs, dtype=np.uint8).reshape(N, kb)
     rows = np.ascontiguousarray(rows, dtype=np.int64).ravel()

@@ -20,6 +20,13 @@
  *     max 448); e5m2 is OCP (bias 15, IEEE-like inf/NaN, max 57344).
  *     The pages give only the names "e4m3"/"e5m2".
  *   - a scale byte s is e8m0: 2^(s-127) for s in 0..254, NaN for 255.
+ *   - e2m1 (the 4-bit member of the F8F6F4 operand family that the pages
+ *     name for the scaled WMMA) is OCP FP4 E2M1: sign | 2-bit exponent,
+ *     bias 1 | 1-bit mantissa, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, no
+ *     inf or NaN.  Its codes are packed two per byte along K (the default
+ *     lhs_k_pack / rhs_k_pack = True of dot_scaled): element k of a row is
+ *     the low nibble of byte k/2 when k is even, the high nibble when odd,
+ *     so a row of K elements takes ceil(K/2) bytes.
  *   - memory layout: A is M x K row-major bytes; B is stored K-contiguous
  *     ("K-major"), B_mem[n*K + k] = B[k,n]; scales are row-major
  *     M x KB and N x KB bytes with KB = ceil(K/32).
@@ -43,6 +50,8 @@
 #define MXREF_FMT_E4M3 0
 #define MXREF_FMT_E5M2 1
 #define MXREF_FMT_E8M0 2
+#define MXREF_FMT_E2M1 4
+#define MXREF_NTAB 5
 
 /* ---- format decoders, written from the OCP 8-bit float / MX definitions -- */
 
@@ -78,6 +87,22 @@ static double dec_e5m2(unsigned c)
     return s ? -v : v;
 }
 
+/* e2m1 (OCP FP4): sign | 2-bit exponent, bias 1 | 1-bit mantissa.
+ * exponent field 0 is subnormal: (m/2) * 2^(1-1); codes above 15 do not
+ * exist (NaN here). */
+static double dec_e2m1(unsigned c)
+{
+    if (c > 15u)
+        return NAN;
+    unsigned s = (c >> 3) & 1u, e = (c >> 1) & 3u, m = c & 1u;
+    double v;
+    if (e == 0u)
+        v = ldexp((double)m, 1 - 1 - 1);            /* m/2 */
+    else
+        v = ldexp((double)(2u + m), (int)e - 1 - 1); /* (1+m/2) * 2^(e-1) */
+    return s ? -v : v;
+}
+
 /* e8m0 scale: unsigned biased exponent, 2^(s-127); 255 is NaN. */
 static double dec_e8m0(unsigned s)
 {
@@ -86,7 +111,7 @@ static double dec_e8m0(unsigned s)
     return ldexp(1.0, (int)s - 127);
 }
 
-static double TAB[3][256];
+static double TAB[MXREF_NTAB][256];
 static pthread_once_t tab_once = PTHREAD_ONCE_INIT;
 
 static void build_tables(void)
@@ -95,6 +120,8 @@ static void build_tables(void)
         TAB[MXREF_FMT_E4M3][c] = dec_e4m3(c);
         TAB[MXREF_FMT_E5M2][c] = dec_e5m2(c);
         TAB[MXREF_FMT_E8M0][c] = dec_e8m0(c);
+        TAB[3][c] = NAN; /* no format 3 */
+        TAB[MXREF_FMT_E2M1][c] = dec_e2m1(c);
     }
 }
 
@@ -106,11 +133,11 @@ static const double *table(int fmt)
 
 int mxref_version(void) { return 1; }
 
-/* Decoded value of one code: fmt 0 = e4m3, 1 = e5m2, 2 = e8m0 scale.
- * Returns NaN for an unknown format. */
+/* Decoded value of one code: fmt 0 = e4m3, 1 = e5m2, 2 = e8m0 scale,
+ * 4 = e2m1 (codes 0..15).  Returns NaN for an unknown format or code. */
 double mxref_decode(int fmt, int code)
 {
-    if (fmt < 0 || fmt > 2 || code < 0 || code > 255)
+    if (fmt < 0 || fmt >= MXREF_NTAB || fmt == 3 || code < 0 || code > 255)
         return NAN;
     return table(fmt)[code];
 }
@@ -143,6 +170,8 @@ struct job {
     const void *Cin;
     int cin_dtype;               /* 0 fp32, 1 bf16 */
     const double *ta, *tb, *te;
+    int packA, packB;            /* e2m1: two codes per byte along K */
+    int64_t ldA, ldB;            /* bytes per operand row */
     int64_t M, N, K, KB;
     const int64_t *rows, *cols;
     int64_t p0, p1;
@@ -156,13 +185,15 @@ static void *run_job(void *arg)
     const struct job *j = (const struct job *)arg;
     for (int64_t p = j->p0; p < j->p1; ++p) {
         const int64_t m = j->rows[p], n = j->cols[p];
-        const uint8_t *a = j->A + m * j->K, *b = j->B + n * j->K;
+        const uint8_t *a = j->A + m * j->ldA, *b = j->B + n * j->ldB;
         const uint8_t *sa = j->As + m * j->KB, *sb = j->Bs + n * j->KB;
         double s = 0.0, mag = 0.0;
         for (int64_t k = 0; k < j->K; ++k) {
             /* decode(A[m,k]) * 2^(sa-127) and decode(B[k,n]) * 2^(sb-127) */
-            double av = j->ta[a[k]] * j->te[sa[k / 32]];
-            double bv = j->tb[b[k]] * j->te[sb[k / 32]];
+            const unsigned ca = j->packA ? (a[k / 2] >> (4 * (k % 2))) & 15u : a[k];
+            const unsigned cb = j->packB ? (b[k / 2] >> (4 * (k % 2))) & 15u : b[k];
+            double av = j->ta[ca] * j->te[sa[k / 32]];
+            double bv = j->tb[cb] * j->te[sb[k / 32]];
             double prod = av * bv;
             s += prod;
             mag += fabs(prod);
@@ -188,7 +219,8 @@ static void *run_job(void *arg)
 /*
  * Compute npts outputs C[rows[p], cols[p]].
  *   A: M*K codes, As: M*KB bytes, B: N*K codes (K-contiguous), Bs: N*KB,
- *   KB = ceil(K/32); fmtA/fmtB: 0 e4m3, 1 e5m2.
+ *   KB = ceil(K/32); fmtA/fmtB: 0 e4m3, 1 e5m2, 4 e2m1 (then the operand
+ *   holds ceil(K/2) bytes per row, two codes per byte, low nibble first).
  *   Cin: NULL (use_acc off) or the M*N incoming C, fp32 (cin_dtype 0) or
  *   bf16 bits (cin_dtype 1).
  *   Outputs (each may be NULL): sum_out/mag_out the double sum and sum of
@@ -206,7 +238,8 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *As, int fmtA,
                       uint16_t *refbf16_out, int nthreads)
 {
     if (!A || !As || !B || !Bs || !rows || !cols || M < 1 || N < 1 || K < 1 ||
-        npts < 0 || (fmtA != 0 && fmtA != 1) || (fmtB != 0 && fmtB != 1) ||
+        npts < 0 || (fmtA != 0 && fmtA != 1 && fmtA != MXREF_FMT_E2M1) ||
+        (fmtB != 0 && fmtB != 1 && fmtB != MXREF_FMT_E2M1) ||
         (Cin && cin_dtype != 0 && cin_dtype != 1))
         return -1;
     for (int64_t p = 0; p < npts; ++p)
@@ -223,6 +256,8 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *As, int fmtA,
     base.A = A; base.As = As; base.B = B; base.Bs = Bs;
     base.Cin = Cin; base.cin_dtype = cin_dtype;
     base.ta = table(fmtA); base.tb = table(fmtB); base.te = table(MXREF_FMT_E8M0);
+    base.packA = fmtA == MXREF_FMT_E2M1; base.packB = fmtB == MXREF_FMT_E2M1;
+    base.ldA = base.packA ? (K + 1) / 2 : K; base.ldB = base.packB ? (K + 1) / 2 : K;
     base.M = M; base.N = N; base.K = K; base.KB = (K + 31) / 32;
     base.rows = rows; base.cols = cols;
     base.sum_out = sum_out; base.mag_out = mag_out;

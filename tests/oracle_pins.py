@@ -487,9 +487,104 @@ def pin_quant_ragged_and_nonfinite(lib):
         raise AssertionError("non-finite input accepted")
 
 
+# ------------------------------------------------------------- e2m1 (FP4) --
+
+def _golden_e2m1():
+    out = []
+    with open(os.path.join(GOLDEN, "ocp_fp4_e2m1_values.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            code, val = line.split()
+            out.append((int(code, 16), _parse_value(val)))
+    return out
+
+
+def pin_e2m1_golden(lib):
+    """The e2m1 decoder against the OCP table (all 16 codes); codes above
+    15 do not exist."""
+    table = _golden_e2m1()
+    assert len(table) == 16
+    for code, val in table:
+        got = lib.mxref_decode(4, code)
+        assert same(got, val, signed_zero=True), f"e2m1 code {code:#x}: {got!r} != {val!r}"
+    assert np.isnan(oracle.decode_table(4, lib)[16:]).all()
+
+
+def _e2m1_as_e4m3(packed: np.ndarray) -> np.ndarray:
+    """Re-encode packed e2m1 codes as e4m3 codes of the same value, using the
+    test's own unpacking (low nibble = even k) and torch's e4m3 table."""
+    e4 = torch_decode(0)
+    vals = np.array([v for _, v in sorted(_golden_e2m1())])
+    codes = mxinputs.unpack_e2m1(packed)
+    want = vals[codes]
+    out = np.empty(codes.shape, np.uint8)
+    for c in range(16):
+        hit = np.flatnonzero((e4 == vals[c]) & (np.signbit(e4) == np.signbit(vals[c])))
+        assert hit.size, f"e2m1 value {vals[c]} is not an e4m3 value"
+        out[codes == c] = hit[0]
+    assert same(e4[out], want, signed_zero=True)
+    return out
+
+
+def pin_e2m1_embeds_in_e4m3(lib):
+    """Every e2m1 value is an e4m3 value, so an e2m1 problem and the same
+    problem re-encoded as e4m3 (unpacked by the test, decoded by torch) have
+    the same exact sums, bit for bit; this ties the packed path (nibble
+    order, row pitch, decode) to the pinned 8-bit path.  Mixed pairs too."""
+    for (M, N, K, fa, fb, seed) in ((5, 7, 64, 4, 4, 1), (3, 4, 1056, 4, 4, 2), (6, 2, 96, 4, 0, 3),
+                                    (2, 5, 128, 1, 4, 4), (1, 1, 32, 4, 4, 5)):
+        p = mxinputs.random_problem(M, N, K, seed=900 + seed, fmtA=fa, fmtB=fb, scale_lo=100,
+                                    scale_hi=150)
+        r = oracle.gemm_full(p.A, p.As, fa, p.B, p.Bs, fb, M, N, K, nthreads=2, lib=lib)
+        A8 = _e2m1_as_e4m3(p.A) if fa == 4 else p.A
+        B8 = _e2m1_as_e4m3(p.B) if fb == 4 else p.B
+        r8 = oracle.gemm_full(A8, p.As, 0 if fa == 4 else fa, B8, p.Bs, 0 if fb == 4 else fb,
+                              M, N, K, nthreads=2, lib=lib)
+        assert np.array_equal(r["sum"], r8["sum"]), f"e2m1 vs e4m3 re-encoding, case {seed}"
+        assert np.array_equal(r["mag"], r8["mag"])
+
+
+def pin_e2m1_integer_gemm(lib):
+    """Integer-valued e2m1 codes (0, +-1, +-2, +-3, +-4, +-6), unit scales:
+    C equals the int64 matrix product of the values the test packed."""
+    g = np.random.Generator(np.random.PCG64(77))
+    M, N, K = 19, 23, 544
+    choices = np.array([0, 1, 2, 3, 4, 6, -1, -2, -3, -4, -6])
+    ia = g.choice(choices, size=(M, K))
+    ib = g.choice(choices, size=(N, K))
+    A = mxinputs.quantize(ia.astype(np.float32), 4)
+    B = mxinputs.quantize(ib.astype(np.float32), 4)
+    assert A.shape == (M, K // 2)
+    As = np.full((M, K // 32), 127, np.uint8)
+    Bs = np.full((N, K // 32), 127, np.uint8)
+    r = oracle.gemm_full(A, As, 4, B, Bs, 4, M, N, K, nthreads=3, lib=lib)
+    want = ia.astype(np.int64) @ ib.astype(np.int64).T
+    assert np.array_equal(r["sum"], want.astype(np.float64)), "e2m1 integer gemm"
+
+
+def pin_e2m1_fraction(lib):
+    """Tiny random e2m1 problems against exact rational sums (values from
+    the golden table, the test's own unpacking)."""
+    vals = {c: Fraction(v) for c, v in _golden_e2m1()}
+    for i, (M, N, K) in enumerate(((2, 3, 64), (3, 2, 96), (1, 4, 32))):
+        p = mxinputs.random_problem(M, N, K, seed=950 + i, fmtA=4, fmtB=4, scale_lo=110,
+                                    scale_hi=140)
+        r = oracle.gemm_full(p.A, p.As, 4, p.B, p.Bs, 4, M, N, K, nthreads=1, lib=lib)
+        ca, cb = mxinputs.unpack_e2m1(p.A), mxinputs.unpack_e2m1(p.B)
+        for m in range(M):
+            for n in range(N):
+                exact = sum(vals[int(ca[m, k])] * Fraction(2) ** (int(p.As[m, k // 32]) - 127)
+                            * vals[int(cb[n, k])] * Fraction(2) ** (int(p.Bs[n, k // 32]) - 127)
+                            for k in range(K))
+                assert Fraction(r["sum"][m, n]) == exact, f"e2m1 case {i} ({m},{n})"
+
+
 ALL_PINS = [pin_tables_match_torch, pin_spot_values, pin_special_counts, pin_bf16_rne,
             pin_bruteforce_fraction, pin_pairwise_products, pin_closed_form,
             pin_integer_gemm, pin_scale_doubling, pin_permutation, pin_numpy_matmul,
             pin_nan_propagation, pin_thread_independence, pin_scale_tile_extent,
             pin_quant_rne_vs_torch, pin_quant_block_exponent, pin_quant_scale_invariance,
-            pin_quant_matches_generator, pin_quant_bf16_input, pin_quant_ragged_and_nonfinite]
+            pin_quant_matches_generator, pin_quant_bf16_input, pin_quant_ragged_and_nonfinite,
+            pin_e2m1_golden, pin_e2m1_embeds_in_e4m3, pin_e2m1_integer_gemm, pin_e2m1_fraction]

@@ -19,9 +19,9 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 
 MUTANTS = {
     "scale_block_16": ("j->te[sa[k / 32]]", "j->te[sa[k / 16]]"),
-    "dropped_b_scale": ("double bv = j->tb[b[k]] * j->te[sb[k / 32]];", "double bv = j->tb[b[k]];"),
+    "dropped_b_scale": ("double bv = j->tb[cb] * j->te[sb[k / 32]];", "double bv = j->tb[cb];"),
     "wrong_sign": ("s += prod;", "s -= prod;"),
-    "transposed_b_row": ("*b = j->B + n * j->K", "*b = j->B + (n % j->M) * j->K"),
+    "transposed_b_row": ("*b = j->B + n * j->ldB", "*b = j->B + (n % j->M) * j->ldB"),
     "a_scale_indexed_by_n": ("*sa = j->As + m * j->KB", "*sa = j->As + (n % j->M) * j->KB"),
     "e4m3_bias_8": ("(int)e - 7 - 3", "(int)e - 8 - 3"),
     "e4m3_no_subnormal": ("v = ldexp((double)m, 1 - 7 - 3);", "v = 0.0;"),
@@ -37,6 +37,12 @@ MUTANTS = {
     "quant_sign_dropped": ("(signbit(v) ? 0x80 : 0)", "0"),
     "quant_scale_inverted": ("ldexp(x[k - k0], 127 - s)", "ldexp(x[k - k0], s - 127)"),
     "quant_e4m3_max_480": ("return fmt == MXREF_FMT_E4M3 ? 448.0", "return fmt == MXREF_FMT_E4M3 ? 480.0"),
+    "e2m1_nibble_order_a": ("(a[k / 2] >> (4 * (k % 2)))", "(a[k / 2] >> (4 * (1 - k % 2)))"),
+    "e2m1_nibble_order_b": ("(b[k / 2] >> (4 * (k % 2)))", "(b[k / 2] >> (4 * (1 - k % 2)))"),
+    "e2m1_bias_0": ("(int)e - 1 - 1", "(int)e - 0 - 1"),
+    "e2m1_no_subnormal": ("v = ldexp((double)m, 1 - 1 - 1);", "v = 0.0;"),
+    "e2m1_row_pitch_k": ("base.ldA = base.packA ? (K + 1) / 2 : K;", "base.ldA = K;"),
+    "e2m1_sign_dropped": ("    return s ? -v : v;\n}\n\n/* e8m0", "    return v;\n}\n\n/* e8m0"),
     "quant_zero_block_scale": ("int s = 0;\n            if (amax > 0.0) {", "int s = 127;\n            if (amax > 0.0) {"),
 }
 
