@@ -46,7 +46,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X published dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}  # MI355X published dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
 METRIC = "MXFP8 GEMM TFLOP/s at 8192\u00b3 (% of dense MXFP8 peak); GB/s (% HBM) at M=64"
 KERNEL_SOURCES = ["level_dsl_amd/csrc/mxgemm.hip", "level_dsl_amd/csrc/mxgemm_common.h",
@@ -361,6 +361,25 @@ def main():
         "note": "v_mfma_scale_f32_32x32x64_f8f6f4; not within 1e-5*sum|ab| (8-product "
                 "groups truncated 13 bits below their largest product)"}
     log(f"bench: native {out['native_scaled_mfma']['value']} TFLOP/s")
+
+    # ---- e2m1 (FP4) operands on the same shape --------------------------------
+    # N(0, 1) -> e2m1 (RNE, saturating at 6), scales U{120..134}, bf16 out; the
+    # scaled MFMA is exact for e2m1, so this is held to the same bound
+    p4 = mi.random_problem(8192, 8192, 8192, seed=850, fmtA=mi.FMT_E2M1, fmtB=mi.FMT_E2M1,
+                           out_dtype=mi.OUT_BF16)
+    log("bench: e2m1 8192^3 generated")
+    wall_4, mean_4 = bench_gemm(gemm, p4, L.MXGEMM_VARIANT_AUTO, steps, warmup, 3)
+    del p4
+    out["mxfp4"] = {
+        "value": round(flops * steps / wall_4 / 1e12, 2), "unit": "TFLOP/s",
+        "config": {"M": 8192, "N": 8192, "K": 8192, "A": "e2m1 (2 per byte)", "B": "e2m1 (2 per byte)",
+                   "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1: exact)", "out": "bf16 (RNE)"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / mean_4 / 1e12, 2),
+                     "peak": PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
+                     "frac": round(flops / mean_4 / 1e12 / PEAK_TFLOPS["fp4"], 4),
+                     "kernel": "mxg::large::kernel<4,4,true,false,false>",
+                     "launch_mean_us": round(mean_4 * 1e6, 2)}}
+    log(f"bench: e2m1 {out['mxfp4']['value']} TFLOP/s")
 
     cpu_src = p
     # ---- skinny: M=64, N=28672, K=8192, fp32 out --------------------------------

@@ -21,8 +21,9 @@
  * with 255 = NaN.
  *
  * Memory layout (all dense, no leading-dimension arguments):
- *   A        M x K codes, row-major (byte A[m*K + k]).
- *   B        N x K codes, K contiguous ("K-major"): byte B[n*K + k] = B[k,n].
+ *   A        M x K codes, row-major (byte A[m*K + k]); e2m1: M x K/2 bytes.
+ *   B        N x K codes, K contiguous ("K-major"): byte B[n*K + k] = B[k,n];
+ *            e2m1: N x K/2 bytes.
  *   A_scale  M x (K/32) bytes, row-major.
  *   B_scale  N x (K/32) bytes, row-major.
  *   C        M x N, row-major, fp32 or bf16 (bit pattern in uint16).
@@ -48,8 +49,19 @@ extern "C" {
 
 typedef struct mxgemm_ctx *mxgemm_t;
 
-/* operand formats (format strings "e4m3" / "e5m2") */
-enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
+/* operand formats (format strings "e4m3" / "e5m2" / "e2m1").
+ *
+ * e2m1 is a reading (the pages name the F8F6F4 operand family of the scaled
+ * MMA lowering, ScaledBlockedToScaledWMMAF8F6F4, and the sub-byte packing
+ * switch lhs_k_pack / rhs_k_pack of dot_scaled, but give no encoding): OCP
+ * FP4 E2M1 (sign, 2-bit exponent with bias 1, 1-bit mantissa; magnitudes 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6; no inf/NaN), packed two codes per byte along K,
+ * the even k in the low nibble (k_pack = True), so an e2m1 operand row is
+ * K/2 bytes.  e2m1 pairs only with e2m1 (MXGEMM_ERR_FMT otherwise).  It runs
+ * on the gfx950 scaled MFMA, whose 8-product windows hold every e2m1
+ * product of a block exactly (measured), so it meets the same
+ * 1e-5 * sum|ab| bound as the exact variants at the fp4 MFMA rate. */
+enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1, MXGEMM_FMT_E2M1 = 4 };
 
 /* output types of C (out_dtype); bf16 is rounded to nearest even from the
  * fp32 accumulator */
@@ -82,7 +94,7 @@ enum {
 enum {
     MXGEMM_OK = 0,
     MXGEMM_ERR_NULL = 1,    /* a required pointer is NULL */
-    MXGEMM_ERR_FMT = 2,     /* fmtA / fmtB not e4m3 or e5m2 */
+    MXGEMM_ERR_FMT = 2,     /* fmtA / fmtB not e4m3, e5m2 or e2m1, or e2m1 with another format */
     MXGEMM_ERR_DTYPE = 3,   /* out_dtype not f32/bf16, or use_acc not 0/1 */
     MXGEMM_ERR_SHAPE = 4,   /* M, N, K out of range or K % 32 != 0 */
     MXGEMM_ERR_ALIGN = 5,   /* A, B or C not 16-byte aligned */
@@ -125,7 +137,8 @@ int mxgemm_destroy(mxgemm_t h);
 /* Select the kernel variant used by later mxgemm_run calls on this handle
  * (MXGEMM_VARIANT_*).  Exact variants differ from each other only in fp32
  * summation order.  Forcing a skinny variant makes mxgemm_run return
- * MXGEMM_ERR_VARIANT for M > 64.  Not synchronised with mxgemm_run calls
+ * MXGEMM_ERR_VARIANT for M > 64, and for e2m1 operands (which run on the
+ * 256 x 256 kernel's scaled MFMA under AUTO, LARGE and LARGE_NATIVE alike).  Not synchronised with mxgemm_run calls
  * running on the same handle in other threads. */
 int mxgemm_set_variant(mxgemm_t h, int variant);
 

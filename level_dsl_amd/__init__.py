@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libmxgemm.so")
 
 MXGEMM_FMT_E4M3 = 0
 MXGEMM_FMT_E5M2 = 1
+MXGEMM_FMT_E2M1 = 4
 MXGEMM_OUT_F32 = 0
 MXGEMM_OUT_BF16 = 1
 MXGEMM_X_F32 = 0
@@ -217,10 +218,14 @@ class Gemm:
 
     def __call__(self, A, A_scale, fmtA, B, B_scale, fmtB, C, use_acc=False,
                  out_dtype=MXGEMM_OUT_F32, stream=None):
-        M, K = A.shape
+        # e2m1 operands hold two codes per byte along K
+        M, ka = A.shape
         N = B.shape[0]
-        if B.shape[1] != K or A_scale.shape != (M, K // 32) or B_scale.shape != (N, K // 32):
-            raise ValueError("operand shapes do not match (A MxK, B NxK, scales K/32)")
+        K = 2 * ka if fmtA == MXGEMM_FMT_E2M1 else ka
+        kb = K // 2 if fmtB == MXGEMM_FMT_E2M1 else K
+        if B.shape[1] != kb or A_scale.shape != (M, K // 32) or B_scale.shape != (N, K // 32):
+            raise ValueError("operand shapes do not match (A MxK, B NxK, scales K/32; "
+                             "e2m1: K/2 bytes per row)")
         want = torch.float32 if out_dtype == MXGEMM_OUT_F32 else torch.bfloat16
         if C.shape != (M, N) or C.dtype != want:
             raise ValueError(f"C must be ({M}, {N}) {want}")

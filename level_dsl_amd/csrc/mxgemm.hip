@@ -188,6 +188,9 @@ hipError_t dispatch(bool skinny, int f, const mxg::GemmArgs &a, hipStream_t s)
         default: return launch_skinny<1, 1, NATIVE>(a, s);
         }
     }
+    if constexpr (NATIVE) {
+        if (f == 4) return launch_large<4, 4, true>(a, s);  // e2m1 x e2m1
+    }
     switch (f) {
     case 0: return launch_large<0, 0, NATIVE>(a, s);
     case 1: return launch_large<0, 1, NATIVE>(a, s);
@@ -207,7 +210,7 @@ const char *mxgemm_status_string(int code)
     switch (code) {
     case MXGEMM_OK: return "ok";
     case MXGEMM_ERR_NULL: return "a required pointer is NULL";
-    case MXGEMM_ERR_FMT: return "operand format must be e4m3 (0) or e5m2 (1)";
+    case MXGEMM_ERR_FMT: return "operand format must be e4m3 (0), e5m2 (1) or e2m1 (4, with e2m1)";
     case MXGEMM_ERR_DTYPE: return "out_dtype must be f32 (0) or bf16 (1) and use_acc 0 or 1";
     case MXGEMM_ERR_SHAPE: return "M, N, K out of range or K not a multiple of 32";
     case MXGEMM_ERR_ALIGN: return "A, B and C must be 16-byte aligned";
@@ -294,8 +297,9 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const 
                          int64_t K, int use_acc, int out_dtype)
 {
     if (!A || !A_scale || !B || !B_scale || !C) return MXGEMM_ERR_NULL;
-    if ((fmtA != MXGEMM_FMT_E4M3 && fmtA != MXGEMM_FMT_E5M2) ||
-        (fmtB != MXGEMM_FMT_E4M3 && fmtB != MXGEMM_FMT_E5M2))
+    if ((fmtA != MXGEMM_FMT_E4M3 && fmtA != MXGEMM_FMT_E5M2 && fmtA != MXGEMM_FMT_E2M1) ||
+        (fmtB != MXGEMM_FMT_E4M3 && fmtB != MXGEMM_FMT_E5M2 && fmtB != MXGEMM_FMT_E2M1) ||
+        ((fmtA == MXGEMM_FMT_E2M1) != (fmtB == MXGEMM_FMT_E2M1)))
         return MXGEMM_ERR_FMT;
     if ((out_dtype != MXGEMM_OUT_F32 && out_dtype != MXGEMM_OUT_BF16) ||
         (use_acc != 0 && use_acc != 1))
@@ -305,7 +309,9 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const 
         return MXGEMM_ERR_SHAPE;
     if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15u) return MXGEMM_ERR_ALIGN;
     const uint64_t csize = (uint64_t)M * (uint64_t)N * (out_dtype == MXGEMM_OUT_F32 ? 4u : 2u);
-    if (overlaps(C, csize, A, (uint64_t)M * K) || overlaps(C, csize, B, (uint64_t)N * K) ||
+    const uint64_t row_bytes = fmtA == MXGEMM_FMT_E2M1 ? (uint64_t)K / 2 : (uint64_t)K;
+    if (overlaps(C, csize, A, (uint64_t)M * row_bytes) ||
+        overlaps(C, csize, B, (uint64_t)N * row_bytes) ||
         overlaps(C, csize, A_scale, (uint64_t)M * (K / 32)) ||
         overlaps(C, csize, B_scale, (uint64_t)N * (K / 32)))
         return MXGEMM_ERR_ALIAS;
@@ -330,9 +336,11 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     a.B = (const uint8_t *)B;
     a.Bs = B_scale;
     a.C = C;
+    // e2m1: two codes per byte along K; the kernels see K as the row pitch in bytes
+    const bool fp4 = fmtA == MXGEMM_FMT_E2M1;
     a.M = (int)M;
     a.N = (int)N;
-    a.K = (int)K;
+    a.K = (int)(fp4 ? K / 2 : K);
     a.KB = (int)(K / 32);
     a.use_acc = use_acc;
     a.out_bf16 = out_dtype == MXGEMM_OUT_BF16;
@@ -342,14 +350,22 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     a.c_vec = (N % 4) == 0;
 
     int variant = h->variant;
-    const bool native = variant == MXGEMM_VARIANT_LARGE_NATIVE ||
-                        variant == MXGEMM_VARIANT_SKINNY_NATIVE;
+    bool native = variant == MXGEMM_VARIANT_LARGE_NATIVE ||
+                  variant == MXGEMM_VARIANT_SKINNY_NATIVE;
     bool skinny;
     if (variant == MXGEMM_VARIANT_AUTO)
         skinny = M <= mxg::skinny::MAX_M;
     else
         skinny = variant == MXGEMM_VARIANT_SKINNY || variant == MXGEMM_VARIANT_SKINNY_NATIVE;
     if (skinny && M > mxg::skinny::MAX_M) return MXGEMM_ERR_VARIANT;
+    if (fp4) {
+        // e2m1 x e2m1 runs on the 256 x 256 kernel's scaled MFMA, which is
+        // exact for it; there is no small-M e2m1 kernel
+        if (variant == MXGEMM_VARIANT_SKINNY || variant == MXGEMM_VARIANT_SKINNY_NATIVE)
+            return MXGEMM_ERR_VARIANT;
+        skinny = false;
+        native = true;
+    }
     a.splits = 1;
     a.ws = nullptr;
     a.cnt = nullptr;
@@ -387,7 +403,7 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
             }
         }
     }
-    const int f = fmtA * 2 + fmtB;
+    const int f = fp4 ? 4 : fmtA * 2 + fmtB;
     const hipError_t e = native ? dispatch<true>(skinny, f, a, stream)
                                 : dispatch<false>(skinny, f, a, stream);
     return e == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;

@@ -56,6 +56,8 @@ def v(**kw):
     ({}, "MXGEMM_OK"),
     ({"A": 0}, "MXGEMM_ERR_NULL"), ({"B_scale": 0}, "MXGEMM_ERR_NULL"), ({"C": 0}, "MXGEMM_ERR_NULL"),
     ({"fmtA": 2}, "MXGEMM_ERR_FMT"), ({"fmtB": -1}, "MXGEMM_ERR_FMT"),
+    ({"fmtA": 4}, "MXGEMM_ERR_FMT"), ({"fmtB": 4}, "MXGEMM_ERR_FMT"), ({"fmtA": 3, "fmtB": 3}, "MXGEMM_ERR_FMT"),
+    ({"fmtA": 4, "fmtB": 4}, "MXGEMM_OK"), ({"fmtA": 4, "fmtB": 4, "K": 48}, "MXGEMM_ERR_SHAPE"),
     ({"out_dtype": 2}, "MXGEMM_ERR_DTYPE"), ({"use_acc": 2}, "MXGEMM_ERR_DTYPE"),
     ({"M": 0}, "MXGEMM_ERR_SHAPE"), ({"N": -3}, "MXGEMM_ERR_SHAPE"), ({"K": 0}, "MXGEMM_ERR_SHAPE"),
     ({"K": 48}, "MXGEMM_ERR_SHAPE"), ({"K": 16}, "MXGEMM_ERR_SHAPE"),

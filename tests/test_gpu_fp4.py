@@ -1,0 +1,161 @@
+"""GPU parity of e2m1 (FP4) operands, two codes per byte along K, against
+the CPU oracle.
+
+e2m1 x e2m1 runs on the 256 x 256 kernel's scaled MFMA (every product of a
+32-element block fits the instruction's 8-product window, so it is exact up
+to the fp32 accumulation), and is held to the same agreement rule as the
+exact variants:
+  * every pair of the 16 codes at several scale pairs, bit for bit;
+  * random problems on full outputs: ragged M, N and K (a partial last
+    stage, K not a multiple of 128 values), use_acc, bf16 output, M = 1 and
+    small M, and both e2m1-capable variants;
+  * a NaN scale at the start of the next row must not leak into a row
+    whose last stage stops inside the scale dword (K = 1152);
+  * split-K, forced and automatic;
+  * the 8192 x 8192 x 8192 benchmark shape on sampled outputs;
+  * the error paths (e2m1 with another format, a small-M variant).
+"""
+import numpy as np
+import pytest
+import torch
+
+import level_dsl_amd as L
+import mxinputs as mi
+import oracle
+from gpu_helpers import alloc_c, compare, log, oracle_full, oracle_points, run, to_dev
+
+pytestmark = pytest.mark.gpu
+
+E2M1 = L.MXGEMM_FMT_E2M1
+AUTO, LARGE, LARGE_NATIVE = L.MXGEMM_VARIANT_AUTO, L.MXGEMM_VARIANT_LARGE, L.MXGEMM_VARIANT_LARGE_NATIVE
+
+
+@pytest.fixture(scope="module")
+def gemm():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    g = L.Gemm()
+    yield g
+    g.close()
+
+
+@pytest.mark.parametrize("sa,sb", [(127, 127), (100, 150), (1, 254), (200, 60)])
+def test_fp4_pairwise_products_exact(gemm, sa, sb):
+    """A[m, 0] = code m, B[n, 0] = code n (16 x 16, K = 32, the rest zero):
+    every C[m, n] is the exact product dec(m) dec(n) 2^(sa+sb-254)."""
+    M = N = 16
+    K = 32
+    A = np.zeros((M, K // 2), np.uint8)
+    B = np.zeros((N, K // 2), np.uint8)
+    A[:, 0] = np.arange(16, dtype=np.uint8)      # k = 0: the low nibble
+    B[:, 0] = np.arange(16, dtype=np.uint8)
+    p = mi.Problem(M, N, K, E2M1, E2M1, A, np.full((M, 1), sa, np.uint8), B,
+                   np.full((N, 1), sb, np.uint8), mi.OUT_F32, False)
+    log(f"fp4 pairwise sa={sa} sb={sb}")
+    got = run(gemm, p, AUTO)
+    ref = oracle_full(p)
+    r = ref["ref32"]
+    normal = (np.abs(r) >= np.float32(2.0**-126)) | (r == 0)
+    assert np.array_equal(got[normal], r[normal]), f"{np.sum(got[normal] != r[normal])} mismatches"
+
+
+FP4_CASES = [
+    # M, N, K, use_acc, out
+    (300, 260, 4096, False, mi.OUT_F32),
+    (257, 300, 2048, True, mi.OUT_BF16),
+    (129, 513, 1056, False, mi.OUT_F32),     # 528 bytes per row: a partial last stage
+    (64, 200, 8192, True, mi.OUT_F32),
+    (1, 5, 32, False, mi.OUT_F32),
+    (517, 389, 1056, True, mi.OUT_BF16),
+    (33, 1000, 640, False, mi.OUT_BF16),
+]
+
+
+@pytest.mark.parametrize("M,N,K,acc,out", FP4_CASES, ids=lambda c: str(c))
+def test_fp4_random_full(gemm, M, N, K, acc, out):
+    p = mi.random_problem(M, N, K, seed=800 + M + K, fmtA=E2M1, fmtB=E2M1, out_dtype=out,
+                          use_acc=acc)
+    ref = oracle_full(p)
+    dev = to_dev(p)
+    for v in (AUTO, LARGE_NATIVE):
+        log(f"fp4 random M={M} N={N} K={K} use_acc={acc} out={out} variant={v}")
+        got = run(gemm, p, v, guard=64, dev_inputs=dev)
+        compare(got, ref, out, f"fp4 {M}x{N}x{K} variant {v}")
+    gemm.set_variant(AUTO)
+
+
+def test_fp4_scale_tail_does_not_read_the_next_row(gemm):
+    """K = 1152: 36 scale bytes per row (a multiple of 4, so scales are read
+    as dwords) and 576 code bytes, 4.5 stages; the last stage's second scale
+    dword lies past the row.  Every other row starts with a NaN scale byte;
+    a kernel that read the next row's first dword there would turn the
+    zero-padded tail of a finite row into NaN."""
+    M, N, K = 64, 96, 1152
+    p = mi.random_problem(M, N, K, seed=820, fmtA=E2M1, fmtB=E2M1)
+    p.As[1::2, 0] = 255
+    p.Bs[1::2, 0] = 255
+    ref = oracle_full(p)
+    log("fp4 scale tail guard")
+    got = run(gemm, p, AUTO)
+    compare(got, ref, p.out_dtype, "fp4 scale tail")
+    assert np.isnan(got[1::2]).all() and np.isnan(got[:, 1::2]).all()
+    assert np.isfinite(got[0::2, 0::2]).all(), "NaN leaked into a finite row"
+
+
+@pytest.mark.parametrize("S", [2, 4, 7])
+def test_fp4_split_k_forced(S):
+    M, N, K = 300, 260, 4096
+    p = mi.random_problem(M, N, K, seed=830 + S, fmtA=E2M1, fmtB=E2M1, out_dtype=mi.OUT_BF16,
+                          use_acc=True)
+    g = L.Gemm()
+    g.enable_split_k()
+    try:
+        g.set_splits(S)
+        log(f"fp4 split-K S={S}")
+        got = run(g, p, AUTO, guard=64)
+        compare(got, oracle_full(p), p.out_dtype, f"fp4 split S={S}")
+    finally:
+        g.close()
+
+
+def test_fp4_split_k_auto_medium_m():
+    M, N, K = 128, 14336, 8192
+    p = mi.random_problem(M, N, K, seed=840, fmtA=E2M1, fmtB=E2M1)
+    g = L.Gemm()
+    g.enable_split_k()
+    try:
+        log("fp4 auto split at M=128")
+        got = run(g, p, AUTO)
+        rows, cols = mi.sample_points(M, N, 8192, seed=840, edge=64)
+        compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "fp4 auto split")
+    finally:
+        g.close()
+
+
+def test_fp4_8192_cube_sampled(gemm):
+    """The e2m1 benchmark shape: 8192^3, N(0, 1) codes, scales U{120..134},
+    bf16 out, 16384 sampled outputs plus the edges."""
+    M = N = K = 8192
+    p = mi.random_problem(M, N, K, seed=850, fmtA=E2M1, fmtB=E2M1, out_dtype=mi.OUT_BF16)
+    log("fp4 8192^3 generated")
+    got = run(gemm, p, AUTO)
+    rows, cols = mi.sample_points(M, N, 16384, seed=850, edge=64)
+    compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "fp4 8192^3")
+
+
+def test_fp4_error_paths(gemm):
+    p = mi.random_problem(64, 64, 128, seed=860, fmtA=E2M1, fmtB=E2M1)
+    A, As, B, Bs = to_dev(p)
+    buf, c = alloc_c(p)
+    # e2m1 with e4m3
+    with pytest.raises(L.MxgemmError) as e:
+        L.mxgemm_run(gemm.h, A, As, E2M1, B, Bs, 0, c, 64, 64, 128, 0, 0)
+    assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_FMT"]
+    # no small-M e2m1 kernel
+    for v in (L.MXGEMM_VARIANT_SKINNY, L.MXGEMM_VARIANT_SKINNY_NATIVE):
+        gemm.set_variant(v)
+        with pytest.raises(L.MxgemmError) as e:
+            L.mxgemm_run(gemm.h, A, As, E2M1, B, Bs, E2M1, c, 64, 64, 128, 0, 0)
+        assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_VARIANT"]
+    gemm.set_variant(AUTO)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(buf).all()), "a rejected call wrote C"
