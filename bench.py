@@ -401,6 +401,25 @@ def main():
     log(f"bench: skinny {out['skinny_m64']['value']} GB/s")
     del ps
 
+    # ---- the same decode shape with e2m1 operands (two codes per byte) ----------
+    # N(0, 1) -> e2m1, scales U{120..134}, f32 out; the small-M kernel's scaled
+    # MFMA, exact for e2m1.  Bytes: A, B at K/2 per row, K/32 scales, C.
+    p4s = mi.random_problem(64, 28672, 8192, seed=870, fmtA=mi.FMT_E2M1, fmtB=mi.FMT_E2M1)
+    log("bench: e2m1 decode shape generated")
+    b4 = (64 + 28672) * (8192 // 2 + 8192 // 32) + 64 * 28672 * 4
+    wall_4s, mean_4s = bench_gemm(gemm, p4s, L.MXGEMM_VARIANT_AUTO, sk_steps, warmup, 3)
+    del p4s
+    out["mxfp4_skinny_m64"] = {
+        "value": round(b4 * sk_steps / wall_4s / 1e9, 1), "unit": "GB/s",
+        "config": {"M": 64, "N": 28672, "K": 8192, "A": "e2m1", "B": "e2m1", "out": "f32"},
+        "roofline": {"bound": "hbm", "achieved": round(b4 / mean_4s / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(b4 / mean_4s / 1e9 / PEAK_HBM_GBS, 4),
+                     "kernel": "mxg::skinny::kernel<4,4,true>",
+                     "launch_mean_us": round(mean_4s * 1e6, 2)},
+        "algorithmic_bytes": b4}
+    log(f"bench: e2m1 decode shape {out['mxfp4_skinny_m64']['value']} GB/s")
+
     # ---- MX block quantization of the skinny weight ------------------------------
     R, K = QUANT_SHAPE
     qbytes = quant_bytes(R, K)

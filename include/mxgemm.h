@@ -137,8 +137,10 @@ int mxgemm_destroy(mxgemm_t h);
 /* Select the kernel variant used by later mxgemm_run calls on this handle
  * (MXGEMM_VARIANT_*).  Exact variants differ from each other only in fp32
  * summation order.  Forcing a skinny variant makes mxgemm_run return
- * MXGEMM_ERR_VARIANT for M > 64, and for e2m1 operands (which run on the
- * 256 x 256 kernel's scaled MFMA under AUTO, LARGE and LARGE_NATIVE alike).  Not synchronised with mxgemm_run calls
+ * MXGEMM_ERR_VARIANT for M > 64.  e2m1 operands always run on the scaled
+ * MFMA (exact for them): LARGE and LARGE_NATIVE on the 256 x 256 kernel,
+ * SKINNY and SKINNY_NATIVE on the small-M kernel, AUTO on the small-M
+ * kernel when M <= 64, else on the 256 x 256 kernel.  Not synchronised with mxgemm_run calls
  * running on the same handle in other threads. */
 int mxgemm_set_variant(mxgemm_t h, int variant);
 

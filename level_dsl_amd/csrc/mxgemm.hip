@@ -67,11 +67,20 @@ hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
                         : launch_large_s<FA, FB, NATIVE, false>(a, s);
 }
 
-template <int FA, int FB, bool NATIVE>
+template <int FA, int FB>
 hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
 {
     const int blocks = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((mxg::skinny::kernel<FA, FB, NATIVE>), dim3(blocks),
+    // e2m1: one 8-byte load for a stage's scale bytes of a row when the scale
+    // rows are 16-byte multiples and aligned
+    if constexpr (FA == 4) {
+        if (a.scale_dword == 2) {
+            hipLaunchKernelGGL((mxg::skinny::kernel<FA, FB, true>), dim3(blocks),
+                               dim3(mxg::skinny::THREADS), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((mxg::skinny::kernel<FA, FB, false>), dim3(blocks),
                        dim3(mxg::skinny::THREADS), 0, s, a);
     return hipGetLastError();
 }
@@ -180,12 +189,15 @@ hipError_t dispatch(bool skinny, int f, const mxg::GemmArgs &a, hipStream_t s)
         default: return launch_stream<1, 1>(a, s);
         }
     }
-    if (skinny) {
-        switch (f) {
-        case 0: return launch_skinny<0, 0, NATIVE>(a, s);
-        case 1: return launch_skinny<0, 1, NATIVE>(a, s);
-        case 2: return launch_skinny<1, 0, NATIVE>(a, s);
-        default: return launch_skinny<1, 1, NATIVE>(a, s);
+    if constexpr (NATIVE) {
+        if (skinny) {
+            switch (f) {
+            case 0: return launch_skinny<0, 0>(a, s);
+            case 1: return launch_skinny<0, 1>(a, s);
+            case 2: return launch_skinny<1, 0>(a, s);
+            case 4: return launch_skinny<4, 4>(a, s);  // e2m1 x e2m1
+            default: return launch_skinny<1, 1>(a, s);
+            }
         }
     }
     if constexpr (NATIVE) {
@@ -359,11 +371,9 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
         skinny = variant == MXGEMM_VARIANT_SKINNY || variant == MXGEMM_VARIANT_SKINNY_NATIVE;
     if (skinny && M > mxg::skinny::MAX_M) return MXGEMM_ERR_VARIANT;
     if (fp4) {
-        // e2m1 x e2m1 runs on the 256 x 256 kernel's scaled MFMA, which is
-        // exact for it; there is no small-M e2m1 kernel
-        if (variant == MXGEMM_VARIANT_SKINNY || variant == MXGEMM_VARIANT_SKINNY_NATIVE)
-            return MXGEMM_ERR_VARIANT;
-        skinny = false;
+        // e2m1 x e2m1 runs on the scaled MFMA, which is exact for it; for
+        // M <= 64 on the small-M kernel's native mode (measured faster than
+        // the 256 x 256 kernel, split or not, from N = 3584 to 28672)
         native = true;
     }
     a.splits = 1;

@@ -1,5 +1,7 @@
-// mxgemm_skinny.h -- small-M (M <= 64) MX-FP8 GEMM kernel for gfx950,
-// native scaled-MFMA variant (the exact variant is mxgemm_stream.h).
+// mxgemm_skinny.h -- small-M (M <= 64) MX GEMM kernel for gfx950 on the
+// scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): the native variant for
+// e4m3 / e5m2 operands, and the e2m1 x e2m1 path (exact for e2m1).  The
+// exact small-M variant for fp8 is mxgemm_stream.h.
 //
 // With M <= 64 the multiply is bound by reading B once from HBM (about 120
 // flop per byte at M = 64, far below the chip's MFMA-to-HBM balance), so
@@ -12,15 +14,18 @@
 //     same time; with a power-of-two row pitch those addresses crowd onto a
 //     few memory channels (measured: 4.5 vs 5.5+ TB/s for the bare stream);
 //   * operands go straight from global memory into registers, so no LDS
-//     staging is needed, and the next stage's loads are in flight while the
-//     current stage's MFMAs run.  Lane l works on row l % 16; with
-//     g = l / 16 it loads K 16g..16g+15 and 64+16g..64+16g+15 of each
-//     128-byte stage (each load instruction reads 64 contiguous bytes of 16
-//     rows).  Exact mode (default): the two chunks are decoded with the
-//     scales of their K blocks (g/2 and 2 + g/2) into 32 bf16 that feed four
-//     16x16x32 bf16 MFMAs.  Native mode: this is the operand layout of
-//     v_mfma_scale_f32_16x16x128_f8f6f4 (as measured on the device) and the
-//     lane supplies the scale of block g to it;
+//     staging is needed; each wave keeps a ring of RING stage buffers, so
+//     RING - 1 of its stages are loading while it multiplies one.  Lane l
+//     works on row l % 16; with g = l / 16 it loads K bytes 16g..16g+15 and
+//     64+16g..64+16g+15 of each 128-byte stage (each load instruction reads
+//     64 contiguous bytes of 16 rows).  fp8: the two chunks are the 32 codes
+//     lane group g contributes to one 16x16x128 step (the instruction's
+//     operand layout, measured on the device) and the lane supplies the
+//     scale of block g.  e2m1 (two codes per byte): a stage is 256 codes,
+//     two steps; each chunk is the 32 codes of one scale block, and the
+//     measured e2m1 layout is lane group g holding block g of the step, so
+//     the low chunk feeds step 0 (block g) and the high chunk step 1 (block
+//     4 + g), with both scale bytes in one dword selected by op_sel;
 //   * A (at most 64 x K bytes) is re-read by every workgroup and stays in L2;
 //   * at the end the four per-wave partial tiles are summed in a fixed order
 //     through LDS (deterministic), use_acc adds the old C, and C is written
@@ -39,23 +44,33 @@ constexpr int THREADS = 256;
 constexpr int WAVES = THREADS / 64;
 constexpr int SUB_M = MAX_M / 16, SUB_N = BN / 16;
 
-template <int FX, int FY>
+template <int FX, int FY, int OP = 0>
 __device__ __forceinline__ v4f mfma16(v8i x, v8i y, v4f c, uint32_t sx, uint32_t sy)
 {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, 0, (int)sx, 0,
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, OP, (int)sx, OP,
                                                            (int)sy);
 }
 
 struct Stage {
     v8i b[SUB_N];
     v8i a[SUB_M];
-    uint32_t sb[SUB_N];  // exact: blocks g/2 (byte 0) and 2 + g/2 (byte 1); native: block g
+    uint32_t sb[SUB_N];  // fp8: block g; e2m1: blocks g (byte 0) and 4 + g (byte 1)
     uint32_t sa[SUB_M];
 };
 
-template <int FA, int FB, bool NATIVE>
+constexpr int RING = 3;  // stage buffers per wave: RING - 1 loading, one multiplied
+
+// SVEC (e2m1 only): a stage's 8 scale bytes of a row are read with one
+// 8-byte load, when K/32 % 16 == 0 with 16-byte aligned scale rows, else
+// byte by byte.  (For fp8 a dword load plus a per-lane shift measured slower:
+// it pushes the kernel into register spills.)
+template <int FA, int FB, bool SVEC>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
+    constexpr bool FP4 = FA == 4;  // e2m1 x e2m1; K is the row pitch in bytes
+    static_assert(FP4 == (FB == 4), "e2m1 pairs only with e2m1");
+    static_assert(!SVEC || FP4, "vector scale loads are for e2m1");
+    constexpr int SPS = FP4 ? 8 : BK / 32;  // scale bytes per row and stage
     __shared__ __attribute__((aligned(16))) float red[WAVES][MAX_M][BN];
 
     const int n0 = blockIdx.x * BN;
@@ -68,45 +83,61 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const rsrc_t rBs = make_rsrc(p.Bs + (size_t)n0 * KB, (uint32_t)rows_b * KB);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, kq = lane >> 4;
 
-    uint32_t boff[SUB_N], aoff[SUB_M], bsoff[SUB_N], asoff[SUB_M];
-    // chunks K 16g.. and 64+16g.. of each stage
+    uint32_t boff[SUB_N], aoff[SUB_M], bsrow[SUB_N], asrow[SUB_M];
+    // chunks K bytes 16g.. and 64+16g.. of each stage; scale rows
     constexpr int LO = 16, HI = 64;
-    const int sb0 = NATIVE ? kq : kq / 2;  // scale block of the low chunk (exact)
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) {
         boff[j] = (uint32_t)(16 * j + r16) * K + kq * LO;
-        bsoff[j] = (uint32_t)(16 * j + r16) * KB + sb0;
+        bsrow[j] = (uint32_t)(16 * j + r16) * KB;
     }
 #pragma unroll
     for (int i = 0; i < SUB_M; ++i) {
         aoff[i] = (uint32_t)(16 * i + r16) * K + kq * LO;
-        asoff[i] = (uint32_t)(16 * i + r16) * KB + sb0;
+        asrow[i] = (uint32_t)(16 * i + r16) * KB;
     }
 
-    auto load_stage = [&](int kt, Stage &s) {
-        const int k0 = kt * BK;
-        const bool lo_in = k0 + kq * LO < K, hi_in = k0 + kq * LO + HI < K;
-        const int kb0 = kt * (BK / 32);
-        // scale bytes: native, block g; exact, blocks g/2 (low chunk) and 2 + g/2
-        const bool s0_in = NATIVE ? k0 + kq * 32 < K : lo_in, s1_in = hi_in;
+    // the stage's scale bytes of one row (byte offset `row` of its K/32 row):
+    // fp8 block g in byte 0; e2m1 blocks g and 4 + g in bytes 0 and 1
+    auto scales_of = [&](rsrc_t rs, uint32_t row, int kb0, bool s0_in, bool s1_in) MXG_INLINE {
+        if constexpr (SVEC) {
+            const v2i v = __builtin_bit_cast(
+                v2i, __builtin_amdgcn_raw_buffer_load_b64(rs, s0_in ? row + kb0 : kOob, 0, 0));
+            return (((uint32_t)v[0] >> (8 * kq)) & 0xffu) | ((((uint32_t)v[1] >> (8 * kq)) & 0xffu) << 8);
+        } else {
+            uint32_t v = load1(rs, s0_in ? row + kb0 + kq : kOob);
+            if constexpr (FP4) v |= load1(rs, s1_in ? row + kb0 + kq + 4 : kOob) << 8;
+            return v;
+        }
+    };
+
+    // every call issues the same loads; a dead stage (kt < 0) reads zeros
+    auto load_stage = [&](int kt, Stage &s) MXG_INLINE {
+        const bool live = kt >= 0;
+        const int k0 = (live ? kt : 0) * BK;
+        const bool lo_in = live && k0 + kq * LO < K, hi_in = live && k0 + kq * LO + HI < K;
+        const int kb0 = (live ? kt : 0) * SPS;
+        // scale bytes: fp8, block g (in range when its 32 codes are);
+        // e2m1, blocks g and 4 + g (each the block of one chunk).  The vector
+        // form needs only the stage to exist (its rows hold whole stages).
+        const bool s0_in = SVEC ? live : (FP4 ? lo_in : live && k0 + kq * 32 < K);
+        const bool s1_in = hi_in;
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) {
             v4i lo = load16(rB, lo_in ? boff[j] + k0 : kOob);
             v4i hi = load16(rB, hi_in ? boff[j] + k0 + HI : kOob);
             s.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            s.sb[j] = load1(rBs, s0_in ? bsoff[j] + kb0 : kOob);
-            if (!NATIVE) s.sb[j] |= load1(rBs, s1_in ? bsoff[j] + kb0 + 2 : kOob) << 8;
+            s.sb[j] = scales_of(rBs, bsrow[j], kb0, s0_in, s1_in);
         }
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) {
             v4i lo = load16(rA, lo_in ? aoff[i] + k0 : kOob);
             v4i hi = load16(rA, hi_in ? aoff[i] + k0 + HI : kOob);
             s.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            s.sa[i] = load1(rAs, s0_in ? asoff[i] + kb0 : kOob);
-            if (!NATIVE) s.sa[i] |= load1(rAs, s1_in ? asoff[i] + kb0 + 2 : kOob) << 8;
+            s.sa[i] = scales_of(rAs, asrow[i], kb0, s0_in, s1_in);
         }
     };
 
@@ -116,47 +147,55 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) acc[i][j] = v4f{};
 
-    const int nk = (K + BK - 1) / BK;
-    const int s0 = (int)(blockIdx.x % (unsigned)nk);  // this workgroup's first stage
-    auto stage_of = [&](int t) { const int s = t + s0; return s < nk ? s : s - nk; };
-    Stage cur, nxt;
-    if (wave < nk) load_stage(stage_of(wave), cur);
-    for (int t = wave; t < nk; t += WAVES) {
-        const bool more = t + WAVES < nk;
-        if (more) load_stage(stage_of(t + WAVES), nxt);
-        if constexpr (NATIVE) {
+    auto multiply = [&](const Stage &cur) MXG_INLINE {
+        if constexpr (FP4) {
+            // step 0: the low chunks (blocks g, scale byte 0); step 1: the high
+            // chunks (blocks 4 + g, scale byte 1)
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j)
+#pragma unroll
+                for (int i = 0; i < SUB_M; ++i) {
+                    const v8i b0 = {cur.b[j][0], cur.b[j][1], cur.b[j][2], cur.b[j][3], 0, 0, 0, 0};
+                    const v8i a0 = {cur.a[i][0], cur.a[i][1], cur.a[i][2], cur.a[i][3], 0, 0, 0, 0};
+                    acc[i][j] = mfma16<FB, FA, 0>(b0, a0, acc[i][j], cur.sb[j], cur.sa[i]);
+                }
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j)
+#pragma unroll
+                for (int i = 0; i < SUB_M; ++i) {
+                    const v8i b1 = {cur.b[j][4], cur.b[j][5], cur.b[j][6], cur.b[j][7], 0, 0, 0, 0};
+                    const v8i a1 = {cur.a[i][4], cur.a[i][5], cur.a[i][6], cur.a[i][7], 0, 0, 0, 0};
+                    acc[i][j] = mfma16<FB, FA, 1>(b1, a1, acc[i][j], cur.sb[j], cur.sa[i]);
+                }
+        } else {
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j)
 #pragma unroll
                 for (int i = 0; i < SUB_M; ++i)
                     acc[i][j] = mfma16<FB, FA>(cur.b[j], cur.a[i], acc[i][j], cur.sb[j], cur.sa[i]);
-        } else {
-            // decode each lane's 32 codes with its block scale into 4 x 8 bf16,
-            // then four 16x16x32 bf16 MFMAs per (i, j)
-            v8bf fa[SUB_M][4], fb[SUB_N][4];
-#pragma unroll
-            for (int i = 0; i < SUB_M; ++i) {
-                decode16<FA>(v4i{cur.a[i][0], cur.a[i][1], cur.a[i][2], cur.a[i][3]},
-                             scale_f32<0>(cur.sa[i]), fa[i][0], fa[i][1]);
-                decode16<FA>(v4i{cur.a[i][4], cur.a[i][5], cur.a[i][6], cur.a[i][7]},
-                             scale_f32<1>(cur.sa[i]), fa[i][2], fa[i][3]);
-            }
-#pragma unroll
-            for (int j = 0; j < SUB_N; ++j) {
-                decode16<FB>(v4i{cur.b[j][0], cur.b[j][1], cur.b[j][2], cur.b[j][3]},
-                             scale_f32<0>(cur.sb[j]), fb[j][0], fb[j][1]);
-                decode16<FB>(v4i{cur.b[j][4], cur.b[j][5], cur.b[j][6], cur.b[j][7]},
-                             scale_f32<1>(cur.sb[j]), fb[j][2], fb[j][3]);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int j = 0; j < SUB_N; ++j)
-#pragma unroll
-                    for (int i = 0; i < SUB_M; ++i)
-                        acc[i][j] = mfma_bf16_16(fb[j][q], fa[i][q], acc[i][j]);
         }
-        if (more) cur = nxt;
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    const int s0 = (int)(blockIdx.x % (unsigned)nk);  // this workgroup's first stage
+    auto stage_of = [&](int t) MXG_INLINE { const int s = t + s0; return s < nk ? s : s - nk; };
+    // wave w runs its stages t = w, w + WAVES, ...; the i-th of them lives in
+    // ring slot i % RING (static indices only: the ring stays in registers)
+    // Loads are issued unconditionally (dead stages read zeros) so that the
+    // compiler's wait counting stays exact across the ring.
+    auto kt_of = [&](int t) MXG_INLINE { return t < nk ? stage_of(t) : -1; };
+    Stage ring[RING];
+    static_for<RING - 1>([&](auto P) MXG_INLINE {
+        load_stage(kt_of(wave + decltype(P)::value * WAVES), ring[decltype(P)::value]);
+    });
+    for (int t0 = wave; t0 < nk; t0 += RING * WAVES) {
+        static_for<RING>([&](auto P) MXG_INLINE {
+            constexpr int pp = decltype(P)::value;
+            const int t = t0 + pp * WAVES;
+            // loads into the slot multiplied last, RING - 1 stages ahead
+            load_stage(kt_of(t + (RING - 1) * WAVES), ring[(pp + RING - 1) % RING]);
+            if (t < nk) multiply(ring[pp]);
+        });
     }
 
     // acc[i][j] register r of lane l: m = 16 i + l % 16, n = 16 j + 4 (l / 16) + r.

@@ -28,6 +28,7 @@ pytestmark = pytest.mark.gpu
 
 E2M1 = L.MXGEMM_FMT_E2M1
 AUTO, LARGE, LARGE_NATIVE = L.MXGEMM_VARIANT_AUTO, L.MXGEMM_VARIANT_LARGE, L.MXGEMM_VARIANT_LARGE_NATIVE
+SKINNY, SKINNY_NATIVE = L.MXGEMM_VARIANT_SKINNY, L.MXGEMM_VARIANT_SKINNY_NATIVE
 
 
 @pytest.fixture(scope="module")
@@ -76,7 +77,7 @@ def test_fp4_random_full(gemm, M, N, K, acc, out):
                           use_acc=acc)
     ref = oracle_full(p)
     dev = to_dev(p)
-    for v in (AUTO, LARGE_NATIVE):
+    for v in (AUTO, LARGE_NATIVE) + ((SKINNY, SKINNY_NATIVE) if M <= 64 else ()):
         log(f"fp4 random M={M} N={N} K={K} use_acc={acc} out={out} variant={v}")
         got = run(gemm, p, v, guard=64, dev_inputs=dev)
         compare(got, ref, out, f"fp4 {M}x{N}x{K} variant {v}")
@@ -142,6 +143,17 @@ def test_fp4_8192_cube_sampled(gemm):
     compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "fp4 8192^3")
 
 
+def test_fp4_decode_size_sampled(gemm):
+    """M = 64, N = 28672, K = 8192 (the decode workload's shape in e2m1): the
+    automatic choice is the small-M kernel; sampled outputs and the edges."""
+    M, N, K = 64, 28672, 8192
+    p = mi.random_problem(M, N, K, seed=870, fmtA=E2M1, fmtB=E2M1)
+    log("fp4 decode shape generated")
+    got = run(gemm, p, AUTO, guard=64)
+    rows, cols = mi.sample_points(M, N, 16384, seed=870, edge=64)
+    compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "fp4 decode shape")
+
+
 def test_fp4_error_paths(gemm):
     p = mi.random_problem(64, 64, 128, seed=860, fmtA=E2M1, fmtB=E2M1)
     A, As, B, Bs = to_dev(p)
@@ -150,12 +162,17 @@ def test_fp4_error_paths(gemm):
     with pytest.raises(L.MxgemmError) as e:
         L.mxgemm_run(gemm.h, A, As, E2M1, B, Bs, 0, c, 64, 64, 128, 0, 0)
     assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_FMT"]
-    # no small-M e2m1 kernel
-    for v in (L.MXGEMM_VARIANT_SKINNY, L.MXGEMM_VARIANT_SKINNY_NATIVE):
+    # a forced small-M variant with M > 64
+    q = mi.random_problem(65, 64, 128, seed=861, fmtA=E2M1, fmtB=E2M1)
+    qA, qAs, qB, qBs = to_dev(q)
+    qbuf, qc = alloc_c(q)
+    for v in (SKINNY, SKINNY_NATIVE):
         gemm.set_variant(v)
         with pytest.raises(L.MxgemmError) as e:
-            L.mxgemm_run(gemm.h, A, As, E2M1, B, Bs, E2M1, c, 64, 64, 128, 0, 0)
+            L.mxgemm_run(gemm.h, qA, qAs, E2M1, qB, qBs, E2M1, qc, 65, 64, 128, 0, 0)
         assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_VARIANT"]
     gemm.set_variant(AUTO)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(qbuf).all()), "a rejected call wrote C"
     torch.cuda.synchronize()
     assert bool(torch.isnan(buf).all()), "a rejected call wrote C"

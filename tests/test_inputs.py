@@ -74,3 +74,23 @@ def test_sample_points_cover_edges():
     assert all((999, j) in pts for j in range(700))
     assert all((i, 699) in pts for i in range(1000))
     assert len(pts) == len(r)
+
+
+def test_e2m1_quantiser_is_nearest_even():
+    """The generator's e2m1 rounding against a brute-force search over the
+    eight magnitudes (ties to the even code), on a dense sweep, every
+    midpoint of both signs, zeros, tiny and saturating values; and packing
+    round-trips."""
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)
+    x = np.concatenate([np.linspace(-7, 7, 20001, dtype=np.float32), mids, -mids,
+                        np.float32([0.0, -0.0, 1e-30, -1e-30, 6.0, -6.0, 100, -100])])
+    got = mi._quantize_e2m1(x)
+    d = np.abs(np.minimum(np.abs(x.astype(np.float64)), 6.0)[:, None] - grid[None, :])
+    cand = d == d.min(axis=1, keepdims=True)
+    even = cand & (np.arange(8) % 2 == 0)
+    idx = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(cand, axis=1))
+    want = (idx | (np.signbit(x) << 3)).astype(np.uint8)
+    assert np.array_equal(got, want)
+    codes = np.random.Generator(np.random.PCG64(5)).integers(0, 16, size=(3, 64), dtype=np.uint8)
+    assert np.array_equal(mi.unpack_e2m1(mi.pack_e2m1(codes)), codes)
