@@ -166,7 +166,8 @@ def gemm_full(A, As, fmtA, B, Bs, fmtB, M, N, K, cin=None, nthreads=None, lib=No
 
 def quantize(X, fmt, lib=None):
     """MX block quantization of an (R, K) matrix: X float32, or uint16 bf16
-    bit patterns.  Returns (codes (R, K) uint8, scales (R, ceil(K/32)) uint8).
+    bit patterns.  Returns (codes (R, K) uint8 -- e2m1: (R, ceil(K/2)), two
+    per byte, the even k in the low nibble -- scales (R, ceil(K/32)) uint8).
     Raises ValueError for non-finite input (the recipe covers finite values)."""
     lib = lib or load()
     X = np.ascontiguousarray(X)
@@ -179,7 +180,7 @@ def quantize(X, fmt, lib=None):
     else:
         raise TypeError("X must be float32 or uint16 (bf16 bits)")
     R, K = X.shape
-    codes = np.empty((R, K), np.uint8)
+    codes = np.empty((R, packed_width(K, fmt)), np.uint8)
     scales = np.empty((R, (K + 31) // 32), np.uint8)
     rc = lib.mxref_quantize(_ptr(X), x_dtype, int(R), int(K), int(fmt), _ptr(codes), _ptr(scales))
     if rc == -2:

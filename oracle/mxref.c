@@ -304,7 +304,10 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *As, int fmtA,
  * Written from that definition: the exponent by exact comparisons with
  * ldexp, the rounding by exhaustive search over the format's codes.
  */
-static double fmt_max(int fmt) { return fmt == MXREF_FMT_E4M3 ? 448.0 : 57344.0; }
+static double fmt_max(int fmt)
+{
+    return fmt == MXREF_FMT_E4M3 ? 448.0 : fmt == MXREF_FMT_E2M1 ? 6.0 : 57344.0;
+}
 
 /* Nearest code of `fmt` to v, ties to an even mantissa field (the lowest
  * bit of the code), largest finite magnitude if |v| exceeds it. */
@@ -312,9 +315,10 @@ static uint8_t nearest_code(int fmt, double v)
 {
     const double *t = table(fmt);
     const double a = fabs(v);
+    const int ncodes = fmt == MXREF_FMT_E2M1 ? 8 : 128; /* the non-negative codes */
     int best = 0;
     double bd = INFINITY;
-    for (int c = 0; c < 128; ++c) {
+    for (int c = 0; c < ncodes; ++c) {
         if (!isfinite(t[c]))
             continue;
         const double d = fabs(t[c] - a);
@@ -323,7 +327,7 @@ static uint8_t nearest_code(int fmt, double v)
             best = c;
         }
     }
-    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+    return (uint8_t)(best | (signbit(v) ? (fmt == MXREF_FMT_E2M1 ? 0x8 : 0x80) : 0));
 }
 
 /* Smallest integer e with amax <= MAX * 2^e, for finite amax > 0. */
@@ -348,9 +352,12 @@ int mxref_quantize(const void *X, int x_dtype, int64_t R, int64_t K, int fmt, ui
                    uint8_t *scales)
 {
     if (!X || !codes || !scales || R < 1 || K < 1 || (x_dtype != 0 && x_dtype != 1) ||
-        (fmt != MXREF_FMT_E4M3 && fmt != MXREF_FMT_E5M2))
+        (fmt != MXREF_FMT_E4M3 && fmt != MXREF_FMT_E5M2 && fmt != MXREF_FMT_E2M1))
         return -1;
     const int64_t KB = (K + 31) / 32;
+    /* e2m1 codes are packed two per byte along K, the even k in the low nibble */
+    const int packed = fmt == MXREF_FMT_E2M1;
+    const int64_t ldc = packed ? (K + 1) / 2 : K;
     for (int64_t r = 0; r < R; ++r) {
         for (int64_t b = 0; b < KB; ++b) {
             const int64_t k0 = 32 * b, k1 = k0 + 32 < K ? k0 + 32 : K;
@@ -371,8 +378,15 @@ int mxref_quantize(const void *X, int x_dtype, int64_t R, int64_t K, int fmt, ui
                 s = s < 0 ? 0 : (s > 254 ? 254 : s);
             }
             scales[r * KB + b] = (uint8_t)s;
-            for (int64_t k = k0; k < k1; ++k)
-                codes[r * K + k] = nearest_code(fmt, ldexp(x[k - k0], 127 - s));
+            for (int64_t k = k0; k < k1; ++k) {
+                const uint8_t c = nearest_code(fmt, ldexp(x[k - k0], 127 - s));
+                if (!packed)
+                    codes[r * ldc + k] = c;
+                else if (k % 2 == 0)
+                    codes[r * ldc + k / 2] = c;
+                else
+                    codes[r * ldc + k / 2] |= (uint8_t)(c << 4);
+            }
         }
     }
     return 0;

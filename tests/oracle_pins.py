@@ -581,10 +581,43 @@ def pin_e2m1_fraction(lib):
                 assert Fraction(r["sum"][m, n]) == exact, f"e2m1 case {i} ({m},{n})"
 
 
+def pin_quant_e2m1(lib):
+    """e2m1 quantization: the scale byte satisfies the block exponent's
+    defining inequality with MAX = 6 (amax <= 6 * 2^e, not <= 6 * 2^(e-1)),
+    and every code is the generator's independent nearest-even e2m1
+    rounding of x * 2^-e, packed low nibble first; zero blocks get byte 0
+    and keep the sign of -0."""
+    g = np.random.Generator(np.random.PCG64(61))
+    R, K = 9, 320
+    X = (g.standard_normal((R, K)) * np.exp2(g.integers(-30, 30, size=(R, 1)))).astype(np.float32)
+    X[0, :32] = 0.0
+    X[0, 5] = -0.0
+    X[1, :32] = np.float32(6.0) * np.float32(2.0 ** 10)       # amax exactly 6 * 2^10
+    X[2, 32:64] = np.linspace(-3, 3, 32, dtype=np.float32)     # ties inside the grid
+    codes, scales = oracle.quantize(X, 4, lib=lib)
+    assert codes.shape == (R, K // 2)
+    unpacked = mxinputs.unpack_e2m1(codes)
+    for r in range(R):
+        for b in range(K // 32):
+            blk = X[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            s = int(scales[r, b])
+            if amax == 0:
+                assert s == 0
+            else:
+                e = s - 127
+                assert amax <= 6.0 * 2.0 ** e and not amax <= 6.0 * 2.0 ** (e - 1), (r, b, s)
+            want = mxinputs._quantize_e2m1((blk * 2.0 ** (127 - s)).astype(np.float32))
+            assert np.array_equal(unpacked[r, 32 * b:32 * b + 32], want), (r, b)
+    assert unpacked[0, 5] == 8 and unpacked[0, 4] == 0
+    assert int(scales[1, 0]) == 127 + 10 and (unpacked[1, :32] == 7).all()
+
+
 ALL_PINS = [pin_tables_match_torch, pin_spot_values, pin_special_counts, pin_bf16_rne,
             pin_bruteforce_fraction, pin_pairwise_products, pin_closed_form,
             pin_integer_gemm, pin_scale_doubling, pin_permutation, pin_numpy_matmul,
             pin_nan_propagation, pin_thread_independence, pin_scale_tile_extent,
             pin_quant_rne_vs_torch, pin_quant_block_exponent, pin_quant_scale_invariance,
             pin_quant_matches_generator, pin_quant_bf16_input, pin_quant_ragged_and_nonfinite,
-            pin_e2m1_golden, pin_e2m1_embeds_in_e4m3, pin_e2m1_integer_gemm, pin_e2m1_fraction]
+            pin_e2m1_golden, pin_e2m1_embeds_in_e4m3, pin_e2m1_integer_gemm, pin_e2m1_fraction,
+            pin_quant_e2m1]

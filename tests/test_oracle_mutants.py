@@ -34,7 +34,7 @@ MUTANTS = {
     "mag_signed": ("mag += fabs(prod);", "mag += prod;"),
     "quant_ties_to_odd": ("(d == bd && (c & 1) == 0)", "(d == bd && (c & 1) == 1)"),
     "quant_exponent_plus_one": ("s = block_exponent(fmt, amax) + 127;", "s = block_exponent(fmt, amax) + 128;"),
-    "quant_sign_dropped": ("(signbit(v) ? 0x80 : 0)", "0"),
+    "quant_sign_dropped": ("(signbit(v) ? (fmt == MXREF_FMT_E2M1 ? 0x8 : 0x80) : 0)", "0"),
     "quant_scale_inverted": ("ldexp(x[k - k0], 127 - s)", "ldexp(x[k - k0], s - 127)"),
     "quant_e4m3_max_480": ("return fmt == MXREF_FMT_E4M3 ? 448.0", "return fmt == MXREF_FMT_E4M3 ? 480.0"),
     "e2m1_nibble_order_a": ("(a[k / 2] >> (4 * (k % 2)))", "(a[k / 2] >> (4 * (1 - k % 2)))"),
@@ -43,6 +43,9 @@ MUTANTS = {
     "e2m1_no_subnormal": ("v = ldexp((double)m, 1 - 1 - 1);", "v = 0.0;"),
     "e2m1_row_pitch_k": ("base.ldA = base.packA ? (K + 1) / 2 : K;", "base.ldA = K;"),
     "e2m1_sign_dropped": ("    return s ? -v : v;\n}\n\n/* e8m0", "    return v;\n}\n\n/* e8m0"),
+    "quant_e2m1_max_4": ("fmt == MXREF_FMT_E2M1 ? 6.0 : 57344.0", "fmt == MXREF_FMT_E2M1 ? 4.0 : 57344.0"),
+    "quant_e2m1_sign_bit_7": ("(fmt == MXREF_FMT_E2M1 ? 0x8 : 0x80)", "0x80"),
+    "quant_e2m1_nibbles_swapped": ("else if (k % 2 == 0)", "else if (k % 2 == 1)"),
     "quant_zero_block_scale": ("int s = 0;\n            if (amax > 0.0) {", "int s = 127;\n            if (amax > 0.0) {"),
 }
 
