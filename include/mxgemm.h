@@ -204,16 +204,18 @@ int mxgemm_run(mxgemm_t h,
  * (the uint8 scale tile of K extent BLOCK_K // 32, TLX async-compute page,
  * "TMEM-backed MX Scales"), laid out like the operands of mxgemm_run:
  *   codes   R x K bytes, row-major (an A operand, or B stored K-contiguous);
+ *           e2m1: R x K/2 bytes, two codes per byte, the even k in the low
+ *           nibble;
  *   scales  R x (K/32) bytes, row-major.
  * The scale rule (a reading; the pages do not fix it): with MAX = 448
- * (e4m3) or 57344 (e5m2), e is the smallest integer with
+ * (e4m3), 57344 (e5m2) or 6 (e2m1), e is the smallest integer with
  * max|x| <= MAX * 2^e over the block (an all-zero block takes the smallest
  * scale), the scale byte is e + 127 clamped to 0..254, and each code is
  * x * 2^(127 - scale byte) rounded to the nearest value of the format, ties
- * to even, -0 kept as 0x80.  Inputs must be finite; for a block holding a NaN
+ * to even, -0 kept as negative zero (0x80; e2m1 0x8).  Inputs must be finite; for a block holding a NaN
  * or an infinity the output is unspecified.
  *
- * Checks (pure host): pointers non-NULL, fmt e4m3/e5m2, x_dtype, 1 <= R <=
+ * Checks (pure host): pointers non-NULL, fmt e4m3/e5m2/e2m1, x_dtype, 1 <= R <=
  * MXGEMM_MAX_M, 32 <= K <= MXGEMM_MAX_K with K % 32 == 0, R * K <=
  * MXGEMM_MAX_QELEMS, X and codes 16-byte aligned, and X, codes and scales
  * pairwise disjoint.  Same status codes as mxgemm_validate_args. */

@@ -248,12 +248,13 @@ class Gemm:
         else:
             raise ValueError("X must be float32 or bfloat16")
         R, K = X.shape
+        kc = K // 2 if fmt == MXGEMM_FMT_E2M1 else K  # e2m1: two codes per byte
         if codes is None:
-            codes = torch.empty((R, K), dtype=torch.uint8, device=X.device)
+            codes = torch.empty((R, kc), dtype=torch.uint8, device=X.device)
         if scales is None:
             scales = torch.empty((R, K // 32), dtype=torch.uint8, device=X.device)
-        if codes.shape != (R, K) or scales.shape != (R, K // 32) or \
+        if codes.shape != (R, kc) or scales.shape != (R, K // 32) or \
                 codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
-            raise ValueError("codes must be (R, K) and scales (R, K/32), uint8")
+            raise ValueError("codes must be (R, K) (e2m1: (R, K/2)) and scales (R, K/32), uint8")
         mxgemm_quantize(self.h, X, xd, R, K, fmt, codes, scales, stream)
         return codes, scales

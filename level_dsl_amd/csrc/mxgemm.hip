@@ -423,7 +423,8 @@ int mxgemm_validate_quantize(const void *X, int x_dtype, int64_t R, int64_t K, i
                              const uint8_t *codes, const uint8_t *scales)
 {
     if (!X || !codes || !scales) return MXGEMM_ERR_NULL;
-    if (fmt != MXGEMM_FMT_E4M3 && fmt != MXGEMM_FMT_E5M2) return MXGEMM_ERR_FMT;
+    if (fmt != MXGEMM_FMT_E4M3 && fmt != MXGEMM_FMT_E5M2 && fmt != MXGEMM_FMT_E2M1)
+        return MXGEMM_ERR_FMT;
     if (x_dtype != MXGEMM_X_F32 && x_dtype != MXGEMM_X_BF16) return MXGEMM_ERR_DTYPE;
     if (R < 1 || K < 32 || R > MXGEMM_MAX_M || K > MXGEMM_MAX_K || (K % 32) != 0 ||
         R * K > MXGEMM_MAX_QELEMS)
@@ -431,8 +432,9 @@ int mxgemm_validate_quantize(const void *X, int x_dtype, int64_t R, int64_t K, i
     if (((uintptr_t)X | (uintptr_t)codes) & 15u) return MXGEMM_ERR_ALIGN;
     const uint64_t n = (uint64_t)R * (uint64_t)K;
     const uint64_t xbytes = n * (x_dtype == MXGEMM_X_F32 ? 4u : 2u);
-    if (overlaps(X, xbytes, codes, n) || overlaps(X, xbytes, scales, n / 32) ||
-        overlaps(codes, n, scales, n / 32))
+    const uint64_t cbytes = fmt == MXGEMM_FMT_E2M1 ? n / 2 : n;  // e2m1: two codes per byte
+    if (overlaps(X, xbytes, codes, cbytes) || overlaps(X, xbytes, scales, n / 32) ||
+        overlaps(codes, cbytes, scales, n / 32))
         return MXGEMM_ERR_ALIAS;
     return MXGEMM_OK;
 }
@@ -461,7 +463,9 @@ int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K
     case 0: hipLaunchKernelGGL((mxg::quant::kernel<0, 0>), grid, block, 0, stream, a); break;
     case 1: hipLaunchKernelGGL((mxg::quant::kernel<0, 1>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((mxg::quant::kernel<1, 0>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((mxg::quant::kernel<1, 1>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((mxg::quant::kernel<1, 1>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((mxg::quant::kernel<4, 0>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((mxg::quant::kernel<4, 1>), grid, block, 0, stream, a); break;
     }
     return hipGetLastError() == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
 }

@@ -5,7 +5,9 @@
 // Scales").  Per block: the scale is the smallest power of two 2^e with
 // max|x| <= MAX * 2^e (MAX = 448 for e4m3, 57344 for e5m2; an all-zero
 // block takes the smallest scale), stored as e + 127 clamped to 0..254, and
-// each code is x * 2^-e rounded to nearest even.
+// each code is x * 2^-e rounded to nearest even.  e2m1 (format 4: MAX = 6,
+// codes packed two per byte along K, the even k in the low nibble) follows
+// the same recipe.
 //
 // The work is a flat stream (K % 32 == 0, so blocks never straddle rows):
 //   * a wave owns 4 x 64 consecutive 16-byte chunks of X; lane l loads
@@ -16,13 +18,15 @@
 //     order for finite values), reduced across the block's lanes with
 //     cross-lane shuffles; the scale byte is read off its exponent and
 //     mantissa fields: max|x| = 1.f * 2^(E-127) <= 0.875 * 2^(e+9) for e4m3
-//     gives e + 127 = E - 8 + (f > 0.75), for e5m2 E - 15 + (f > 0.75);
+//     gives e + 127 = E - 8 + (f > 0.75), for e5m2 E - 15 + (f > 0.75), for
+//     e2m1 (6 = 1.5 * 2^2) E - 2 + (f > 0.5);
 //   * x * 2^(127 - scale) is exact (a power-of-two product whose magnitude
-//     is at most MAX), and v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 round it to
-//     nearest even, two values per instruction;
+//     is at most MAX), and v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 /
+//     v_cvt_scalef32_pk_fp4_f32 (scale 1) round it to nearest even, two
+//     values per instruction;
 //   * codes leave as one 4-byte (fp32 input) or 8-byte (bf16 input) store
-//     per lane and chunk, 256 or 512 contiguous bytes per instruction; the
-//     first lane of each block stores its scale byte.
+//     per lane and chunk -- e2m1: 2 or 4 bytes -- contiguous across the
+//     wave; the first lane of each block stores its scale byte.
 // Descriptors are rebased per wave, so every offset stays far below 2^32 and
 // the tail of the stream is masked by the descriptors' range checks.
 #pragma once
@@ -54,14 +58,24 @@ __device__ __forceinline__ uint32_t cvt_pair(float a, float b, uint32_t old, boo
                              : __builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, false));
 }
 
+// e2m1: two values into byte B of `old` (round to nearest even)
+template <int B>
+__device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t old, float a, float b)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, B);
+}
+
 template <int FMT, int XBF16>
 __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
 {
+    constexpr bool FP4 = FMT == 4;
     constexpr int EPL = XBF16 ? 8 : 4;    // elements per 16-byte chunk
     constexpr int LPB = 32 / EPL;         // lanes per block
     constexpr int ESZ = XBF16 ? 2 : 4;
     constexpr int WAVE_ELEMS = WAVE_BYTES / ESZ;
-    constexpr uint32_t OFF = FMT == 0 ? 8 : 15;  // scale byte = E - OFF + (f > 0.75)
+    // scale byte = E - OFF + (f > THR / 2^23)
+    constexpr uint32_t OFF = FMT == 0 ? 8 : FMT == 1 ? 15 : 2;
+    constexpr uint32_t THR = FP4 ? 0x400000u : 0x600000u;
 
     const int lane = threadIdx.x & 63;
     const uint64_t e0 = ((uint64_t)blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6)) * WAVE_ELEMS;
@@ -69,7 +83,7 @@ __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
     const uint64_t left = p.n - e0;
     const uint32_t ne = left < (uint64_t)WAVE_ELEMS ? (uint32_t)left : (uint32_t)WAVE_ELEMS;
     const rsrc_t rX = make_rsrc(p.X + e0 * ESZ, ne * ESZ);
-    const rsrc_t rQ = make_rsrc(p.codes + e0, ne);
+    const rsrc_t rQ = FP4 ? make_rsrc(p.codes + e0 / 2, ne / 2) : make_rsrc(p.codes + e0, ne);
     const rsrc_t rS = make_rsrc(p.scales + e0 / 32, ne / 32);
 
     v4i x[CHUNKS];
@@ -94,20 +108,33 @@ __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
 #pragma unroll
         for (int d = 1; d < LPB; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
         const int E = (int)(m >> 23);
-        int s = E - (int)OFF + ((m & 0x7fffffu) > 0x600000u ? 1 : 0);
+        int s = E - (int)OFF + ((m & 0x7fffffu) > THR ? 1 : 0);
         s = s < 0 ? 0 : (s > 254 ? 254 : s);
         const int sh = 127 - s;
-        uint32_t w[EPL / 4];
-#pragma unroll
-        for (int q = 0; q < EPL / 4; ++q) {
-            uint32_t v = cvt_pair<FMT>(__builtin_ldexpf(f[4 * q], sh), __builtin_ldexpf(f[4 * q + 1], sh), 0u, false);
-            w[q] = cvt_pair<FMT>(__builtin_ldexpf(f[4 * q + 2], sh), __builtin_ldexpf(f[4 * q + 3], sh), v, true);
-        }
         const uint32_t c = (uint32_t)(64 * j + lane);  // chunk index within the wave
-        if constexpr (XBF16)
-            store8(rQ, c * 8, v2i{(int)w[0], (int)w[1]});
-        else
-            store4(rQ, c * 4, w[0]);
+        if constexpr (FP4) {
+            // EPL codes -> EPL / 2 bytes, the even element in the low nibble
+            uint32_t w = cvt_fp4_pair<0>(0u, __builtin_ldexpf(f[0], sh), __builtin_ldexpf(f[1], sh));
+            w = cvt_fp4_pair<1>(w, __builtin_ldexpf(f[2], sh), __builtin_ldexpf(f[3], sh));
+            if constexpr (XBF16) {
+                w = cvt_fp4_pair<2>(w, __builtin_ldexpf(f[4], sh), __builtin_ldexpf(f[5], sh));
+                w = cvt_fp4_pair<3>(w, __builtin_ldexpf(f[6], sh), __builtin_ldexpf(f[7], sh));
+                store4(rQ, c * 4, w);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)w, rQ, c * 2, 0, 0);
+            }
+        } else {
+            uint32_t w[EPL / 4];
+#pragma unroll
+            for (int q = 0; q < EPL / 4; ++q) {
+                uint32_t v = cvt_pair<FMT>(__builtin_ldexpf(f[4 * q], sh), __builtin_ldexpf(f[4 * q + 1], sh), 0u, false);
+                w[q] = cvt_pair<FMT>(__builtin_ldexpf(f[4 * q + 2], sh), __builtin_ldexpf(f[4 * q + 3], sh), v, true);
+            }
+            if constexpr (XBF16)
+                store8(rQ, c * 8, v2i{(int)w[0], (int)w[1]});
+            else
+                store4(rQ, c * 4, w[0]);
+        }
         if (lane % LPB == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)s, rS, c / LPB, 0, 0);
     }
 }

@@ -101,7 +101,8 @@ def vq(**kw):
 @pytest.mark.parametrize("kw,code", [
     ({}, "MXGEMM_OK"), ({"x_dtype": 1}, "MXGEMM_OK"), ({"fmt": 1, "R": 1, "K": 32}, "MXGEMM_OK"),
     ({"X": 0}, "MXGEMM_ERR_NULL"), ({"codes": 0}, "MXGEMM_ERR_NULL"), ({"scales": 0}, "MXGEMM_ERR_NULL"),
-    ({"fmt": 2}, "MXGEMM_ERR_FMT"), ({"x_dtype": 2}, "MXGEMM_ERR_DTYPE"),
+    ({"fmt": 2}, "MXGEMM_ERR_FMT"), ({"fmt": 3}, "MXGEMM_ERR_FMT"), ({"fmt": 4}, "MXGEMM_OK"),
+    ({"x_dtype": 2}, "MXGEMM_ERR_DTYPE"),
     ({"R": 0}, "MXGEMM_ERR_SHAPE"), ({"K": 16}, "MXGEMM_ERR_SHAPE"), ({"K": 48}, "MXGEMM_ERR_SHAPE"),
     ({"K": (1 << 21) + 32}, "MXGEMM_ERR_SHAPE"), ({"R": 1 << 20, "K": 1 << 19}, "MXGEMM_ERR_SHAPE"),
     ({"X": 0x100008}, "MXGEMM_ERR_ALIGN"), ({"codes": 0x200004}, "MXGEMM_ERR_ALIGN"),

@@ -20,7 +20,7 @@ from gpu_helpers import log
 
 pytestmark = pytest.mark.gpu
 
-QMAX = {0: 448.0, 1: 57344.0}
+QMAX = {0: 448.0, 1: 57344.0, 4: 6.0}
 
 
 @pytest.fixture(scope="module")
@@ -38,10 +38,11 @@ def gpu_quantize(gemm, X: np.ndarray, fmt: int):
     else:
         t = torch.from_numpy(X).to("cuda:0")
     R, K = X.shape
+    kc = K // 2 if fmt == 4 else K  # e2m1: two codes per byte
     # guard bytes around both outputs: nothing may be written outside them
-    cbuf = torch.full((R * K + 512,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    cbuf = torch.full((R * kc + 512,), 0xA5, dtype=torch.uint8, device="cuda:0")
     sbuf = torch.full((R * K // 32 + 512,), 0x5A, dtype=torch.uint8, device="cuda:0")
-    codes = cbuf[256:256 + R * K].view(R, K)
+    codes = cbuf[256:256 + R * kc].view(R, kc)
     scales = sbuf[256:256 + R * K // 32].view(R, K // 32)
     gemm.quantize(t, fmt, codes, scales)
     torch.cuda.synchronize()
@@ -67,14 +68,14 @@ def wide_rows(R, K, seed):
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 4])
 @pytest.mark.parametrize("R,K", [(37, 1120), (1, 32), (3, 96), (129, 4096)])
 def test_random_fp32(gemm, fmt, R, K):
     log(f"quantize fp32 {R}x{K} fmt={fmt}")
     check(gemm, wide_rows(R, K, seed=R * 31 + K + fmt), fmt, f"fp32 {R}x{K}")
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 4])
 @pytest.mark.parametrize("R,K", [(37, 1120), (5, 64)])
 def test_random_bf16(gemm, fmt, R, K):
     x = wide_rows(R, K, seed=R * 17 + K + fmt)
@@ -134,3 +135,56 @@ def test_skinny_weight_matches_workload(gemm):
     rows = np.random.Generator(np.random.PCG64(3)).choice(raw.shape[0], 64, replace=False)
     want_c, want_s = oracle.quantize(np.ascontiguousarray(raw[rows]), 0)
     assert np.array_equal(got_c[rows], want_c) and np.array_equal(got_s[rows], want_s)
+
+
+
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_e2m1_ties_extremes_and_zeros(gemm, xdt):
+    """e2m1: every midpoint of the grid (a tie) and its fp32 neighbours, at
+    three block scales; the largest magnitude sitting exactly on 6 * 2^e or
+    one ulp above; blocks of zeros of both signs, tiny and huge blocks."""
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(9))])
+    rows = []
+    for e in (-20, 0, 17):
+        for sign in (1, -1):
+            blk = np.zeros(32, np.float32)
+            blk[:vals.size] = vals[:32] if vals.size >= 32 else vals
+            blk[-1] = 6.0                              # the block maximum is exactly 6
+            rows.append(sign * blk * np.float32(2.0 ** e))
+    top = np.full(32, 0.3, np.float32)
+    top[0] = np.nextafter(np.float32(6.0), np.float32(9))   # one ulp above 6: next scale up
+    rows.append(top)
+    rows.append(np.zeros(32, np.float32))
+    rows.append(-np.zeros(32, np.float32))
+    rows.append(np.full(32, 1e-40, np.float32))             # subnormal block
+    rows.append(np.full(32, 3.0e38, np.float32))            # near the fp32 maximum
+    X = np.stack(rows).reshape(len(rows), 32)
+    X = np.concatenate([X, X[::-1]], axis=1)                # K = 64, two blocks per row
+    if xdt == "bf16":
+        X = torch.from_numpy(X).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    log(f"e2m1 quantize ties/extremes {xdt}")
+    check(gemm, X, 4, f"e2m1 ties {xdt}")
+
+
+def test_e2m1_quantize_feeds_the_multiply(gemm):
+    """Quantize fp32 A and B to e2m1 on the GPU and multiply them: the
+    product equals the oracle's product of the oracle's quantization."""
+    g = np.random.Generator(np.random.PCG64(71))
+    M, N, K = 96, 200, 1024
+    Xa = g.standard_normal((M, K)).astype(np.float32)
+    Xb = (0.02 * g.standard_normal((N, K))).astype(np.float32)
+    qa, sa = gpu_quantize(gemm, Xa, 4)
+    qb, sb = gpu_quantize(gemm, Xb, 4)
+    ra, rsa = oracle.quantize(Xa, 4)
+    rb, rsb = oracle.quantize(Xb, 4)
+    assert np.array_equal(qa, ra) and np.array_equal(sa, rsa)
+    assert np.array_equal(qb, rb) and np.array_equal(sb, rsb)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    gemm(t(qa), t(sa), 4, t(qb), t(sb), 4, C)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_full(ra, rsa, 4, rb, rsb, 4, M, N, K)
+    err = np.abs(C.cpu().numpy().astype(np.float64) - ref["ref32"])
+    assert np.all(err <= 1e-5 * ref["mag"])
