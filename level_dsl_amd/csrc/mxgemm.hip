@@ -70,18 +70,24 @@ hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
 template <int FA, int FB>
 hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
 {
+    namespace sk = mxg::skinny;
     const int blocks = a.tiles_m * a.tiles_n;
-    // e2m1: one 8-byte load for a stage's scale bytes of a row when the scale
-    // rows are 16-byte multiples and aligned
+    // scale table in LDS when the scale rows are 16-byte multiples, aligned,
+    // and all of K fits; else (e2m1) 8-byte loads per stage, or byte loads
+    if (a.scale_dword == 2 && sk::table_fits(a.KB)) {
+        hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_TABLE>), dim3(blocks), dim3(sk::THREADS),
+                           0, s, a);
+        return hipGetLastError();
+    }
     if constexpr (FA == 4) {
         if (a.scale_dword == 2) {
-            hipLaunchKernelGGL((mxg::skinny::kernel<FA, FB, true>), dim3(blocks),
-                               dim3(mxg::skinny::THREADS), 0, s, a);
+            hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_VEC>), dim3(blocks),
+                               dim3(sk::THREADS), 0, s, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((mxg::skinny::kernel<FA, FB, false>), dim3(blocks),
-                       dim3(mxg::skinny::THREADS), 0, s, a);
+    hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_BYTES>), dim3(blocks), dim3(sk::THREADS), 0,
+                       s, a);
     return hipGetLastError();
 }
 

@@ -56,22 +56,41 @@ struct Stage {
     v8i a[SUB_M];
     uint32_t sb[SUB_N];  // fp8: block g; e2m1: blocks g (byte 0) and 4 + g (byte 1)
     uint32_t sa[SUB_M];
+    int kt;              // the K stage (scale table mode reads its scales at multiply time)
 };
+
+// scale modes: how a stage's scale bytes reach the MFMA
+enum { SCALES_BYTES = 0,  // byte loads per row and stage
+       SCALES_VEC = 1,    // e2m1: one 8-byte load per row and stage
+       SCALES_TABLE = 2 }; // the workgroup's whole scale table, loaded once into LDS
+constexpr int TABLE_ROWS = MAX_M + BN;  // A rows 0..63, then this workgroup's B rows
+// table row pitch for K/32 = kb scale bytes (kb % 16 == 0): an odd number of
+// dwords, so that the 16 rows of one read fall in different banks
+__host__ __device__ constexpr int table_pitch(int kb) { return kb + 4; }
+constexpr int TABLE_BYTES = WAVES * MAX_M * BN * 4;  // shares the reduction buffer
+__host__ __device__ constexpr bool table_fits(int kb) { return TABLE_ROWS * table_pitch(kb) <= TABLE_BYTES; }
 
 constexpr int RING = 3;  // stage buffers per wave: RING - 1 loading, one multiplied
 
-// SVEC (e2m1 only): a stage's 8 scale bytes of a row are read with one
-// 8-byte load, when K/32 % 16 == 0 with 16-byte aligned scale rows, else
-// byte by byte.  (For fp8 a dword load plus a per-lane shift measured slower:
-// it pushes the kernel into register spills.)
-template <int FA, int FB, bool SVEC>
+// SMODE (the host picks it): SCALES_TABLE when K/32 % 16 == 0 with 16-byte
+// aligned scale rows and the table fits: every workgroup loads its scale
+// rows (all of K) into LDS with coalesced 16-byte loads once, and reads a
+// stage's bytes from there (scattered per-row scale loads had cost about as
+// much as A's loads: measured 41 -> 31 us at e2m1, M = 64, N = 28672,
+// K = 8192 without them).  Else SCALES_VEC for e2m1 (one 8-byte load per row
+// and stage) or byte loads.  (For fp8 a per-stage dword load plus a per-lane
+// shift measured slower: it pushes the kernel into register spills.)
+template <int FA, int FB, int SMODE>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
     constexpr bool FP4 = FA == 4;  // e2m1 x e2m1; K is the row pitch in bytes
     static_assert(FP4 == (FB == 4), "e2m1 pairs only with e2m1");
-    static_assert(!SVEC || FP4, "vector scale loads are for e2m1");
+    static_assert(SMODE != SCALES_VEC || FP4, "vector scale loads are for e2m1");
+    constexpr bool SVEC = SMODE == SCALES_VEC, STAB = SMODE == SCALES_TABLE;
     constexpr int SPS = FP4 ? 8 : BK / 32;  // scale bytes per row and stage
     __shared__ __attribute__((aligned(16))) float red[WAVES][MAX_M][BN];
+    static_assert(sizeof(red) == TABLE_BYTES, "the scale table shares the reduction buffer");
+    uint8_t *const tab = reinterpret_cast<uint8_t *>(&red[0][0][0]);
 
     const int n0 = blockIdx.x * BN;
     const int rows_b = min(BN, p.N - n0);
@@ -114,9 +133,34 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         }
     };
 
+    // table mode: the workgroup's scale rows, all of K, into LDS (row r < 64:
+    // A row r; else B row r - 64 of this workgroup; missing rows read zero)
+    const int tpitch = table_pitch(KB);
+    if constexpr (STAB) {
+        const int per_row = KB / 16;  // 16-byte pieces per row
+        for (int q = tid; q < TABLE_ROWS * per_row; q += THREADS) {
+            const int r = q / per_row, c = (q % per_row) * 16;
+            const bool is_a = r < MAX_M;
+            const v4i v = load16(is_a ? rAs : rBs, (uint32_t)((is_a ? r : r - MAX_M) * KB + c));
+            uint32_t *d = reinterpret_cast<uint32_t *>(tab + r * tpitch + c);
+            d[0] = (uint32_t)v[0];
+            d[1] = (uint32_t)v[1];
+            d[2] = (uint32_t)v[2];
+            d[3] = (uint32_t)v[3];
+        }
+        __syncthreads();
+    }
+    // table mode: the stage's scale bytes of table row r (fp8: block g;
+    // e2m1: blocks g and 4 + g)
+    auto table_scales = [&](int r, int kt) MXG_INLINE {
+        const uint8_t *t = tab + r * tpitch + kt * SPS + kq;
+        return FP4 ? (uint32_t)t[0] | ((uint32_t)t[4] << 8) : (uint32_t)t[0];
+    };
+
     // every call issues the same loads; a dead stage (kt < 0) reads zeros
     auto load_stage = [&](int kt, Stage &s) MXG_INLINE {
         const bool live = kt >= 0;
+        s.kt = kt;
         const int k0 = (live ? kt : 0) * BK;
         const bool lo_in = live && k0 + kq * LO < K, hi_in = live && k0 + kq * LO + HI < K;
         const int kb0 = (live ? kt : 0) * SPS;
@@ -130,14 +174,14 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             v4i lo = load16(rB, lo_in ? boff[j] + k0 : kOob);
             v4i hi = load16(rB, hi_in ? boff[j] + k0 + HI : kOob);
             s.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            s.sb[j] = scales_of(rBs, bsrow[j], kb0, s0_in, s1_in);
+            if constexpr (!STAB) s.sb[j] = scales_of(rBs, bsrow[j], kb0, s0_in, s1_in);
         }
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) {
             v4i lo = load16(rA, lo_in ? aoff[i] + k0 : kOob);
             v4i hi = load16(rA, hi_in ? aoff[i] + k0 + HI : kOob);
             s.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            s.sa[i] = scales_of(rAs, asrow[i], kb0, s0_in, s1_in);
+            if constexpr (!STAB) s.sa[i] = scales_of(rAs, asrow[i], kb0, s0_in, s1_in);
         }
     };
 
@@ -147,7 +191,14 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) acc[i][j] = v4f{};
 
-    auto multiply = [&](const Stage &cur) MXG_INLINE {
+    auto multiply = [&](const Stage &cur_) MXG_INLINE {
+        Stage cur = cur_;
+        if constexpr (STAB) {
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) cur.sb[j] = table_scales(MAX_M + 16 * j + r16, cur.kt);
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i) cur.sa[i] = table_scales(16 * i + r16, cur.kt);
+        }
         if constexpr (FP4) {
             // step 0: the low chunks (blocks g, scale byte 0); step 1: the high
             // chunks (blocks 4 + g, scale byte 1)
@@ -199,6 +250,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     }
 
     // acc[i][j] register r of lane l: m = 16 i + l % 16, n = 16 j + 4 (l / 16) + r.
+    if constexpr (STAB) __syncthreads();  // every wave is done with the scale table
 #pragma unroll
     for (int i = 0; i < SUB_M; ++i)
 #pragma unroll
