@@ -199,7 +199,8 @@ def test_deterministic(gemm):
 
 
 NATIVE_CASES = [(256, 256, 256, 0, 0, mi.OUT_F32, False), (517, 389, 1056, 1, 0, mi.OUT_F32, True),
-                (64, 448, 1024, 0, 1, mi.OUT_BF16, False), (33, 300, 2048, 1, 1, mi.OUT_F32, True)]
+                (64, 448, 1024, 0, 1, mi.OUT_BF16, False), (33, 300, 2048, 1, 1, mi.OUT_F32, True),
+                (16, 120, 24576, 0, 0, mi.OUT_F32, False)]  # small-M scales without the LDS table
 
 
 @pytest.mark.parametrize("case", NATIVE_CASES, ids=lambda c: "x".join(map(str, c[:3])))
