@@ -67,28 +67,44 @@ hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
                         : launch_large_s<FA, FB, NATIVE, false>(a, s);
 }
 
-template <int FA, int FB>
-hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
+template <int FA, int FB, int MT>
+hipError_t launch_skinny_mt(const mxg::GemmArgs &a, hipStream_t s)
 {
     namespace sk = mxg::skinny;
     const int blocks = a.tiles_m * a.tiles_n;
     // scale table in LDS when the scale rows are 16-byte multiples, aligned,
     // and all of K fits; else (e2m1) 8-byte loads per stage, or byte loads
     if (a.scale_dword == 2 && sk::table_fits(a.KB)) {
-        hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_TABLE>), dim3(blocks), dim3(sk::THREADS),
-                           0, s, a);
+        hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_TABLE, MT>), dim3(blocks),
+                           dim3(sk::THREADS), 0, s, a);
         return hipGetLastError();
     }
     if constexpr (FA == 4) {
         if (a.scale_dword == 2) {
-            hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_VEC>), dim3(blocks),
+            hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_VEC, MT>), dim3(blocks),
                                dim3(sk::THREADS), 0, s, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_BYTES>), dim3(blocks), dim3(sk::THREADS), 0,
-                       s, a);
+    hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_BYTES, MT>), dim3(blocks),
+                       dim3(sk::THREADS), 0, s, a);
     return hipGetLastError();
+}
+
+// e2m1 runs only ceil(M/16) tiles of A; the fp8 native variant (an opt-in)
+// keeps all four, which holds down the number of kernels built
+template <int FA, int FB>
+hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
+{
+    if constexpr (FA == 4) {
+        switch ((a.M + 15) / 16) {
+        case 1: return launch_skinny_mt<FA, FB, 1>(a, s);
+        case 2: return launch_skinny_mt<FA, FB, 2>(a, s);
+        case 3: return launch_skinny_mt<FA, FB, 3>(a, s);
+        default: break;
+        }
+    }
+    return launch_skinny_mt<FA, FB, 4>(a, s);
 }
 
 template <int FA, int FB, int MT>

@@ -51,11 +51,12 @@ __device__ __forceinline__ v4f mfma16(v8i x, v8i y, v4f c, uint32_t sx, uint32_t
                                                            (int)sy);
 }
 
+template <int MT>  // 16-row tiles of A (M <= 16 MT)
 struct Stage {
     v8i b[SUB_N];
-    v8i a[SUB_M];
+    v8i a[MT];
     uint32_t sb[SUB_N];  // fp8: block g; e2m1: blocks g (byte 0) and 4 + g (byte 1)
-    uint32_t sa[SUB_M];
+    uint32_t sa[MT];
     int kt;              // the K stage (scale table mode reads its scales at multiply time)
 };
 
@@ -80,9 +81,13 @@ constexpr int RING = 3;  // stage buffers per wave: RING - 1 loading, one multip
 // K = 8192 without them).  Else SCALES_VEC for e2m1 (one 8-byte load per row
 // and stage) or byte loads.  (For fp8 a per-stage dword load plus a per-lane
 // shift measured slower: it pushes the kernel into register spills.)
-template <int FA, int FB, int SMODE>
+// MT: 16-row tiles of A loaded and multiplied (M <= 16 MT), so a
+// decode-size M pays only for its own rows.
+template <int FA, int FB, int SMODE, int MT>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
+    static_assert(MT >= 1 && MT <= SUB_M, "M tiles");
+    using Stage = mxg::skinny::Stage<MT>;
     constexpr bool FP4 = FA == 4;  // e2m1 x e2m1; K is the row pitch in bytes
     static_assert(FP4 == (FB == 4), "e2m1 pairs only with e2m1");
     static_assert(SMODE != SCALES_VEC || FP4, "vector scale loads are for e2m1");
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, kq = lane >> 4;
 
-    uint32_t boff[SUB_N], aoff[SUB_M], bsrow[SUB_N], asrow[SUB_M];
+    uint32_t boff[SUB_N], aoff[MT], bsrow[SUB_N], asrow[MT];
     // chunks K bytes 16g.. and 64+16g.. of each stage; scale rows
     constexpr int LO = 16, HI = 64;
 #pragma unroll
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         bsrow[j] = (uint32_t)(16 * j + r16) * KB;
     }
 #pragma unroll
-    for (int i = 0; i < SUB_M; ++i) {
+    for (int i = 0; i < MT; ++i) {
         aoff[i] = (uint32_t)(16 * i + r16) * K + kq * LO;
         asrow[i] = (uint32_t)(16 * i + r16) * KB;
     }
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             if constexpr (!STAB) s.sb[j] = scales_of(rBs, bsrow[j], kb0, s0_in, s1_in);
         }
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) {
+        for (int i = 0; i < MT; ++i) {
             v4i lo = load16(rA, lo_in ? aoff[i] + k0 : kOob);
             v4i hi = load16(rA, hi_in ? aoff[i] + k0 + HI : kOob);
             s.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -185,9 +190,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         }
     };
 
-    v4f acc[SUB_M][SUB_N];
+    v4f acc[MT][SUB_N];
 #pragma unroll
-    for (int i = 0; i < SUB_M; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) acc[i][j] = v4f{};
 
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j) cur.sb[j] = table_scales(MAX_M + 16 * j + r16, cur.kt);
 #pragma unroll
-            for (int i = 0; i < SUB_M; ++i) cur.sa[i] = table_scales(16 * i + r16, cur.kt);
+            for (int i = 0; i < MT; ++i) cur.sa[i] = table_scales(16 * i + r16, cur.kt);
         }
         if constexpr (FP4) {
             // step 0: the low chunks (blocks g, scale byte 0); step 1: the high
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j)
 #pragma unroll
-                for (int i = 0; i < SUB_M; ++i) {
+                for (int i = 0; i < MT; ++i) {
                     const v8i b0 = {cur.b[j][0], cur.b[j][1], cur.b[j][2], cur.b[j][3], 0, 0, 0, 0};
                     const v8i a0 = {cur.a[i][0], cur.a[i][1], cur.a[i][2], cur.a[i][3], 0, 0, 0, 0};
                     acc[i][j] = mfma16<FB, FA, 0>(b0, a0, acc[i][j], cur.sb[j], cur.sa[i]);
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j)
 #pragma unroll
-                for (int i = 0; i < SUB_M; ++i) {
+                for (int i = 0; i < MT; ++i) {
                     const v8i b1 = {cur.b[j][4], cur.b[j][5], cur.b[j][6], cur.b[j][7], 0, 0, 0, 0};
                     const v8i a1 = {cur.a[i][4], cur.a[i][5], cur.a[i][6], cur.a[i][7], 0, 0, 0, 0};
                     acc[i][j] = mfma16<FB, FA, 1>(b1, a1, acc[i][j], cur.sb[j], cur.sa[i]);
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j)
 #pragma unroll
-                for (int i = 0; i < SUB_M; ++i)
+                for (int i = 0; i < MT; ++i)
                     acc[i][j] = mfma16<FB, FA>(cur.b[j], cur.a[i], acc[i][j], cur.sb[j], cur.sa[i]);
         }
     };
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // acc[i][j] register r of lane l: m = 16 i + l % 16, n = 16 j + 4 (l / 16) + r.
     if constexpr (STAB) __syncthreads();  // every wave is done with the scale table
 #pragma unroll
-    for (int i = 0; i < SUB_M; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j)
             *reinterpret_cast<v4f *>(&red[wave][16 * i + r16][16 * j + 4 * kq]) = acc[i][j];

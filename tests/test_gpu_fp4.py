@@ -69,6 +69,8 @@ FP4_CASES = [
     (517, 389, 1056, True, mi.OUT_BF16),
     (33, 1000, 640, False, mi.OUT_BF16),
     (16, 120, 24576, False, mi.OUT_F32),     # M <= 64 with K too long for the LDS scale table
+    (20, 333, 2048, True, mi.OUT_BF16),      # two 16-row tiles of A on the small-M kernel
+    (48, 250, 4096, False, mi.OUT_F32),      # three
 ]
 
 
