@@ -415,7 +415,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(b4 / mean_4s / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(b4 / mean_4s / 1e9 / PEAK_HBM_GBS, 4),
-                     "kernel": "mxg::skinny::kernel<4,4,2> (LDS scale table)",
+                     "kernel": "mxg::skinny::kernel<4,4,2,4> (LDS scale table)",
                      "launch_mean_us": round(mean_4s * 1e6, 2)},
         "algorithmic_bytes": b4}
     log(f"bench: e2m1 decode shape {out['mxfp4_skinny_m64']['value']} GB/s")
