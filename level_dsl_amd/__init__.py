@@ -128,7 +128,8 @@ def mxgemm_set_workspace(h, ws, nbytes: int, stream=None) -> None:
 
 
 def mxgemm_set_splits(h, splits: int) -> None:
-    """K splits of exact small-M calls: 0 automatic, 1 never, S >= 2 forced."""
+    """K splits of later calls: 0 automatic, 1 never, S >= 2 forced (not the
+    fp8 native small-M variant)."""
     _check(load_library().mxgemm_set_splits(h, int(splits)), "mxgemm_set_splits")
 
 

@@ -67,28 +67,39 @@ hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
                         : launch_large_s<FA, FB, NATIVE, false>(a, s);
 }
 
-template <int FA, int FB, int MT>
-hipError_t launch_skinny_mt(const mxg::GemmArgs &a, hipStream_t s)
+template <int FA, int FB, int MT, bool SPLIT>
+hipError_t launch_skinny_s(const mxg::GemmArgs &a, hipStream_t s)
 {
     namespace sk = mxg::skinny;
-    const int blocks = a.tiles_m * a.tiles_n;
+    const int blocks = a.tiles_m * a.tiles_n * a.splits;
     // scale table in LDS when the scale rows are 16-byte multiples, aligned,
     // and all of K fits; else (e2m1) 8-byte loads per stage, or byte loads
     if (a.scale_dword == 2 && sk::table_fits(a.KB)) {
-        hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_TABLE, MT>), dim3(blocks),
+        hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_TABLE, MT, SPLIT>), dim3(blocks),
                            dim3(sk::THREADS), 0, s, a);
         return hipGetLastError();
     }
     if constexpr (FA == 4) {
         if (a.scale_dword == 2) {
-            hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_VEC, MT>), dim3(blocks),
+            hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_VEC, MT, SPLIT>), dim3(blocks),
                                dim3(sk::THREADS), 0, s, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_BYTES, MT>), dim3(blocks),
+    hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_BYTES, MT, SPLIT>), dim3(blocks),
                        dim3(sk::THREADS), 0, s, a);
     return hipGetLastError();
+}
+
+// split launches (e2m1 only) use their own instantiation, as for the
+// 256 x 256 kernel
+template <int FA, int FB, int MT>
+hipError_t launch_skinny_mt(const mxg::GemmArgs &a, hipStream_t s)
+{
+    if constexpr (FA == 4) {
+        if (a.splits > 1) return launch_skinny_s<FA, FB, MT, true>(a, s);
+    }
+    return launch_skinny_s<FA, FB, MT, false>(a, s);
 }
 
 // e2m1 runs only ceil(M/16) tiles of A; the fp8 native variant (an opt-in)
@@ -149,15 +160,17 @@ static_assert(MXGEMM_WORKSPACE_BYTES_LARGE ==
                   kCounterBytes + (size_t)mxg::stream::MAX_SPLITS_TILES * kLargePartial,
               "large workspace layout");
 
-// K splits of an exact small-M call: none unless asked for or the column
-// tiles leave more than half of the 256 CUs idle; then the largest power of
-// two that keeps every split at least 8 K stages (1 KiB) long, tiles_n * S
-// within one workgroup per CU, and S <= 8 (measured: more splits cost more in
-// the reduction than they gain in streaming).  With K a multiple of 1 KiB * S
-// every split is a whole number of the kernel's 8-stage rings.
-int choose_splits(int forced, int tiles_n, int nk)
+// K splits of a small-M call: none unless asked for or the column tiles
+// leave more than half of the 256 CUs idle; then the largest power of two
+// that keeps every split at least kMinStages 128-byte K stages long, tiles_n
+// * S within one workgroup per CU, and S <= 8 (measured: more splits cost
+// more in the reduction than they gain in streaming).  The exact kernel
+// takes kMinStages = 8: with K a multiple of 1 KiB * S every split is a whole
+// number of its 8-stage rings.  The e2m1 kernel takes 4, one stage per wave
+// (measured at N = 3584, K = 8192: 12.0 us at 8 splits, 12.7 at 4, 23.8 unsplit).
+int choose_splits(int forced, int tiles_n, int nk, int kMinStages)
 {
-    constexpr int kTarget = mxg::stream::MAX_SPLITS_TILES, kMinStages = 8, kMaxAuto = 8;
+    constexpr int kTarget = mxg::stream::MAX_SPLITS_TILES, kMaxAuto = 8;
     int s;
     if (forced >= 1) {
         s = forced;
@@ -404,9 +417,10 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     if (skinny) {
         a.tiles_m = 1;
         a.tiles_n = (int)((N + mxg::skinny::BN - 1) / mxg::skinny::BN);
-        if (!native) {
-            const int nk = (int)((K + mxg::stream::BK - 1) / mxg::stream::BK);
-            a.splits = choose_splits(h->splits, a.tiles_n, nk);
+        if (!native || fp4) {  // the fp8 native small-M variant is not split
+            const int nk = native ? (a.K + mxg::skinny::BK - 1) / mxg::skinny::BK
+                                  : (int)((K + mxg::stream::BK - 1) / mxg::stream::BK);
+            a.splits = choose_splits(h->splits, a.tiles_n, nk, native ? 4 : 8);
             if (a.splits > 1 && !h->ws) {
                 if (h->splits >= 2) return MXGEMM_ERR_WORKSPACE;
                 a.splits = 1;

@@ -29,7 +29,10 @@
 //   * A (at most 64 x K bytes) is re-read by every workgroup and stays in L2;
 //   * at the end the four per-wave partial tiles are summed in a fixed order
 //     through LDS (deterministic), use_acc adds the old C, and C is written
-//     with coalesced 16-byte (fp32) or 8-byte (bf16) buffer stores.
+//     with coalesced 16-byte (fp32) or 8-byte (bf16) buffer stores;
+//   * e2m1 with few column tiles (N up to 128 tiles of 112) splits K over
+//     several workgroups per tile, whose partial tiles are added in split
+//     order through a caller-owned workspace.
 #pragma once
 
 #include "mxgemm_common.h"
@@ -83,10 +86,13 @@ constexpr int RING = 3;  // stage buffers per wave: RING - 1 loading, one multip
 // shift measured slower: it pushes the kernel into register spills.)
 // MT: 16-row tiles of A loaded and multiplied (M <= 16 MT), so a
 // decode-size M pays only for its own rows.
-template <int FA, int FB, int SMODE, int MT>
+// SPLIT (e2m1): workgroup tile + tiles_n * sp runs K split sp of p.splits and
+// the splits' partial tiles are summed in split order through the workspace.
+template <int FA, int FB, int SMODE, int MT, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
     static_assert(MT >= 1 && MT <= SUB_M, "M tiles");
+    static_assert(!SPLIT || FA == 4, "split K is built for e2m1 only");
     using Stage = mxg::skinny::Stage<MT>;
     constexpr bool FP4 = FA == 4;  // e2m1 x e2m1; K is the row pitch in bytes
     static_assert(FP4 == (FB == 4), "e2m1 pairs only with e2m1");
@@ -97,9 +103,15 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     static_assert(sizeof(red) == TABLE_BYTES, "the scale table shares the reduction buffer");
     uint8_t *const tab = reinterpret_cast<uint8_t *>(&red[0][0][0]);
 
-    const int n0 = blockIdx.x * BN;
+    const int tile = SPLIT ? (int)(blockIdx.x % (unsigned)p.tiles_n) : (int)blockIdx.x;
+    const int sp = SPLIT ? (int)(blockIdx.x / (unsigned)p.tiles_n) : 0;
+    const int n0 = tile * BN;
     const int rows_b = min(BN, p.N - n0);
     const int M = p.M, N = p.N, K = p.K, KB = p.KB;
+    // this workgroup's K stages [kbeg, kbeg + nk) of nk_all
+    const int nk_all = (K + BK - 1) / BK;
+    const int kbeg = SPLIT ? (int)((int64_t)sp * nk_all / p.splits) : 0;
+    const int nk = SPLIT ? (int)((int64_t)(sp + 1) * nk_all / p.splits) - kbeg : nk_all;
 
     const rsrc_t rA = make_rsrc(p.A, (uint32_t)M * K);
     const rsrc_t rB = make_rsrc(p.B + (size_t)n0 * K, (uint32_t)rows_b * K);
@@ -138,13 +150,16 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         }
     };
 
-    // table mode: the workgroup's scale rows, all of K, into LDS (row r < 64:
-    // A row r; else B row r - 64 of this workgroup; missing rows read zero)
+    // table mode: the workgroup's scale rows into LDS (row r < 64: A row r;
+    // else B row r - 64 of this workgroup; missing rows read zero), the
+    // 16-byte pieces that cover this workgroup's stages, at their places in
+    // the row
     const int tpitch = table_pitch(KB);
     if constexpr (STAB) {
-        const int per_row = KB / 16;  // 16-byte pieces per row
+        const int c_lo = kbeg * SPS / 16, c_hi = min(KB / 16, ((kbeg + nk) * SPS + 15) / 16);
+        const int per_row = c_hi - c_lo;  // 16-byte pieces per row
         for (int q = tid; q < TABLE_ROWS * per_row; q += THREADS) {
-            const int r = q / per_row, c = (q % per_row) * 16;
+            const int r = q / per_row, c = (c_lo + q % per_row) * 16;
             const bool is_a = r < MAX_M;
             const v4i v = load16(is_a ? rAs : rBs, (uint32_t)((is_a ? r : r - MAX_M) * KB + c));
             uint32_t *d = reinterpret_cast<uint32_t *>(tab + r * tpitch + c);
@@ -232,9 +247,8 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         }
     };
 
-    const int nk = (K + BK - 1) / BK;
-    const int s0 = (int)(blockIdx.x % (unsigned)nk);  // this workgroup's first stage
-    auto stage_of = [&](int t) MXG_INLINE { const int s = t + s0; return s < nk ? s : s - nk; };
+    const int s0 = tile % nk;  // this workgroup's first stage, counted from kbeg
+    auto stage_of = [&](int t) MXG_INLINE { const int s = t + s0; return kbeg + (s < nk ? s : s - nk); };
     // wave w runs its stages t = w, w + WAVES, ...; the i-th of them lives in
     // ring slot i % RING (static indices only: the ring stays in registers)
     // Loads are issued unconditionally (dead stages read zeros) so that the
@@ -265,6 +279,72 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     const rsrc_t rC = make_rsrc((uint8_t *)p.C, (uint32_t)M * N * (p.out_bf16 ? 2 : 4));
     constexpr int Q = MAX_M * BN / 4;  // float4 groups in the tile
+    if constexpr (SPLIT) {
+        // Every split leaves its fp32 partial tile in the workspace
+        // ([split][tile][64 rows][112 columns]); a counter per tile counts the
+        // splits that are done, and the workgroup that completes the count
+        // adds the partials in split order 0, 1, ..., so the result does not
+        // depend on which split finishes last, and resets the counter for the
+        // next call.  Partials are written and read with device-scope
+        // coherent (sc1) buffer accesses, which bypass the per-XCD L2s'
+        // non-coherent copies: the wait for the stores to complete, then the
+        // barrier, is the whole release (no L2 writeback).
+        constexpr int TILE_F = MAX_M * BN;
+        constexpr int SC1 = 16;  // cache-policy bit of the buffer intrinsics
+        __shared__ uint32_t last;
+        const rsrc_t rW = make_rsrc(p.ws, (uint32_t)(p.splits * p.tiles_n * TILE_F * 4));
+        const uint32_t tile_off = (uint32_t)(tile * TILE_F) * 4;
+        const uint32_t split_pitch = (uint32_t)(p.tiles_n * TILE_F) * 4;
+        for (int q = tid; q < Q; q += THREADS) {
+            const int m = q / (BN / 4), nl = (q % (BN / 4)) * 4;
+            if (m >= M) continue;
+            v4f v = *reinterpret_cast<const v4f *>(&red[0][m][nl]);
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const v4f *>(&red[w][m][nl]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rW,
+                                                   tile_off + sp * split_pitch + (uint32_t)(m * BN + nl) * 4,
+                                                   0, SC1);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores are complete
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();                     // ... and so are every thread's
+        if (tid == 0) {
+            uint32_t *cnt = p.cnt + tile;
+            const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = old == (uint32_t)(p.splits - 1);
+            if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!last) return;
+        // up to QB splits' partials in flight at once (a split past the last
+        // reads zeros through the range check and is not added)
+        constexpr int QB = 8;
+        for (int q = tid; q < Q; q += THREADS) {
+            const int m = q / (BN / 4), nl = (q % (BN / 4)) * 4;
+            if (m >= M) continue;
+            const uint32_t off = tile_off + (uint32_t)(m * BN + nl) * 4;
+            v4f v = {};
+            for (int q0 = 0; q0 < p.splits; q0 += QB) {
+                v4f part[QB];
+#pragma unroll
+                for (int qq = 0; qq < QB; ++qq)
+                    part[qq] = __builtin_bit_cast(
+                        v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                 rW, q0 + qq < p.splits ? off + (q0 + qq) * split_pitch : kOob, 0, SC1));
+#pragma unroll
+                for (int qq = 0; qq < QB; ++qq) {
+                    if (q0 + qq == 0)
+                        v = part[qq];
+                    else if (q0 + qq < p.splits)
+                        v += part[qq];
+                }
+            }
+            const int n = n0 + nl;
+            store_c4(rC, (uint32_t)m * N + n, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
+        }
+        return;
+    }
     for (int q = tid; q < Q; q += THREADS) {
         const int m = q / (BN / 4), nl = (q % (BN / 4)) * 4;
         if (m >= M) continue;

@@ -11,7 +11,9 @@ exact variants:
     small M, and both e2m1-capable variants;
   * a NaN scale at the start of the next row must not leak into a row
     whose last stage stops inside the scale dword (K = 1152);
-  * split-K, forced and automatic;
+  * split-K, forced and automatic, on both kernels (the small-M kernel's
+    split in its three scale modes, bitwise repeatable, its arrival
+    counters shared with the other kernels' splits);
   * the 8192 x 8192 x 8192 benchmark shape on sampled outputs;
   * the error paths (e2m1 with another format, a small-M variant).
 """
@@ -119,6 +121,91 @@ def test_fp4_split_k_forced(S):
         compare(got, oracle_full(p), p.out_dtype, f"fp4 split S={S}")
     finally:
         g.close()
+
+
+SMALL_M_SPLIT_CASES = [
+    # M, N, K, splits, use_acc, out  (scale mode the host picks)
+    (16, 250, 8192, 8, False, mi.OUT_F32),     # LDS scale table
+    (33, 130, 4160, 5, True, mi.OUT_BF16),     # 17 stages, the last partial; byte scale loads
+    (64, 500, 2048, 3, False, mi.OUT_F32),     # four A tiles, table
+    (1, 3, 1024, 8, False, mi.OUT_F32),        # 4 stages: asks for 8, runs 4
+    (48, 112, 3072, 7, True, mi.OUT_F32),      # 12 stages over 7 splits (one or two each)
+    (16, 120, 24576, 4, False, mi.OUT_BF16),   # K too long for the table: 8-byte scale loads
+]
+
+
+@pytest.mark.parametrize("M,N,K,S,acc,out", SMALL_M_SPLIT_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}_s{c[3]}" for c in SMALL_M_SPLIT_CASES])
+def test_fp4_small_m_split_k_forced(M, N, K, S, acc, out):
+    """Split K on the small-M scaled-MFMA kernel (M <= 64), against the
+    oracle on full outputs, with the guard bands around C intact."""
+    p = mi.random_problem(M, N, K, seed=850 + S + M, fmtA=E2M1, fmtB=E2M1, out_dtype=out,
+                          use_acc=acc)
+    g = L.Gemm()
+    g.enable_split_k()
+    try:
+        g.set_splits(S)
+        log(f"fp4 small-M split-K S={S} M={M} N={N} K={K} use_acc={acc} out={out}")
+        got = run(g, p, AUTO, guard=64)
+        compare(got, oracle_full(p), out, f"fp4 small-M split S={S}")
+    finally:
+        g.close()
+
+
+def test_fp4_small_m_split_k_repeatable_and_counters_reset():
+    """Splits add their partials in split order: repeated calls give the
+    same bits.  Calls of other shapes and kernels in between (the exact
+    small-M kernel's split, the 256 x 256 kernel's split) share the arrival
+    counters; each call leaves them at zero, so every result stays right."""
+    g = L.Gemm()
+    g.enable_split_k()
+    try:
+        p = mi.random_problem(64, 336, 8192, seed=860, fmtA=E2M1, fmtB=E2M1)
+        dev = to_dev(p)
+        g.set_splits(8)
+        outs = [run(g, p, AUTO, dev_inputs=dev) for _ in range(3)]
+        log("fp4 small-M split repeatability: 3 calls, S=8, 64x336x8192")
+        for o in outs[1:]:
+            assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+        compare(outs[0], oracle_full(p), p.out_dtype, "S=8")
+        others = [mi.random_problem(40, 300, 2048, seed=861),
+                  mi.random_problem(200, 300, 2048, seed=862, fmtA=E2M1, fmtB=E2M1),
+                  mi.random_problem(16, 250, 4096, seed=863, fmtA=E2M1, fmtB=E2M1)]
+        for S in (3, 5):
+            g.set_splits(S)
+            for q in others:
+                log(f"fp4 counters: S={S} M={q.M} N={q.N} K={q.K} fmt={q.fmtA}")
+                compare(run(g, q, AUTO, guard=16), oracle_full(q), q.out_dtype, f"S={S} M={q.M}")
+            again = run(g, p, AUTO, dev_inputs=dev)
+            compare(again, oracle_full(p), p.out_dtype, f"after S={S}")
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_fp4_small_m_split_k_auto_sharded_decode(M):
+    """One GPU's share of the decode shape split by columns over 8 GPUs:
+    N = 3584 leaves 32 column tiles, so the automatic choice splits K 8 ways;
+    sampled outputs against the oracle, and the unsplit call agrees."""
+    N, K = 3584, 8192
+    p = mi.random_problem(M, N, K, seed=870 + M, fmtA=E2M1, fmtB=E2M1)
+    dev = to_dev(p)
+    rows, cols = mi.sample_points(M, N, 8192, seed=870 + M, edge=64)
+    ref = oracle_points(p, rows, cols)
+    g = L.Gemm()
+    g.enable_split_k()
+    try:
+        log(f"fp4 small-M auto split M={M} N={N} K={K}")
+        got = run(g, p, AUTO, guard=64, dev_inputs=dev)
+        compare(got[rows, cols], ref, p.out_dtype, "fp4 small-M auto split")
+    finally:
+        g.close()
+    g = L.Gemm()
+    try:
+        plain = run(g, p, AUTO, dev_inputs=dev)
+    finally:
+        g.close()
+    compare(plain[rows, cols], ref, p.out_dtype, "fp4 small-M unsplit")
 
 
 def test_fp4_split_k_auto_medium_m():
