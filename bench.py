@@ -29,7 +29,9 @@ Counter passes (HBM traffic per launch):
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o p -- python bench.py --traffic
   python bench.py --traffic-report D1/p_counter_collection.csv D2/p_counter_collection.csv
 --traffic launches a plain negating copy of COPY_BYTES (read once, written once)
-and three launches each of the two timed kernels; --traffic-report scales the
+and three launches each of the timed GEMM kernels (the 256 x 256 kernel in
+its exact, native and e2m1 modes, the exact small-M kernel) and of the MX
+quantization; --traffic-report scales the
 counters by what they read for that copy and writes profiles/hbm_traffic.json.
 """
 from __future__ import annotations
@@ -143,11 +145,38 @@ def bench_gemm(gemm, p, variant, steps, warmup, copies):
 
 
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
-# key: (kernel name as rocprofv3 prints it, workload id, variant, C bytes per element)
+# key: (kernel name as rocprofv3 prints it, workload id (or "e2m1_8192": the
+# e2m1 8192^3 problem of the bench), variant, C bytes per element)
 TRAFFIC_KERNELS = {"large_exact": ("void mxg::large::kernel<0, 0, false, true, false>", 2,
                                    "MXGEMM_VARIANT_LARGE", 2),
                    "skinny_exact": ("void mxg::stream::kernel<0, 0, true, 4>", 3,
-                                    "MXGEMM_VARIANT_SKINNY", 4)}
+                                    "MXGEMM_VARIANT_SKINNY", 4),
+                   "large_native": ("void mxg::large::kernel<0, 0, true, false, false>", 2,
+                                    "MXGEMM_VARIANT_LARGE_NATIVE", 2),
+                   "mxfp4_large": ("void mxg::large::kernel<4, 4, true, false, false>", "e2m1_8192",
+                                   "MXGEMM_VARIANT_AUTO", 2)}
+
+
+def e2m1_8192():
+    """The e2m1 8192^3 problem of the bench: N(0, 1) codes, scales
+    U{120..134}, bf16 out."""
+    import mxinputs as mi
+    return mi.random_problem(8192, 8192, 8192, seed=850, fmtA=mi.FMT_E2M1, fmtB=mi.FMT_E2M1,
+                             out_dtype=mi.OUT_BF16)
+
+
+def traffic_problem(wid):
+    import mxinputs as mi
+    return e2m1_8192() if wid == "e2m1_8192" else mi.workload(wid)
+
+
+def traffic_shape(wid):
+    """(name, M, N, K, bytes per row of A or B, C bytes per element)"""
+    import mxinputs as mi
+    if wid == "e2m1_8192":
+        return "mxfp4_e2m1_8192cube_bf16", 8192, 8192, 8192, 4096
+    w = mi.WORKLOADS[wid]
+    return w["name"], w["M"], w["N"], w["K"], w["K"]
 QUANT_KERNEL = "void mxg::quant::kernel<0, 0>"
 QUANT_SHAPE = (28672, 8192)  # the skinny workload's weight, N x K
 
@@ -192,7 +221,7 @@ def traffic_launches():
     del x, y
     gemm = L.Gemm()
     for key, (_, wid, var, _) in TRAFFIC_KERNELS.items():
-        p = mi.workload(wid)
+        p = traffic_problem(wid)
         log(f"traffic: {key} on {p.name}")
         bench_gemm(gemm, p, getattr(L, var), 3, 0, 3)
     log("traffic: mx_quantize")
@@ -243,10 +272,10 @@ def traffic_report(fetch_csv: str, write_csv: str, out_path: str = None):
         v = vals.get(key, {})
         if "FETCH_SIZE" not in v or "WRITE_SIZE" not in v:
             continue
-        p = mi.WORKLOADS[wid]
-        alg = mi.algorithmic_bytes(p["M"], p["N"], p["K"],
-                                   mi.OUT_BF16 if cbytes == 2 else mi.OUT_F32)
-        out["kernels"][key] = {"kernel": kname, "workload": p["name"],
+        wname, M, N, K, row = traffic_shape(wid)
+        # A and B rows (e2m1: two codes per byte), one scale byte per 32, C once
+        alg = (M + N) * (row + K // 32) + M * N * cbytes
+        out["kernels"][key] = {"kernel": kname, "workload": wname,
                                "fetch_bytes": round(v["FETCH_SIZE"]),
                                "write_bytes": round(v["WRITE_SIZE"]),
                                "bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
@@ -358,6 +387,7 @@ def main():
         "achieved_per_launch": round(flops / mean_n / 1e12, 2), "peak": PEAK_TFLOPS["fp8"],
         "frac": round(flops / mean_n / 1e12 / PEAK_TFLOPS["fp8"], 4),
         "launch_mean_us": round(mean_n * 1e6, 2),
+        "traffic": traffic_from_profiles("large_native"),
         "note": "v_mfma_scale_f32_32x32x64_f8f6f4; not within 1e-5*sum|ab| (8-product "
                 "groups truncated 13 bits below their largest product)"}
     log(f"bench: native {out['native_scaled_mfma']['value']} TFLOP/s")
@@ -365,8 +395,7 @@ def main():
     # ---- e2m1 (FP4) operands on the same shape --------------------------------
     # N(0, 1) -> e2m1 (RNE, saturating at 6), scales U{120..134}, bf16 out; the
     # scaled MFMA is exact for e2m1, so this is held to the same bound
-    p4 = mi.random_problem(8192, 8192, 8192, seed=850, fmtA=mi.FMT_E2M1, fmtB=mi.FMT_E2M1,
-                           out_dtype=mi.OUT_BF16)
+    p4 = e2m1_8192()
     log("bench: e2m1 8192^3 generated")
     wall_4, mean_4 = bench_gemm(gemm, p4, L.MXGEMM_VARIANT_AUTO, steps, warmup, 3)
     del p4
@@ -377,6 +406,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops / mean_4 / 1e12, 2),
                      "peak": PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
                      "frac": round(flops / mean_4 / 1e12 / PEAK_TFLOPS["fp4"], 4),
+                     "traffic": traffic_from_profiles("mxfp4_large"),
                      "kernel": "mxg::large::kernel<4,4,true,false,false>",
                      "launch_mean_us": round(mean_4 * 1e6, 2)}}
     log(f"bench: e2m1 {out['mxfp4']['value']} TFLOP/s")
@@ -415,7 +445,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(b4 / mean_4s / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(b4 / mean_4s / 1e9 / PEAK_HBM_GBS, 4),
-                     "kernel": "mxg::skinny::kernel<4,4,2,4> (LDS scale table)",
+                     "kernel": "mxg::skinny::kernel<4,4,2,4,false> (LDS scale table)",
                      "launch_mean_us": round(mean_4s * 1e6, 2)},
         "algorithmic_bytes": b4}
     log(f"bench: e2m1 decode shape {out['mxfp4_skinny_m64']['value']} GB/s")
