@@ -51,9 +51,11 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}  # MI355X published dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
 METRIC = "MXFP8 GEMM TFLOP/s at 8192\u00b3 (% of dense MXFP8 peak); GB/s (% HBM) at M=64"
-KERNEL_SOURCES = ["level_dsl_amd/csrc/mxgemm.hip", "level_dsl_amd/csrc/mxgemm_common.h",
-                  "level_dsl_amd/csrc/mxgemm_large.h", "level_dsl_amd/csrc/mxgemm_skinny.h",
-                  "level_dsl_amd/csrc/mxgemm_stream.h", "level_dsl_amd/csrc/mxquant.h"]
+KERNEL_SOURCES = ["level_dsl_amd/csrc/" + f for f in (
+    "mxgemm.hip", "mxgemm_common.h", "mxgemm_large.h", "mxgemm_skinny.h", "mxgemm_stream.h",
+    "mxquant.h", "mxgemm_launch.h", "launch_large.h", "launch_skinny.h", "k_large_exact.hip",
+    "k_large_exact_b.hip", "k_large_native.hip", "k_large_e2m1.hip", "k_stream.hip", "k_skinny_fp8.hip",
+    "k_skinny_e2m1.hip", "k_quant.hip")]
 
 
 def kernel_hash() -> str:

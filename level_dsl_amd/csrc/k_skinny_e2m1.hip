@@ -1,0 +1,9 @@
+// k_skinny_e2m1.hip -- the small-M scaled-MFMA kernel, e2m1 x e2m1.
+#include "launch_skinny.h"
+#include "mxgemm_launch.h"
+
+namespace mxg {
+
+hipError_t launch_skinny_e2m1(const GemmArgs &a, hipStream_t s) { return launch_skinny<4, 4>(a, s); }
+
+} // namespace mxg

@@ -2,7 +2,8 @@
 //
 // Argument checking, variant selection and the launch on the caller's
 // stream.  Everything the multiply computes runs in the gfx950 kernels
-// (mxgemm_large.h, mxgemm_skinny.h); this file does no arithmetic on the
+// (mxgemm_large.h, mxgemm_skinny.h, mxgemm_stream.h, mxquant.h, launched
+// from the k_*.hip translation units); this file does no arithmetic on the
 // operands.
 #include <hip/hip_runtime.h>
 
@@ -13,9 +14,9 @@
 
 #include "mxgemm.h"
 #include "mxgemm_large.h"
+#include "mxgemm_launch.h"
 #include "mxgemm_skinny.h"
 #include "mxgemm_stream.h"
-#include "mxquant.h"
 
 static_assert(mxg::stream::BN == mxg::skinny::BN && mxg::stream::MAX_M == mxg::skinny::MAX_M,
               "both small-M kernels tile N and bound M alike");
@@ -38,106 +39,6 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb)
 {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
-}
-
-template <int FA, int FB, bool NATIVE, bool SPLIT>
-hipError_t launch_large_s(const mxg::GemmArgs &a, hipStream_t s)
-{
-    const int blocks = a.tiles_m * a.tiles_n * a.splits;
-    // 16-byte scale windows need K % 512 == 0 and 16-byte aligned scale rows;
-    // the native variant has no registers to spare for them
-    if constexpr (!NATIVE) {
-        if (a.scale_dword == 2) {
-            hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, true, SPLIT>), dim3(blocks),
-                               dim3(mxg::large::THREADS), 0, s, a);
-            return hipGetLastError();
-        }
-    }
-    hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, false, SPLIT>), dim3(blocks),
-                       dim3(mxg::large::THREADS), 0, s, a);
-    return hipGetLastError();
-}
-
-// Split launches use their own instantiation, so that the split epilogue
-// adds nothing to the register budget of the unsplit kernel.
-template <int FA, int FB, bool NATIVE>
-hipError_t launch_large(const mxg::GemmArgs &a, hipStream_t s)
-{
-    return a.splits > 1 ? launch_large_s<FA, FB, NATIVE, true>(a, s)
-                        : launch_large_s<FA, FB, NATIVE, false>(a, s);
-}
-
-template <int FA, int FB, int MT, bool SPLIT>
-hipError_t launch_skinny_s(const mxg::GemmArgs &a, hipStream_t s)
-{
-    namespace sk = mxg::skinny;
-    const int blocks = a.tiles_m * a.tiles_n * a.splits;
-    // scale table in LDS when the scale rows are 16-byte multiples, aligned,
-    // and all of K fits; else (e2m1) 8-byte loads per stage, or byte loads
-    if (a.scale_dword == 2 && sk::table_fits(a.KB)) {
-        hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_TABLE, MT, SPLIT>), dim3(blocks),
-                           dim3(sk::THREADS), 0, s, a);
-        return hipGetLastError();
-    }
-    if constexpr (FA == 4) {
-        if (a.scale_dword == 2) {
-            hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_VEC, MT, SPLIT>), dim3(blocks),
-                               dim3(sk::THREADS), 0, s, a);
-            return hipGetLastError();
-        }
-    }
-    hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_BYTES, MT, SPLIT>), dim3(blocks),
-                       dim3(sk::THREADS), 0, s, a);
-    return hipGetLastError();
-}
-
-// split launches (e2m1 only) use their own instantiation, as for the
-// 256 x 256 kernel
-template <int FA, int FB, int MT>
-hipError_t launch_skinny_mt(const mxg::GemmArgs &a, hipStream_t s)
-{
-    if constexpr (FA == 4) {
-        if (a.splits > 1) return launch_skinny_s<FA, FB, MT, true>(a, s);
-    }
-    return launch_skinny_s<FA, FB, MT, false>(a, s);
-}
-
-// e2m1 runs only ceil(M/16) tiles of A; the fp8 native variant (an opt-in)
-// keeps all four, which holds down the number of kernels built
-template <int FA, int FB>
-hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
-{
-    if constexpr (FA == 4) {
-        switch ((a.M + 15) / 16) {
-        case 1: return launch_skinny_mt<FA, FB, 1>(a, s);
-        case 2: return launch_skinny_mt<FA, FB, 2>(a, s);
-        case 3: return launch_skinny_mt<FA, FB, 3>(a, s);
-        default: break;
-        }
-    }
-    return launch_skinny_mt<FA, FB, 4>(a, s);
-}
-
-template <int FA, int FB, int MT>
-hipError_t launch_stream_mt(const mxg::GemmArgs &a, hipStream_t s)
-{
-    const dim3 grid(a.tiles_n * a.splits), block(mxg::stream::threads_for<MT>());
-    if (a.scale_dword)
-        hipLaunchKernelGGL((mxg::stream::kernel<FA, FB, true, MT>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((mxg::stream::kernel<FA, FB, false, MT>), grid, block, 0, s, a);
-    return hipGetLastError();
-}
-
-template <int FA, int FB>
-hipError_t launch_stream(const mxg::GemmArgs &a, hipStream_t s)
-{
-    switch ((a.M + 15) / 16) {
-    case 1: return launch_stream_mt<FA, FB, 1>(a, s);
-    case 2: return launch_stream_mt<FA, FB, 2>(a, s);
-    case 3: return launch_stream_mt<FA, FB, 3>(a, s);
-    default: return launch_stream_mt<FA, FB, 4>(a, s);
-    }
 }
 
 __global__ void zero_words(uint32_t *p, int n)
@@ -213,37 +114,14 @@ int choose_splits_large(int forced, int tiles, int units, int unit_stages, size_
     return std::max(s, 1);
 }
 
-template <bool NATIVE>
-hipError_t dispatch(bool skinny, int f, const mxg::GemmArgs &a, hipStream_t s)
+hipError_t dispatch(bool native, bool skinny, int f, const mxg::GemmArgs &a, hipStream_t s)
 {
-    if (skinny && !NATIVE) {
-        switch (f) {
-        case 0: return launch_stream<0, 0>(a, s);
-        case 1: return launch_stream<0, 1>(a, s);
-        case 2: return launch_stream<1, 0>(a, s);
-        default: return launch_stream<1, 1>(a, s);
-        }
+    if (skinny) {
+        if (!native) return mxg::launch_stream_exact(f, a, s);
+        return f == 4 ? mxg::launch_skinny_e2m1(a, s) : mxg::launch_skinny_native(f, a, s);
     }
-    if constexpr (NATIVE) {
-        if (skinny) {
-            switch (f) {
-            case 0: return launch_skinny<0, 0>(a, s);
-            case 1: return launch_skinny<0, 1>(a, s);
-            case 2: return launch_skinny<1, 0>(a, s);
-            case 4: return launch_skinny<4, 4>(a, s);  // e2m1 x e2m1
-            default: return launch_skinny<1, 1>(a, s);
-            }
-        }
-    }
-    if constexpr (NATIVE) {
-        if (f == 4) return launch_large<4, 4, true>(a, s);  // e2m1 x e2m1
-    }
-    switch (f) {
-    case 0: return launch_large<0, 0, NATIVE>(a, s);
-    case 1: return launch_large<0, 1, NATIVE>(a, s);
-    case 2: return launch_large<1, 0, NATIVE>(a, s);
-    default: return launch_large<1, 1, NATIVE>(a, s);
-    }
+    if (f == 4) return mxg::launch_large_e2m1(a, s);  // e2m1 x e2m1 (always native)
+    return native ? mxg::launch_large_native(f, a, s) : mxg::launch_large_exact(f, a, s);
 }
 
 } // namespace
@@ -450,8 +328,7 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
         }
     }
     const int f = fp4 ? 4 : fmtA * 2 + fmtB;
-    const hipError_t e = native ? dispatch<true>(skinny, f, a, stream)
-                                : dispatch<false>(skinny, f, a, stream);
+    const hipError_t e = dispatch(native, skinny, f, a, stream);
     return e == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
 }
 
@@ -495,15 +372,7 @@ int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K
     const dim3 grid((unsigned)((a.n + per_block - 1) / per_block));
     const dim3 block(mxg::quant::THREADS);
     const int sel = fmt * 2 + (x_dtype == MXGEMM_X_BF16 ? 1 : 0);
-    switch (sel) {
-    case 0: hipLaunchKernelGGL((mxg::quant::kernel<0, 0>), grid, block, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((mxg::quant::kernel<0, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((mxg::quant::kernel<1, 0>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((mxg::quant::kernel<1, 1>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((mxg::quant::kernel<4, 0>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((mxg::quant::kernel<4, 1>), grid, block, 0, stream, a); break;
-    }
-    return hipGetLastError() == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
+    return mxg::launch_quant(sel, a, grid, block, stream) == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
 }
 
 } // extern "C"
