@@ -151,7 +151,7 @@ int mxgemm_set_variant(mxgemm_t h, int variant);
 /* Attach a caller-owned device buffer of at least MXGEMM_WORKSPACE_BYTES
  * (256-byte aligned) to the handle, or detach it with ws = NULL.  With a
  * workspace attached, calls that leave most of the 256 CUs idle split K
- * over several workgroups: exact and e2m1 small-M calls (M <= 64) whose N
+ * over several workgroups: small-M calls (M <= 64, every variant) whose N
  * gives at most 128 column tiles of 112, and M > 64 calls with at most 128 output
  * tiles of 256 x 256 (as many splits as the workspace holds partials for,
  * `bytes` counting; MXGEMM_WORKSPACE_BYTES_LARGE never limits them).  The TLX
@@ -170,9 +170,7 @@ int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream)
  * splits, S >= 2 forces S splits, reduced to at most the number of 128-byte
  * K stages (of 4-stage groups where the large kernel reads 16-byte scale
  * windows, i.e. K % 512 == 0), to 256 / output tiles, and to the partials
- * the workspace holds.  Applies to the exact small-M kernel, to e2m1 on the
- * small-M kernel and to both large-kernel variants; the fp8 native small-M
- * variant is never split.  A forced S >= 2
+ * the workspace holds.  Applies to every kernel.  A forced S >= 2
  * that survives this makes mxgemm_run return MXGEMM_ERR_WORKSPACE when no
  * workspace is attached.  MXGEMM_ERR_SHAPE for S < 0. */
 int mxgemm_set_splits(mxgemm_t h, int splits);

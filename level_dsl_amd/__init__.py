@@ -128,8 +128,7 @@ def mxgemm_set_workspace(h, ws, nbytes: int, stream=None) -> None:
 
 
 def mxgemm_set_splits(h, splits: int) -> None:
-    """K splits of later calls: 0 automatic, 1 never, S >= 2 forced (not the
-    fp8 native small-M variant)."""
+    """K splits of later calls: 0 automatic, 1 never, S >= 2 forced."""
     _check(load_library().mxgemm_set_splits(h, int(splits)), "mxgemm_set_splits")
 
 

@@ -31,15 +31,12 @@ hipError_t launch_skinny_s(const mxg::GemmArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-// split launches (e2m1 only) use their own instantiation, as for the
-// 256 x 256 kernel
+// split launches use their own instantiation, as for the 256 x 256 kernel
 template <int FA, int FB, int MT>
 hipError_t launch_skinny_mt(const mxg::GemmArgs &a, hipStream_t s)
 {
-    if constexpr (FA == 4) {
-        if (a.splits > 1) return launch_skinny_s<FA, FB, MT, true>(a, s);
-    }
-    return launch_skinny_s<FA, FB, MT, false>(a, s);
+    return a.splits > 1 ? launch_skinny_s<FA, FB, MT, true>(a, s)
+                        : launch_skinny_s<FA, FB, MT, false>(a, s);
 }
 
 // e2m1 runs only ceil(M/16) tiles of A; the fp8 native variant (an opt-in)

@@ -67,7 +67,7 @@ static_assert(MXGEMM_WORKSPACE_BYTES_LARGE ==
 // * S within one workgroup per CU, and S <= 8 (measured: more splits cost
 // more in the reduction than they gain in streaming).  The exact kernel
 // takes kMinStages = 8: with K a multiple of 1 KiB * S every split is a whole
-// number of its 8-stage rings.  The e2m1 kernel takes 4, one stage per wave
+// number of its 8-stage rings.  The scaled-MFMA kernel takes 4, one stage per wave
 // (measured at N = 3584, K = 8192: 12.0 us at 8 splits, 12.7 at 4, 23.8 unsplit).
 int choose_splits(int forced, int tiles_n, int nk, int kMinStages)
 {
@@ -295,18 +295,16 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     if (skinny) {
         a.tiles_m = 1;
         a.tiles_n = (int)((N + mxg::skinny::BN - 1) / mxg::skinny::BN);
-        if (!native || fp4) {  // the fp8 native small-M variant is not split
-            const int nk = native ? (a.K + mxg::skinny::BK - 1) / mxg::skinny::BK
-                                  : (int)((K + mxg::stream::BK - 1) / mxg::stream::BK);
-            a.splits = choose_splits(h->splits, a.tiles_n, nk, native ? 4 : 8);
-            if (a.splits > 1 && !h->ws) {
-                if (h->splits >= 2) return MXGEMM_ERR_WORKSPACE;
-                a.splits = 1;
-            }
-            if (a.splits > 1) {
-                a.cnt = (uint32_t *)h->ws;
-                a.ws = (float *)(h->ws + kCounterBytes);
-            }
+        const int nk = native ? (a.K + mxg::skinny::BK - 1) / mxg::skinny::BK
+                              : (int)((K + mxg::stream::BK - 1) / mxg::stream::BK);
+        a.splits = choose_splits(h->splits, a.tiles_n, nk, native ? 4 : 8);
+        if (a.splits > 1 && !h->ws) {
+            if (h->splits >= 2) return MXGEMM_ERR_WORKSPACE;
+            a.splits = 1;
+        }
+        if (a.splits > 1) {
+            a.cnt = (uint32_t *)h->ws;
+            a.ws = (float *)(h->ws + kCounterBytes);
         }
     } else {
         a.tiles_m = (int)((M + mxg::large::BM - 1) / mxg::large::BM);

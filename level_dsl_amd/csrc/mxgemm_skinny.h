@@ -30,7 +30,7 @@
 //   * at the end the four per-wave partial tiles are summed in a fixed order
 //     through LDS (deterministic), use_acc adds the old C, and C is written
 //     with coalesced 16-byte (fp32) or 8-byte (bf16) buffer stores;
-//   * e2m1 with few column tiles (N up to 128 tiles of 112) splits K over
+//   * with few column tiles (N up to 128 tiles of 112) K is split over
 //     several workgroups per tile, whose partial tiles are added in split
 //     order through a caller-owned workspace.
 #pragma once
@@ -86,13 +86,12 @@ constexpr int RING = 3;  // stage buffers per wave: RING - 1 loading, one multip
 // shift measured slower: it pushes the kernel into register spills.)
 // MT: 16-row tiles of A loaded and multiplied (M <= 16 MT), so a
 // decode-size M pays only for its own rows.
-// SPLIT (e2m1): workgroup tile + tiles_n * sp runs K split sp of p.splits and
-// the splits' partial tiles are summed in split order through the workspace.
+// SPLIT: workgroup tile + tiles_n * sp runs K split sp of p.splits and the
+// splits' partial tiles are summed in split order through the workspace.
 template <int FA, int FB, int SMODE, int MT, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
     static_assert(MT >= 1 && MT <= SUB_M, "M tiles");
-    static_assert(!SPLIT || FA == 4, "split K is built for e2m1 only");
     using Stage = mxg::skinny::Stage<MT>;
     constexpr bool FP4 = FA == 4;  // e2m1 x e2m1; K is the row pitch in bytes
     static_assert(FP4 == (FB == 4), "e2m1 pairs only with e2m1");

@@ -86,6 +86,40 @@ def test_split_k_forced(gemm_ws, M, N, K, S, fa, fb, acc, out):
         compare(got[rows, cols], oracle_points(p, rows, cols), out, f"S={S} sampled")
 
 
+NATIVE_SPLIT_CASES = [
+    # M, N, K, splits, fmtA, fmtB, use_acc, out
+    (64, 250, 8192, 8, 0, 0, False, mi.OUT_F32),     # LDS scale table
+    (17, 112, 4128, 5, 0, 1, True, mi.OUT_BF16),     # 33 stages, the last partial; byte scales
+    (1, 3, 1024, 8, 1, 0, False, mi.OUT_F32),        # 8 stages, two per split
+    (40, 3584, 8192, 0, 1, 1, False, mi.OUT_F32),    # automatic: 32 column tiles, 8 splits
+]
+
+
+@pytest.mark.parametrize("M,N,K,S,fa,fb,acc,out", NATIVE_SPLIT_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}_s{c[3]}" for c in NATIVE_SPLIT_CASES])
+def test_native_small_m_split_k(gemm_ws, M, N, K, S, fa, fb, acc, out):
+    """Split K on the small-M scaled-MFMA kernel with fp8 operands (the
+    native opt-in), held to the native variants' bound; the unsplit call
+    meets it too."""
+    p = mi.random_problem(M, N, K, seed=700 + S + M, fmtA=fa, fmtB=fb, out_dtype=out, use_acc=acc)
+    log(f"native small-M split-K S={S} M={M} N={N} K={K} fmt={fa}{fb} use_acc={acc} out={out}")
+    dev = to_dev(p)
+    gemm_ws.set_splits(S)
+    try:
+        got = run(gemm_ws, p, L.MXGEMM_VARIANT_SKINNY_NATIVE, guard=64, dev_inputs=dev)
+    finally:
+        gemm_ws.set_splits(0)
+        gemm_ws.set_variant(L.MXGEMM_VARIANT_AUTO)
+    extra = native_group_extra(p)
+    if M * N <= 64 * 500:
+        ref = oracle_full(p)
+        compare_native(got, ref, out, extra, f"native S={S}")
+    else:
+        rows, cols = mi.sample_points(M, N, 8192, seed=S + M, edge=64)
+        ref = oracle_points(p, rows, cols)
+        compare_native(got[rows, cols], ref, out, extra[rows, cols], f"native S={S} sampled")
+
+
 def test_split_k_bitwise_repeatable(gemm_ws):
     """The partials are added in split order whatever order the splits
     finish in: repeated calls give identical bits."""
