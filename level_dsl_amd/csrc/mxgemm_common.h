@@ -79,6 +79,12 @@ __device__ __forceinline__ v4i load16(rsrc_t r, uint32_t off)
 {
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// non-temporal (the NT cache-policy bit) 16-byte load, for data read once
+__device__ __forceinline__ v4i load16_nt(rsrc_t r, uint32_t off)
+{
+    constexpr int kNT = 2;
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
+}
 
 __device__ __forceinline__ uint32_t load4(rsrc_t r, uint32_t off)
 {

@@ -88,7 +88,10 @@ __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
 
     v4i x[CHUNKS];
 #pragma unroll
-    for (int j = 0; j < CHUNKS; ++j) x[j] = load16(rX, (uint32_t)(64 * j + lane) * 16);
+    // X is read once: non-temporal loads (measured 2% faster than plain ones
+    // on the 28672 x 8192 fp32 weight; the same hint on the small-M GEMMs'
+    // B stream measured no gain)
+    for (int j = 0; j < CHUNKS; ++j) x[j] = load16_nt(rX, (uint32_t)(64 * j + lane) * 16);
 
 #pragma unroll
     for (int j = 0; j < CHUNKS; ++j) {
