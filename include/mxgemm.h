@@ -144,7 +144,8 @@ int mxgemm_destroy(mxgemm_t h);
  * MXGEMM_ERR_VARIANT for M > 64.  e2m1 operands always run on the scaled
  * MFMA (exact for them): LARGE and LARGE_NATIVE on the 256 x 256 kernel,
  * SKINNY and SKINNY_NATIVE on the small-M kernel, AUTO on the small-M
- * kernel when M <= 64, else on the 256 x 256 kernel.  Not synchronised with mxgemm_run calls
+ * kernel when M <= 64, in two launches of it (rows 0..63, then the rest)
+ * when 64 < M <= 128, else on the 256 x 256 kernel.  Not synchronised with mxgemm_run calls
  * running on the same handle in other threads. */
 int mxgemm_set_variant(mxgemm_t h, int variant);
 

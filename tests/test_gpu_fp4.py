@@ -11,6 +11,7 @@ exact variants:
     small M, and both e2m1-capable variants;
   * a NaN scale at the start of the next row must not leak into a row
     whose last stage stops inside the scale dword (K = 1152);
+  * 64 < M <= 128 under AUTO (two launches of the small-M kernel);
   * split-K, forced and automatic, on both kernels (the small-M kernel's
     split in its three scale modes, bitwise repeatable, its arrival
     counters shared with the other kernels' splits);
@@ -208,14 +209,53 @@ def test_fp4_small_m_split_k_auto_sharded_decode(M):
     compare(plain[rows, cols], ref, p.out_dtype, "fp4 small-M unsplit")
 
 
-def test_fp4_split_k_auto_medium_m():
-    M, N, K = 128, 14336, 8192
+@pytest.mark.parametrize("M,N,K,acc,out", [
+    (65, 250, 2048, False, mi.OUT_F32),     # one row in the second launch
+    (96, 130, 4160, True, mi.OUT_BF16),     # ragged K, byte scale loads
+    (128, 336, 8192, False, mi.OUT_F32),    # two full halves
+])
+def test_fp4_two_half_launches(M, N, K, acc, out):
+    """e2m1 with 64 < M <= 128 under AUTO runs the small-M kernel on rows
+    0..63 and then on the rest: full outputs against the oracle, and the
+    guard bands around C intact."""
+    p = mi.random_problem(M, N, K, seed=880 + M, fmtA=E2M1, fmtB=E2M1, out_dtype=out, use_acc=acc)
+    g = L.Gemm()
+    try:
+        log(f"fp4 two half launches M={M} N={N} K={K} use_acc={acc} out={out}")
+        got = run(g, p, AUTO, guard=64)
+        compare(got, oracle_full(p), out, f"fp4 halves M={M}")
+    finally:
+        g.close()
+
+
+def test_fp4_two_half_launches_split_sharded():
+    """The same at one GPU's share of N (3584 columns) with a workspace: each
+    half splits K 8 ways; sampled outputs against the oracle."""
+    M, N, K = 112, 3584, 8192
+    p = mi.random_problem(M, N, K, seed=890, fmtA=E2M1, fmtB=E2M1)
+    g = L.Gemm()
+    g.enable_split_k()
+    try:
+        log(f"fp4 two half launches with split M={M} N={N} K={K}")
+        got = run(g, p, AUTO, guard=64)
+        rows, cols = mi.sample_points(M, N, 8192, seed=890, edge=64)
+        compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "fp4 halves split")
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("M,variant", [(128, LARGE), (192, AUTO)])
+def test_fp4_split_k_auto_medium_m(M, variant):
+    """The 256 x 256 kernel's automatic split at medium M (56 output tiles):
+    M = 128 with the variant forced (AUTO takes two small-M launches there),
+    M = 192 under AUTO."""
+    N, K = 14336, 8192
     p = mi.random_problem(M, N, K, seed=840, fmtA=E2M1, fmtB=E2M1)
     g = L.Gemm()
     g.enable_split_k()
     try:
-        log("fp4 auto split at M=128")
-        got = run(g, p, AUTO)
+        log(f"fp4 auto split at M={M}")
+        got = run(g, p, variant)
         rows, cols = mi.sample_points(M, N, 8192, seed=840, edge=64)
         compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "fp4 auto split")
     finally:
