@@ -255,19 +255,20 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
     if (dev != h->device) return MXGEMM_ERR_DEVICE;
 
-    // e2m1 with 64 < M <= 128 under AUTO: the small-M kernel on rows 0..63,
-    // then on the rest (B is streamed twice).  Measured faster than the
-    // 256 x 256 kernel at K = 8192 for M = 80, 96, 128 and N = 3584, 14336,
-    // 28672 (e.g. 27.6 vs 56.7 us at M = 80, N = 3584; 68.3 vs 78.8 us at
-    // M = 128, N = 28672); with more rows B's extra passes cost more.
-    if (fmtA == MXGEMM_FMT_E2M1 && h->variant == MXGEMM_VARIANT_AUTO && M > mxg::skinny::MAX_M &&
-        M <= 2 * mxg::skinny::MAX_M) {
+    // 64 < M <= 128 under AUTO: the small-M kernel (exact, or e2m1's) on
+    // rows 0..63, then on the rest, streaming B twice.  Measured faster than
+    // the 256 x 256 kernel at K = 8192 for M = 80, 96, 128 and N = 3584 to
+    // 28672 (e4m3: 34.1 vs 65.2 us at M = 80, N = 3584, 110.1 vs 114.6 us at
+    // M = 128, N = 28672; e2m1: 27.1 vs 57.8 and 69.6 vs 79.0 us); with more
+    // rows B's extra passes cost more than the 256 x 256 kernel.
+    if (h->variant == MXGEMM_VARIANT_AUTO && M > mxg::skinny::MAX_M && M <= 2 * mxg::skinny::MAX_M) {
         constexpr int64_t H = mxg::skinny::MAX_M;
+        const int64_t row_bytes = fmtA == MXGEMM_FMT_E2M1 ? K / 2 : K;
         const size_t esz = out_dtype == MXGEMM_OUT_F32 ? 4 : 2;
         const int r0 = mxgemm_run(h, A, A_scale, fmtA, B, B_scale, fmtB, C, H, N, K, use_acc,
                                   out_dtype, stream);
         if (r0 != MXGEMM_OK) return r0;
-        return mxgemm_run(h, (const uint8_t *)A + H * (K / 2), A_scale + H * (K / 32), fmtA, B,
+        return mxgemm_run(h, (const uint8_t *)A + H * row_bytes, A_scale + H * (K / 32), fmtA, B,
                           B_scale, fmtB, (uint8_t *)C + (size_t)H * N * esz, M - H, N, K, use_acc,
                           out_dtype, stream);
     }

@@ -10,6 +10,8 @@
   of different shapes in a row stay correct; the automatic choice at one
   GPU's share of the M=64 decode workload (N = 3584) against sampled
   oracle outputs; and the error paths.
+* 64 < M <= 128 under AUTO: two launches of the exact small-M kernel, on
+  full outputs and, with a workspace, split.
 * Split-K of the 256 x 256-tile kernel (M > 64): forced split counts over
   4-stage scale windows (K % 512 == 0) and over single stages (other K),
   both variants (the native one against its own bound), use_acc and bf16;
@@ -257,20 +259,25 @@ def test_large_split_k_forced(gemm_ws, M, N, K, S, fa, fb, acc, out):
 
 @pytest.mark.parametrize("M,N,K", [(128, 28672, 8192), (1024, 1024, 8192), (200, 3000, 4096)])
 def test_large_split_k_auto(gemm_ws, M, N, K):
-    """Automatic split at medium M (one row of tiles) and at few output
-    tiles, against sampled oracle outputs; the unsplit result agrees too."""
+    """Automatic split of the 256 x 256 kernel (variant LARGE: AUTO takes
+    two small-M launches at M = 128) at medium M (one row of tiles) and at
+    few output tiles, against sampled oracle outputs; the unsplit result
+    agrees too."""
     p = mi.random_problem(M, N, K, seed=720 + M)
     dev = to_dev(p)
     rows, cols = mi.sample_points(M, N, 8192, seed=720 + M, edge=64)
     ref = oracle_points(p, rows, cols)
     log(f"large auto split M={M} N={N} K={K}")
-    got = run(gemm_ws, p, L.MXGEMM_VARIANT_AUTO, guard=64, dev_inputs=dev)
-    compare(got[rows, cols], ref, p.out_dtype, "auto split")
-    again = run(gemm_ws, p, L.MXGEMM_VARIANT_AUTO, dev_inputs=dev)
-    assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "not repeatable"
+    try:
+        got = run(gemm_ws, p, LARGE, guard=64, dev_inputs=dev)
+        compare(got[rows, cols], ref, p.out_dtype, "auto split")
+        again = run(gemm_ws, p, LARGE, dev_inputs=dev)
+        assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "not repeatable"
+    finally:
+        gemm_ws.set_variant(L.MXGEMM_VARIANT_AUTO)
     g = L.Gemm()
     try:
-        plain = run(g, p, L.MXGEMM_VARIANT_AUTO, dev_inputs=dev)
+        plain = run(g, p, LARGE, dev_inputs=dev)
     finally:
         g.close()
     compare(plain[rows, cols], ref, p.out_dtype, "unsplit")
@@ -303,3 +310,27 @@ def test_large_split_k_small_workspace_is_respected():
         assert bool((buf[L.MXGEMM_WORKSPACE_BYTES:] == 0x5A).all()), "write past the workspace"
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("M,N,K,fa,fb,acc,out", [
+    (65, 250, 1056, 0, 0, False, mi.OUT_F32),     # one row in the second launch, ragged stages
+    (100, 130, 2080, 1, 0, True, mi.OUT_BF16),
+    (128, 336, 4096, 0, 1, False, mi.OUT_F32),    # two full halves
+])
+def test_two_half_launches_exact(gemm, M, N, K, fa, fb, acc, out):
+    """64 < M <= 128 under AUTO: the exact small-M kernel on rows 0..63, then
+    on the rest; full outputs against the oracle, guard bands intact."""
+    p = mi.random_problem(M, N, K, seed=740 + M, fmtA=fa, fmtB=fb, out_dtype=out, use_acc=acc)
+    log(f"two half launches M={M} N={N} K={K} fmt={fa}{fb} use_acc={acc} out={out}")
+    got = run(gemm, p, L.MXGEMM_VARIANT_AUTO, guard=64)
+    compare(got, oracle_full(p), out, f"halves M={M}")
+
+
+def test_two_half_launches_exact_split_sharded(gemm_ws):
+    """The same at N = 3584 with a workspace, so that each half splits K."""
+    M, N, K = 96, 3584, 8192
+    p = mi.random_problem(M, N, K, seed=750)
+    log(f"two half launches with split M={M} N={N} K={K}")
+    got = run(gemm_ws, p, L.MXGEMM_VARIANT_AUTO, guard=64)
+    rows, cols = mi.sample_points(M, N, 8192, seed=750, edge=64)
+    compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "halves split")
