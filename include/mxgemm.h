@@ -88,9 +88,9 @@ enum { MXGEMM_X_F32 = 0, MXGEMM_X_BF16 = 1 };
  * the window holds every product of a block, so the result meets the exact
  * variants' bound (see MXGEMM_FMT_E2M1). */
 enum {
-    MXGEMM_VARIANT_AUTO = 0,          /* exact; skinny for M <= 64, two skinny launches
-                                         (rows 0..63, then the rest) for M <= 128,
-                                         else large */
+    MXGEMM_VARIANT_AUTO = 0,          /* exact; skinny for M <= 64, one skinny launch
+                                         per 64 rows for M <= 128 (M <= 192 when N
+                                         gives at most 64 tiles of 112), else large */
     MXGEMM_VARIANT_LARGE = 1,         /* exact, 256x256 tiles (MFMA-bound shapes) */
     MXGEMM_VARIANT_SKINNY = 2,        /* exact, M <= 64, streams B once (HBM-bound) */
     MXGEMM_VARIANT_LARGE_NATIVE = 3,  /* native scaled-MFMA accumulation, 256x256 tiles */
@@ -146,8 +146,9 @@ int mxgemm_destroy(mxgemm_t h);
  * MXGEMM_ERR_VARIANT for M > 64.  e2m1 operands always run on the scaled
  * MFMA (exact for them): LARGE and LARGE_NATIVE on the 256 x 256 kernel,
  * SKINNY and SKINNY_NATIVE on the small-M kernel, AUTO on the small-M
- * kernel when M <= 64, in two launches of it (rows 0..63, then the rest)
- * when 64 < M <= 128 (as for e4m3 / e5m2), else on the 256 x 256 kernel.  Not synchronised with mxgemm_run calls
+ * kernel when M <= 64, in one launch of it per 64 rows when 64 < M <= 128
+ * or, with N <= 7168, M <= 192 (as for e4m3 / e5m2), else on the 256 x 256
+ * kernel.  Not synchronised with mxgemm_run calls
  * running on the same handle in other threads. */
 int mxgemm_set_variant(mxgemm_t h, int variant);
 

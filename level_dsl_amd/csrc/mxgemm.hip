@@ -255,22 +255,29 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
     if (dev != h->device) return MXGEMM_ERR_DEVICE;
 
-    // 64 < M <= 128 under AUTO: the small-M kernel (exact, or e2m1's) on
-    // rows 0..63, then on the rest, streaming B twice.  Measured faster than
-    // the 256 x 256 kernel at K = 8192 for M = 80, 96, 128 and N = 3584 to
-    // 28672 (e4m3: 34.1 vs 65.2 us at M = 80, N = 3584, 110.1 vs 114.6 us at
-    // M = 128, N = 28672; e2m1: 27.1 vs 57.8 and 69.6 vs 79.0 us); with more
-    // rows B's extra passes cost more than the 256 x 256 kernel.
-    if (h->variant == MXGEMM_VARIANT_AUTO && M > mxg::skinny::MAX_M && M <= 2 * mxg::skinny::MAX_M) {
+    // 64 < M <= 192 under AUTO: the small-M kernel (exact, or e2m1's) on
+    // rows 0..63, 64..127, ..., streaming B once per 64 rows, instead of the
+    // 256 x 256 kernel.  Measured at K = 8192: two launches are faster for
+    // M <= 128 at N = 3584 to 28672 (e4m3: 34.1 vs 65.2 us at M = 80,
+    // N = 3584, 110.1 vs 114.6 us at M = 128, N = 28672; e2m1: 27.1 vs 57.8
+    // and 69.6 vs 79.0 us); three are faster for M <= 192 only while N gives
+    // at most 64 column tiles (e4m3 M = 160, N = 3584: 57.0 vs 67.2 us; at
+    // N = 14336: 96.0 vs 78.9 us); four never were.
+    if (h->variant == MXGEMM_VARIANT_AUTO && M > mxg::skinny::MAX_M) {
         constexpr int64_t H = mxg::skinny::MAX_M;
-        const int64_t row_bytes = fmtA == MXGEMM_FMT_E2M1 ? K / 2 : K;
-        const size_t esz = out_dtype == MXGEMM_OUT_F32 ? 4 : 2;
-        const int r0 = mxgemm_run(h, A, A_scale, fmtA, B, B_scale, fmtB, C, H, N, K, use_acc,
-                                  out_dtype, stream);
-        if (r0 != MXGEMM_OK) return r0;
-        return mxgemm_run(h, (const uint8_t *)A + H * row_bytes, A_scale + H * (K / 32), fmtA, B,
-                          B_scale, fmtB, (uint8_t *)C + (size_t)H * N * esz, M - H, N, K, use_acc,
-                          out_dtype, stream);
+        const int64_t tiles_n = (N + mxg::skinny::BN - 1) / mxg::skinny::BN;
+        if (M <= 2 * H || (M <= 3 * H && tiles_n <= 64)) {
+            const int64_t row_bytes = fmtA == MXGEMM_FMT_E2M1 ? K / 2 : K;
+            const size_t esz = out_dtype == MXGEMM_OUT_F32 ? 4 : 2;
+            for (int64_t r = 0; r < M; r += H) {
+                const int rc_r = mxgemm_run(h, (const uint8_t *)A + r * row_bytes,
+                                            A_scale + r * (K / 32), fmtA, B, B_scale, fmtB,
+                                            (uint8_t *)C + (size_t)r * N * esz, std::min(H, M - r), N,
+                                            K, use_acc, out_dtype, stream);
+                if (rc_r != MXGEMM_OK) return rc_r;
+            }
+            return MXGEMM_OK;
+        }
     }
 
     mxg::GemmArgs a;

@@ -213,6 +213,7 @@ def test_fp4_small_m_split_k_auto_sharded_decode(M):
     (65, 250, 2048, False, mi.OUT_F32),     # one row in the second launch
     (96, 130, 4160, True, mi.OUT_BF16),     # ragged K, byte scale loads
     (128, 336, 8192, False, mi.OUT_F32),    # two full halves
+    (192, 200, 4096, True, mi.OUT_F32),     # three launches
 ])
 def test_fp4_two_half_launches(M, N, K, acc, out):
     """e2m1 with 64 < M <= 128 under AUTO runs the small-M kernel on rows

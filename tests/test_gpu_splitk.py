@@ -316,10 +316,13 @@ def test_large_split_k_small_workspace_is_respected():
     (65, 250, 1056, 0, 0, False, mi.OUT_F32),     # one row in the second launch, ragged stages
     (100, 130, 2080, 1, 0, True, mi.OUT_BF16),
     (128, 336, 4096, 0, 1, False, mi.OUT_F32),    # two full halves
+    (150, 250, 2048, 1, 1, True, mi.OUT_F32),     # three launches (3 column tiles)
+    (192, 7168, 512, 0, 0, False, mi.OUT_BF16),   # three launches at 64 column tiles
 ])
 def test_two_half_launches_exact(gemm, M, N, K, fa, fb, acc, out):
-    """64 < M <= 128 under AUTO: the exact small-M kernel on rows 0..63, then
-    on the rest; full outputs against the oracle, guard bands intact."""
+    """64 < M <= 128 (M <= 192 with at most 64 column tiles) under AUTO: the
+    exact small-M kernel once per 64 rows; full outputs against the oracle,
+    guard bands intact."""
     p = mi.random_problem(M, N, K, seed=740 + M, fmtA=fa, fmtB=fb, out_dtype=out, use_acc=acc)
     log(f"two half launches M={M} N={N} K={K} fmt={fa}{fb} use_acc={acc} out={out}")
     got = run(gemm, p, L.MXGEMM_VARIANT_AUTO, guard=64)
