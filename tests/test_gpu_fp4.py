@@ -16,6 +16,8 @@ exact variants:
     split in its three scale modes, bitwise repeatable, its arrival
     counters shared with the other kernels' splits);
   * the 8192 x 8192 x 8192 benchmark shape on sampled outputs;
+  * the limits of the C ABI: the largest K and N, many row tiles, and the
+    row-chunked small-M launches at the largest N;
   * the error paths (e2m1 with another format, a small-M variant).
 """
 import numpy as np
@@ -307,3 +309,38 @@ def test_fp4_error_paths(gemm):
     assert bool(torch.isnan(qbuf).all()), "a rejected call wrote C"
     torch.cuda.synchronize()
     assert bool(torch.isnan(buf).all()), "a rejected call wrote C"
+
+
+E2M1_EDGE_CASES = [
+    # M, N, K, out, variants
+    (2, 3, 1 << 21, mi.OUT_F32, (AUTO, LARGE)),          # the largest K: 1 MiB packed rows
+    (3, 1 << 20, 64, mi.OUT_BF16, (AUTO, LARGE)),        # the largest N (9363 small-M workgroups)
+    (70000, 40, 64, mi.OUT_F32, (AUTO,)),                # many row tiles, ragged last tile
+]
+
+
+@pytest.mark.parametrize("case", E2M1_EDGE_CASES, ids=lambda c: "x".join(map(str, c[:3])))
+def test_fp4_edge_full(gemm, case):
+    """e2m1 at the limits of the C ABI, full outputs against the oracle on
+    every variant listed, with the guard bands around C intact."""
+    M, N, K, out, variants = case
+    p = mi.random_problem(M, N, K, seed=(M * 7 + N * 3 + K) % 100003, fmtA=E2M1, fmtB=E2M1,
+                          out_dtype=out)
+    ref = oracle_full(p)
+    dev = to_dev(p)
+    for v in variants:
+        log(f"fp4 edge {M}x{N}x{K} variant={v}")
+        got = run(gemm, p, v, guard=64, dev_inputs=dev)
+        compare(got, ref, out, f"fp4 edge {M}x{N}x{K} variant {v}")
+    gemm.set_variant(AUTO)
+
+
+def test_fp4_two_launches_largest_n_sampled(gemm):
+    """AUTO's row-chunked small-M launches at the largest N (M = 100: rows
+    0..63, then 64..99), sampled outputs against the oracle."""
+    M, N, K = 100, 1 << 20, 64
+    p = mi.random_problem(M, N, K, seed=895, fmtA=E2M1, fmtB=E2M1)
+    log(f"fp4 two launches at the largest N: {M}x{N}x{K}")
+    got = run(gemm, p, AUTO, guard=64)
+    rows, cols = mi.sample_points(M, N, 16384, seed=895, edge=64)
+    compare(got[rows, cols], oracle_points(p, rows, cols), p.out_dtype, "fp4 largest N halves")
