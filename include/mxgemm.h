@@ -18,7 +18,7 @@
  * Encodings (the pages give the names only): e4m3 is OCP E4M3 "FN"
  * (bias 7, no infinities, S.1111.111 = NaN, max 448); e5m2 is OCP E5M2
  * (bias 15, IEEE inf/NaN, max 57344); a scale byte s is E8M0, 2^(s-127),
- * with 255 = NaN.
+ * with 255 = NaN (every product of its block is NaN, also for code 0).
  *
  * Memory layout (all dense, no leading-dimension arguments):
  *   A        M x K codes, row-major (byte A[m*K + k]); e2m1: M x K/2 bytes.
@@ -73,16 +73,30 @@ enum { MXGEMM_X_F32 = 0, MXGEMM_X_BF16 = 1 };
 /* kernel variants (mxgemm_set_variant).
  *
  * Exact variants (AUTO, LARGE, SKINNY) decode every code with its block
- * scale to bf16 (exact for scaled magnitudes inside the bf16 normal range)
- * and multiply on the bf16 MFMA, whose sums keep fp32 precision: results
- * agree with the exact sum to |err| <= 1e-5 * sum_k |a_k b_k|.
+ * scale to bf16 and multiply on the bf16 MFMA, which forms exact products
+ * and rounds once to fp32 per instruction (16 or 32 K).  The decode is
+ * exact for every code when the scale byte lies in the format's window,
+ * 10..246 for e4m3 and 17..239 for e5m2; a wave that meets any other byte
+ * (0, 255 and the bytes near them are legal) recomputes its outputs on a
+ * slower fallback that decodes with the byte clamped into the window and
+ * scales each 32-K block's partial sum by the rest (exactly, by a power of
+ * two), so every scale byte 0..255 gives the defined result.  Error bound:
+ * |err| <= (K/16 + S) * 2^-24 * sum_k |a_k b_k| (S = K splits, 1 without),
+ * which is within 1e-5 * sum|ab| for K <= 2684; at larger K the rounding
+ * errors of random-sign data cancel, and the measured error stays far
+ * inside 1e-5 * sum|ab| (about 6e-7 at K = 8192, 1e-6 at K = 16384).
+ * Outputs whose sum|ab| exceeds the fp32 range may be +-inf or NaN (an fp32
+ * partial sum overflows), and outputs below the fp32 normal range
+ * (2^-126) may lose subnormal bits.
  *
  * Native variants feed the codes and scales to the gfx950 scaled MFMA
- * (v_mfma_scale_f32_*_f8f6f4) at twice the bf16 rate.  That instruction
- * sums each aligned group of 8 products in a fixed-point window reaching
- * 13 bits below the group's largest product and truncates the rest, so its
- * error is bounded only by about 2^-10 of each group's largest |product|
- * (measured: up to ~3e-5 * sum|ab| on N(0,1) data).
+ * (v_mfma_scale_f32_*_f8f6f4) at twice the bf16 rate, for every scale byte.
+ * That instruction sums each aligned group of 8 products in a fixed-point
+ * window reaching 13 bits below the group's largest product and drops the
+ * rest (toward zero; measured), so its error is bounded only by about
+ * 2^-10 of each group's largest |product|: a product 2^-14 below the
+ * largest of its group is lost outright (6e-5 * sum|ab|), and on N(0,1)
+ * data at K = 256 about 1% of outputs miss 1e-5 * sum|ab|.
  *
  * e2m1 x e2m1 operands run on the scaled MFMA under every variant: for them
  * the window holds every product of a block, so the result meets the exact
@@ -234,6 +248,19 @@ int mxgemm_validate_quantize(const void *X, int x_dtype, int64_t R, int64_t K, i
  * allocated.  On an error nothing is launched. */
 int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K, int fmt,
                     uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+/* Streaming copy of `bytes` bytes from src to dst with raw buffer loads and
+ * stores (the buffer_load / buffer_store example of the TLX global-memory
+ * page), asynchronously on `stream`; both are device pointers on the
+ * handle's device, owned by the caller.  It computes nothing: its rate is
+ * the measured "achievable HBM" bandwidth that the memory-bound kernels are
+ * compared with.  mxgemm_validate_copy is its pure host check: pointers
+ * non-NULL, both 16-byte aligned, 16 <= bytes <= MXGEMM_MAX_COPY_BYTES with
+ * bytes % 16 == 0, and the two ranges disjoint (MXGEMM_ERR_ALIAS).  On an
+ * error nothing is launched. */
+#define MXGEMM_MAX_COPY_BYTES ((uint64_t)1 << 40)
+int mxgemm_validate_copy(const void *dst, const void *src, uint64_t bytes);
+int mxgemm_copy(mxgemm_t h, void *dst, const void *src, uint64_t bytes, hipStream_t stream);
 
 /* Static text for a status code ("unknown status" for others). */
 const char *mxgemm_status_string(int code);

@@ -55,6 +55,8 @@ SIGNATURES = {
                           _i32, _vp]),
     "mxgemm_validate_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _u8p, _u8p]),
     "mxgemm_quantize": (_i32, [_vp, _vp, _i32, _i64, _i64, _i32, _u8p, _u8p, _vp]),
+    "mxgemm_validate_copy": (_i32, [_vp, _vp, ctypes.c_uint64]),
+    "mxgemm_copy": (_i32, [_vp, _vp, _vp, ctypes.c_uint64, _vp]),
     "mxgemm_status_string": (ctypes.c_char_p, [_i32]),
 }
 
@@ -178,6 +180,18 @@ def mxgemm_quantize(h, X, x_dtype, R, K, fmt, codes, scales, stream=None) -> Non
     _check(load_library().mxgemm_quantize(
         h, _ptr(X), int(x_dtype), int(R), int(K), int(fmt), _ptr(codes), _ptr(scales), stream),
         "mxgemm_quantize")
+
+
+def mxgemm_validate_copy(dst, src, nbytes) -> int:
+    """Returns the status code (0 = valid); pure host check."""
+    return load_library().mxgemm_validate_copy(_ptr(dst), _ptr(src), int(nbytes))
+
+
+def mxgemm_copy(h, dst, src, nbytes, stream=None) -> None:
+    """Streaming copy of nbytes from src to dst on `stream` (default: torch's
+    current stream); the achievable-bandwidth reference of the benchmark."""
+    _check(load_library().mxgemm_copy(h, _ptr(dst), _ptr(src), int(nbytes), _stream(stream)),
+           "mxgemm_copy")
 
 
 class Gemm:

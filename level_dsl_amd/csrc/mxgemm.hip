@@ -398,4 +398,26 @@ int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K
     return mxg::launch_quant(sel, a, grid, block, stream) == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
 }
 
+int mxgemm_validate_copy(const void *dst, const void *src, uint64_t bytes)
+{
+    if (!dst || !src) return MXGEMM_ERR_NULL;
+    if (bytes < 16 || bytes > MXGEMM_MAX_COPY_BYTES || (bytes & 15u)) return MXGEMM_ERR_SHAPE;
+    if (((uintptr_t)dst | (uintptr_t)src) & 15u) return MXGEMM_ERR_ALIGN;
+    if (overlaps(dst, bytes, src, bytes)) return MXGEMM_ERR_ALIAS;
+    return MXGEMM_OK;
+}
+
+int mxgemm_copy(mxgemm_t h, void *dst, const void *src, uint64_t bytes, hipStream_t stream)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    const int rc = mxgemm_validate_copy(dst, src, bytes);
+    if (rc != MXGEMM_OK) return rc;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
+    if (dev != h->device) return MXGEMM_ERR_DEVICE;
+    return mxg::launch_copy((const uint8_t *)src, (uint8_t *)dst, bytes, stream) == hipSuccess
+               ? MXGEMM_OK
+               : MXGEMM_ERR_HIP;
+}
+
 } // extern "C"

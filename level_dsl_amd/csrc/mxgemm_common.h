@@ -223,12 +223,83 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s)
 }
 
 // Byte `b` of the scale dword d as the fp32 2^(s-127), valid for s in
-// 1..254 (one shift): the exact variants' bf16 decode is only exact for
-// scale bytes well inside that range, so the endpoints need no fix-up there.
+// 1..254 (one shift).  The fast loops of the exact kernels only use it for
+// bytes inside the format's scale window (below); a wave that meets any
+// other byte recomputes its outputs on the fallback path, which decodes with
+// clamped scales.
 template <int b>
 __device__ __forceinline__ float scale_f32(uint32_t d)
 {
     return __builtin_bit_cast(float, ((d >> (8 * b)) & 0xffu) << 23);
+}
+
+// ---- scale windows of the exact (decode-to-bf16) path ----------------------
+// A code of format F (0 e4m3, 1 e5m2) times 2^(s-127) is a bf16 normal
+// number (or zero, or the code's own inf/NaN) for every code exactly when the
+// scale byte s lies in [scale_lo<F>, scale_hi<F>]: the smallest nonzero
+// magnitude (e4m3 2^-9, e5m2 2^-16) must reach 2^-126 and the largest (448 =
+// 1.75 * 2^8, 57344 = 1.75 * 2^15) must stay below 2^128.  Inside the window
+// the decode is exact and the bf16 MFMA forms exact products.
+template <int F>
+__device__ __forceinline__ constexpr int scale_lo() { return F == 0 ? 10 : 17; }
+template <int F>
+__device__ __forceinline__ constexpr int scale_hi() { return F == 0 ? 246 : 239; }
+
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+// Running check of the scale bytes one lane has seen against a window
+// [lo, hi], in one register: bytes 0, 2 and bytes 1, 3 of each dword are
+// spread into two packed-u16 pairs (v_perm_b32), lo is subtracted with u16
+// wrap-around (a byte below lo becomes 65536 - lo + byte, far above any
+// window width), and the packed maximum is kept.  A byte lies outside the
+// window exactly when its value exceeds hi - lo.  lo2 is lo in each u16 half.
+struct ScaleRange {
+    v2u16 mx;
+    __device__ __forceinline__ void init() { mx = v2u16{0, 0}; }
+    __device__ __forceinline__ void add(uint32_t d, v2u16 lo2)
+    {
+        // selector bytes: 0x0c is the constant 0x00, 0..3 are the bytes of d
+        const v2u16 e = __builtin_bit_cast(v2u16, __builtin_amdgcn_perm(0u, d, 0x0c020c00u));
+        const v2u16 o = __builtin_bit_cast(v2u16, __builtin_amdgcn_perm(0u, d, 0x0c030c01u));
+        mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(e - lo2, o - lo2));
+    }
+    // width = hi - lo of the window the bytes were checked against
+    __device__ __forceinline__ bool outside(int width) const
+    {
+        const int m = mx[0] > mx[1] ? mx[0] : mx[1];
+        return m > width;
+    }
+};
+
+// The window of format F as (lo in each u16 half, hi - lo).
+template <int F>
+__device__ __forceinline__ constexpr v2u16 window_lo2()
+{
+    return v2u16{(unsigned short)scale_lo<F>(), (unsigned short)scale_lo<F>()};
+}
+template <int F>
+__device__ __forceinline__ constexpr int window_width() { return scale_hi<F>() - scale_lo<F>(); }
+
+// Bytes of dword d at or past byte `valid` (0..4) replaced by 127, a byte
+// inside every window (scale bytes past the end of a row are not data).
+__device__ __forceinline__ uint32_t mask_scale_tail(uint32_t d, int valid)
+{
+    const uint32_t keep = valid >= 4 ? 0xffffffffu : ((1u << (8 * valid)) - 1u);
+    return (d & keep) | (0x7f7f7f7fu & ~keep);
+}
+
+// The fallback's decode scale and remainder for scale byte s of format F: the
+// operand is decoded with the clamped byte c (exact, inside the window), and
+// the block's partial sum is later multiplied by 2^(s - c) (ldexp), which is
+// exact unless the true contribution leaves the fp32 range.  Byte 255 (NaN)
+// is returned through `nan` (NaN, else 0), to be added to the result.
+template <int F>
+__device__ __forceinline__ void clamp_scale(uint32_t s, float &dec, int &rem, float &nan)
+{
+    const int c = (int)s < scale_lo<F>() ? scale_lo<F>() : ((int)s > scale_hi<F>() ? scale_hi<F>() : (int)s);
+    dec = __builtin_bit_cast(float, (uint32_t)c << 23);
+    rem = (int)s - c;
+    nan = s == 255u ? __builtin_nanf("") : 0.0f;
 }
 
 // Two fp8 codes (bytes 2*hi, 2*hi+1 of w) -> two bf16 equal to the codes' values
@@ -256,6 +327,15 @@ __device__ __forceinline__ void decode16(v4i x, float scale, v8bf &lo, v8bf &hi)
     const v2bf d0 = cvt2<F, false>((uint32_t)x[3], scale), d1 = cvt2<F, true>((uint32_t)x[3], scale);
     lo = v8bf{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
     hi = v8bf{c0[0], c0[1], c1[0], c1[1], d0[0], d0[1], d1[0], d1[1]};
+}
+
+// 8 fp8 codes (bytes 0..7 of x) scaled -> 8 bf16, one MFMA operand.
+template <int F>
+__device__ __forceinline__ v8bf decode8(v2i x, float scale)
+{
+    const v2bf a0 = cvt2<F, false>((uint32_t)x[0], scale), a1 = cvt2<F, true>((uint32_t)x[0], scale);
+    const v2bf b0 = cvt2<F, false>((uint32_t)x[1], scale), b1 = cvt2<F, true>((uint32_t)x[1], scale);
+    return v8bf{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
 }
 
 // bf16 MFMAs: products of bf16 operands are exact and, as measured on the

@@ -187,22 +187,24 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // wn*128 + 32j + lrow.  SCALE16: 16 bytes (4 stages) per row and load;
     // otherwise one dword (or four bytes) per row and stage.
     const uint32_t sra = (uint32_t)(wm * WAVE_M + lrow), srb = (uint32_t)(wn * WAVE_N + lrow);
+    auto srow_a = [&](int i) MXG_INLINE { return sra + 32 * i; };
+    auto srow_b = [&](int j) MXG_INLINE { return srb + 32 * j; };
     auto scale16 = [&](int kt, v4i *xa, v4i *xb) MXG_INLINE {  // window starting at local stage kt
         const int kb0 = (ks0 + kt) * (BK / 32);
         const bool in = kb0 < KB;
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) xa[i] = load16(rAs, in ? (sra + 32 * i) * KB + kb0 : kOob);
+        for (int i = 0; i < SUB_M; ++i) xa[i] = load16(rAs, in ? srow_a(i) * KB + kb0 : kOob);
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) xb[j] = load16(rBs, in ? (srb + 32 * j) * KB + kb0 : kOob);
+        for (int j = 0; j < SUB_N; ++j) xb[j] = load16(rBs, in ? srow_b(j) * KB + kb0 : kOob);
     };
     // local stage kt: its first 4 scale bytes per row into xa/xb, and for
     // e2m1 the next 4 into xa2/xb2 (a dword past the row's end reads zero)
     auto scale4 = [&](int kt, uint32_t *xa, uint32_t *xb, uint32_t *xa2, uint32_t *xb2) MXG_INLINE {
         const int kb0 = (ks0 + kt) * SPS;
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) xa[i] = load_scale4(rAs, sra + 32 * i, KB, kb0, p.scale_dword);
+        for (int i = 0; i < SUB_M; ++i) xa[i] = load_scale4(rAs, srow_a(i), KB, kb0, p.scale_dword);
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) xb[j] = load_scale4(rBs, srb + 32 * j, KB, kb0, p.scale_dword);
+        for (int j = 0; j < SUB_N; ++j) xb[j] = load_scale4(rBs, srow_b(j), KB, kb0, p.scale_dword);
         if constexpr (FP4) {
             const int kb1 = kb0 + 4;
             const bool in = kb1 < KB;
@@ -214,6 +216,33 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                 xb2[j] = in ? load_scale4(rBs, srb + 32 * j, KB, kb1, p.scale_dword) : 0u;
         }
     };
+    // Exact mode: every scale byte the fast loop decodes with passes
+    // through this check; a byte outside its format's window (where the
+    // bf16 decode would round, overflow or misread byte 0 / 255) sends the
+    // wave to the fallback after the loop.  The two lane halves hold the same
+    // rows' scales, so the lower half checks the A rows and the upper half
+    // the B rows.  Rows past the tile's end and bytes past the end of K are
+    // not data: they read as zero and are replaced by an in-window byte.
+    ScaleRange rg;
+    rg.init();
+    const bool chk_b = khalf != 0;
+    const v2u16 chk_lo2 = chk_b ? window_lo2<FB == 1 ? 1 : 0>() : window_lo2<FA == 1 ? 1 : 0>();
+    bool live[SUB_M];
+    static_assert(SUB_M == SUB_N, "one check per fragment row of A or B");
+#pragma unroll
+    for (int i = 0; i < SUB_M; ++i) live[i] = chk_b ? (int)srow_b(i) < rows_b : (int)srow_a(i) < rows_a;
+    auto track4 = [&](int kt, const uint32_t *xa, const uint32_t *xb) MXG_INLINE {  // local stage kt
+        if constexpr (!NATIVE) {
+            const int valid = KB - (ks0 + kt) * (BK / 32);
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i) {
+                uint32_t d = chk_b ? xb[i] : xa[i];
+                if constexpr (!SCALE16) d = mask_scale_tail(d, valid);  // SCALE16: KB % 16 == 0
+                rg.add(live[i] ? d : 0x7f7f7f7fu, chk_lo2);
+            }
+        }
+    };
+
     // native mode: the upper lane half supplies the odd K blocks (fp8: of
     // each 64-element MFMA step; e2m1: each lane half holds one block)
     auto native_shift = [&](uint32_t *xa, uint32_t *xb) MXG_INLINE {
@@ -449,11 +478,13 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                     for (int i = 0; i < SUB_M; ++i) csa[i] = (uint32_t)wa[i][nx];
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) csb[j] = (uint32_t)wb[j][nx];
+                    track4(kt + 1, csa, csb);
                 } else {
 #pragma unroll
                     for (int i = 0; i < SUB_M; ++i) csa[i] = sa1[i];
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) csb[j] = sb1[j];
+                    track4(kt + 1, csa, csb);
                     if constexpr (FP4) {
 #pragma unroll
                         for (int i = 0; i < SUB_M; ++i) csa2[i] = sa2_1[i];
@@ -490,11 +521,13 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         for (int i = 0; i < SUB_M; ++i) csa[i] = (uint32_t)wa[i][0];
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) csb[j] = (uint32_t)wb[j][0];
+        track4(0, csa, csb);
     } else {
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) csa[i] = sa1[i];
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) csb[j] = sb1[j];
+        track4(0, csa, csb);
         if constexpr (FP4) {
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) csa2[i] = sa2_1[i];
@@ -537,6 +570,55 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     };
     constexpr int GROUPS = SUB_M * SUB_N * 4;  // 16-byte groups per lane
 
+    // ---- fallback for scale bytes outside the window (exact mode) ---------
+    // A wave whose A rows or B rows carry a scale byte outside its format's
+    // window (over its K range) recomputes its 128 x 128 outputs here, one
+    // 32 x 32 sub-tile at a time, straight from global memory: each 32-K
+    // block is decoded with clamped scale bytes (exact), its two bf16 MFMAs
+    // are summed into a fresh block partial t, and t * 2^(remainder of the
+    // A row + remainder of the B row) is added to the sub-tile's sum.  Byte
+    // 255 makes its row's (column's) outputs NaN, as in the definition.
+    bool slow = false;
+    if constexpr (!NATIVE) {
+        constexpr int wa = window_width<FA == 1 ? 1 : 0>(), wb = window_width<FB == 1 ? 1 : 0>();
+        slow = __builtin_amdgcn_ballot_w64(rg.outside(chk_b ? wb : wa)) != 0;
+    }
+    auto slow_tile = [&](int i, int j) MXG_INLINE {
+        v16f s = {};
+        if constexpr (!NATIVE) {
+            const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+            const int lr = ln & 31, kh = ln >> 5;
+            const uint32_t ar = (uint32_t)(wm * WAVE_M + 32 * i + lr);
+            const uint32_t br = (uint32_t)(wn * WAVE_N + 32 * j + lr);
+            const int kb0 = ks0 * (BK / 32), kb1 = min(KB, (ks0 + nk) * (BK / 32));
+            constexpr int kNanCode = 4096;  // a B remainder that marks scale byte 255
+            for (int kb = kb0; kb < kb1; ++kb) {
+                const v4i xa = load16(rA, ar * K + 32 * kb + 16 * kh);  // rows past the tile read 0
+                const v4i xb = load16(rB, br * K + 32 * kb + 16 * kh);
+                const uint32_t ba = load1(rAs, ar * KB + kb), bb = load1(rBs, br * KB + kb);
+                float da, db, na, nb;
+                int ea, eb;
+                clamp_scale<FA>(ba, da, ea, na);
+                clamp_scale<FB>(bb, db, eb, nb);
+                v8bf a0, a1, b0, b1;
+                decode16<FA>(xa, da, a0, a1);
+                decode16<FB>(xb, db, b0, b1);
+                v16f t = mfma_bf16_32(b0, a0, v16f{});
+                t = mfma_bf16_32(b1, a1, t);
+                // register r holds output row n = 8 (r/4) + 4 kh + r%4 of
+                // the sub-tile, whose B remainder sits in lane n
+                const int code = bb == 255u ? kNanCode : eb;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c = __shfl(code, 8 * (r / 4) + 4 * kh + (r % 4), 64);
+                    const float nbr = c == kNanCode ? __builtin_nanf("") : 0.0f;
+                    s[r] += __builtin_amdgcn_ldexpf(t[r], ea + (c == kNanCode ? 0 : c)) + (na + nbr);
+                }
+            }
+        }
+        return s;
+    };
+
     if constexpr (SPLIT) {
         // Split K (p.splits > 1): every split stores its wave's fp32 partial
         // (the 64 groups of each lane, 1 KiB per store instruction) with
@@ -556,14 +638,24 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         const rsrc_t rW = make_rsrc(p.ws, (uint32_t)p.splits * ntiles * WAVES * WAVE_PART);
         const uint32_t lane_off = (uint32_t)(tile * WAVES + wave) * WAVE_PART + lane * 16;
         const uint32_t split_pitch = (uint32_t)ntiles * WAVES * WAVE_PART;
-        static_for<GROUPS>([&](auto X) MXG_INLINE {
-            constexpr int x = decltype(X)::value, i = x / (SUB_N * 4), j = (x / 4) % SUB_N,
-                          g = x % 4;
-            const v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                           acc[i][j][4 * g + 3]};
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rW,
-                                                   lane_off + sp * split_pitch + x * 1024, 0, SC1);
-        });
+        // group x = 4 (SUB_N i + j) + g of the partial
+        auto put = [&](int i, int j, const v16f &v) MXG_INLINE {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const v4f q = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(v4i, q), rW,
+                    lane_off + sp * split_pitch + (4 * (SUB_N * i + j) + g) * 1024, 0, SC1);
+            }
+        };
+        if (slow) {
+            for (int t = 0; t < SUB_M * SUB_N; ++t) put(t / SUB_N, t % SUB_N, slow_tile(t / SUB_N, t % SUB_N));
+        } else {
+            static_for<SUB_M * SUB_N>([&](auto T) MXG_INLINE {
+                constexpr int t = decltype(T)::value;
+                put(t / SUB_N, t % SUB_N, acc[t / SUB_N][t % SUB_N]);
+            });
+        }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partial has reached the coherent level
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -596,20 +688,18 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         });
 
     } else {
+        auto put = [&](int i, int j, const v16f &v) MXG_INLINE {
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) {
-            const int m = wm * WAVE_M + i * 32 + lrow;  // tile-local row
-#pragma unroll
-            for (int j = 0; j < SUB_N; ++j) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * WAVE_N + j * 32 + 8 * g + 4 * khalf;  // global column
-                    const uint32_t e0 = (uint32_t)m * N + n;                        // element index
-                    v4f v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                             acc[i][j][4 * g + 3]};
-                    store_c4(rC, e0, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
-                }
-            }
+            for (int g = 0; g < 4; ++g)
+                store_group(i, j, g, v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]});
+        };
+        if (slow) {
+            for (int t = 0; t < SUB_M * SUB_N; ++t) put(t / SUB_N, t % SUB_N, slow_tile(t / SUB_N, t % SUB_N));
+        } else {
+            static_for<SUB_M * SUB_N>([&](auto T) MXG_INLINE {
+                constexpr int t = decltype(T)::value;
+                put(t / SUB_N, t % SUB_N, acc[t / SUB_N][t % SUB_N]);
+            });
         }
     }
 }

@@ -23,5 +23,6 @@ hipError_t launch_skinny_e2m1(const GemmArgs &a, hipStream_t s);          // k_s
 // sel = 2 fmt + (x_dtype == bf16), fmt in {0, 1, 4}
 hipError_t launch_quant(int sel, const quant::QuantArgs &a, dim3 grid, dim3 block,
                         hipStream_t s);                                    // k_quant.hip
+hipError_t launch_copy(const uint8_t *src, uint8_t *dst, uint64_t bytes, hipStream_t s);  // k_quant.hip
 
 } // namespace mxg

@@ -123,6 +123,7 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
     __shared__ __attribute__((aligned(1024))) uint8_t a8_lds[ADEPTH][A8];   // raw A, row-major
     __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][A_SLOT];       // decoded A (bf16)
     __shared__ __attribute__((aligned(16))) uint32_t s_lds[SROWS][SPITCH];  // scale dwords
+    __shared__ uint32_t slow_lds;  // nonzero: a scale byte outside its window (fallback)
 
     // workgroup -> (column tile, K split): split sp takes stages
     // [sp * nk / splits, (sp + 1) * nk / splits)
@@ -153,6 +154,14 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
     // (row r < 64: A row r; else B row r - 64 of this workgroup), column u - u0.
     // (all loads are issued before the first LDS write, so the chunk costs one
     // round trip)
+    //
+    // Every scale byte of real data loaded here is also checked against its
+    // format's window (mxgemm_common.h, scale_lo / scale_hi): a byte outside
+    // it (where the fast loop's bf16 decode would round, overflow or misread
+    // byte 0 / 255) sets slow_lds, and the consumers then recompute their
+    // outputs on the fallback path after the loop.  Dead stages, rows past M
+    // or past this workgroup's columns, and bytes past the end of K are not
+    // data and are not checked.
     auto load_scales = [&](int u0) MXG_INLINE {
         constexpr int PER = (SROWS * SCH + THREADS - 1) / THREADS;
         uint32_t v[PER];
@@ -172,7 +181,33 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
             const int e = tid + THREADS * i;
             if (e < SROWS * SCH) s_lds[e / SCH][e % SCH] = v[i];
         }
+        // the check reads this thread's entries back from LDS, so that the
+        // loaded registers are free by then (the fence keeps the compiler
+        // from forwarding the stored values)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        ScaleRange rga, rgb;
+        rga.init();
+        rgb.init();
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + THREADS * i;
+            const int r = e / SCH, u = u0 + e % SCH;
+            const bool live = u < nk && e < SROWS * SCH;
+            const bool is_a = r < MAX_M;
+            const bool data = live && (is_a ? r < M : r - MAX_M < rows_b);
+            // valid bytes of the dword (0: none)
+            const uint32_t d = mask_scale_tail(live ? s_lds[r][e % SCH] : 0u,
+                                               data ? KB - kt_of(u) * (BK / 32) : 0);
+            if (is_a)
+                rga.add(d, window_lo2<FA == 1 ? 1 : 0>());
+            else
+                rgb.add(d, window_lo2<FB == 1 ? 1 : 0>());
+        }
+        if (rga.outside(window_width<FA == 1 ? 1 : 0>()) || rgb.outside(window_width<FB == 1 ? 1 : 0>()))
+            slow_lds = 1u;
     };
+    if (tid == 0) slow_lds = 0u;
+    lds_barrier();  // the flag is clear before any wave checks its scales
 
     if (wave >= CONSUMERS) {
         // ----------------------------------------------------------- producers
@@ -277,6 +312,50 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
             });
         }
         lds_barrier();  // every wave is done with this chunk's scales
+    }
+
+    // Fallback (a scale byte outside its window somewhere in this
+    // workgroup's rows): recompute acc over this split's K blocks straight
+    // from global memory.  Per 32-K block, lane group g decodes K 8g..8g+7 of
+    // its B row and of its A row with clamped scale bytes (exact), one
+    // 16x16x32 bf16 MFMA forms the block's partial t, and t * 2^(A row
+    // remainder + B column remainder) is added; byte 255 makes the row's or
+    // column's outputs NaN.
+    if (__builtin_amdgcn_readfirstlane(slow_lds)) {
+        const rsrc_t rA = make_rsrc(p.A, (uint32_t)M * K);
+        const int kb0 = kbeg * (BK / 32), kb1 = min(KB, (kbeg + nk) * (BK / 32));
+        constexpr int kNanCode = 4096;  // a B remainder that marks scale byte 255
+        const uint32_t bro = (uint32_t)(16 * w + r16);  // this lane's B row in the workgroup
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i] = v4f{};
+        for (int kb = kb0; kb < kb1; ++kb) {
+            const v2i xb = __builtin_bit_cast(
+                v2i, __builtin_amdgcn_raw_buffer_load_b64(rB, bro * K + 32 * kb + 8 * g, 0, 0));
+            const uint32_t bb = load1(rBs, bro * KB + kb);
+            float db, nb;
+            int eb;
+            clamp_scale<FB>(bb, db, eb, nb);
+            const v8bf b8 = decode8<FB>(xb, db);
+            const int code = bb == 255u ? kNanCode : eb;
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const uint32_t aro = (uint32_t)(16 * i + r16);  // rows past M read as zero
+                const v2i xa = __builtin_bit_cast(
+                    v2i, __builtin_amdgcn_raw_buffer_load_b64(rA, aro * K + 32 * kb + 8 * g, 0, 0));
+                const uint32_t ba = load1(rAs, aro * KB + kb);
+                float da, na;
+                int ea;
+                clamp_scale<FA>(ba, da, ea, na);
+                const v4f t = mfma_bf16_16(b8, decode8<FA>(xa, da), v4f{});
+                // register r holds column 4 g + r, whose B remainder sits in lane 4 g + r
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int c = __shfl(code, 4 * g + r, 64);
+                    const float nbr = c == kNanCode ? __builtin_nanf("") : 0.0f;
+                    acc[i][r] += __builtin_amdgcn_ldexpf(t[r], ea + (c == kNanCode ? 0 : c)) + (na + nbr);
+                }
+            }
+        }
     }
 
     // acc[i] register r of lane l: m = 16 i + l % 16, n = 16 w + 4 (l / 16) + r.

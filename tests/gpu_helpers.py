@@ -92,7 +92,7 @@ def compare(got, ref: dict, out_dtype: int, where: str = ""):
     else:
         g = bf16_to_f32(np.asarray(got).ravel()).astype(np.float64)
         r = bf16_to_f32(ref["refbf16"].ravel()).astype(np.float64)
-        tol = TOL_REL * ref["mag"].ravel() + np.maximum(bf16_ulp(r), bf16_ulp(g))
+        tol = TOL_REL * ref["mag"].ravel() + bf16_ulp(r)
     nan_r, nan_g = np.isnan(r), np.isnan(g)
     assert np.array_equal(nan_r, nan_g), f"{where}: NaN pattern differs ({nan_g.sum()} vs {nan_r.sum()})"
     inf_r = np.isinf(r) | np.isinf(g)
@@ -143,6 +143,6 @@ def compare_native(got, ref: dict, out_dtype: int, extra, where: str = ""):
     else:
         g = bf16_to_f32(got).astype(np.float64)
         r = bf16_to_f32(ref["refbf16"]).astype(np.float64)
-        tol = TOL_REL * ref["mag"] + extra + np.maximum(bf16_ulp(r), bf16_ulp(g))
+        tol = TOL_REL * ref["mag"] + extra + bf16_ulp(r)
     bad = np.abs(g - r) > tol
     assert not bad.any(), f"{where}: {bad.sum()} outside the native bound"

@@ -143,3 +143,16 @@ def test_large_workspace_size_matches_header():
     assert m, "MXGEMM_WORKSPACE_BYTES_LARGE not found"
     a, b, c, d, e = map(int, m.groups())
     assert a + b * c * d * e == L.MXGEMM_WORKSPACE_BYTES_LARGE
+
+
+@pytest.mark.parametrize("dst,src,n,code", [
+    (0x100000, 0x200000, 1 << 16, "MXGEMM_OK"),
+    (0, 0x200000, 1 << 16, "MXGEMM_ERR_NULL"), (0x100000, 0, 1 << 16, "MXGEMM_ERR_NULL"),
+    (0x100000, 0x200000, 0, "MXGEMM_ERR_SHAPE"), (0x100000, 0x200000, 24, "MXGEMM_ERR_SHAPE"),
+    (0x100000, 0x200000, (1 << 40) + 16, "MXGEMM_ERR_SHAPE"),
+    (0x100008, 0x200000, 64, "MXGEMM_ERR_ALIGN"), (0x100000, 0x200004, 64, "MXGEMM_ERR_ALIGN"),
+    (0x100000, 0x100000 + 64, 128, "MXGEMM_ERR_ALIAS"), (0x100000 + 64, 0x100000, 128, "MXGEMM_ERR_ALIAS"),
+    (0x100000, 0x100000 + 128, 128, "MXGEMM_OK"),
+])
+def test_validate_copy(dst, src, n, code):
+    assert L.mxgemm_validate_copy(dst, src, n) == L.STATUS_CODE[code]

@@ -72,19 +72,25 @@ def test_permutation_probe_exact(gemm, variant, which):
     assert np.array_equal(got, ref["ref32"]), f"{np.sum(got != ref['ref32'])} mismatches"
 
 
-@pytest.mark.parametrize("variant", [LARGE, LARGE_NATIVE], ids=lambda v: VNAME[v])
+# scale-byte pairs: the middle, the edges of the e4m3 window (10..246) and of
+# the e5m2 window (17..239), bytes outside both, 0 (2^-127), 254 (2^127),
+# skewed pairs whose product is moderate, pairs that overflow or underflow
+# fp32, and 255 (NaN)
+PAIR_SCALES = [(127, 127), (10, 239), (140, 100), (1, 254), (0, 254), (254, 0), (0, 0),
+               (254, 254), (2, 3), (9, 17), (16, 238), (247, 5), (240, 240), (246, 10),
+               (255, 127), (127, 255)]
+
+
+@pytest.mark.parametrize("variant", ALL_VARIANTS, ids=lambda v: VNAME[v])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (0, 1), (1, 0), (1, 1)])
-@pytest.mark.parametrize("sa,sb", [(127, 127), (10, 239), (140, 100), (1, 254)])
+@pytest.mark.parametrize("sa,sb", PAIR_SCALES, ids=lambda x: str(x))
 def test_pairwise_products_exact(gemm, variant, fa, fb, sa, sb):
     """A[m,0] = code m, B[0,n] = code n (finite codes only), all else zero:
-    C[m,n] = dec(m) dec(n) 2^(sa+sb-254) exactly, for every pair.  The exact
-    variants decode to bf16 with the scale applied, which is exact for scale
-    bytes 3..246 (e4m3) and 10..239 (e5m2); outside that range (1, 254) only
-    the native variant is graded."""
-    rng_ = {0: (3, 246), 1: (10, 239)}
-    in_range = rng_[fa][0] <= sa <= rng_[fa][1] and rng_[fb][0] <= sb <= rng_[fb][1]
-    if variant == LARGE and not in_range:
-        pytest.skip("scale byte outside the exact variants' bf16 range")
+    C[m,n] = dec(m) dec(n) 2^(sa+sb-254) exactly, for every pair and every
+    scale byte.  Results in the fp32 normal range (and infinities) must be
+    bit-identical to the oracle's, zeros must be zero, NaN (scale byte 255)
+    must be NaN; fp32-subnormal results are not graded.  Small-M variants run
+    the 256 rows as four calls of 64."""
     M = N = 256
     K = 32
     tab = {f: oracle.decode_table(f) for f in (0, 1)}
@@ -99,14 +105,113 @@ def test_pairwise_products_exact(gemm, variant, fa, fb, sa, sb):
     p = mi.Problem(M, N, K, fa, fb, A, np.full((M, 1), sa, np.uint8), B,
                    np.full((N, 1), sb, np.uint8), mi.OUT_F32, False)
     log(f"pairwise fa={fa} fb={fb} sa={sa} sb={sb} variant={VNAME[variant]}")
-    got = run(gemm, p, variant)
+    if _is_skinny(variant):
+        parts = []
+        for r0 in range(0, M, 64):
+            q = mi.Problem(64, N, K, fa, fb, A[r0:r0 + 64].copy(), p.As[r0:r0 + 64].copy(), B,
+                           p.Bs, mi.OUT_F32, False)
+            parts.append(run(gemm, q, variant))
+        got = np.concatenate(parts)
+    else:
+        got = run(gemm, p, variant)
     ref = oracle_full(p)
-    # products that are fp32-normal are exact; record the rest separately
     r = ref["ref32"]
-    normal = np.abs(r) >= np.float32(2.0**-126)
-    assert np.array_equal(got[normal], r[normal]), f"{np.sum(got[normal] != r[normal])} mismatches"
+    assert np.array_equal(np.isnan(got), np.isnan(r)), \
+        f"NaN pattern differs: {np.isnan(got).sum()} vs {np.isnan(r).sum()}"
+    graded = ~np.isnan(r) & (np.abs(r) >= np.float32(2.0**-126))  # normal or inf
+    assert np.array_equal(got[graded], r[graded]), f"{np.sum(got[graded] != r[graded])} mismatches"
     zero = r == 0
     assert np.all(got[zero] == 0)
+
+
+def _extreme_problem(M, N, K, fa, fb, seed, normal_rows, normal_cols, out=mi.OUT_F32, acc=False):
+    """Scale bytes outside the decode windows, with every product moderate.
+    Even 32-K blocks carry the 'normal' rows and columns (scales U{120..134});
+    odd blocks carry the others, whose scales sit outside the windows with
+    the A and B bytes of a block summing to about 254 (blocks 1 mod 4: A low,
+    B high; 3 mod 4: A high, B low).  A row's codes are zero in the blocks of
+    the other kind, and normal rows keep byte 127 there, so normal x normal
+    outputs see only in-window bytes, other x other outputs only extreme ones,
+    and mixed outputs are exactly zero."""
+    p = mi.random_problem(M, N, K, seed=seed, fmtA=fa, fmtB=fb, out_dtype=out, use_acc=acc)
+    g = np.random.Generator(np.random.PCG64(seed + 17))
+    lo = {0: (0, 9), 1: (0, 16)}
+    hi = {0: (247, 254), 1: (240, 254)}
+    kb = K // 32
+    ra = np.arange(M) < normal_rows
+    cb = np.arange(N) < normal_cols
+    for b in range(kb):
+        rows_k = slice(32 * b, 32 * b + 32)
+        if b % 2 == 0:
+            p.A[~ra, rows_k] = 0
+            p.B[~cb, rows_k] = 0
+            continue
+        p.A[ra, rows_k] = 0
+        p.B[cb, rows_k] = 0
+        p.As[ra, b] = 127
+        p.Bs[cb, b] = 127
+        (al, ah), (bl, bh) = (lo[fa], hi[fb]) if b % 4 == 1 else (hi[fa], lo[fb])
+        p.As[~ra, b] = g.integers(al, ah + 1, size=(~ra).sum())
+        p.Bs[~cb, b] = g.integers(bl, bh + 1, size=(~cb).sum())
+    return p
+
+
+EXTREME_CASES = [
+    # M, N, K, fmtA, fmtB, normal rows, normal cols, out, use_acc
+    (300, 280, 1024, 0, 0, 128, 128, mi.OUT_F32, False),   # 16-byte scale windows
+    (300, 280, 1056, 0, 0, 128, 128, mi.OUT_F32, False),   # a partial last scale dword
+    (270, 260, 512, 1, 0, 200, 64, mi.OUT_BF16, False),
+    (256, 300, 640, 1, 1, 0, 0, mi.OUT_F32, True),         # every wave on the fallback
+    (64, 300, 1024, 0, 1, 32, 200, mi.OUT_F32, False),
+    (40, 520, 1056, 1, 0, 40, 100, mi.OUT_BF16, True),
+]
+
+
+@pytest.mark.parametrize("case", EXTREME_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"_f{c[3]}{c[4]}")
+def test_extreme_scales(gemm, case):
+    """Scale bytes outside the bf16 decode windows (0..9 and 247..254 for
+    e4m3, 0..16 and 240..254 for e5m2) in some waves of a launch: those waves
+    recompute on the fallback path, the others keep the fast loop; every
+    output meets the agreement rule, with and without split K."""
+    M, N, K, fa, fb, nr, nc, out, acc = case
+    p = _extreme_problem(M, N, K, fa, fb, seed=M + N + K + fa, normal_rows=nr, normal_cols=nc,
+                         out=out, acc=acc)
+    ref = oracle_full(p)
+    dev = to_dev(p)
+    gemm.enable_split_k()
+    try:
+        for v in _variants_for(M) + [AUTO]:
+            for splits in (1, 2):
+                gemm.set_splits(splits)
+                log(f"extreme {case} variant={VNAME[v]} splits={splits}")
+                got = run(gemm, p, v, guard=64, dev_inputs=dev)
+                compare(got, ref, out, f"extreme {case} {VNAME[v]} splits={splits}")
+    finally:
+        gemm.set_splits(0)
+        gemm.disable_split_k()
+
+
+def test_quantized_tiny_blocks(gemm):
+    """A quantized operand whose blocks are tiny gets scale byte 0 (2^-127)
+    from the quantizer; multiplying it with an operand of large scales
+    (moderate products) matches the oracle."""
+    g = np.random.Generator(np.random.PCG64(404))
+    M, N, K = 96, 160, 512
+    X = (g.standard_normal((M, K)) * 1e-39).astype(np.float32)
+    X[:, :32] = g.standard_normal((M, 32)).astype(np.float32)  # one ordinary block per row
+    xd = torch.from_numpy(X).to("cuda:0")
+    codes, scales = gemm.quantize(xd, L.MXGEMM_FMT_E4M3)
+    torch.cuda.synchronize()
+    As = scales.cpu().numpy()
+    assert (As[:, 1:] <= 2).all() and (As[:, 1:] == 0).any(), "expected scale bytes at the bottom"
+    p = mi.random_problem(M, N, K, seed=405, scale_lo=230, scale_hi=254)
+    p.A = codes.cpu().numpy()
+    p.As = As
+    p.Bs[:, 0] = 127
+    ref = oracle_full(p)
+    for v in (LARGE, AUTO):
+        log(f"quantized tiny blocks variant={VNAME[v]}")
+        compare(run(gemm, p, v), ref, mi.OUT_F32, f"quantized tiny blocks {VNAME[v]}")
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 260, 544), (64, 200, 1024), (1, 5, 32)])
@@ -331,6 +436,9 @@ def test_nonfinite_pattern(gemm, fa, fb):
     nan_a = 0x7F if fa == 0 else 0x7E
     p.A[3, 5] = nan_a                 # NaN code in row 3
     p.As[10, 2] = 255                 # NaN scale for row 10, block 2
+    p.A[20, 64:96] = 0x38             # row 20, block 2: all +1.0 ...
+    p.As[20, 2] = 255                 # ... with a NaN scale: NaN, not +inf
+    p.Bs[50, 5] = 255                 # NaN scale for column 50, block 5
     if fb == 1:
         p.B[7, 40] = 0x7C             # +inf in column 7
         p.B[8, 41] = 0xFC             # -inf in column 8
