@@ -147,7 +147,10 @@ int mxgemm_version(void);
 /* Create a handle bound to the current HIP device.  Fails with
  * MXGEMM_ERR_DEVICE if that device is not gfx950, MXGEMM_ERR_NULL if out is
  * NULL, MXGEMM_ERR_HIP if the runtime fails.  The handle owns only host
- * memory. */
+ * memory.  The first handle on a device also sets up that device's copy of
+ * the library's fixed scratch array (mxgemm_run_noalloc): it resolves the
+ * array's address and clears its counters with a kernel on the null
+ * stream, which it waits for. */
 int mxgemm_create(mxgemm_t *out);
 
 /* Destroy a handle (NULL is accepted and ignored).  Work already launched
@@ -218,6 +221,26 @@ int mxgemm_run(mxgemm_t h,
                const void *B, const uint8_t *B_scale, int fmtB,
                void *C, int64_t M, int64_t N, int64_t K,
                int use_acc, int out_dtype, hipStream_t stream);
+
+/* mxgemm_run for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * operation, arguments, results and errors are those of mxgemm_run on a
+ * handle with a workspace of MXGEMM_NOALLOC_SCRATCH_BYTES attached (a
+ * workspace attached to h is not used).  The split-K scratch is a fixed
+ * array inside the library instead, one per GPU, resolved when the handle is
+ * created and held until the process ends, so the call allocates nothing and
+ * needs no workspace.  Every call on one GPU shares that array: calls that
+ * overlap on one GPU (several streams, several host threads) race, and the
+ * caller must order them.  A forced split count (mxgemm_set_splits) whose
+ * partial tiles do not fit in the array returns MXGEMM_ERR_WORKSPACE
+ * (automatic splits are chosen to fit); MXGEMM_ERR_HIP if the handle's
+ * set-up could not resolve the array. */
+#define MXGEMM_NOALLOC_SCRATCH_BYTES MXGEMM_WORKSPACE_BYTES
+int mxgemm_run_noalloc(mxgemm_t h,
+                       const void *A, const uint8_t *A_scale, int fmtA,
+                       const void *B, const uint8_t *B_scale, int fmtB,
+                       void *C, int64_t M, int64_t N, int64_t K,
+                       int use_acc, int out_dtype, hipStream_t stream);
 
 /* MX block quantization: the step that produces the multiply's operands.
  * X is R x K, row-major, fp32 or bf16 (x_dtype MXGEMM_X_*); each row is cut

@@ -33,6 +33,7 @@ MXGEMM_VARIANT_LARGE_NATIVE = 3
 MXGEMM_VARIANT_SKINNY_NATIVE = 4
 MXGEMM_WORKSPACE_BYTES = 4096 + 256 * 64 * 112 * 4
 MXGEMM_WORKSPACE_BYTES_LARGE = 4096 + 256 * 256 * 256 * 4
+MXGEMM_NOALLOC_SCRATCH_BYTES = MXGEMM_WORKSPACE_BYTES
 
 STATUS = {0: "MXGEMM_OK", 1: "MXGEMM_ERR_NULL", 2: "MXGEMM_ERR_FMT", 3: "MXGEMM_ERR_DTYPE",
           4: "MXGEMM_ERR_SHAPE", 5: "MXGEMM_ERR_ALIGN", 6: "MXGEMM_ERR_DEVICE",
@@ -53,6 +54,8 @@ SIGNATURES = {
                                     _i32, _i32]),
     "mxgemm_run": (_i32, [_vp, _vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64, _i32,
                           _i32, _vp]),
+    "mxgemm_run_noalloc": (_i32, [_vp, _vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64,
+                                  _i32, _i32, _vp]),
     "mxgemm_validate_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _u8p, _u8p]),
     "mxgemm_quantize": (_i32, [_vp, _vp, _i32, _i64, _i64, _i32, _u8p, _u8p, _vp]),
     "mxgemm_validate_copy": (_i32, [_vp, _vp, ctypes.c_uint64]),
@@ -162,6 +165,15 @@ def mxgemm_run(h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc, out_d
     _check(load_library().mxgemm_run(
         h, _ptr(A), _ptr(A_scale), int(fmtA), _ptr(B), _ptr(B_scale), int(fmtB), _ptr(C),
         int(M), int(N), int(K), int(use_acc), int(out_dtype), stream), "mxgemm_run")
+
+
+def mxgemm_run_noalloc(h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc, out_dtype,
+                       stream=None) -> None:
+    """mxgemm_run with the library's fixed split-K scratch instead of an
+    attached workspace: allocates nothing (calls on one GPU must not overlap)."""
+    _check(load_library().mxgemm_run_noalloc(
+        h, _ptr(A), _ptr(A_scale), int(fmtA), _ptr(B), _ptr(B_scale), int(fmtB), _ptr(C),
+        int(M), int(N), int(K), int(use_acc), int(out_dtype), _stream(stream)), "mxgemm_run_noalloc")
 
 
 def mxgemm_validate_quantize(X, x_dtype, R, K, fmt, codes, scales) -> int:

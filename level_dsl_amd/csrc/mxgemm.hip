@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "mxgemm.h"
@@ -30,6 +31,14 @@ struct mxgemm_ctx {
     size_t ws_bytes;
 };
 
+// The split-K scratch of mxgemm_run_noalloc: 4 KiB of arrival counters, then
+// partial tiles, laid out like a caller's workspace of the same size.  Each
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address is resolved once per device (scratch_setup) and only that
+// address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[MXGEMM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr uint32_t kMagic = 0x4d584732u;  // "MXG2"
@@ -48,6 +57,13 @@ __global__ void zero_words(uint32_t *p, int n)
 }
 
 constexpr size_t kCounterBytes = 4096;
+
+constexpr size_t kScratchBytes = MXGEMM_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes >= MXGEMM_WORKSPACE_BYTES, "the scratch holds every small-M split");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch[kMaxDevices];  // device address of `scratch` on each device, or NULL
 static_assert(MXGEMM_WORKSPACE_BYTES ==
                   kCounterBytes + (size_t)mxg::stream::MAX_SPLITS_TILES * mxg::stream::MAX_M *
                                       mxg::stream::BN * sizeof(float),
@@ -60,6 +76,26 @@ constexpr size_t kLargePartial = (size_t)mxg::large::BM * mxg::large::BN * sizeo
 static_assert(MXGEMM_WORKSPACE_BYTES_LARGE ==
                   kCounterBytes + (size_t)mxg::stream::MAX_SPLITS_TILES * kLargePartial,
               "large workspace layout");
+
+// Once per device, with that device current: resolve the device address of
+// its copy of `scratch` and clear the arrival counters (every split-K call
+// leaves them at zero again).  The clearing is a kernel on the null stream,
+// waited for here, at set-up, outside any caller's stream work.
+int scratch_setup(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return MXGEMM_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev]) return MXGEMM_OK;
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MXGEMM_ERR_HIP;
+    constexpr int words = (int)(kCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words, dim3((words + 255) / 256), dim3(256), 0, nullptr, (uint32_t *)p,
+                       words);
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    g_scratch[dev] = (uint8_t *)p;
+    return MXGEMM_OK;
+}
 
 // K splits of a small-M call: none unless asked for or the column tiles
 // leave more than half of the 256 CUs idle; then the largest power of two
@@ -158,6 +194,8 @@ int mxgemm_create(mxgemm_t *out)
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXGEMM_ERR_HIP;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MXGEMM_ERR_DEVICE;
+    const int rs = scratch_setup(dev);
+    if (rs != MXGEMM_OK) return rs;
     mxgemm_ctx *h = new (std::nothrow) mxgemm_ctx;
     if (!h) return MXGEMM_ERR_HIP;
     h->magic = kMagic;
@@ -243,9 +281,17 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const 
     return MXGEMM_OK;
 }
 
-int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const void *B,
-               const uint8_t *B_scale, int fmtB, void *C, int64_t M, int64_t N, int64_t K,
-               int use_acc, int out_dtype, hipStream_t stream)
+} // extern "C"
+
+namespace {
+
+// The multiply behind mxgemm_run and mxgemm_run_noalloc: ws / ws_bytes is
+// the split-K workspace (NULL / 0: none), and `strict` turns a forced split
+// count that the workspace cannot hold into MXGEMM_ERR_WORKSPACE instead of
+// fewer splits.
+int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const void *B,
+             const uint8_t *B_scale, int fmtB, void *C, int64_t M, int64_t N, int64_t K, int use_acc,
+             int out_dtype, hipStream_t stream, uint8_t *ws, size_t ws_bytes, bool strict)
 {
     if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
     const int rc = mxgemm_validate_args(A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc,
@@ -270,10 +316,10 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
             const int64_t row_bytes = fmtA == MXGEMM_FMT_E2M1 ? K / 2 : K;
             const size_t esz = out_dtype == MXGEMM_OUT_F32 ? 4 : 2;
             for (int64_t r = 0; r < M; r += H) {
-                const int rc_r = mxgemm_run(h, (const uint8_t *)A + r * row_bytes,
-                                            A_scale + r * (K / 32), fmtA, B, B_scale, fmtB,
-                                            (uint8_t *)C + (size_t)r * N * esz, std::min(H, M - r), N,
-                                            K, use_acc, out_dtype, stream);
+                const int rc_r = run_impl(h, (const uint8_t *)A + r * row_bytes,
+                                          A_scale + r * (K / 32), fmtA, B, B_scale, fmtB,
+                                          (uint8_t *)C + (size_t)r * N * esz, std::min(H, M - r), N,
+                                          K, use_acc, out_dtype, stream, ws, ws_bytes, strict);
                 if (rc_r != MXGEMM_OK) return rc_r;
             }
             return MXGEMM_OK;
@@ -323,13 +369,13 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
         const int nk = native ? (a.K + mxg::skinny::BK - 1) / mxg::skinny::BK
                               : (int)((K + mxg::stream::BK - 1) / mxg::stream::BK);
         a.splits = choose_splits(h->splits, a.tiles_n, nk, native ? 4 : 8);
-        if (a.splits > 1 && !h->ws) {
+        if (a.splits > 1 && !ws) {
             if (h->splits >= 2) return MXGEMM_ERR_WORKSPACE;
             a.splits = 1;
         }
         if (a.splits > 1) {
-            a.cnt = (uint32_t *)h->ws;
-            a.ws = (float *)(h->ws + kCounterBytes);
+            a.cnt = (uint32_t *)ws;
+            a.ws = (float *)(ws + kCounterBytes);
         }
     } else {
         a.tiles_m = (int)((M + mxg::large::BM - 1) / mxg::large::BM);
@@ -339,14 +385,17 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
             const int nk = (int)((K + mxg::large::BK - 1) / mxg::large::BK);
             const bool scale16 = !native && a.scale_dword == 2;  // the kernel's SCALE16
             const int unit = scale16 ? mxg::large::WINDOW : 1;
-            a.splits = choose_splits_large(h->splits, (int)tiles, nk / unit, unit, h->ws_bytes);
-            if (a.splits > 1 && !h->ws) {
+            a.splits = choose_splits_large(h->splits, (int)tiles, nk / unit, unit, ws_bytes);
+            if (strict && h->splits >= 2 &&
+                a.splits < choose_splits_large(h->splits, (int)tiles, nk / unit, unit, 0))
+                return MXGEMM_ERR_WORKSPACE;  // the forced split needs more partials than fit
+            if (a.splits > 1 && !ws) {
                 if (h->splits >= 2) return MXGEMM_ERR_WORKSPACE;
                 a.splits = 1;
             }
             if (a.splits > 1) {
-                a.cnt = (uint32_t *)h->ws;
-                a.ws = (float *)(h->ws + kCounterBytes);
+                a.cnt = (uint32_t *)ws;
+                a.ws = (float *)(ws + kCounterBytes);
             }
         }
     }
@@ -354,6 +403,31 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
     const hipError_t e = dispatch(native, skinny, f, a, stream);
     return e == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
 }
+
+} // namespace
+
+extern "C" {
+
+int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const void *B,
+               const uint8_t *B_scale, int fmtB, void *C, int64_t M, int64_t N, int64_t K,
+               int use_acc, int out_dtype, hipStream_t stream)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    return run_impl(h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc, out_dtype, stream,
+                    h->ws, h->ws_bytes, false);
+}
+
+int mxgemm_run_noalloc(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const void *B,
+                       const uint8_t *B_scale, int fmtB, void *C, int64_t M, int64_t N, int64_t K,
+                       int use_acc, int out_dtype, hipStream_t stream)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    uint8_t *const sp = h->device >= 0 && h->device < kMaxDevices ? g_scratch[h->device] : nullptr;
+    if (!sp) return MXGEMM_ERR_HIP;  // set-up in mxgemm_create did not resolve the array
+    return run_impl(h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc, out_dtype, stream,
+                    sp, kScratchBytes, true);
+}
+
 
 int mxgemm_validate_quantize(const void *X, int x_dtype, int64_t R, int64_t K, int fmt,
                              const uint8_t *codes, const uint8_t *scales)
