@@ -18,11 +18,20 @@ Also reported on the same line:
     copies;
   * roofline: algorithmic work per launch / mean launch duration, from one
     pair of HIP events recorded on the launch stream around the timed
-    launches;
+    launches, against the dense MXFP8 peak (5.0 PFLOP/s) that the metric
+    names; bf16_ceiling gives the same rate against the dense bf16 peak
+    (2.5 PFLOP/s), the ceiling of the exact path's bf16 MFMAs;
+  * protocol: the five workloads (256^3, 4096^3, 8192^3 bf16, M = 64, and
+    16384^3 e5m2 x e4m3 with use_acc) launched one at a time, each launch
+    preceded (untimed) by a read of 1 GiB that leaves no operand in L2 or the
+    256 MiB Infinity Cache (and, with use_acc, a restore of C), each timed
+    by its own HIP event pair: median, min and quartiles, the rate at the
+    median against the MXFP8 peak (HBM peak for M = 64); and the library's
+    buffer-load/store streaming copy of 1 GiB as the achievable HBM rate;
   * cpu_baseline: the CPU oracle timed on a bounded sample of outputs of
     the 8192^3 workload on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--protocol-runs 50]
 
 Counter passes (HBM traffic per launch):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o p -- python bench.py --traffic
@@ -144,6 +153,89 @@ def bench_gemm(gemm, p, variant, steps, warmup, copies):
     del sets, C
     torch.cuda.empty_cache()
     return wall, mean_s
+
+
+FLUSH_BYTES = 1 << 30  # read before every protocol launch: more than L2 + the 256 MiB Infinity Cache
+
+
+def launch_stats(times_s, work, unit_scale, peak):
+    """Median / min / quartiles of per-launch durations (seconds) and the
+    rate at the median: work / median / unit_scale, also as a fraction of
+    peak."""
+    t = np.sort(np.asarray(times_s) * 1e6)
+    q1, med, q3 = np.percentile(t, [25, 50, 75])
+    rate = work / (med * 1e-6) / unit_scale
+    return {"median_us": round(float(med), 2), "min_us": round(float(t[0]), 2),
+            "p25_us": round(float(q1), 2), "p75_us": round(float(q3), 2),
+            "iqr_us": round(float(q3 - q1), 2), "rate_at_median": round(rate, 2),
+            "rate_at_min": round(work / (t[0] * 1e-6) / unit_scale, 2),
+            "frac_at_median": round(rate / peak, 4)}
+
+
+def protocol_gemm(gemm, p, variant, runs, warmup):
+    """Per-launch timing: before every launch (untimed) C is restored from a
+    pristine copy when use_acc is set, then a FLUSH_BYTES buffer is read
+    (summed) so that no operand is left in L2 or the Infinity Cache.  A read
+    leaves the caches holding clean lines; a write of the same size would
+    leave 256 MiB of dirty lines whose write-back then competes with the
+    launch (measured: the M = 64 workload took 103 instead of 63 us).  Each
+    launch is bracketed by its own pair of HIP events on the launch stream.
+    Returns the durations in seconds."""
+    import torch
+    import level_dsl_amd as L
+    A, As, B, Bs = upload(p, 1)[0]
+    dt = torch.float32 if p.out_dtype == 0 else torch.bfloat16
+    C = torch.empty((p.M, p.N), dtype=dt, device="cuda:0")
+    C0 = None
+    if p.use_acc:
+        C0 = torch.from_numpy(p.Cin if p.out_dtype == 0 else p.Cin.view(np.int16)).to("cuda:0").view(dt)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    gemm.set_variant(variant)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(runs)]
+    for i in range(warmup + runs):
+        if C0 is not None:
+            C.copy_(C0)
+        flush.sum()
+        if i >= warmup:
+            ev[i - warmup][0].record(stream)
+        L.mxgemm_run(gemm.h, A, As, p.fmtA, B, Bs, p.fmtB, C, p.M, p.N, p.K, int(p.use_acc),
+                     p.out_dtype, stream.cuda_stream)
+        if i >= warmup:
+            ev[i - warmup][1].record(stream)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    del A, As, B, Bs, C, C0, flush
+    torch.cuda.empty_cache()
+    return t
+
+
+def achievable_hbm(gemm, runs=30, nbytes=1 << 30):
+    """The library's buffer-load/store streaming copy of nbytes (read once,
+    written once), per-launch events; GB/s of bytes moved at the median."""
+    import torch
+    import level_dsl_amd as L
+    src = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(runs)]
+    for i in range(5 + runs):
+        if i >= 5:
+            ev[i - 5][0].record(stream)
+        L.mxgemm_copy(gemm.h, dst, src, nbytes, stream.cuda_stream)
+        if i >= 5:
+            ev[i - 5][1].record(stream)
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(dst[:1 << 20], src[:1 << 20]))
+    t = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    del src, dst
+    torch.cuda.empty_cache()
+    st = launch_stats(t, 2 * nbytes, 1e9, PEAK_HBM_GBS)
+    st.update({"unit": "GB/s", "bytes_moved": 2 * nbytes, "copy_ok": ok,
+               "kernel": "mxg::copy::kernel (mxgemm_copy)"})
+    return st
 
 
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
@@ -329,6 +421,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--protocol-runs", type=int, default=50,
+                    help="timed launches per workload in the flushed per-launch protocol (0: skip)")
     ap.add_argument("--traffic", action="store_true",
                     help="only launch the counter-pass workload (under rocprofv3 --pmc)")
     ap.add_argument("--traffic-report", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -376,10 +470,15 @@ def main():
                    "scales": "e8m0 per 32 K", "mfma": "bf16 32x32x16 after exact scaled decode",
                    "accumulate": "f32", "out": "bf16 (RNE)", "input_rotation": 3},
         "pct_of_mxfp8_peak": round(100 * value / PEAK_TFLOPS["fp8"], 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp8"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp8"], 4),
                      "traffic": traffic, "kernel": "mxg::large::kernel<0,0,false,true,false>",
                      "launch_mean_us": round(mean_s * 1e6, 2)},
+        # the exact path multiplies on the bf16 MFMA after the scaled decode
+        # (the scaled MFMA misses the 1e-5 rule), so its own ceiling is the
+        # dense bf16 peak
+        "bf16_ceiling": {"peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK_TFLOPS["bf16"], 4)},
     })
 
     # ---- native scaled-MFMA variant on the same workload ----------------------
@@ -471,6 +570,34 @@ def main():
                      "launch_mean_us": round(mean_q * 1e6, 2)},
         "algorithmic_bytes": qbytes, "steps": q_steps, "x_rotation": 3}
     log(f"bench: mx_quantize {out['mx_quantize']['value']} GB/s")
+    # ---- the measurement protocol: per-launch events after a cache flush ------
+    # C1 256^3 f32, C2 4096^3 f32, C3 8192^3 bf16 (the headline), C4 M = 64,
+    # C5 16384^3 e5m2 x e4m3 with use_acc; `runs` launches each after
+    # `warmup`, every launch preceded (untimed) by a 1 GiB read and, for C5,
+    # a restore of C
+    runs = args.protocol_runs
+    proto = {"flush_bytes": FLUSH_BYTES, "runs": runs, "warmup": 5,
+             "timing": "one HIP event pair per launch on the launch stream"}
+    if runs > 0:
+        for key, wid in (("C1", 0), ("C2", 1), ("C3", 2), ("C4", 3), ("C5", 4)):
+            q = p if wid == 2 else mi.workload(wid)
+            log(f"bench: protocol {key} ({q.name})")
+            t = protocol_gemm(gemm, q, L.MXGEMM_VARIANT_AUTO, runs, 5)
+            if wid == 3:
+                qb = mi.algorithmic_bytes(q.M, q.N, q.K, q.out_dtype, q.use_acc)
+                st = launch_stats(t, qb, 1e9, PEAK_HBM_GBS)
+                st.update({"unit": "GB/s", "bound": "hbm", "algorithmic_bytes": qb})
+            else:
+                st = launch_stats(t, mi.algorithmic_flops(q.M, q.N, q.K), 1e12, PEAK_TFLOPS["fp8"])
+                st.update({"unit": "TFLOP/s", "bound": "mfma (frac: of the dense MXFP8 peak)"})
+            st["workload"] = q.name
+            proto[key] = st
+            log(f"bench: protocol {key} median {st['median_us']} us, {st['rate_at_median']} {st['unit']}")
+            if wid != 2:
+                del q
+        proto["achievable_hbm"] = achievable_hbm(gemm)
+        log(f"bench: streaming copy {proto['achievable_hbm']['rate_at_median']} GB/s")
+    out["protocol"] = proto
     gemm.close()
 
     if not args.no_cpu:

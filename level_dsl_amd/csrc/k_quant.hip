@@ -21,11 +21,11 @@ hipError_t launch_quant(int sel, const quant::QuantArgs &a, dim3 grid, dim3 bloc
 
 hipError_t launch_copy(const uint8_t *src, uint8_t *dst, uint64_t bytes, hipStream_t stream)
 {
-    // enough waves to keep about 128 KiB per CU in flight, but no more than
-    // there are pieces
+    // two workgroups per CU (measured best on 1 GiB), but no more than there
+    // are pieces
     const uint64_t pieces = (bytes + copy::PIECE - 1) / copy::PIECE;
     const uint64_t per_block = copy::THREADS / 64;
-    const uint64_t blocks = std::min<uint64_t>((pieces + per_block - 1) / per_block, 256 * 4);
+    const uint64_t blocks = std::min<uint64_t>((pieces + per_block - 1) / per_block, 256 * 2);
     hipLaunchKernelGGL(copy::kernel, dim3((unsigned)blocks), dim3(copy::THREADS), 0, stream, src, dst,
                        bytes);
     return hipGetLastError();

@@ -73,3 +73,12 @@ def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_hash() == h0
     f0.write_text(f0.read_text() + "\nint extra_symbol;\n")
     assert bench.kernel_hash() != h0
+
+
+def test_launch_stats():
+    t = [1e-3, 2e-3, 3e-3, 4e-3, 5e-3]  # seconds
+    st = bench.launch_stats(t, 3e9, 1e9, 10.0)  # 3e9 units, reported in 1e9
+    assert st["median_us"] == 3000.0 and st["min_us"] == 1000.0
+    assert st["p25_us"] == 2000.0 and st["p75_us"] == 4000.0 and st["iqr_us"] == 2000.0
+    assert abs(st["rate_at_median"] - 1000.0) < 1e-9 and abs(st["rate_at_min"] - 3000.0) < 1e-9
+    assert abs(st["frac_at_median"] - 100.0) < 1e-9
