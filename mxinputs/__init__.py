@@ -37,12 +37,79 @@ import torch
 SEED_ROOT = 0x4D58
 FMT_E4M3 = 0
 FMT_E5M2 = 1
+FMT_E2M3 = 2
+FMT_E3M2 = 3
 FMT_E2M1 = 4
 OUT_F32 = 0
 OUT_BF16 = 1
 
 # largest finite value of each format (OCP e4m3fn / e5m2)
-FMT_MAX = {FMT_E4M3: 448.0, FMT_E5M2: 57344.0, FMT_E2M1: 6.0}
+FMT_MAX = {FMT_E4M3: 448.0, FMT_E5M2: 57344.0, FMT_E2M3: 7.5, FMT_E3M2: 28.0, FMT_E2M1: 6.0}
+CODE_BITS = {FMT_E4M3: 8, FMT_E5M2: 8, FMT_E2M3: 6, FMT_E3M2: 6, FMT_E2M1: 4}
+
+
+def _fp6_grid(fmt: int) -> np.ndarray:
+    """The 32 non-negative magnitudes of a 6-bit format in code order (the
+    code's low 5 bits), from the OCP FP6 bit fields: e2m3 is exponent bias 1
+    with 3 mantissa bits, e3m2 bias 3 with 2; exponent field 0 is
+    subnormal."""
+    mb, bias = (3, 1) if fmt == FMT_E2M3 else (2, 3)
+    out = []
+    for c in range(32):
+        e, m = c >> mb, c & ((1 << mb) - 1)
+        if e == 0:
+            out.append(m / (1 << mb) * 2.0 ** (1 - bias))
+        else:
+            out.append((1 + m / (1 << mb)) * 2.0 ** (e - bias))
+    return np.array(out)
+
+
+def _quantize_fp6(x: np.ndarray, fmt: int) -> np.ndarray:
+    """fp32 values -> 6-bit codes 0..63 (unpacked): round to the nearest
+    grid magnitude, ties to the even code, saturating at the largest; the
+    sign (bit 5) is kept, so -0 and tiny negatives give code 32."""
+    grid = _fp6_grid(fmt)
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    lo = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 31)
+    hi = np.minimum(lo + 1, 31)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    idx = np.where(up, hi, lo).astype(np.uint8)
+    return idx | (np.signbit(x).astype(np.uint8) << 5)
+
+
+def pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
+    """(rows, K) codes of `bits` bits -> (rows, ceil(bits*K/8)) bytes: code k
+    at bits bits*k .. bits*k+bits-1 of the row read as one little-endian bit
+    string (e2m1: the even k in the low nibble; 6-bit: four codes in three
+    bytes)."""
+    c = np.asarray(codes, dtype=np.uint64)
+    rows, K = c.shape
+    nbytes = (K * bits + 7) // 8
+    out = np.zeros((rows, nbytes), np.uint8)
+    for k in range(K):
+        bit = k * bits
+        b, sh = bit // 8, bit % 8
+        v = c[:, k] << np.uint64(sh)
+        out[:, b] |= (v & np.uint64(0xff)).astype(np.uint8)
+        if sh + bits > 8:
+            out[:, b + 1] |= (v >> np.uint64(8)).astype(np.uint8)
+    return out
+
+
+def unpack_bits(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Inverse of pack_bits: (rows, ceil(bits*K/8)) bytes -> (rows, K) codes."""
+    p = np.asarray(packed, dtype=np.uint64)
+    out = np.empty((p.shape[0], K), np.uint8)
+    for k in range(K):
+        bit = k * bits
+        b, sh = bit // 8, bit % 8
+        v = p[:, b] >> np.uint64(sh)
+        if sh + bits > 8:
+            v |= p[:, b + 1] << np.uint64(8 - sh)
+        out[:, k] = (v & np.uint64((1 << bits) - 1)).astype(np.uint8)
+    return out
 _TORCH_FP8 = {FMT_E4M3: torch.float8_e4m3fn, FMT_E5M2: torch.float8_e5m2}
 
 T_A, T_B, T_AS, T_BS, T_CIN = 0, 1, 2, 3, 4
@@ -83,9 +150,13 @@ def unpack_e2m1(packed: np.ndarray) -> np.ndarray:
 
 def quantize(x: np.ndarray, fmt: int) -> np.ndarray:
     """fp32 values -> uint8 codes: clamp to +-max, then round to nearest even.
-    e2m1 codes come back packed two per byte along the last axis."""
+    e2m1 and 6-bit codes come back packed along the last axis (pack_bits)."""
     if fmt == FMT_E2M1:
         return pack_e2m1(_quantize_e2m1(x))
+    if fmt in (FMT_E2M3, FMT_E3M2):
+        x = np.asarray(x, dtype=np.float32)
+        return pack_bits(_quantize_fp6(x.reshape(-1, x.shape[-1]), fmt), 6).reshape(
+            x.shape[:-1] + ((x.shape[-1] * 6 + 7) // 8,))
     lim = np.float32(FMT_MAX[fmt])
     x = np.clip(np.asarray(x, dtype=np.float32), -lim, lim)
     t = torch.from_numpy(np.ascontiguousarray(x)).to(_TORCH_FP8[fmt])

@@ -25,7 +25,9 @@ _LIB = os.path.join(_HERE, "libmxref.so")
 
 FMT_E4M3 = 0
 FMT_E5M2 = 1
-FMT_E8M0 = 2
+FMT_E2M3 = 2
+FMT_E3M2 = 3
+FMT_E8M0 = 8
 
 GCC_FLAGS = ["-O2", "-std=c99", "-Wall", "-Wextra", "-ffp-contract=off",
              "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
@@ -79,16 +81,17 @@ def default_threads() -> int:
 
 
 FMT_E2M1 = 4
+CODE_BITS = {FMT_E4M3: 8, FMT_E5M2: 8, FMT_E2M3: 6, FMT_E3M2: 6, FMT_E2M1: 4}
 
 
 def packed_width(K: int, fmt: int) -> int:
-    """Bytes per operand row: K codes, or ceil(K/2) for e2m1 (two per byte)."""
-    return (K + 1) // 2 if fmt == FMT_E2M1 else K
+    """Bytes per operand row: K codes of 8, 6 or 4 bits (ceil(bits*K/8))."""
+    return (K * CODE_BITS[fmt] + 7) // 8
 
 
 def decode_table(fmt: int, lib=None) -> np.ndarray:
-    """All 256 decoded values of a format (0 e4m3, 1 e5m2, 2 e8m0, 4 e2m1,
-    whose codes above 15 decode to NaN)."""
+    """All 256 decoded values of a format (0 e4m3, 1 e5m2, 2 e2m3, 3 e3m2,
+    4 e2m1, 8 e8m0; codes past a sub-byte format's range decode to NaN)."""
     lib = lib or load()
     return np.array([lib.mxref_decode(fmt, c) for c in range(256)], dtype=np.float64)
 
@@ -108,9 +111,10 @@ def gemm_points(A, As, fmtA, B, Bs, fmtB, M, N, K, rows, cols,
                 cin=None, nthreads=None, lib=None):
     """Oracle outputs at points (rows[p], cols[p]).
 
-    A: (M, K) uint8 codes; B: (N, K) uint8 codes (K contiguous); an e2m1
-    operand (fmt 4) is (rows, ceil(K/2)) bytes, two codes per byte, the even
-    k in the low nibble;
+    A: (M, K) uint8 codes; B: (N, K) uint8 codes (K contiguous); a sub-byte
+    operand (e2m3 / e3m2: 6 bits, e2m1: 4 bits per code) is
+    (rows, ceil(bits*K/8)) bytes, code k at bits bits*k .. bits*k+bits-1 of
+    the row read as one little-endian bit string;
     As: (M, ceil(K/32)) and Bs: (N, ceil(K/32)) uint8 e8m0 bytes.
     cin: None (use_acc off), or the incoming (M, N) C as float32, or as
     uint16 bf16 bit patterns.
@@ -166,8 +170,8 @@ def gemm_full(A, As, fmtA, B, Bs, fmtB, M, N, K, cin=None, nthreads=None, lib=No
 
 def quantize(X, fmt, lib=None):
     """MX block quantization of an (R, K) matrix: X float32, or uint16 bf16
-    bit patterns.  Returns (codes (R, K) uint8 -- e2m1: (R, ceil(K/2)), two
-    per byte, the even k in the low nibble -- scales (R, ceil(K/32)) uint8).
+    bit patterns.  Returns (codes (R, K) uint8 -- sub-byte formats packed as
+    the operands of gemm_points are -- scales (R, ceil(K/32)) uint8).
     Raises ValueError for non-finite input (the recipe covers finite values)."""
     lib = lib or load()
     X = np.ascontiguousarray(X)

@@ -27,6 +27,13 @@
  *     lhs_k_pack / rhs_k_pack = True of dot_scaled): element k of a row is
  *     the low nibble of byte k/2 when k is even, the high nibble when odd,
  *     so a row of K elements takes ceil(K/2) bytes.
+ *   - e2m3 and e3m2 (the 6-bit members of that family) are OCP FP6 E2M3
+ *     (sign | 2-bit exponent, bias 1 | 3-bit mantissa; max 7.5) and E3M2
+ *     (sign | 3-bit exponent, bias 3 | 2-bit mantissa; max 28), neither with
+ *     inf or NaN.  Their codes are packed four per three bytes along K:
+ *     element k of a row occupies bits 6k .. 6k+5 of the row read as one
+ *     little-endian bit string, so a row of K elements takes ceil(6K/8)
+ *     bytes.
  *   - memory layout: A is M x K row-major bytes; B is stored K-contiguous
  *     ("K-major"), B_mem[n*K + k] = B[k,n]; scales are row-major
  *     M x KB and N x KB bytes with KB = ceil(K/32).
@@ -49,9 +56,11 @@
 
 #define MXREF_FMT_E4M3 0
 #define MXREF_FMT_E5M2 1
-#define MXREF_FMT_E8M0 2
+#define MXREF_FMT_E2M3 2
+#define MXREF_FMT_E3M2 3
 #define MXREF_FMT_E2M1 4
-#define MXREF_NTAB 5
+#define MXREF_FMT_E8M0 8
+#define MXREF_NTAB 9
 
 /* ---- format decoders, written from the OCP 8-bit float / MX definitions -- */
 
@@ -103,6 +112,38 @@ static double dec_e2m1(unsigned c)
     return s ? -v : v;
 }
 
+/* e2m3 (OCP FP6): sign | 2-bit exponent, bias 1 | 3-bit mantissa.
+ * exponent field 0 is subnormal: (m/8) * 2^(1-1); codes above 63 do not
+ * exist (NaN here). */
+static double dec_e2m3(unsigned c)
+{
+    if (c > 63u)
+        return NAN;
+    unsigned s = (c >> 5) & 1u, e = (c >> 3) & 3u, m = c & 7u;
+    double v;
+    if (e == 0u)
+        v = ldexp((double)m, 1 - 1 - 3);            /* m/8 */
+    else
+        v = ldexp((double)(8u + m), (int)e - 1 - 3); /* (1+m/8) * 2^(e-1) */
+    return s ? -v : v;
+}
+
+/* e3m2 (OCP FP6): sign | 3-bit exponent, bias 3 | 2-bit mantissa.
+ * exponent field 0 is subnormal: (m/4) * 2^(1-3); codes above 63 do not
+ * exist (NaN here). */
+static double dec_e3m2(unsigned c)
+{
+    if (c > 63u)
+        return NAN;
+    unsigned s = (c >> 5) & 1u, e = (c >> 2) & 7u, m = c & 3u;
+    double v;
+    if (e == 0u)
+        v = ldexp((double)m, 1 - 3 - 2);            /* m/4 * 2^-2 */
+    else
+        v = ldexp((double)(4u + m), (int)e - 3 - 2); /* (1+m/4) * 2^(e-3) */
+    return s ? -v : v;
+}
+
 /* e8m0 scale: unsigned biased exponent, 2^(s-127); 255 is NaN. */
 static double dec_e8m0(unsigned s)
 {
@@ -119,9 +160,11 @@ static void build_tables(void)
     for (unsigned c = 0; c < 256u; ++c) {
         TAB[MXREF_FMT_E4M3][c] = dec_e4m3(c);
         TAB[MXREF_FMT_E5M2][c] = dec_e5m2(c);
-        TAB[MXREF_FMT_E8M0][c] = dec_e8m0(c);
-        TAB[3][c] = NAN; /* no format 3 */
+        TAB[MXREF_FMT_E2M3][c] = dec_e2m3(c);
+        TAB[MXREF_FMT_E3M2][c] = dec_e3m2(c);
         TAB[MXREF_FMT_E2M1][c] = dec_e2m1(c);
+        TAB[5][c] = TAB[6][c] = TAB[7][c] = NAN; /* no formats 5..7 */
+        TAB[MXREF_FMT_E8M0][c] = dec_e8m0(c);
     }
 }
 
@@ -133,13 +176,60 @@ static const double *table(int fmt)
 
 int mxref_version(void) { return 1; }
 
-/* Decoded value of one code: fmt 0 = e4m3, 1 = e5m2, 2 = e8m0 scale,
- * 4 = e2m1 (codes 0..15).  Returns NaN for an unknown format or code. */
+/* Decoded value of one code: fmt 0 = e4m3, 1 = e5m2, 2 = e2m3 and
+ * 3 = e3m2 (codes 0..63), 4 = e2m1 (codes 0..15), 8 = e8m0 scale.  Returns
+ * NaN for an unknown format or code. */
 double mxref_decode(int fmt, int code)
 {
-    if (fmt < 0 || fmt >= MXREF_NTAB || fmt == 3 || code < 0 || code > 255)
+    if (fmt < 0 || fmt >= MXREF_NTAB || (fmt > 4 && fmt != MXREF_FMT_E8M0) || code < 0 ||
+        code > 255)
         return NAN;
     return table(fmt)[code];
+}
+
+/* Bits per code of an operand format (8, 6 or 4), 0 for an unknown one. */
+static int code_bits(int fmt)
+{
+    switch (fmt) {
+    case MXREF_FMT_E4M3:
+    case MXREF_FMT_E5M2: return 8;
+    case MXREF_FMT_E2M3:
+    case MXREF_FMT_E3M2: return 6;
+    case MXREF_FMT_E2M1: return 4;
+    default: return 0;
+    }
+}
+
+/* Bytes per operand row of K codes of `bits` bits each. */
+static int64_t row_bytes(int64_t K, int bits) { return (K * bits + 7) / 8; }
+
+/* Code k of a row of `bits`-bit codes: bits bits*k .. bits*k+bits-1 of the
+ * row read as one little-endian bit string. */
+static unsigned code_at(const uint8_t *row, int64_t k, int bits)
+{
+    if (bits == 8)
+        return row[k];
+    const int64_t bit = k * bits;
+    const unsigned sh = (unsigned)(bit % 8);
+    unsigned v = row[bit / 8] >> sh;
+    if (sh + (unsigned)bits > 8u)
+        v |= (unsigned)row[bit / 8 + 1] << (8u - sh);
+    return v & ((1u << bits) - 1u);
+}
+
+/* Store code c as code k of a row of `bits`-bit codes (the row must start
+ * zeroed: bits are OR-ed in). */
+static void put_code(uint8_t *row, int64_t k, int bits, unsigned c)
+{
+    if (bits == 8) {
+        row[k] = (uint8_t)c;
+        return;
+    }
+    const int64_t bit = k * bits;
+    const unsigned sh = (unsigned)(bit % 8);
+    row[bit / 8] |= (uint8_t)(c << sh);
+    if (sh + (unsigned)bits > 8u)
+        row[bit / 8 + 1] |= (uint8_t)(c >> (8u - sh));
 }
 
 /* fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays a
@@ -170,7 +260,7 @@ struct job {
     const void *Cin;
     int cin_dtype;               /* 0 fp32, 1 bf16 */
     const double *ta, *tb, *te;
-    int packA, packB;            /* e2m1: two codes per byte along K */
+    int bitsA, bitsB;            /* bits per code: 8, 6 (packed 4 per 3 bytes) or 4 */
     int64_t ldA, ldB;            /* bytes per operand row */
     int64_t M, N, K, KB;
     const int64_t *rows, *cols;
@@ -190,8 +280,8 @@ static void *run_job(void *arg)
         double s = 0.0, mag = 0.0;
         for (int64_t k = 0; k < j->K; ++k) {
             /* decode(A[m,k]) * 2^(sa-127) and decode(B[k,n]) * 2^(sb-127) */
-            const unsigned ca = j->packA ? (a[k / 2] >> (4 * (k % 2))) & 15u : a[k];
-            const unsigned cb = j->packB ? (b[k / 2] >> (4 * (k % 2))) & 15u : b[k];
+            const unsigned ca = code_at(a, k, j->bitsA);
+            const unsigned cb = code_at(b, k, j->bitsB);
             double av = j->ta[ca] * j->te[sa[k / 32]];
             double bv = j->tb[cb] * j->te[sb[k / 32]];
             double prod = av * bv;
@@ -219,8 +309,9 @@ static void *run_job(void *arg)
 /*
  * Compute npts outputs C[rows[p], cols[p]].
  *   A: M*K codes, As: M*KB bytes, B: N*K codes (K-contiguous), Bs: N*KB,
- *   KB = ceil(K/32); fmtA/fmtB: 0 e4m3, 1 e5m2, 4 e2m1 (then the operand
- *   holds ceil(K/2) bytes per row, two codes per byte, low nibble first).
+ *   KB = ceil(K/32); fmtA/fmtB: 0 e4m3, 1 e5m2, 2 e2m3, 3 e3m2, 4 e2m1
+ *   (a row of sub-byte codes holds ceil(bits*K/8) bytes, packed as
+ *   code_at reads them).
  *   Cin: NULL (use_acc off) or the M*N incoming C, fp32 (cin_dtype 0) or
  *   bf16 bits (cin_dtype 1).
  *   Outputs (each may be NULL): sum_out/mag_out the double sum and sum of
@@ -238,8 +329,7 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *As, int fmtA,
                       uint16_t *refbf16_out, int nthreads)
 {
     if (!A || !As || !B || !Bs || !rows || !cols || M < 1 || N < 1 || K < 1 ||
-        npts < 0 || (fmtA != 0 && fmtA != 1 && fmtA != MXREF_FMT_E2M1) ||
-        (fmtB != 0 && fmtB != 1 && fmtB != MXREF_FMT_E2M1) ||
+        npts < 0 || code_bits(fmtA) == 0 || code_bits(fmtB) == 0 ||
         (Cin && cin_dtype != 0 && cin_dtype != 1))
         return -1;
     for (int64_t p = 0; p < npts; ++p)
@@ -256,8 +346,8 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *As, int fmtA,
     base.A = A; base.As = As; base.B = B; base.Bs = Bs;
     base.Cin = Cin; base.cin_dtype = cin_dtype;
     base.ta = table(fmtA); base.tb = table(fmtB); base.te = table(MXREF_FMT_E8M0);
-    base.packA = fmtA == MXREF_FMT_E2M1; base.packB = fmtB == MXREF_FMT_E2M1;
-    base.ldA = base.packA ? (K + 1) / 2 : K; base.ldB = base.packB ? (K + 1) / 2 : K;
+    base.bitsA = code_bits(fmtA); base.bitsB = code_bits(fmtB);
+    base.ldA = row_bytes(K, base.bitsA); base.ldB = row_bytes(K, base.bitsB);
     base.M = M; base.N = N; base.K = K; base.KB = (K + 31) / 32;
     base.rows = rows; base.cols = cols;
     base.sum_out = sum_out; base.mag_out = mag_out;
@@ -306,7 +396,13 @@ int mxref_gemm_points(const uint8_t *A, const uint8_t *As, int fmtA,
  */
 static double fmt_max(int fmt)
 {
-    return fmt == MXREF_FMT_E4M3 ? 448.0 : fmt == MXREF_FMT_E2M1 ? 6.0 : 57344.0;
+    switch (fmt) {
+    case MXREF_FMT_E4M3: return 448.0;
+    case MXREF_FMT_E5M2: return 57344.0;
+    case MXREF_FMT_E2M3: return 7.5;
+    case MXREF_FMT_E3M2: return 28.0;
+    default: return 6.0; /* e2m1 */
+    }
 }
 
 /* Nearest code of `fmt` to v, ties to an even mantissa field (the lowest
@@ -315,7 +411,8 @@ static uint8_t nearest_code(int fmt, double v)
 {
     const double *t = table(fmt);
     const double a = fabs(v);
-    const int ncodes = fmt == MXREF_FMT_E2M1 ? 8 : 128; /* the non-negative codes */
+    const int bits = code_bits(fmt);
+    const int ncodes = 1 << (bits - 1); /* the non-negative codes: below the sign bit */
     int best = 0;
     double bd = INFINITY;
     for (int c = 0; c < ncodes; ++c) {
@@ -327,7 +424,7 @@ static uint8_t nearest_code(int fmt, double v)
             best = c;
         }
     }
-    return (uint8_t)(best | (signbit(v) ? (fmt == MXREF_FMT_E2M1 ? 0x8 : 0x80) : 0));
+    return (uint8_t)(best | (signbit(v) ? ncodes : 0));
 }
 
 /* Smallest integer e with amax <= MAX * 2^e, for finite amax > 0. */
@@ -345,19 +442,22 @@ static int block_exponent(int fmt, double amax)
 /*
  * Quantize the R x K matrix X (row-major; x_dtype 0: fp32, 1: bf16 bit
  * patterns) to codes (R x K) and scales (R x ceil(K/32)) of format fmt
- * (0 e4m3, 1 e5m2).  Returns 0; -1 on bad arguments; -2 if X holds a NaN or
- * an infinity (the recipe is defined for finite inputs only).
+ * (0 e4m3, 1 e5m2, 2 e2m3, 3 e3m2, 4 e2m1; sub-byte codes packed along K as
+ * the operands are).  Returns 0; -1 on bad arguments; -2 if X holds a NaN
+ * or an infinity (the recipe is defined for finite inputs only).
  */
 int mxref_quantize(const void *X, int x_dtype, int64_t R, int64_t K, int fmt, uint8_t *codes,
                    uint8_t *scales)
 {
     if (!X || !codes || !scales || R < 1 || K < 1 || (x_dtype != 0 && x_dtype != 1) ||
-        (fmt != MXREF_FMT_E4M3 && fmt != MXREF_FMT_E5M2 && fmt != MXREF_FMT_E2M1))
+        code_bits(fmt) == 0)
         return -1;
     const int64_t KB = (K + 31) / 32;
-    /* e2m1 codes are packed two per byte along K, the even k in the low nibble */
-    const int packed = fmt == MXREF_FMT_E2M1;
-    const int64_t ldc = packed ? (K + 1) / 2 : K;
+    /* sub-byte codes are packed along K as the operands are (code_at) */
+    const int bits = code_bits(fmt);
+    const int64_t ldc = row_bytes(K, bits);
+    if (bits < 8)
+        memset(codes, 0, (size_t)(R * ldc));
     for (int64_t r = 0; r < R; ++r) {
         for (int64_t b = 0; b < KB; ++b) {
             const int64_t k0 = 32 * b, k1 = k0 + 32 < K ? k0 + 32 : K;
@@ -380,12 +480,7 @@ int mxref_quantize(const void *X, int x_dtype, int64_t R, int64_t K, int fmt, ui
             scales[r * KB + b] = (uint8_t)s;
             for (int64_t k = k0; k < k1; ++k) {
                 const uint8_t c = nearest_code(fmt, ldexp(x[k - k0], 127 - s));
-                if (!packed)
-                    codes[r * ldc + k] = c;
-                else if (k % 2 == 0)
-                    codes[r * ldc + k / 2] = c;
-                else
-                    codes[r * ldc + k / 2] |= (uint8_t)(c << 4);
+                put_code(codes + r * ldc, k, bits, c);
             }
         }
     }

@@ -122,7 +122,7 @@ def native_group_extra(p: mi.Problem):
     group's largest product (measured on the device), so the bound adds
     8 * sum_g 2^(E_g - 13), E_g = floor(log2 max_{k in g} |a_k b_k|)."""
     M, N, K = p.M, p.N, p.K
-    ta, tb, te = oracle.decode_table(p.fmtA), oracle.decode_table(p.fmtB), oracle.decode_table(2)
+    ta, tb, te = oracle.decode_table(p.fmtA), oracle.decode_table(p.fmtB), oracle.decode_table(oracle.FMT_E8M0)
     a = ta[p.A] * np.repeat(te[p.As], 32, axis=1)[:, :K]
     b = tb[p.B] * np.repeat(te[p.Bs], 32, axis=1)[:, :K]
     gmax = np.zeros((M, N))

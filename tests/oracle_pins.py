@@ -32,8 +32,9 @@ import oracle
 import mxinputs
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-FMT_NAMES = {"e4m3": 0, "e5m2": 1, "e8m0": 2}
-_TORCH = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2, 2: torch.float8_e8m0fnu}
+E8 = oracle.FMT_E8M0  # the scale format
+FMT_NAMES = {"e4m3": 0, "e5m2": 1, "e8m0": E8}
+_TORCH = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2, E8: torch.float8_e8m0fnu}
 
 
 def torch_decode(fmt: int) -> np.ndarray:
@@ -80,7 +81,7 @@ def golden_spot_values():
 # ---------------------------------------------------------------- formats --
 
 def pin_tables_match_torch(lib):
-    for fmt in (0, 1, 2):
+    for fmt in (0, 1, E8):
         got = oracle.decode_table(fmt, lib)
         want = torch_decode(fmt)
         assert same(got, want, signed_zero=True), \
@@ -96,7 +97,7 @@ def pin_spot_values(lib):
 def pin_special_counts(lib):
     e4 = oracle.decode_table(0, lib)
     e5 = oracle.decode_table(1, lib)
-    e8 = oracle.decode_table(2, lib)
+    e8 = oracle.decode_table(oracle.FMT_E8M0, lib)
     assert np.isnan(e4).sum() == 2 and np.isinf(e4).sum() == 0
     assert np.isnan(e5).sum() == 6 and np.isinf(e5).sum() == 2
     assert np.isnan(e8).sum() == 1 and np.isinf(e8).sum() == 0
@@ -136,7 +137,7 @@ def pin_bruteforce_fraction(lib):
     recursive-summation bound of the exact rational sum, its fp32 result is
     the correct rounding whenever the double sum is exact, and never more
     than one fp32 ulp away."""
-    dec = {f: torch_decode(f) for f in (0, 1, 2)}
+    dec = {f: torch_decode(f) for f in (0, 1, E8)}
     cases = [(3, 4, 64, 0, 0, False, 0), (2, 3, 96, 1, 0, False, 0), (4, 2, 40, 0, 1, False, 0),
              (3, 3, 256, 1, 1, True, 0), (2, 2, 33, 0, 0, True, 1), (1, 1, 1, 1, 1, False, 0),
              (4, 4, 160, 0, 0, True, 0)]
@@ -150,8 +151,8 @@ def pin_bruteforce_fraction(lib):
                 exact = Fraction(0)
                 mag = Fraction(0)
                 for k in range(K):
-                    t = (_exact_value(p.A[m, k], fa, dec) * _exact_value(p.As[m, k // 32], 2, dec)
-                         * _exact_value(p.B[n, k], fb, dec) * _exact_value(p.Bs[n, k // 32], 2, dec))
+                    t = (_exact_value(p.A[m, k], fa, dec) * _exact_value(p.As[m, k // 32], E8, dec)
+                         * _exact_value(p.B[n, k], fb, dec) * _exact_value(p.Bs[n, k // 32], E8, dec))
                     exact += t
                     mag += abs(t)
                 if acc:
@@ -269,7 +270,7 @@ def pin_scale_doubling(lib):
 def pin_permutation(lib):
     """A a permutation matrix of 1.0 codes with scale bytes 127: C[m,n] is the
     scaled B element at K index pi(m); and the same with B a permutation."""
-    dec = {f: torch_decode(f) for f in (0, 1, 2)}
+    dec = {f: torch_decode(f) for f in (0, 1, E8)}
     g = np.random.Generator(np.random.PCG64(11))
     M = N = 64
     K = 128
@@ -278,13 +279,13 @@ def pin_permutation(lib):
     A = np.zeros((M, K), np.uint8); A[np.arange(M), pi] = 0x38
     As = np.full((M, K // 32), 127, np.uint8)
     r = oracle.gemm_full(A, As, 0, p.B, p.Bs, 1, M, N, K, lib=lib)
-    want = dec[1][p.B[:, pi].T] * dec[2][p.Bs[:, pi // 32].T]
+    want = dec[1][p.B[:, pi].T] * dec[E8][p.Bs[:, pi // 32].T]
     assert same(r["sum"], want), "A = permutation"
     sigma = g.permutation(K)[:N]
     B = np.zeros((N, K), np.uint8); B[np.arange(N), sigma] = 0x38
     Bs = np.full((N, K // 32), 127, np.uint8)
     r = oracle.gemm_full(p.A, p.As, 0, B, Bs, 0, M, N, K, lib=lib)
-    want = dec[0][p.A[:, sigma]] * dec[2][p.As[:, sigma // 32]]
+    want = dec[0][p.A[:, sigma]] * dec[E8][p.As[:, sigma // 32]]
     assert same(r["sum"], want), "B = permutation"
 
 
@@ -297,9 +298,9 @@ def pin_numpy_matmul(lib):
             (48, 17, 96, 0, 1, True, 1), (20, 20, 1000, 1, 1, False, 0))):
         p = mxinputs.random_problem(M, N, K, seed=300 + i, fmtA=fa, fmtB=fb, use_acc=acc,
                                     out_dtype=outd)
-        dec = {f: torch_decode(f) for f in (0, 1, 2)}
-        sa = np.repeat(dec[2][p.As], 32, axis=1)[:, :K]
-        sb = np.repeat(dec[2][p.Bs], 32, axis=1)[:, :K]
+        dec = {f: torch_decode(f) for f in (0, 1, E8)}
+        sa = np.repeat(dec[E8][p.As], 32, axis=1)[:, :K]
+        sb = np.repeat(dec[E8][p.Bs], 32, axis=1)[:, :K]
         a = dec[fa][p.A] * sa
         b = dec[fb][p.B] * sb
         want = a @ b.T
@@ -613,6 +614,159 @@ def pin_quant_e2m1(lib):
     assert int(scales[1, 0]) == 127 + 10 and (unpacked[1, :32] == 7).all()
 
 
+# ------------------------------------------------- e2m3 / e3m2 (FP6) --
+
+FP6 = {"e2m3": 2, "e3m2": 3}
+
+
+def _golden_fp6(name):
+    out = []
+    with open(os.path.join(GOLDEN, f"ocp_fp6_{name}_values.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            code, val = line.split()
+            out.append((int(code, 16), _parse_value(val)))
+    return out
+
+
+def pin_fp6_golden(lib):
+    """The 6-bit decoders against the OCP tables (all 64 codes of each);
+    codes above 63 do not exist."""
+    for name, fmt in FP6.items():
+        table = _golden_fp6(name)
+        assert len(table) == 64
+        for code, val in table:
+            got = lib.mxref_decode(fmt, code)
+            assert same(got, val, signed_zero=True), f"{name} code {code:#x}: {got!r} != {val!r}"
+        assert np.isnan(oracle.decode_table(fmt, lib)[64:]).all()
+
+
+def _unpack6(packed, K):
+    """The test's own reading of a packed 6-bit row: four codes in three
+    bytes, code 4q + i at bits 6i .. 6i + 5 of bytes 3q .. 3q + 2 (little
+    endian)."""
+    p = np.asarray(packed, np.uint32)
+    out = np.empty((p.shape[0], K), np.uint8)
+    for q in range(K // 4):
+        v = p[:, 3 * q] | (p[:, 3 * q + 1] << 8) | (p[:, 3 * q + 2] << 16)
+        for i in range(4):
+            out[:, 4 * q + i] = (v >> (6 * i)) & 63
+    return out
+
+
+def _fp6_as_e4m3(packed, name, K):
+    """Re-encode packed 6-bit codes as e4m3 codes of the same value, using the
+    test's own unpacking and torch's e4m3 table."""
+    e4 = torch_decode(0)
+    vals = np.array([v for _, v in sorted(_golden_fp6(name))])
+    codes = _unpack6(packed, K)
+    out = np.empty(codes.shape, np.uint8)
+    for c in range(64):
+        hit = np.flatnonzero((e4 == vals[c]) & (np.signbit(e4) == np.signbit(vals[c])))
+        assert hit.size, f"{name} value {vals[c]} is not an e4m3 value"
+        out[codes == c] = hit[0]
+    assert same(e4[out], vals[codes], signed_zero=True)
+    return out
+
+
+def pin_fp6_embeds_in_e4m3(lib):
+    """Every e2m3 and e3m2 value is an e4m3 value, so a 6-bit problem and the
+    same problem re-encoded as e4m3 (unpacked by the test, decoded by torch)
+    have the same exact sums, bit for bit; this ties the packed path (bit
+    order, row pitch, decode) to the pinned 8-bit path.  Mixed pairs too."""
+    cases = ((5, 7, 64, 2, 2, 1), (3, 4, 1056, 2, 2, 2), (4, 3, 96, 3, 3, 3), (6, 2, 128, 2, 0, 4),
+             (2, 5, 160, 1, 3, 5), (1, 1, 32, 3, 2, 6), (3, 3, 64, 4, 2, 7))
+    names = {2: "e2m3", 3: "e3m2"}
+    for (M, N, K, fa, fb, seed) in cases:
+        p = mxinputs.random_problem(M, N, K, seed=1200 + seed, fmtA=fa, fmtB=fb, scale_lo=100,
+                                    scale_hi=150, sigma=2.0)
+        r = oracle.gemm_full(p.A, p.As, fa, p.B, p.Bs, fb, M, N, K, nthreads=2, lib=lib)
+
+        def as8(x, f):
+            if f in names:
+                return _fp6_as_e4m3(x, names[f], K), 0
+            if f == 4:
+                return _e2m1_as_e4m3(x), 0
+            return x, f
+        A8, f8a = as8(p.A, fa)
+        B8, f8b = as8(p.B, fb)
+        r8 = oracle.gemm_full(A8, p.As, f8a, B8, p.Bs, f8b, M, N, K, nthreads=2, lib=lib)
+        assert np.array_equal(r["sum"], r8["sum"]), f"6-bit vs e4m3 re-encoding, case {seed}"
+        assert np.array_equal(r["mag"], r8["mag"])
+
+
+def pin_fp6_integer_gemm(lib):
+    """Integer-valued e2m3 codes (0, +-1 .. +-7, all exact in e2m3), unit
+    scales: C equals the int64 matrix product of the values the test packed."""
+    g = np.random.Generator(np.random.PCG64(78))
+    M, N, K = 17, 21, 544
+    ia = g.integers(-7, 8, size=(M, K))
+    ib = g.integers(-7, 8, size=(N, K))
+    A = mxinputs.quantize(ia.astype(np.float32), 2)
+    B = mxinputs.quantize(ib.astype(np.float32), 2)
+    assert A.shape == (M, 3 * K // 4)
+    assert np.array_equal(_unpack6(A, K) & 31, np.array([[{0: 0, 1: 8, 2: 16, 3: 20, 4: 24, 5: 26,
+                                                           6: 28, 7: 30}[abs(v)] for v in row]
+                                                         for row in ia]))
+    As = np.full((M, K // 32), 127, np.uint8)
+    Bs = np.full((N, K // 32), 127, np.uint8)
+    r = oracle.gemm_full(A, As, 2, B, Bs, 2, M, N, K, nthreads=3, lib=lib)
+    want = ia.astype(np.int64) @ ib.astype(np.int64).T
+    assert np.array_equal(r["sum"], want.astype(np.float64)), "e2m3 integer gemm"
+
+
+def pin_fp6_fraction(lib):
+    """Tiny random 6-bit problems against exact rational sums (values from
+    the golden tables, the test's own unpacking)."""
+    for i, (M, N, K, name) in enumerate(((2, 3, 64, "e2m3"), (3, 2, 96, "e3m2"), (1, 4, 32, "e2m3"))):
+        fmt = FP6[name]
+        vals = {c: Fraction(v) for c, v in _golden_fp6(name)}
+        p = mxinputs.random_problem(M, N, K, seed=1250 + i, fmtA=fmt, fmtB=fmt, scale_lo=110,
+                                    scale_hi=140)
+        r = oracle.gemm_full(p.A, p.As, fmt, p.B, p.Bs, fmt, M, N, K, nthreads=1, lib=lib)
+        ca, cb = _unpack6(p.A, K), _unpack6(p.B, K)
+        for m in range(M):
+            for n in range(N):
+                exact = sum(vals[int(ca[m, k])] * Fraction(2) ** (int(p.As[m, k // 32]) - 127)
+                            * vals[int(cb[n, k])] * Fraction(2) ** (int(p.Bs[n, k // 32]) - 127)
+                            for k in range(K))
+                assert Fraction(r["sum"][m, n]) == exact, f"{name} case {i} ({m},{n})"
+
+
+def pin_quant_fp6(lib):
+    """6-bit quantization: the scale byte satisfies the block exponent's
+    defining inequality with MAX = 7.5 (e2m3) or 28 (e3m2), and every code
+    is the generator's independent nearest-even rounding of x * 2^-e,
+    packed four per three bytes; zero blocks get byte 0 and keep -0."""
+    g = np.random.Generator(np.random.PCG64(62))
+    R, K = 7, 256
+    for name, fmt in FP6.items():
+        mx = 7.5 if fmt == 2 else 28.0
+        X = (g.standard_normal((R, K)) * np.exp2(g.integers(-30, 30, size=(R, 1)))).astype(np.float32)
+        X[0, :32] = 0.0
+        X[0, 5] = -0.0
+        X[1, :32] = np.float32(mx) * np.float32(2.0 ** 7)
+        codes, scales = oracle.quantize(X, fmt, lib=lib)
+        assert codes.shape == (R, 3 * K // 4)
+        unpacked = _unpack6(codes, K)
+        for r in range(R):
+            for b in range(K // 32):
+                blk = X[r, 32 * b:32 * b + 32].astype(np.float64)
+                amax = np.abs(blk).max()
+                s = int(scales[r, b])
+                if amax == 0:
+                    assert s == 0
+                else:
+                    e = s - 127
+                    assert amax <= mx * 2.0 ** e and not amax <= mx * 2.0 ** (e - 1), (name, r, b, s)
+                want = mxinputs._quantize_fp6((blk * 2.0 ** (127 - s)).astype(np.float32), fmt)
+                assert np.array_equal(unpacked[r, 32 * b:32 * b + 32], want), (name, r, b)
+        assert unpacked[0, 5] == 32 and unpacked[0, 4] == 0
+        assert int(scales[1, 0]) == 127 + 7 and (unpacked[1, :32] == 31).all()
+
+
 ALL_PINS = [pin_tables_match_torch, pin_spot_values, pin_special_counts, pin_bf16_rne,
             pin_bruteforce_fraction, pin_pairwise_products, pin_closed_form,
             pin_integer_gemm, pin_scale_doubling, pin_permutation, pin_numpy_matmul,
@@ -620,4 +774,6 @@ ALL_PINS = [pin_tables_match_torch, pin_spot_values, pin_special_counts, pin_bf1
             pin_quant_rne_vs_torch, pin_quant_block_exponent, pin_quant_scale_invariance,
             pin_quant_matches_generator, pin_quant_bf16_input, pin_quant_ragged_and_nonfinite,
             pin_e2m1_golden, pin_e2m1_embeds_in_e4m3, pin_e2m1_integer_gemm, pin_e2m1_fraction,
+            pin_fp6_golden, pin_fp6_embeds_in_e4m3, pin_fp6_integer_gemm, pin_fp6_fraction,
+            pin_quant_fp6,
             pin_quant_e2m1]

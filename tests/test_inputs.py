@@ -94,3 +94,26 @@ def test_e2m1_quantiser_is_nearest_even():
     assert np.array_equal(got, want)
     codes = np.random.Generator(np.random.PCG64(5)).integers(0, 16, size=(3, 64), dtype=np.uint8)
     assert np.array_equal(mi.unpack_e2m1(mi.pack_e2m1(codes)), codes)
+
+
+def test_pack_bits_round_trip_and_layout():
+    g = np.random.Generator(np.random.PCG64(5))
+    for bits in (4, 6, 8):
+        c = g.integers(0, 1 << bits, size=(3, 64), dtype=np.uint8)
+        p = mi.pack_bits(c, bits)
+        assert p.shape == (3, 64 * bits // 8)
+        assert np.array_equal(mi.unpack_bits(p, bits, 64), c)
+    # e2m1: the even k in the low nibble; 6-bit: code 4q+i at bits 6i of bytes 3q..3q+2
+    assert np.array_equal(mi.pack_bits(np.array([[1, 2]], np.uint8), 4), [[0x21]])
+    assert np.array_equal(mi.pack_bits(np.array([[1, 2, 3, 4]], np.uint8), 6),
+                          [[1 | (2 << 6) & 0xff, (2 >> 2) | (3 << 4) & 0xff, (3 >> 4) | (4 << 2)]])
+
+
+def test_fp6_quantize_grid_and_ties():
+    for fmt, mx in ((mi.FMT_E2M3, 7.5), (mi.FMT_E3M2, 28.0)):
+        grid = mi._fp6_grid(fmt)
+        assert grid[0] == 0 and grid[-1] == mx and np.all(np.diff(grid) > 0)
+        mids = (grid[:-1] + grid[1:]) / 2
+        c = mi._quantize_fp6(mids.astype(np.float32), fmt)
+        assert np.all(c % 2 == 0)  # ties go to the even code
+        assert mi._quantize_fp6(np.array([1e9, -1e9], np.float32), fmt).tolist() == [31, 63]

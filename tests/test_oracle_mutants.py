@@ -34,18 +34,25 @@ MUTANTS = {
     "mag_signed": ("mag += fabs(prod);", "mag += prod;"),
     "quant_ties_to_odd": ("(d == bd && (c & 1) == 0)", "(d == bd && (c & 1) == 1)"),
     "quant_exponent_plus_one": ("s = block_exponent(fmt, amax) + 127;", "s = block_exponent(fmt, amax) + 128;"),
-    "quant_sign_dropped": ("(signbit(v) ? (fmt == MXREF_FMT_E2M1 ? 0x8 : 0x80) : 0)", "0"),
+    "quant_sign_dropped": ("(signbit(v) ? ncodes : 0)", "0"),
     "quant_scale_inverted": ("ldexp(x[k - k0], 127 - s)", "ldexp(x[k - k0], s - 127)"),
-    "quant_e4m3_max_480": ("return fmt == MXREF_FMT_E4M3 ? 448.0", "return fmt == MXREF_FMT_E4M3 ? 480.0"),
-    "e2m1_nibble_order_a": ("(a[k / 2] >> (4 * (k % 2)))", "(a[k / 2] >> (4 * (1 - k % 2)))"),
-    "e2m1_nibble_order_b": ("(b[k / 2] >> (4 * (k % 2)))", "(b[k / 2] >> (4 * (1 - k % 2)))"),
+    "quant_e4m3_max_480": ("case MXREF_FMT_E4M3: return 448.0;", "case MXREF_FMT_E4M3: return 480.0;"),
+    "packed_bit_order": ("const unsigned sh = (unsigned)(bit % 8);\n    unsigned v = row[bit / 8] >> sh;",
+                         "const unsigned sh = (unsigned)(8 - bits - bit % 8) % 8u;\n    unsigned v = row[bit / 8] >> sh;"),
+    "packed_a_read_as_b_width": ("const unsigned ca = code_at(a, k, j->bitsA);", "const unsigned ca = code_at(a, k, j->bitsB);"),
+    "packed_straddle_dropped": ("    if (sh + (unsigned)bits > 8u)\n        v |= ", "    if (0)\n        v |= "),
     "e2m1_bias_0": ("(int)e - 1 - 1", "(int)e - 0 - 1"),
     "e2m1_no_subnormal": ("v = ldexp((double)m, 1 - 1 - 1);", "v = 0.0;"),
-    "e2m1_row_pitch_k": ("base.ldA = base.packA ? (K + 1) / 2 : K;", "base.ldA = K;"),
+    "packed_row_pitch_k": ("base.ldA = row_bytes(K, base.bitsA);", "base.ldA = K;"),
+    "e2m3_bias_0": ("(int)e - 1 - 3); /* (1+m/8) * 2^(e-1) */", "(int)e - 0 - 3); /* (1+m/8) * 2^(e-1) */"),
+    "e3m2_mantissa_bits_3": ("unsigned s = (c >> 5) & 1u, e = (c >> 2) & 7u, m = c & 3u;",
+                             "unsigned s = (c >> 5) & 1u, e = (c >> 3) & 3u, m = c & 7u;"),
+    "e2m3_no_subnormal": ("v = ldexp((double)m, 1 - 1 - 3);            /* m/8 */", "v = 0.0;"),
+    "quant_fp6_max_6": ("case MXREF_FMT_E2M3: return 7.5;", "case MXREF_FMT_E2M3: return 6.0;"),
     "e2m1_sign_dropped": ("    return s ? -v : v;\n}\n\n/* e8m0", "    return v;\n}\n\n/* e8m0"),
-    "quant_e2m1_max_4": ("fmt == MXREF_FMT_E2M1 ? 6.0 : 57344.0", "fmt == MXREF_FMT_E2M1 ? 4.0 : 57344.0"),
-    "quant_e2m1_sign_bit_7": ("(fmt == MXREF_FMT_E2M1 ? 0x8 : 0x80)", "0x80"),
-    "quant_e2m1_nibbles_swapped": ("else if (k % 2 == 0)", "else if (k % 2 == 1)"),
+    "quant_e2m1_max_4": ("default: return 6.0; /* e2m1 */", "default: return 4.0; /* e2m1 */"),
+    "quant_sign_bit_7": ("(signbit(v) ? ncodes : 0)", "(signbit(v) ? 0x80 : 0)"),
+    "quant_packed_bit_order": ("    row[bit / 8] |= (uint8_t)(c << sh);", "    row[bit / 8] |= (uint8_t)(c << (8 - bits - sh) % 8u);"),
     "quant_zero_block_scale": ("int s = 0;\n            if (amax > 0.0) {", "int s = 127;\n            if (amax > 0.0) {"),
 }
 
