@@ -12,6 +12,8 @@ Also reported on the same line:
   * skinny: the M=64, N=28672, K=8192 workload in GB/s of algorithmic bytes
     (A, scales and B read once, C written once), B rotated over 3 copies;
   * native: the same 8192^3 workload on the native scaled-MFMA variant;
+  * mxfp4 / mxfp6: the 8192^3 shape with e2m1 / e2m3 operands (exact on the
+    scaled MFMA), and the M = 64 decode shape with them;
   * mx_quantize: MX block quantization of the skinny workload's fp32 weight
     (28672 x 8192 -> e4m3 codes + e8m0 scales) in GB/s of algorithmic bytes
     (X read once, codes and scales written once), inputs rotated over 3
@@ -57,7 +59,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}  # MI355X published dense MFMA peaks
+# MI355X published dense MFMA peaks; fp6 runs at the fp4 rate
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 PEAK_HBM_GBS = 8000.0
 METRIC = "MXFP8 GEMM TFLOP/s at 8192\u00b3 (% of dense MXFP8 peak); GB/s (% HBM) at M=64"
 KERNEL_SOURCES = ["level_dsl_amd/csrc/" + f for f in (
@@ -512,6 +515,26 @@ def main():
                      "launch_mean_us": round(mean_4 * 1e6, 2)}}
     log(f"bench: e2m1 {out['mxfp4']['value']} TFLOP/s")
 
+    # ---- e2m3 (FP6) operands on the same shape --------------------------------
+    # N(0, 1) -> e2m3 (RNE, saturating at 7.5), scales U{120..134}, bf16 out;
+    # exact on the scaled MFMA like e2m1
+    p6 = mi.random_problem(8192, 8192, 8192, seed=860, fmtA=mi.FMT_E2M3, fmtB=mi.FMT_E2M3,
+                           out_dtype=mi.OUT_BF16)
+    log("bench: e2m3 8192^3 generated")
+    wall_6, mean_6 = bench_gemm(gemm, p6, L.MXGEMM_VARIANT_AUTO, steps, warmup, 3)
+    del p6
+    out["mxfp6"] = {
+        "value": round(flops * steps / wall_6 / 1e12, 2), "unit": "TFLOP/s",
+        "config": {"M": 8192, "N": 8192, "K": 8192, "A": "e2m3 (4 per 3 bytes)",
+                   "B": "e2m3 (4 per 3 bytes)",
+                   "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (e2m3: exact)", "out": "bf16 (RNE)"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / mean_6 / 1e12, 2),
+                     "peak": PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
+                     "frac": round(flops / mean_6 / 1e12 / PEAK_TFLOPS["fp4"], 4),
+                     "kernel": "mxg::large::kernel<2,2,true,false,false>",
+                     "launch_mean_us": round(mean_6 * 1e6, 2)}}
+    log(f"bench: e2m3 {out['mxfp6']['value']} TFLOP/s")
+
     cpu_src = p
     # ---- skinny: M=64, N=28672, K=8192, fp32 out --------------------------------
     ps = mi.workload(3)
@@ -550,6 +573,23 @@ def main():
                      "launch_mean_us": round(mean_4s * 1e6, 2)},
         "algorithmic_bytes": b4}
     log(f"bench: e2m1 decode shape {out['mxfp4_skinny_m64']['value']} GB/s")
+
+    # ---- and with e2m3 operands (four codes per three bytes) --------------------
+    p6s = mi.random_problem(64, 28672, 8192, seed=871, fmtA=mi.FMT_E2M3, fmtB=mi.FMT_E2M3)
+    log("bench: e2m3 decode shape generated")
+    b6 = (64 + 28672) * (3 * 8192 // 4 + 8192 // 32) + 64 * 28672 * 4
+    wall_6s, mean_6s = bench_gemm(gemm, p6s, L.MXGEMM_VARIANT_AUTO, sk_steps, warmup, 3)
+    del p6s
+    out["mxfp6_skinny_m64"] = {
+        "value": round(b6 * sk_steps / wall_6s / 1e9, 1), "unit": "GB/s",
+        "config": {"M": 64, "N": 28672, "K": 8192, "A": "e2m3", "B": "e2m3", "out": "f32"},
+        "roofline": {"bound": "hbm", "achieved": round(b6 / mean_6s / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(b6 / mean_6s / 1e9 / PEAK_HBM_GBS, 4),
+                     "kernel": "mxg::skinny::kernel<2,2,2,4,false> (LDS scale table)",
+                     "launch_mean_us": round(mean_6s * 1e6, 2)},
+        "algorithmic_bytes": b6}
+    log(f"bench: e2m3 decode shape {out['mxfp6_skinny_m64']['value']} GB/s")
 
     # ---- MX block quantization of the skinny weight ------------------------------
     R, K = QUANT_SHAPE

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libmxgemm.so")
 
 MXGEMM_FMT_E4M3 = 0
 MXGEMM_FMT_E5M2 = 1
+MXGEMM_FMT_E2M3 = 2
 MXGEMM_FMT_E2M1 = 4
 MXGEMM_OUT_F32 = 0
 MXGEMM_OUT_BF16 = 1
@@ -244,14 +245,15 @@ class Gemm:
 
     def __call__(self, A, A_scale, fmtA, B, B_scale, fmtB, C, use_acc=False,
                  out_dtype=MXGEMM_OUT_F32, stream=None):
-        # e2m1 operands hold two codes per byte along K
+        # sub-byte operands are packed along K: e2m1 two codes per byte,
+        # e2m3 four codes per three bytes
         M, ka = A.shape
         N = B.shape[0]
-        K = 2 * ka if fmtA == MXGEMM_FMT_E2M1 else ka
-        kb = K // 2 if fmtB == MXGEMM_FMT_E2M1 else K
+        K = 2 * ka if fmtA == MXGEMM_FMT_E2M1 else (4 * ka // 3 if fmtA == MXGEMM_FMT_E2M3 else ka)
+        kb = K // 2 if fmtB == MXGEMM_FMT_E2M1 else (3 * K // 4 if fmtB == MXGEMM_FMT_E2M3 else K)
         if B.shape[1] != kb or A_scale.shape != (M, K // 32) or B_scale.shape != (N, K // 32):
             raise ValueError("operand shapes do not match (A MxK, B NxK, scales K/32; "
-                             "e2m1: K/2 bytes per row)")
+                             "e2m1: K/2 bytes per row, e2m3: 3K/4)")
         want = torch.float32 if out_dtype == MXGEMM_OUT_F32 else torch.bfloat16
         if C.shape != (M, N) or C.dtype != want:
             raise ValueError(f"C must be ({M}, {N}) {want}")

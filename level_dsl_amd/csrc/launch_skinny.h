@@ -39,12 +39,12 @@ hipError_t launch_skinny_mt(const mxg::GemmArgs &a, hipStream_t s)
                         : launch_skinny_s<FA, FB, MT, false>(a, s);
 }
 
-// e2m1 runs only ceil(M/16) tiles of A; the fp8 native variant (an opt-in)
+// e2m1 and e2m3 run only ceil(M/16) tiles of A; the fp8 native variant (an opt-in)
 // keeps all four, which holds down the number of kernels built
 template <int FA, int FB>
 hipError_t launch_skinny(const mxg::GemmArgs &a, hipStream_t s)
 {
-    if constexpr (FA == 4) {
+    if constexpr (FA == 4 || FA == 2) {
         switch ((a.M + 15) / 16) {
         case 1: return launch_skinny_mt<FA, FB, 1>(a, s);
         case 2: return launch_skinny_mt<FA, FB, 2>(a, s);

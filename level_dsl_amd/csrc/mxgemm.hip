@@ -150,13 +150,26 @@ int choose_splits_large(int forced, int tiles, int units, int unit_stages, size_
     return std::max(s, 1);
 }
 
+// Bytes of an operand row of K codes: e2m1 packs two codes per byte, e2m3
+// four codes per three bytes, e4m3 / e5m2 one per byte.
+int64_t row_bytes(int fmt, int64_t K)
+{
+    return fmt == MXGEMM_FMT_E2M1 ? K / 2 : fmt == MXGEMM_FMT_E2M3 ? 3 * K / 4 : K;
+}
+
+// f: 2 fmtA + fmtB for the fp8 pairs (0..3), kF4 for e2m1 x e2m1, kF6 for
+// e2m3 x e2m3 (both always on the scaled MFMA)
+constexpr int kF4 = 4, kF6 = 5;
+
 hipError_t dispatch(bool native, bool skinny, int f, const mxg::GemmArgs &a, hipStream_t s)
 {
     if (skinny) {
-        if (!native) return mxg::launch_stream_exact(f, a, s);
-        return f == 4 ? mxg::launch_skinny_e2m1(a, s) : mxg::launch_skinny_native(f, a, s);
+        if (f == kF4) return mxg::launch_skinny_e2m1(a, s);
+        if (f == kF6) return mxg::launch_skinny_e2m3(a, s);
+        return native ? mxg::launch_skinny_native(f, a, s) : mxg::launch_stream_exact(f, a, s);
     }
-    if (f == 4) return mxg::launch_large_e2m1(a, s);  // e2m1 x e2m1 (always native)
+    if (f == kF4) return mxg::launch_large_e2m1(a, s);
+    if (f == kF6) return mxg::launch_large_e2m3(a, s);
     return native ? mxg::launch_large_native(f, a, s) : mxg::launch_large_exact(f, a, s);
 }
 
@@ -171,7 +184,8 @@ const char *mxgemm_status_string(int code)
     switch (code) {
     case MXGEMM_OK: return "ok";
     case MXGEMM_ERR_NULL: return "a required pointer is NULL";
-    case MXGEMM_ERR_FMT: return "operand format must be e4m3 (0), e5m2 (1) or e2m1 (4, with e2m1)";
+    case MXGEMM_ERR_FMT:
+        return "operand format must be e4m3 (0), e5m2 (1), e2m3 (2, with e2m3) or e2m1 (4, with e2m1)";
     case MXGEMM_ERR_DTYPE: return "out_dtype must be f32 (0) or bf16 (1) and use_acc 0 or 1";
     case MXGEMM_ERR_SHAPE: return "M, N, K out of range or K not a multiple of 32";
     case MXGEMM_ERR_ALIGN: return "A, B and C must be 16-byte aligned";
@@ -260,9 +274,13 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const 
                          int64_t K, int use_acc, int out_dtype)
 {
     if (!A || !A_scale || !B || !B_scale || !C) return MXGEMM_ERR_NULL;
-    if ((fmtA != MXGEMM_FMT_E4M3 && fmtA != MXGEMM_FMT_E5M2 && fmtA != MXGEMM_FMT_E2M1) ||
-        (fmtB != MXGEMM_FMT_E4M3 && fmtB != MXGEMM_FMT_E5M2 && fmtB != MXGEMM_FMT_E2M1) ||
-        ((fmtA == MXGEMM_FMT_E2M1) != (fmtB == MXGEMM_FMT_E2M1)))
+    auto known = [](int f) {
+        return f == MXGEMM_FMT_E4M3 || f == MXGEMM_FMT_E5M2 || f == MXGEMM_FMT_E2M3 ||
+               f == MXGEMM_FMT_E2M1;
+    };
+    // the sub-byte formats pair only with themselves; e3m2 is not accepted
+    if (!known(fmtA) || !known(fmtB) || ((fmtA == MXGEMM_FMT_E2M1) != (fmtB == MXGEMM_FMT_E2M1)) ||
+        ((fmtA == MXGEMM_FMT_E2M3) != (fmtB == MXGEMM_FMT_E2M3)))
         return MXGEMM_ERR_FMT;
     if ((out_dtype != MXGEMM_OUT_F32 && out_dtype != MXGEMM_OUT_BF16) ||
         (use_acc != 0 && use_acc != 1))
@@ -272,9 +290,9 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const 
         return MXGEMM_ERR_SHAPE;
     if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15u) return MXGEMM_ERR_ALIGN;
     const uint64_t csize = (uint64_t)M * (uint64_t)N * (out_dtype == MXGEMM_OUT_F32 ? 4u : 2u);
-    const uint64_t row_bytes = fmtA == MXGEMM_FMT_E2M1 ? (uint64_t)K / 2 : (uint64_t)K;
-    if (overlaps(C, csize, A, (uint64_t)M * row_bytes) ||
-        overlaps(C, csize, B, (uint64_t)N * row_bytes) ||
+    const uint64_t rb = (uint64_t)row_bytes(fmtA, K);
+    if (overlaps(C, csize, A, (uint64_t)M * rb) ||
+        overlaps(C, csize, B, (uint64_t)N * rb) ||
         overlaps(C, csize, A_scale, (uint64_t)M * (K / 32)) ||
         overlaps(C, csize, B_scale, (uint64_t)N * (K / 32)))
         return MXGEMM_ERR_ALIAS;
@@ -313,10 +331,10 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
         constexpr int64_t H = mxg::skinny::MAX_M;
         const int64_t tiles_n = (N + mxg::skinny::BN - 1) / mxg::skinny::BN;
         if (M <= 2 * H || (M <= 3 * H && tiles_n <= 64)) {
-            const int64_t row_bytes = fmtA == MXGEMM_FMT_E2M1 ? K / 2 : K;
+            const int64_t rb = row_bytes(fmtA, K);
             const size_t esz = out_dtype == MXGEMM_OUT_F32 ? 4 : 2;
             for (int64_t r = 0; r < M; r += H) {
-                const int rc_r = run_impl(h, (const uint8_t *)A + r * row_bytes,
+                const int rc_r = run_impl(h, (const uint8_t *)A + r * rb,
                                           A_scale + r * (K / 32), fmtA, B, B_scale, fmtB,
                                           (uint8_t *)C + (size_t)r * N * esz, std::min(H, M - r), N,
                                           K, use_acc, out_dtype, stream, ws, ws_bytes, strict);
@@ -332,11 +350,12 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
     a.B = (const uint8_t *)B;
     a.Bs = B_scale;
     a.C = C;
-    // e2m1: two codes per byte along K; the kernels see K as the row pitch in bytes
-    const bool fp4 = fmtA == MXGEMM_FMT_E2M1;
+    // sub-byte codes are packed along K; the kernels see K as the row pitch in bytes
+    const bool fp4 = fmtA == MXGEMM_FMT_E2M1, fp6 = fmtA == MXGEMM_FMT_E2M3;
     a.M = (int)M;
     a.N = (int)N;
-    a.K = (int)(fp4 ? K / 2 : K);
+    a.K = (int)row_bytes(fmtA, K);
+    const int stage_bytes = fp6 ? 96 : 128;  // bytes of a row per K stage of the scaled-MFMA kernels
     a.KB = (int)(K / 32);
     a.use_acc = use_acc;
     a.out_bf16 = out_dtype == MXGEMM_OUT_BF16;
@@ -354,10 +373,11 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
     else
         skinny = variant == MXGEMM_VARIANT_SKINNY || variant == MXGEMM_VARIANT_SKINNY_NATIVE;
     if (skinny && M > mxg::skinny::MAX_M) return MXGEMM_ERR_VARIANT;
-    if (fp4) {
-        // e2m1 x e2m1 runs on the scaled MFMA, which is exact for it; for
-        // M <= 64 on the small-M kernel's native mode (measured faster than
-        // the 256 x 256 kernel, split or not, from N = 3584 to 28672)
+    if (fp4 || fp6) {
+        // e2m1 x e2m1 and e2m3 x e2m3 run on the scaled MFMA, which is exact
+        // for them; for M <= 64 on the small-M kernel's native mode (measured
+        // faster than the 256 x 256 kernel for e2m1, split or not, from
+        // N = 3584 to 28672)
         native = true;
     }
     a.splits = 1;
@@ -366,7 +386,7 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
     if (skinny) {
         a.tiles_m = 1;
         a.tiles_n = (int)((N + mxg::skinny::BN - 1) / mxg::skinny::BN);
-        const int nk = native ? (a.K + mxg::skinny::BK - 1) / mxg::skinny::BK
+        const int nk = native ? (a.K + stage_bytes - 1) / stage_bytes
                               : (int)((K + mxg::stream::BK - 1) / mxg::stream::BK);
         a.splits = choose_splits(h->splits, a.tiles_n, nk, native ? 4 : 8);
         if (a.splits > 1 && !ws) {
@@ -382,7 +402,8 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
         a.tiles_n = (int)((N + mxg::large::BN - 1) / mxg::large::BN);
         const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
         if (tiles <= mxg::stream::MAX_SPLITS_TILES / 2) {
-            const int nk = (int)((K + mxg::large::BK - 1) / mxg::large::BK);
+            // stages as the kernel counts them (bytes of a row per stage)
+            const int nk = (a.K + stage_bytes - 1) / stage_bytes;
             const bool scale16 = !native && a.scale_dword == 2;  // the kernel's SCALE16
             const int unit = scale16 ? mxg::large::WINDOW : 1;
             a.splits = choose_splits_large(h->splits, (int)tiles, nk / unit, unit, ws_bytes);
@@ -399,7 +420,7 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
             }
         }
     }
-    const int f = fp4 ? 4 : fmtA * 2 + fmtB;
+    const int f = fp4 ? kF4 : fp6 ? kF6 : fmtA * 2 + fmtB;
     const hipError_t e = dispatch(native, skinny, f, a, stream);
     return e == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
 }

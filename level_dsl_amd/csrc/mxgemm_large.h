@@ -125,6 +125,18 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     constexpr bool FP4 = FA == 4;
     static_assert(FP4 == (FB == 4), "e2m1 pairs only with e2m1");
     static_assert(!FP4 || (NATIVE && !SCALE16), "e2m1 runs on the scaled MFMA");
+    // e2m3 operands (format 2, four codes per three bytes): every product of
+    // a 32-element block fits the scaled MFMA's 8-product window as well, so
+    // they too run on it.  A stage is 128 codes, 96 bytes of a row: its four
+    // 24-byte blocks sit in LDS padded to 32 bytes (LDS chunks 2b and 2b + 1
+    // hold bytes 24b .. 24b + 15 and 24b + 16 .. 24b + 31 of the stage, the
+    // last 8 unused), so that the lane half taking block b reads one whole
+    // chunk and the first half of the next.  Scales and MFMA steps are laid
+    // out as in the fp8 native mode (two 64-code steps per stage).
+    constexpr bool FP6 = FA == 2;
+    static_assert(FP6 == (FB == 2), "e2m3 pairs only with e2m3");
+    static_assert(!FP6 || (NATIVE && !SCALE16), "e2m3 runs on the scaled MFMA");
+    constexpr int SB = FP6 ? 96 : BK;                     // bytes of a row per stage
     constexpr int SPS = FP4 ? 8 : 4;                     // scale bytes per row and stage
     constexpr int BLOCKS = NATIVE && !FP4 ? 2 : 4;        // blocks per stage
     constexpr int MF = NATIVE ? SUB_M * SUB_N : 2 * SUB_M * SUB_N;  // MFMAs per block
@@ -151,7 +163,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int lrow = lane & 31, khalf = lane >> 5;
-    const int nk_all = (K + BK - 1) / BK;
+    const int nk_all = (K + SB - 1) / SB;
     constexpr int SPLIT_UNIT = SCALE16 ? WINDOW : 1;  // stages a split boundary is a multiple of
     const int nu_all = nk_all / SPLIT_UNIT;           // SCALE16 needs K % 512 == 0: no remainder
     const int ks0 = SPLIT ? (int)((int64_t)sp * nu_all / p.splits) * SPLIT_UNIT : 0;
@@ -169,15 +181,19 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // read as zero (every offset is out of range), so the call needs no guard.
     const int gc0 = (lane & 7) ^ (lane >> 3);  // chunk for even segments; odd: gc0 ^ 1
     const uint32_t grow = (uint32_t)(8 * SEGS_PER_WAVE * wave + (lane >> 3)) * K;
-    // operand OP (0: A, 1: B) of the stage starting at local K offset kl into LDS stage st
-    auto gload = [&](int st, int kl, auto OP) MXG_INLINE {
+    // operand OP (0: A, 1: B) of local stage kt into LDS stage st
+    auto gload = [&](int st, int kt, auto OP) MXG_INLINE {
         constexpr int op = decltype(OP)::value;
-        const int k0 = kl + ks0 * BK;
+        const int k0 = (kt + ks0) * SB;
 #pragma unroll
         for (int j = 0; j < SEGS_PER_WAVE; ++j) {
             const int s = SEGS_PER_WAVE * wave + j;
             const int c = gc0 ^ (j & 1);
-            const uint32_t off = k0 + 16 * c < K ? grow + (uint32_t)(8 * j) * K + 16 * c + k0 : kOob;
+            // byte of the stage that LDS chunk c starts with, and whether its
+            // data exist (e2m3: the chunk's 24-byte block lies in the row)
+            const int g = FP6 ? 24 * (c >> 1) + 16 * (c & 1) : 16 * c;
+            const bool in = FP6 ? k0 + 24 * (c >> 1) < K : k0 + g < K;
+            const uint32_t off = in ? grow + (uint32_t)(8 * j) * K + g + k0 : kOob;
             load16_lds(op == 0 ? rA : rB, &lds[st][op][s * SEG], off);
         }
     };
@@ -275,6 +291,24 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             for (int j = 0; j < SUB_N; ++j) {
                 const v4i x = *reinterpret_cast<const v4i *>(lb + j * 32 * BK + o);
                 f.b[j] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+            }
+        } else if constexpr (FP6) {
+            // step blk: lane half h takes block 2 blk + h, LDS chunk 2 (2 blk + h)
+            // (16 bytes) and the first 8 bytes of the next: its 32 codes in
+            // operand dwords 0..5
+            const int pc = 2 * (2 * blk + khalf);
+            const uint32_t o0 = ((pc ^ sw) << 4), o1 = (((pc + 1) ^ sw) << 4);
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i) {
+                const v4i lo = *reinterpret_cast<const v4i *>(la + i * 32 * BK + o0);
+                const v2i hi = *reinterpret_cast<const v2i *>(la + i * 32 * BK + o1);
+                f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) {
+                const v4i lo = *reinterpret_cast<const v4i *>(lb + j * 32 * BK + o0);
+                const v2i hi = *reinterpret_cast<const v2i *>(lb + j * 32 * BK + o1);
+                f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
             }
         } else if constexpr (NATIVE) {
             const int c0 = blk * 4 + khalf;  // K 64blk+16h .. +15; chunk c0 + 2: K +32
@@ -447,7 +481,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             if constexpr (blk + 1 < BLOCKS) {
                 read_block(st, blk + 1, raw, nxt);
                 // B tile of stage kt+1 (its buffer was freed at the last barrier)
-                if constexpr (blk == 0 && !NATIVE) gload(st ^ 1, (kt + 1) * BK, int_c<1>{});
+                if constexpr (blk == 0 && !NATIVE) gload(st ^ 1, kt + 1, int_c<1>{});
                 mfma_range(BLK, int_c<0>{}, int_c<MF>{}, cur, ksa, ksb, ksa2, ksb2);
                 prep_block(int_c<blk + 1>{}, raw, csa, csb, nxt);
                 if constexpr (blk == 0 && !NATIVE)
@@ -463,8 +497,8 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                 wait_vmem();
                 __syncthreads();
                 read_block(st ^ 1, 0, raw, nxt);
-                gload(st, (kt + 2) * BK, int_c<0>{});  // A tile of stage kt+2
-                if constexpr (NATIVE) gload(st, (kt + 2) * BK, int_c<1>{});  // and its B tile
+                gload(st, kt + 2, int_c<0>{});  // A tile of stage kt+2
+                if constexpr (NATIVE) gload(st, kt + 2, int_c<1>{});  // and its B tile
                 // scale dwords of stage kt+1
                 if constexpr (SCALE16) {
                     if constexpr (ss == WINDOW - 1) {
@@ -514,8 +548,8 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     }
     wait_vmem();
     __syncthreads();
-    gload(1, BK, int_c<0>{});  // exact mode: stage 1's B tile follows in stage 0's first block
-    if constexpr (NATIVE) gload(1, BK, int_c<1>{});
+    gload(1, 1, int_c<0>{});  // exact mode: stage 1's B tile follows in stage 0's first block
+    if constexpr (NATIVE) gload(1, 1, int_c<1>{});
     if constexpr (SCALE16) {
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) csa[i] = (uint32_t)wa[i][0];

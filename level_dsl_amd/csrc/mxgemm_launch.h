@@ -17,9 +17,11 @@ hipError_t launch_large_exact(int f, const GemmArgs &a, hipStream_t s);   // k_l
 hipError_t launch_large_exact_b(int f, const GemmArgs &a, hipStream_t s); // k_large_exact_b.hip (f = 2, 3)
 hipError_t launch_large_native(int f, const GemmArgs &a, hipStream_t s);  // k_large_native.hip
 hipError_t launch_large_e2m1(const GemmArgs &a, hipStream_t s);           // k_large_e2m1.hip
+hipError_t launch_large_e2m3(const GemmArgs &a, hipStream_t s);           // k_large_e2m1.hip
 hipError_t launch_stream_exact(int f, const GemmArgs &a, hipStream_t s);  // k_stream.hip
 hipError_t launch_skinny_native(int f, const GemmArgs &a, hipStream_t s); // k_skinny_fp8.hip
 hipError_t launch_skinny_e2m1(const GemmArgs &a, hipStream_t s);          // k_skinny_e2m1.hip
+hipError_t launch_skinny_e2m3(const GemmArgs &a, hipStream_t s);          // k_skinny_e2m1.hip
 // sel = 2 fmt + (x_dtype == bf16), fmt in {0, 1, 4}
 hipError_t launch_quant(int sel, const quant::QuantArgs &a, dim3 grid, dim3 block,
                         hipStream_t s);                                    // k_quant.hip

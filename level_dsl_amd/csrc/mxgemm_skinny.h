@@ -95,9 +95,16 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     using Stage = mxg::skinny::Stage<MT>;
     constexpr bool FP4 = FA == 4;  // e2m1 x e2m1; K is the row pitch in bytes
     static_assert(FP4 == (FB == 4), "e2m1 pairs only with e2m1");
+    // e2m3 x e2m3 (four codes per three bytes): a stage is 128 codes, 96
+    // bytes of a row, one 16x16x128 step; lane group g loads the 24 bytes of
+    // block g (16 + 8 bytes) into operand dwords 0..5 and supplies its scale,
+    // as for fp8
+    constexpr bool FP6 = FA == 2;
+    static_assert(FP6 == (FB == 2), "e2m3 pairs only with e2m3");
     static_assert(SMODE != SCALES_VEC || FP4, "vector scale loads are for e2m1");
     constexpr bool SVEC = SMODE == SCALES_VEC, STAB = SMODE == SCALES_TABLE;
     constexpr int SPS = FP4 ? 8 : BK / 32;  // scale bytes per row and stage
+    constexpr int SB = FP6 ? 96 : BK;       // bytes of a row per stage
     __shared__ __attribute__((aligned(16))) float red[WAVES][MAX_M][BN];
     static_assert(sizeof(red) == TABLE_BYTES, "the scale table shares the reduction buffer");
     uint8_t *const tab = reinterpret_cast<uint8_t *>(&red[0][0][0]);
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int rows_b = min(BN, p.N - n0);
     const int M = p.M, N = p.N, K = p.K, KB = p.KB;
     // this workgroup's K stages [kbeg, kbeg + nk) of nk_all
-    const int nk_all = (K + BK - 1) / BK;
+    const int nk_all = (K + SB - 1) / SB;
     const int kbeg = SPLIT ? (int)((int64_t)sp * nk_all / p.splits) : 0;
     const int nk = SPLIT ? (int)((int64_t)(sp + 1) * nk_all / p.splits) - kbeg : nk_all;
 
@@ -122,8 +129,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int r16 = lane & 15, kq = lane >> 4;
 
     uint32_t boff[SUB_N], aoff[MT], bsrow[SUB_N], asrow[MT];
-    // chunks K bytes 16g.. and 64+16g.. of each stage; scale rows
-    constexpr int LO = 16, HI = 64;
+    // chunks K bytes 16g.. and 64+16g.. of each stage (e2m3: bytes 24g..
+    // and 24g+16.. of block g); scale rows
+    constexpr int LO = FP6 ? 24 : 16, HI = FP6 ? 16 : 64;
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) {
         boff[j] = (uint32_t)(16 * j + r16) * K + kq * LO;
@@ -180,26 +188,35 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     auto load_stage = [&](int kt, Stage &s) MXG_INLINE {
         const bool live = kt >= 0;
         s.kt = kt;
-        const int k0 = (live ? kt : 0) * BK;
-        const bool lo_in = live && k0 + kq * LO < K, hi_in = live && k0 + kq * LO + HI < K;
+        const int k0 = (live ? kt : 0) * SB;
+        // e2m3: both pieces belong to block g, which lies in the row or not
+        const bool lo_in = live && k0 + kq * LO < K, hi_in = FP6 ? lo_in : live && k0 + kq * LO + HI < K;
         const int kb0 = (live ? kt : 0) * SPS;
         // scale bytes: fp8, block g (in range when its 32 codes are);
         // e2m1, blocks g and 4 + g (each the block of one chunk).  The vector
         // form needs only the stage to exist (its rows hold whole stages).
-        const bool s0_in = SVEC ? live : (FP4 ? lo_in : live && k0 + kq * 32 < K);
+        const bool s0_in = SVEC ? live : (FP4 || FP6 ? lo_in : live && k0 + kq * 32 < K);
         const bool s1_in = hi_in;
+        // two pieces per row: 16 + 16 bytes (e2m3: 16 + 8, operand dwords 6, 7 zero)
+        auto piece = [&](rsrc_t r, uint32_t off) MXG_INLINE {
+            const v4i lo = load16(r, lo_in ? off + k0 : kOob);
+            if constexpr (FP6) {
+                const v2i hi = __builtin_bit_cast(
+                    v2i, __builtin_amdgcn_raw_buffer_load_b64(r, hi_in ? off + k0 + HI : kOob, 0, 0));
+                return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+            } else {
+                const v4i hi = load16(r, hi_in ? off + k0 + HI : kOob);
+                return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        };
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) {
-            v4i lo = load16(rB, lo_in ? boff[j] + k0 : kOob);
-            v4i hi = load16(rB, hi_in ? boff[j] + k0 + HI : kOob);
-            s.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            s.b[j] = piece(rB, boff[j]);
             if constexpr (!STAB) s.sb[j] = scales_of(rBs, bsrow[j], kb0, s0_in, s1_in);
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-            v4i lo = load16(rA, lo_in ? aoff[i] + k0 : kOob);
-            v4i hi = load16(rA, hi_in ? aoff[i] + k0 + HI : kOob);
-            s.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            s.a[i] = piece(rA, aoff[i]);
             if constexpr (!STAB) s.sa[i] = scales_of(rAs, asrow[i], kb0, s0_in, s1_in);
         }
     };
