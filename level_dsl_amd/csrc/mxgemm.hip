@@ -362,7 +362,7 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
     const uintptr_t salign = ((uintptr_t)A_scale) | ((uintptr_t)B_scale);
     a.scale_dword = (a.KB % 16 == 0 && (salign & 15u) == 0) ? 2
                     : (a.KB % 4 == 0 && (salign & 3u) == 0) ? 1 : 0;
-    a.c_vec = (N % 4) == 0;
+    a.c_vec = N % 8 == 0 ? 2 : (N % 4 == 0 ? 1 : 0);
 
     int variant = h->variant;
     bool native = variant == MXGEMM_VARIANT_LARGE_NATIVE ||

@@ -63,7 +63,8 @@ struct GemmArgs {
     int out_bf16;          // 0 fp32, 1 bf16
     int scale_dword;       // 2: KB % 16 == 0 and scale bases 16-byte aligned;
                            // 1: KB % 4 == 0 and 4-byte aligned; 0: neither
-    int c_vec;             // 1: N % 4 == 0 (aligned vector stores of C)
+    int c_vec;             // 1: N % 4 == 0 (aligned vector stores of C); 2: also N % 8 == 0
+                           // (16-byte stores of 8 bf16)
     int splits;            // small-M exact path: K splits per column tile (1: none)
     float *ws;             // split-K partial tiles (splits > 1)
     uint32_t *cnt;         // split-K arrival counters, zero between calls
@@ -198,6 +199,34 @@ __device__ __forceinline__ void store_c4(rsrc_t rC, uint32_t e0, int n, int N, v
             store2(rC, off, (uint16_t)bf16_bits(x));
         }
     }
+}
+
+// Epilogue store of 8 consecutive columns n..n+7 of one row of C as bf16,
+// element index e0 = row * N + n (N % 8 == 0 and n % 8 == 0, so the 16
+// bytes are aligned): use_acc adds the previous C (bf16 widened) before the
+// single rounding; one 16-byte store (buffer_store_dwordx4).  Columns at
+// or past N are dropped (off = kOob), rows past the descriptor by the
+// hardware.
+__device__ __forceinline__ void store_bf16x8(rsrc_t rC, uint32_t e0, int n, int N, v4f lo, v4f hi,
+                                             int use_acc)
+{
+    const uint32_t off = n < N ? e0 * 2 : kOob;
+    if (use_acc) {
+        const v4i old = load16(rC, off);
+        lo[0] += bf16_to_f32((uint32_t)old[0] & 0xffffu);
+        lo[1] += bf16_to_f32((uint32_t)old[0] >> 16);
+        lo[2] += bf16_to_f32((uint32_t)old[1] & 0xffffu);
+        lo[3] += bf16_to_f32((uint32_t)old[1] >> 16);
+        hi[0] += bf16_to_f32((uint32_t)old[2] & 0xffffu);
+        hi[1] += bf16_to_f32((uint32_t)old[2] >> 16);
+        hi[2] += bf16_to_f32((uint32_t)old[3] & 0xffffu);
+        hi[3] += bf16_to_f32((uint32_t)old[3] >> 16);
+    }
+    const v4i o = {(int)(bf16_bits(lo[0]) | (bf16_bits(lo[1]) << 16)),
+                   (int)(bf16_bits(lo[2]) | (bf16_bits(lo[3]) << 16)),
+                   (int)(bf16_bits(hi[0]) | (bf16_bits(hi[1]) << 16)),
+                   (int)(bf16_bits(hi[2]) | (bf16_bits(hi[3]) << 16))};
+    __builtin_amdgcn_raw_buffer_store_b128(o, rC, off, 0, 0);
 }
 
 // One 32x32x64 scaled MFMA: D = (X * 2^(sx-127)) @ (Y * 2^(sy-127)) + C where

@@ -603,6 +603,23 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         store_c4(rC, (uint32_t)m * N + n, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
     };
     constexpr int GROUPS = SUB_M * SUB_N * 4;  // 16-byte groups per lane
+    // bf16 output with N % 8 == 0: groups g (even) and g + 1 of a sub-tile
+    // are stored as 16-byte rows of 8 bf16.  Lane l holds columns 8g + 4 kh
+    // .. + 3 of both groups (kh = l / 32) and the lane l ^ 32 the other four
+    // of each, so the two lane halves swap one group: the lower half keeps
+    // group g and takes its partner's half of it, the upper half group g + 1.
+    const bool wide_bf16 = p.out_bf16 && p.c_vec == 2;
+    auto store_pair = [&](int i, int j, int g, v4f x, v4f y) MXG_INLINE {  // groups g, g + 1
+        const int kh = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
+        const int lr = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 31);
+        v4f send = kh ? x : y, recv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) recv[e] = __shfl_xor(send[e], 32, 64);
+        const v4f lo = kh ? recv : x, hi = kh ? y : recv;
+        const int m = wm * WAVE_M + i * 32 + lr;                       // tile-local row
+        const int n = n0 + wn * WAVE_N + j * 32 + 8 * (g + kh);      // global column
+        store_bf16x8(rC, (uint32_t)m * N + n, n, N, lo, hi, p.use_acc);
+    };
 
     // ---- fallback for scale bytes outside the window (exact mode) ---------
     // A wave whose A rows or B rows carry a scale byte outside its format's
@@ -715,17 +732,31 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
                 for (int y = 0; y < PER; ++y) sum[y] = q == 0 ? part[y] : sum[y] + part[y];
             }
-            static_for<PER>([&](auto Y) MXG_INLINE {
-                constexpr int x = b * PER + decltype(Y)::value;
-                store_group(x / (SUB_N * 4), (x / 4) % SUB_N, x % 4, sum[decltype(Y)::value]);
-            });
+            if (wide_bf16) {
+                static_for<PER / 2>([&](auto Y) MXG_INLINE {
+                    constexpr int y = 2 * decltype(Y)::value, x = b * PER + y;
+                    store_pair(x / (SUB_N * 4), (x / 4) % SUB_N, x % 4, sum[y], sum[y + 1]);
+                });
+            } else {
+                static_for<PER>([&](auto Y) MXG_INLINE {
+                    constexpr int x = b * PER + decltype(Y)::value;
+                    store_group(x / (SUB_N * 4), (x / 4) % SUB_N, x % 4, sum[decltype(Y)::value]);
+                });
+            }
         });
 
     } else {
         auto put = [&](int i, int j, const v16f &v) MXG_INLINE {
+            if (wide_bf16) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                store_group(i, j, g, v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]});
+                for (int g = 0; g < 4; g += 2)
+                    store_pair(i, j, g, v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]},
+                               v4f{v[4 * g + 4], v[4 * g + 5], v[4 * g + 6], v[4 * g + 7]});
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    store_group(i, j, g, v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]});
+            }
         };
         if (slow) {
             for (int t = 0; t < SUB_M * SUB_N; ++t) put(t / SUB_N, t % SUB_N, slow_tile(t / SUB_N, t % SUB_N));

@@ -295,6 +295,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     const rsrc_t rC = make_rsrc((uint8_t *)p.C, (uint32_t)M * N * (p.out_bf16 ? 2 : 4));
     constexpr int Q = MAX_M * BN / 4;  // float4 groups in the tile
+    // bf16 output with N % 8 == 0: rows of 8 columns, one 16-byte store each
+    const bool wide_bf16 = p.out_bf16 && p.c_vec == 2;
+    static_assert(BN % 8 == 0, "whole 8-column groups");
     if constexpr (SPLIT) {
         // Every split leaves its fp32 partial tile in the workspace
         // ([split][tile][64 rows][112 columns]); a counter per tile counts the
@@ -336,10 +339,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         // up to QB splits' partials in flight at once (a split past the last
         // reads zeros through the range check and is not added)
         constexpr int QB = 8;
-        for (int q = tid; q < Q; q += THREADS) {
-            const int m = q / (BN / 4), nl = (q % (BN / 4)) * 4;
-            if (m >= M) continue;
-            const uint32_t off = tile_off + (uint32_t)(m * BN + nl) * 4;
+        auto split_sum = [&](uint32_t off) MXG_INLINE {
             v4f v = {};
             for (int q0 = 0; q0 < p.splits; q0 += QB) {
                 v4f part[QB];
@@ -356,19 +356,48 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                         v += part[qq];
                 }
             }
+            return v;
+        };
+        if (wide_bf16) {
+            for (int q = tid; q < Q / 2; q += THREADS) {
+                const int m = q / (BN / 8), nl = (q % (BN / 8)) * 8;
+                if (m >= M) continue;
+                const uint32_t off = tile_off + (uint32_t)(m * BN + nl) * 4;
+                const v4f lo = split_sum(off), hi = split_sum(off + 16);
+                const int n = n0 + nl;
+                store_bf16x8(rC, (uint32_t)m * N + n, n, N, lo, hi, p.use_acc);
+            }
+            return;
+        }
+        for (int q = tid; q < Q; q += THREADS) {
+            const int m = q / (BN / 4), nl = (q % (BN / 4)) * 4;
+            if (m >= M) continue;
+            const v4f v = split_sum(tile_off + (uint32_t)(m * BN + nl) * 4);
             const int n = n0 + nl;
             store_c4(rC, (uint32_t)m * N + n, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
+        }
+        return;
+    }
+    auto tile_sum = [&](int m, int nl) MXG_INLINE {
+        v4f v = *reinterpret_cast<const v4f *>(&red[0][m][nl]);
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const v4f *>(&red[w][m][nl]);
+        return v;
+    };
+    if (wide_bf16) {
+        for (int q = tid; q < Q / 2; q += THREADS) {
+            const int m = q / (BN / 8), nl = (q % (BN / 8)) * 8;
+            if (m >= M) continue;
+            const int n = n0 + nl;
+            store_bf16x8(rC, (uint32_t)m * N + n, n, N, tile_sum(m, nl), tile_sum(m, nl + 4), p.use_acc);
         }
         return;
     }
     for (int q = tid; q < Q; q += THREADS) {
         const int m = q / (BN / 4), nl = (q % (BN / 4)) * 4;
         if (m >= M) continue;
-        v4f v = *reinterpret_cast<const v4f *>(&red[0][m][nl]);
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const v4f *>(&red[w][m][nl]);
         const int n = n0 + nl;
-        store_c4(rC, (uint32_t)m * N + n, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
+        store_c4(rC, (uint32_t)m * N + n, n, N, tile_sum(m, nl), p.out_bf16, p.use_acc, p.c_vec);
     }
 }
 

@@ -422,6 +422,22 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
                 }
         }
     }
+    if (p.out_bf16 && p.c_vec == 2) {
+        // bf16 output with N % 8 == 0: lane groups g and g ^ 1 hold the two
+        // halves of one 8-column group of the same row; the even group takes
+        // its partner's four columns and stores all eight with one 16-byte
+        // store (the odd group stores nothing)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            v4f hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hi[e] = __shfl_xor(acc[i][e], 16, 64);
+            const int m = 16 * i + r16;
+            const int n8 = (g & 1) ? N : n;  // odd groups: dropped
+            store_bf16x8(rC, (uint32_t)m * N + n, n8, N, acc[i], hi, p.use_acc);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
         const int m = 16 * i + r16;

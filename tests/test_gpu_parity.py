@@ -274,6 +274,10 @@ RANDOM_CASES = [
     (33, 300, 2048, 1, 0, mi.OUT_BF16, True),
     (64, 1000, 4128, 0, 0, mi.OUT_F32, False),
     (17, 1234, 160, 1, 0, mi.OUT_F32, True),
+    # bf16 output with N % 8 == 0 (16-byte stores of 8 bf16), with and without use_acc
+    (300, 520, 1024, 0, 0, mi.OUT_BF16, True),
+    (64, 448, 1024, 1, 0, mi.OUT_BF16, True),
+    (20, 1000, 512, 0, 1, mi.OUT_BF16, False),
 ]
 
 
