@@ -25,8 +25,9 @@
  *            e2m3: M x 3K/4 bytes (packed along K, see the formats below).
  *   B        N x K codes, K contiguous ("K-major"): byte B[n*K + k] = B[k,n];
  *            e2m1: N x K/2 bytes, e2m3: N x 3K/4 bytes.
- *   A_scale  M x (K/32) bytes, row-major.
- *   B_scale  N x (K/32) bytes, row-major.
+ *   A_scale  M x (K/32) bytes, row-major (or preshuffled, see
+ *            mxgemm_set_scale_layout).
+ *   B_scale  N x (K/32) bytes, row-major (or preshuffled).
  *   C        M x N, row-major, fp32 or bf16 (bit pattern in uint16).
  *
  * Ownership: the caller owns every buffer, including the optional split-K
@@ -209,13 +210,60 @@ int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream)
  * workspace is attached.  MXGEMM_ERR_SHAPE for S < 0. */
 int mxgemm_set_splits(mxgemm_t h, int splits);
 
+/* Layout of the scale bytes that mxgemm_run / mxgemm_run_noalloc read and
+ * mxgemm_quantize writes with this handle (default row-major).
+ *
+ * The pages name preshuffled MXFP scales only as what the tiles_per_warp
+ * option of the scaled dot serves (each warp holding 2 x 2 WMMA tiles for
+ * better reuse of scale registers, on gfx1250; TLX async-compute page,
+ * "Scaled dot") and give no byte order.
+ * The layout here is a reading: the order in which the MFMA's lanes
+ * consume scales.  A 32 x 32 fragment gives lane l (l < 32) row l of the
+ * tile and takes one scale word (4 consecutive K blocks) per lane, so:
+ *   rows are taken in groups of 32 and K blocks in groups of 4, and the
+ *   pair of groups (r / 32, kb / 4) is one 128-byte unit holding the 32
+ *   rows' 4-byte words in row order:
+ *     byte(r, kb) = (r / 32) * 32 * (K/32) + (kb / 4) * 128 + (r % 32) * 4 + kb % 4.
+ * A wave then reads a stage's scales of 32 rows as one 128-byte line
+ * instead of 32 scattered words.  The buffer holds ceil(rows / 32) * 32 rows
+ * (mxgemm_scale_bytes); bytes of the padding rows are never used for an
+ * output.  A group of 32 rows is the same byte range in both layouts.
+ *
+ * With MXGEMM_SCALES_PRESHUFFLED, mxgemm_run also requires K % 128 == 0
+ * (MXGEMM_ERR_SHAPE), 16-byte aligned scale pointers (MXGEMM_ERR_ALIGN),
+ * and C disjoint from the padded scale buffers (MXGEMM_ERR_ALIAS);
+ * mxgemm_quantize requires K % 128 == 0 and writes only the bytes of real
+ * rows.  MXGEMM_ERR_VARIANT for another layout value. */
+#define MXGEMM_SCALES_ROW_MAJOR 0
+#define MXGEMM_SCALES_PRESHUFFLED 1
+int mxgemm_set_scale_layout(mxgemm_t h, int layout);
+
+/* Bytes of the scale buffer of a rows x K operand in `layout`: rows * K/32
+ * (row-major) or ceil(rows / 32) * 32 * K/32 (preshuffled); 0 if rows < 1,
+ * K < 32, K % 32 != 0 (preshuffled: K % 128 != 0) or the layout is unknown. */
+int64_t mxgemm_scale_bytes(int layout, int64_t rows, int64_t K);
+
+/* Convert the row-major scale bytes of a rows x K operand (src,
+ * rows x K/32 bytes, any alignment) to the preshuffled layout (dst,
+ * mxgemm_scale_bytes(MXGEMM_SCALES_PRESHUFFLED, rows, K) bytes, 16-byte
+ * aligned), asynchronously on `stream`; the padding rows are written as
+ * zeros.  Both are device pointers on the handle's device, owned by the
+ * caller.  Errors: MXGEMM_ERR_NULL, MXGEMM_ERR_SHAPE (1 <= rows <=
+ * MXGEMM_MAX_M, 128 <= K <= MXGEMM_MAX_K with K % 128 == 0, rows * K <=
+ * MXGEMM_MAX_QELEMS), MXGEMM_ERR_ALIGN, MXGEMM_ERR_ALIAS (src and dst
+ * overlap); on an error nothing is launched. */
+int mxgemm_preshuffle_scales(mxgemm_t h, const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K,
+                             hipStream_t stream);
+
 /* Check the arguments of mxgemm_run without touching the GPU: pointers
  * non-NULL, formats, out_dtype, use_acc in {0,1}, 1 <= M <= MXGEMM_MAX_M,
  * 1 <= N <= MXGEMM_MAX_N, M * N <= MXGEMM_MAX_MN, 32 <= K <= MXGEMM_MAX_K
  * with K % 32 == 0,
  * A, B, C 16-byte aligned, and C not overlapping A, B or the scales
  * (byte ranges A[M*K], B[N*K], A_scale[M*K/32], B_scale[N*K/32],
- * C[M*N*sizeof(out)]).  Scales need no alignment. */
+ * C[M*N*sizeof(out)]).  Scales need no alignment.  These are the checks
+ * for row-major scales; a handle set to preshuffled scales adds those of
+ * mxgemm_set_scale_layout in mxgemm_run. */
 int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA,
                          const void *B, const uint8_t *B_scale, int fmtB,
                          const void *C, int64_t M, int64_t N, int64_t K,
@@ -263,7 +311,8 @@ int mxgemm_run_noalloc(mxgemm_t h,
  *   codes   R x K bytes, row-major (an A operand, or B stored K-contiguous);
  *           e2m1: R x K/2 bytes, two codes per byte, the even k in the low
  *           nibble;
- *   scales  R x (K/32) bytes, row-major.
+ *   scales  R x (K/32) bytes, row-major, or in the handle's preshuffled
+ *           layout (mxgemm_set_scale_layout).
  * The scale rule (a reading; the pages do not fix it): with MAX = 448
  * (e4m3), 57344 (e5m2) or 6 (e2m1), e is the smallest integer with
  * max|x| <= MAX * 2^e over the block (an all-zero block takes the smallest

@@ -35,6 +35,8 @@ MXGEMM_VARIANT_SKINNY_NATIVE = 4
 MXGEMM_WORKSPACE_BYTES = 4096 + 256 * 64 * 112 * 4
 MXGEMM_WORKSPACE_BYTES_LARGE = 4096 + 256 * 256 * 256 * 4
 MXGEMM_NOALLOC_SCRATCH_BYTES = MXGEMM_WORKSPACE_BYTES
+MXGEMM_SCALES_ROW_MAJOR = 0
+MXGEMM_SCALES_PRESHUFFLED = 1
 
 STATUS = {0: "MXGEMM_OK", 1: "MXGEMM_ERR_NULL", 2: "MXGEMM_ERR_FMT", 3: "MXGEMM_ERR_DTYPE",
           4: "MXGEMM_ERR_SHAPE", 5: "MXGEMM_ERR_ALIGN", 6: "MXGEMM_ERR_DEVICE",
@@ -51,6 +53,9 @@ SIGNATURES = {
     "mxgemm_set_variant": (_i32, [_vp, _i32]),
     "mxgemm_set_workspace": (_i32, [_vp, _vp, ctypes.c_size_t, _vp]),
     "mxgemm_set_splits": (_i32, [_vp, _i32]),
+    "mxgemm_set_scale_layout": (_i32, [_vp, _i32]),
+    "mxgemm_scale_bytes": (_i64, [_i32, _i64, _i64]),
+    "mxgemm_preshuffle_scales": (_i32, [_vp, _u8p, _u8p, _i64, _i64, _vp]),
     "mxgemm_validate_args": (_i32, [_vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64,
                                     _i32, _i32]),
     "mxgemm_run": (_i32, [_vp, _vp, _u8p, _i32, _vp, _u8p, _i32, _vp, _i64, _i64, _i64, _i32,
@@ -138,6 +143,25 @@ def mxgemm_set_splits(h, splits: int) -> None:
     _check(load_library().mxgemm_set_splits(h, int(splits)), "mxgemm_set_splits")
 
 
+def mxgemm_set_scale_layout(h, layout: int) -> None:
+    """Scale layout of later multiplies and quantizations through h:
+    MXGEMM_SCALES_ROW_MAJOR (default) or MXGEMM_SCALES_PRESHUFFLED."""
+    _check(load_library().mxgemm_set_scale_layout(h, int(layout)), "mxgemm_set_scale_layout")
+
+
+def mxgemm_scale_bytes(layout: int, rows: int, K: int) -> int:
+    """Bytes of a rows x K operand's scale buffer in `layout` (0: invalid)."""
+    return int(load_library().mxgemm_scale_bytes(int(layout), int(rows), int(K)))
+
+
+def mxgemm_preshuffle_scales(h, src, dst, rows: int, K: int, stream=None) -> None:
+    """Row-major scale bytes (rows x K/32) to the preshuffled layout, on
+    `stream` (default: torch's current stream)."""
+    _check(load_library().mxgemm_preshuffle_scales(h, _ptr(src), _ptr(dst), int(rows), int(K),
+                                                   _stream(stream)),
+           "mxgemm_preshuffle_scales")
+
+
 def _ptr(x) -> int:
     if x is None:
         return None
@@ -212,6 +236,7 @@ class Gemm:
 
     def __init__(self):
         self.h = mxgemm_create()
+        self.scale_layout = MXGEMM_SCALES_ROW_MAJOR
 
     def close(self):
         if self.h:
@@ -243,6 +268,29 @@ class Gemm:
     def set_splits(self, splits: int):
         mxgemm_set_splits(self.h, splits)
 
+    def set_scale_layout(self, layout: int):
+        """Scales of later calls are row-major (R, K/32) tensors, or with
+        MXGEMM_SCALES_PRESHUFFLED (ceil(R/32)*32, K/32) tensors holding the
+        preshuffled bytes."""
+        mxgemm_set_scale_layout(self.h, layout)
+        self.scale_layout = layout
+
+    def _scale_shape(self, rows: int, K: int):
+        if self.scale_layout == MXGEMM_SCALES_PRESHUFFLED:
+            return ((rows + 31) // 32 * 32, K // 32)
+        return (rows, K // 32)
+
+    def preshuffle_scales(self, S, stream=None):
+        """A contiguous (R, K/32) uint8 device tensor of row-major scale
+        bytes -> a new (ceil(R/32)*32, K/32) tensor in the preshuffled
+        layout (padding rows zero)."""
+        if S.dim() != 2 or S.dtype != torch.uint8 or not S.is_contiguous() or S.device.type != "cuda":
+            raise ValueError("S must be a contiguous 2-D uint8 device tensor")
+        R, kb = S.shape
+        out = torch.empty(((R + 31) // 32 * 32, kb), dtype=torch.uint8, device=S.device)
+        mxgemm_preshuffle_scales(self.h, S, out, R, 32 * kb, stream)
+        return out
+
     def __call__(self, A, A_scale, fmtA, B, B_scale, fmtB, C, use_acc=False,
                  out_dtype=MXGEMM_OUT_F32, stream=None):
         # sub-byte operands are packed along K: e2m1 two codes per byte,
@@ -251,9 +299,10 @@ class Gemm:
         N = B.shape[0]
         K = 2 * ka if fmtA == MXGEMM_FMT_E2M1 else (4 * ka // 3 if fmtA == MXGEMM_FMT_E2M3 else ka)
         kb = K // 2 if fmtB == MXGEMM_FMT_E2M1 else (3 * K // 4 if fmtB == MXGEMM_FMT_E2M3 else K)
-        if B.shape[1] != kb or A_scale.shape != (M, K // 32) or B_scale.shape != (N, K // 32):
-            raise ValueError("operand shapes do not match (A MxK, B NxK, scales K/32; "
-                             "e2m1: K/2 bytes per row, e2m3: 3K/4)")
+        if B.shape[1] != kb or A_scale.shape != self._scale_shape(M, K) or \
+                B_scale.shape != self._scale_shape(N, K):
+            raise ValueError("operand shapes do not match (A MxK, B NxK, scales K/32 per row, "
+                             "preshuffled: rows padded to 32; e2m1: K/2 bytes per row, e2m3: 3K/4)")
         want = torch.float32 if out_dtype == MXGEMM_OUT_F32 else torch.bfloat16
         if C.shape != (M, N) or C.dtype != want:
             raise ValueError(f"C must be ({M}, {N}) {want}")
@@ -280,9 +329,12 @@ class Gemm:
         if codes is None:
             codes = torch.empty((R, kc), dtype=torch.uint8, device=X.device)
         if scales is None:
-            scales = torch.empty((R, K // 32), dtype=torch.uint8, device=X.device)
-        if codes.shape != (R, kc) or scales.shape != (R, K // 32) or \
+            # preshuffled: the padding rows, which the quantizer does not
+            # write, start as zeros
+            scales = torch.zeros(self._scale_shape(R, K), dtype=torch.uint8, device=X.device)
+        if codes.shape != (R, kc) or scales.shape != self._scale_shape(R, K) or \
                 codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
-            raise ValueError("codes must be (R, K) (e2m1: (R, K/2)) and scales (R, K/32), uint8")
+            raise ValueError("codes must be (R, K) (e2m1: (R, K/2)) and scales (R, K/32) "
+                             "(preshuffled: rows padded to 32), uint8")
         mxgemm_quantize(self.h, X, xd, R, K, fmt, codes, scales, stream)
         return codes, scales

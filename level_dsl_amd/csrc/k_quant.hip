@@ -1,4 +1,5 @@
-// k_quant.hip -- the MX block quantization kernel and the streaming copy.
+// k_quant.hip -- the MX block quantization kernel, the streaming copy and the
+// conversion of scale bytes to the preshuffled layout.
 #include <algorithm>
 
 #include "mxcopy.h"
@@ -28,6 +29,40 @@ hipError_t launch_copy(const uint8_t *src, uint8_t *dst, uint64_t bytes, hipStre
     const uint64_t blocks = std::min<uint64_t>((pieces + per_block - 1) / per_block, 256 * 2);
     hipLaunchKernelGGL(copy::kernel, dim3((unsigned)blocks), dim3(copy::THREADS), 0, stream, src, dst,
                        bytes);
+    return hipGetLastError();
+}
+
+namespace {
+
+// Row-major scale bytes (rows x KB) to the preshuffled layout: thread t
+// writes word t of dst, which is word w = u % (KB / 4) of row 32 g + t % 32
+// for unit u = t / 32 of group g = u / (KB / 4) (mxgemm_common.h, scale_at);
+// rows past `rows` (the last group's padding) are written as zeros.
+__global__ __launch_bounds__(256) void preshuffle_kernel(const uint8_t *src, uint32_t *dst,
+                                                         uint64_t rows, uint32_t KB, uint64_t words)
+{
+    const uint64_t t = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+    if (t >= words) return;
+    const uint32_t W = KB / 4;
+    const uint64_t u = t >> 5;
+    const uint64_t g = u / W;
+    const uint32_t w = (uint32_t)(u - g * W);
+    const uint64_t r = 32 * g + (t & 31u);
+    uint32_t v = 0;
+    if (r < rows) {
+        const uint8_t *s = src + r * KB + 4 * w;
+        v = (uint32_t)s[0] | ((uint32_t)s[1] << 8) | ((uint32_t)s[2] << 16) | ((uint32_t)s[3] << 24);
+    }
+    dst[t] = v;
+}
+
+} // namespace
+
+hipError_t launch_preshuffle(const uint8_t *src, uint8_t *dst, uint64_t rows, int KB, hipStream_t stream)
+{
+    const uint64_t words = (rows + 31) / 32 * 32 * (uint64_t)KB / 4;
+    hipLaunchKernelGGL(preshuffle_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                       src, (uint32_t *)dst, rows, (uint32_t)KB, words);
     return hipGetLastError();
 }
 

@@ -13,14 +13,15 @@ hipError_t launch_skinny_s(const mxg::GemmArgs &a, hipStream_t s)
     namespace sk = mxg::skinny;
     const int blocks = a.tiles_m * a.tiles_n * a.splits;
     // scale table in LDS when the scale rows are 16-byte multiples, aligned,
-    // and all of K fits; else (e2m1) 8-byte loads per stage, or byte loads
+    // and all of K fits; else (e2m1, row-major scales) 8-byte loads per
+    // stage, or byte loads
     if (a.scale_dword == 2 && sk::table_fits(a.KB)) {
         hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_TABLE, MT, SPLIT>), dim3(blocks),
                            dim3(sk::THREADS), 0, s, a);
         return hipGetLastError();
     }
     if constexpr (FA == 4) {
-        if (a.scale_dword == 2) {
+        if (a.scale_dword == 2 && !a.scale_ps) {
             hipLaunchKernelGGL((sk::kernel<FA, FB, sk::SCALES_VEC, MT, SPLIT>), dim3(blocks),
                                dim3(sk::THREADS), 0, s, a);
             return hipGetLastError();

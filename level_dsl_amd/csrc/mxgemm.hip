@@ -29,6 +29,7 @@ struct mxgemm_ctx {
     int splits;      // 0 automatic, 1 never, S >= 2 forced
     uint8_t *ws;     // caller's split-K workspace, or NULL
     size_t ws_bytes;
+    int scale_layout;  // MXGEMM_SCALES_*
 };
 
 // The split-K scratch of mxgemm_run_noalloc: 4 KiB of arrival counters, then
@@ -187,13 +188,14 @@ const char *mxgemm_status_string(int code)
     case MXGEMM_ERR_FMT:
         return "operand format must be e4m3 (0), e5m2 (1), e2m3 (2, with e2m3) or e2m1 (4, with e2m1)";
     case MXGEMM_ERR_DTYPE: return "out_dtype must be f32 (0) or bf16 (1) and use_acc 0 or 1";
-    case MXGEMM_ERR_SHAPE: return "M, N, K out of range or K not a multiple of 32";
-    case MXGEMM_ERR_ALIGN: return "A, B and C must be 16-byte aligned";
+    case MXGEMM_ERR_SHAPE:
+        return "M, N, K out of range or K not a multiple of 32 (of 128 with preshuffled scales)";
+    case MXGEMM_ERR_ALIGN: return "A, B, C (and preshuffled scales) must be 16-byte aligned";
     case MXGEMM_ERR_DEVICE: return "device is not gfx950 or not the handle's device";
     case MXGEMM_ERR_HIP: return "HIP runtime error";
     case MXGEMM_ERR_HANDLE: return "invalid handle";
     case MXGEMM_ERR_ALIAS: return "C overlaps an input";
-    case MXGEMM_ERR_VARIANT: return "unknown kernel variant";
+    case MXGEMM_ERR_VARIANT: return "unknown kernel variant or scale layout";
     case MXGEMM_ERR_WORKSPACE: return "split-K workspace missing, too small or misaligned";
     default: return "unknown status";
     }
@@ -218,6 +220,7 @@ int mxgemm_create(mxgemm_t *out)
     h->splits = 0;
     h->ws = nullptr;
     h->ws_bytes = 0;
+    h->scale_layout = MXGEMM_SCALES_ROW_MAJOR;
     *out = h;
     return MXGEMM_OK;
 }
@@ -269,6 +272,43 @@ int mxgemm_set_splits(mxgemm_t h, int splits)
     return MXGEMM_OK;
 }
 
+int mxgemm_set_scale_layout(mxgemm_t h, int layout)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    if (layout != MXGEMM_SCALES_ROW_MAJOR && layout != MXGEMM_SCALES_PRESHUFFLED)
+        return MXGEMM_ERR_VARIANT;
+    h->scale_layout = layout;
+    return MXGEMM_OK;
+}
+
+int64_t mxgemm_scale_bytes(int layout, int64_t rows, int64_t K)
+{
+    if (rows < 1 || K < 32 || K % 32 != 0 || rows > MXGEMM_MAX_M || K > MXGEMM_MAX_K) return 0;
+    if (layout == MXGEMM_SCALES_ROW_MAJOR) return rows * (K / 32);
+    if (layout == MXGEMM_SCALES_PRESHUFFLED && K % 128 == 0) return (rows + 31) / 32 * 32 * (K / 32);
+    return 0;
+}
+
+int mxgemm_preshuffle_scales(mxgemm_t h, const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K,
+                             hipStream_t stream)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    if (!src || !dst) return MXGEMM_ERR_NULL;
+    if (rows < 1 || K < 128 || rows > MXGEMM_MAX_M || K > MXGEMM_MAX_K || K % 128 != 0 ||
+        rows * K > MXGEMM_MAX_QELEMS)
+        return MXGEMM_ERR_SHAPE;
+    if ((uintptr_t)dst & 15u) return MXGEMM_ERR_ALIGN;
+    if (overlaps(src, (uint64_t)(rows * (K / 32)), dst,
+                 (uint64_t)mxgemm_scale_bytes(MXGEMM_SCALES_PRESHUFFLED, rows, K)))
+        return MXGEMM_ERR_ALIAS;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
+    if (dev != h->device) return MXGEMM_ERR_DEVICE;
+    return mxg::launch_preshuffle(src, dst, (uint64_t)rows, (int)(K / 32), stream) == hipSuccess
+               ? MXGEMM_OK
+               : MXGEMM_ERR_HIP;
+}
+
 int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const void *B,
                          const uint8_t *B_scale, int fmtB, const void *C, int64_t M, int64_t N,
                          int64_t K, int use_acc, int out_dtype)
@@ -315,6 +355,16 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
     const int rc = mxgemm_validate_args(A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc,
                                         out_dtype);
     if (rc != MXGEMM_OK) return rc;
+    const bool ps = h->scale_layout == MXGEMM_SCALES_PRESHUFFLED;
+    if (ps) {
+        // the preshuffled layout's own conditions (mxgemm_set_scale_layout)
+        if (K % 128 != 0) return MXGEMM_ERR_SHAPE;
+        if (((uintptr_t)A_scale | (uintptr_t)B_scale) & 15u) return MXGEMM_ERR_ALIGN;
+        const uint64_t csize = (uint64_t)M * (uint64_t)N * (out_dtype == MXGEMM_OUT_F32 ? 4u : 2u);
+        if (overlaps(C, csize, A_scale, (uint64_t)mxgemm_scale_bytes(MXGEMM_SCALES_PRESHUFFLED, M, K)) ||
+            overlaps(C, csize, B_scale, (uint64_t)mxgemm_scale_bytes(MXGEMM_SCALES_PRESHUFFLED, N, K)))
+            return MXGEMM_ERR_ALIAS;
+    }
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
     if (dev != h->device) return MXGEMM_ERR_DEVICE;
@@ -334,6 +384,7 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
             const int64_t rb = row_bytes(fmtA, K);
             const size_t esz = out_dtype == MXGEMM_OUT_F32 ? 4 : 2;
             for (int64_t r = 0; r < M; r += H) {
+                // 64-row steps: whole 32-row groups, the same scale offset in both layouts
                 const int rc_r = run_impl(h, (const uint8_t *)A + r * rb,
                                           A_scale + r * (K / 32), fmtA, B, B_scale, fmtB,
                                           (uint8_t *)C + (size_t)r * N * esz, std::min(H, M - r), N,
@@ -362,6 +413,7 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
     const uintptr_t salign = ((uintptr_t)A_scale) | ((uintptr_t)B_scale);
     a.scale_dword = (a.KB % 16 == 0 && (salign & 15u) == 0) ? 2
                     : (a.KB % 4 == 0 && (salign & 3u) == 0) ? 1 : 0;
+    a.scale_ps = ps ? 1 : 0;  // then KB % 4 == 0 and 16-byte aligned: scale_dword >= 1
     a.c_vec = N % 8 == 0 ? 2 : (N % 4 == 0 ? 1 : 0);
 
     int variant = h->variant;
@@ -404,7 +456,7 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
         if (tiles <= mxg::stream::MAX_SPLITS_TILES / 2) {
             // stages as the kernel counts them (bytes of a row per stage)
             const int nk = (a.K + stage_bytes - 1) / stage_bytes;
-            const bool scale16 = !native && a.scale_dword == 2;  // the kernel's SCALE16
+            const bool scale16 = !native && a.scale_dword == 2 && !ps;  // the kernel's SCALE16
             const int unit = scale16 ? mxg::large::WINDOW : 1;
             a.splits = choose_splits_large(h->splits, (int)tiles, nk / unit, unit, ws_bytes);
             if (strict && h->splits >= 2 &&
@@ -476,6 +528,17 @@ int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K
     if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
     const int rc = mxgemm_validate_quantize(X, x_dtype, R, K, fmt, codes, scales);
     if (rc != MXGEMM_OK) return rc;
+    const bool ps = h->scale_layout == MXGEMM_SCALES_PRESHUFFLED;
+    const uint64_t sbytes = (uint64_t)mxgemm_scale_bytes(h->scale_layout, R, K);
+    if (ps) {
+        // the padded scale buffer must hold no byte of X or the codes
+        if (K % 128 != 0) return MXGEMM_ERR_SHAPE;
+        const uint64_t n = (uint64_t)R * (uint64_t)K;
+        const uint64_t xbytes = n * (x_dtype == MXGEMM_X_F32 ? 4u : 2u);
+        const uint64_t cbytes = fmt == MXGEMM_FMT_E2M1 ? n / 2 : n;
+        if (overlaps(X, xbytes, scales, sbytes) || overlaps(codes, cbytes, scales, sbytes))
+            return MXGEMM_ERR_ALIAS;
+    }
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
     if (dev != h->device) return MXGEMM_ERR_DEVICE;
@@ -485,6 +548,9 @@ int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K
     a.codes = codes;
     a.scales = scales;
     a.n = (uint64_t)R * (uint64_t)K;
+    a.KB = (int)(K / 32);
+    a.ps = ps ? 1 : 0;
+    a.scale_bytes = sbytes;
     const uint64_t esz = x_dtype == MXGEMM_X_F32 ? 4 : 2;
     const uint64_t per_block = (uint64_t)(mxg::quant::THREADS / 64) * mxg::quant::WAVE_BYTES / esz;
     const dim3 grid((unsigned)((a.n + per_block - 1) / per_block));

@@ -61,8 +61,9 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int use_acc;           // 0 / 1
     int out_bf16;          // 0 fp32, 1 bf16
-    int scale_dword;       // 2: KB % 16 == 0 and scale bases 16-byte aligned;
-                           // 1: KB % 4 == 0 and 4-byte aligned; 0: neither
+    int scale_dword;       // 2: KB % 16 == 0 and scale bases 16-byte aligned (preshuffled:
+                           // KB % 16 == 0); 1: KB % 4 == 0 and 4-byte aligned; 0: neither
+    int scale_ps;          // 1: scales in the preshuffled layout (scale_at), else row-major
     int c_vec;             // 1: N % 4 == 0 (aligned vector stores of C); 2: also N % 8 == 0
                            // (16-byte stores of 8 bf16)
     int splits;            // small-M exact path: K splits per column tile (1: none)
@@ -110,12 +111,43 @@ __device__ __forceinline__ void load16_lds(rsrc_t r, void *lds_base, uint32_t of
 // track (s_waitcnt vmcnt(0)).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// ---- scale layouts ---------------------------------------------------------
+// Row-major: scale byte (r, kb) of an operand with KB = K/32 blocks per row
+// at r * KB + kb.  Preshuffled (KB % 4 == 0): rows in groups of 32 and blocks
+// in groups of 4; the pair of groups (r / 32, kb / 4) is one 128-byte unit
+// at (r / 32) * 32 KB + (kb / 4) * 128 that holds the 32 rows' 4-byte words
+// in row order, so the word that lane l of a 32-row MFMA fragment needs is
+// byte 4 l of the unit and one wave's load of it is one 128-byte line.  A
+// group of 32 rows spans 32 KB bytes in both layouts: a row offset that is
+// a multiple of 32 moves the base pointer alike.  The last group is padded
+// to 32 rows (bytes of rows past the operand are never used for an output).
+// The offset is a row part plus a block part.
+__device__ __forceinline__ uint32_t scale_row(uint32_t r, int KB, int ps)
+{
+    return ps ? (r & ~31u) * (uint32_t)KB + (r & 31u) * 4u : r * (uint32_t)KB;
+}
+__device__ __forceinline__ uint32_t scale_col(uint32_t kb, int ps)
+{
+    return ps ? (kb & ~3u) * 32u + (kb & 3u) : kb;
+}
+__device__ __forceinline__ uint32_t scale_at(uint32_t r, uint32_t kb, int KB, int ps)
+{
+    return scale_row(r, KB, ps) + scale_col(kb, ps);
+}
+// bytes of `rows` scale rows from a multiple of 32 (preshuffled: whole groups)
+__device__ __forceinline__ uint32_t scale_span(int rows, int KB, int ps)
+{
+    return (uint32_t)(ps ? (rows + 31) & ~31 : rows) * (uint32_t)KB;
+}
+
 // Scale bytes kb0 .. kb0+3 of scale row r as one little-endian dword; bytes
 // past KB read as zero.  `dword` selects one aligned 4-byte load (KB % 4 == 0
-// and a 4-byte aligned base), else four byte loads.
-__device__ __forceinline__ uint32_t load_scale4(rsrc_t rs, uint32_t r, int KB, int kb0, int dword)
+// and a 4-byte aligned base; always so when preshuffled), else four byte
+// loads.
+__device__ __forceinline__ uint32_t load_scale4(rsrc_t rs, uint32_t r, int KB, int kb0, int dword,
+                                                int ps)
 {
-    if (dword) return __builtin_amdgcn_raw_buffer_load_b32(rs, r * KB + kb0, 0, 0);
+    if (dword) return __builtin_amdgcn_raw_buffer_load_b32(rs, scale_at(r, kb0, KB, ps), 0, 0);
     uint32_t v = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b)

@@ -155,8 +155,10 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     const rsrc_t rA = make_rsrc(p.A + (size_t)m0 * K, (uint32_t)rows_a * K);
     const rsrc_t rB = make_rsrc(p.B + (size_t)n0 * K, (uint32_t)rows_b * K);
-    const rsrc_t rAs = make_rsrc(p.As + (size_t)m0 * KB, (uint32_t)rows_a * KB);
-    const rsrc_t rBs = make_rsrc(p.Bs + (size_t)n0 * KB, (uint32_t)rows_b * KB);
+    // tiles start at multiples of 32 rows: the same base in both scale layouts
+    const int ps = p.scale_ps;
+    const rsrc_t rAs = make_rsrc(p.As + (size_t)m0 * KB, scale_span(rows_a, KB, ps));
+    const rsrc_t rBs = make_rsrc(p.Bs + (size_t)n0 * KB, scale_span(rows_b, KB, ps));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -201,7 +203,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // ---- scales ---------------------------------------------------------
     // Fragment rows of this lane: A rows wm*128 + 32i + lrow, B rows
     // wn*128 + 32j + lrow.  SCALE16: 16 bytes (4 stages) per row and load;
-    // otherwise one dword (or four bytes) per row and stage.
+    // otherwise one dword (or four bytes) per row and stage.  SCALE16 reads
+    // row-major scales only; preshuffled scales take the per-stage dword
+    // loads, each one 128-byte line for the wave's 32 rows.
     const uint32_t sra = (uint32_t)(wm * WAVE_M + lrow), srb = (uint32_t)(wn * WAVE_N + lrow);
     auto srow_a = [&](int i) MXG_INLINE { return sra + 32 * i; };
     auto srow_b = [&](int j) MXG_INLINE { return srb + 32 * j; };
@@ -218,18 +222,18 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     auto scale4 = [&](int kt, uint32_t *xa, uint32_t *xb, uint32_t *xa2, uint32_t *xb2) MXG_INLINE {
         const int kb0 = (ks0 + kt) * SPS;
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) xa[i] = load_scale4(rAs, srow_a(i), KB, kb0, p.scale_dword);
+        for (int i = 0; i < SUB_M; ++i) xa[i] = load_scale4(rAs, srow_a(i), KB, kb0, p.scale_dword, ps);
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) xb[j] = load_scale4(rBs, srow_b(j), KB, kb0, p.scale_dword);
+        for (int j = 0; j < SUB_N; ++j) xb[j] = load_scale4(rBs, srow_b(j), KB, kb0, p.scale_dword, ps);
         if constexpr (FP4) {
             const int kb1 = kb0 + 4;
             const bool in = kb1 < KB;
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i)
-                xa2[i] = in ? load_scale4(rAs, sra + 32 * i, KB, kb1, p.scale_dword) : 0u;
+                xa2[i] = in ? load_scale4(rAs, sra + 32 * i, KB, kb1, p.scale_dword, ps) : 0u;
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j)
-                xb2[j] = in ? load_scale4(rBs, srb + 32 * j, KB, kb1, p.scale_dword) : 0u;
+                xb2[j] = in ? load_scale4(rBs, srb + 32 * j, KB, kb1, p.scale_dword, ps) : 0u;
         }
     };
     // Exact mode: every scale byte the fast loop decodes with passes
@@ -646,7 +650,8 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             for (int kb = kb0; kb < kb1; ++kb) {
                 const v4i xa = load16(rA, ar * K + 32 * kb + 16 * kh);  // rows past the tile read 0
                 const v4i xb = load16(rB, br * K + 32 * kb + 16 * kh);
-                const uint32_t ba = load1(rAs, ar * KB + kb), bb = load1(rBs, br * KB + kb);
+                const uint32_t ba = load1(rAs, scale_at(ar, kb, KB, p.scale_ps)),
+                               bb = load1(rBs, scale_at(br, kb, KB, p.scale_ps));
                 float da, db, na, nb;
                 int ea, eb;
                 clamp_scale<FA>(ba, da, ea, na);

@@ -26,5 +26,8 @@ hipError_t launch_skinny_e2m3(const GemmArgs &a, hipStream_t s);          // k_s
 hipError_t launch_quant(int sel, const quant::QuantArgs &a, dim3 grid, dim3 block,
                         hipStream_t s);                                    // k_quant.hip
 hipError_t launch_copy(const uint8_t *src, uint8_t *dst, uint64_t bytes, hipStream_t s);  // k_quant.hip
+// row-major scale bytes (rows x KB, KB % 4 == 0) to the preshuffled layout
+hipError_t launch_preshuffle(const uint8_t *src, uint8_t *dst, uint64_t rows, int KB,
+                             hipStream_t s);                               // k_quant.hip
 
 } // namespace mxg

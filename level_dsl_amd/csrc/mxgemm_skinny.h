@@ -121,8 +121,12 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     const rsrc_t rA = make_rsrc(p.A, (uint32_t)M * K);
     const rsrc_t rB = make_rsrc(p.B + (size_t)n0 * K, (uint32_t)rows_b * K);
-    const rsrc_t rAs = make_rsrc(p.As, (uint32_t)M * KB);
-    const rsrc_t rBs = make_rsrc(p.Bs + (size_t)n0 * KB, (uint32_t)rows_b * KB);
+    // Scale rows: A from row 0; B from row n0, or with preshuffled scales
+    // from the 32-row group that holds it (row n0 is row nsb of the range)
+    const int ps = p.scale_ps;
+    const int nsb = ps ? n0 & 31 : 0;
+    const rsrc_t rAs = make_rsrc(p.As, scale_span(M, KB, ps));
+    const rsrc_t rBs = make_rsrc(p.Bs + (size_t)(n0 - nsb) * KB, scale_span(nsb + rows_b, KB, ps));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -135,24 +139,24 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) {
         boff[j] = (uint32_t)(16 * j + r16) * K + kq * LO;
-        bsrow[j] = (uint32_t)(16 * j + r16) * KB;
+        bsrow[j] = scale_row((uint32_t)(nsb + 16 * j + r16), KB, ps);
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
         aoff[i] = (uint32_t)(16 * i + r16) * K + kq * LO;
-        asrow[i] = (uint32_t)(16 * i + r16) * KB;
+        asrow[i] = scale_row((uint32_t)(16 * i + r16), KB, ps);
     }
 
-    // the stage's scale bytes of one row (byte offset `row` of its K/32 row):
-    // fp8 block g in byte 0; e2m1 blocks g and 4 + g in bytes 0 and 1
+    // the stage's scale bytes of one row (`row`: the row part of its scale
+    // offsets): fp8 block g in byte 0; e2m1 blocks g and 4 + g in bytes 0 and 1
     auto scales_of = [&](rsrc_t rs, uint32_t row, int kb0, bool s0_in, bool s1_in) MXG_INLINE {
-        if constexpr (SVEC) {
+        if constexpr (SVEC) {  // row-major scales only
             const v2i v = __builtin_bit_cast(
                 v2i, __builtin_amdgcn_raw_buffer_load_b64(rs, s0_in ? row + kb0 : kOob, 0, 0));
             return (((uint32_t)v[0] >> (8 * kq)) & 0xffu) | ((((uint32_t)v[1] >> (8 * kq)) & 0xffu) << 8);
         } else {
-            uint32_t v = load1(rs, s0_in ? row + kb0 + kq : kOob);
-            if constexpr (FP4) v |= load1(rs, s1_in ? row + kb0 + kq + 4 : kOob) << 8;
+            uint32_t v = load1(rs, s0_in ? row + scale_col(kb0 + kq, ps) : kOob);
+            if constexpr (FP4) v |= load1(rs, s1_in ? row + scale_col(kb0 + kq + 4, ps) : kOob) << 8;
             return v;
         }
     };
@@ -165,15 +169,31 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     if constexpr (STAB) {
         const int c_lo = kbeg * SPS / 16, c_hi = min(KB / 16, ((kbeg + nk) * SPS + 15) / 16);
         const int per_row = c_hi - c_lo;  // 16-byte pieces per row
-        for (int q = tid; q < TABLE_ROWS * per_row; q += THREADS) {
-            const int r = q / per_row, c = (c_lo + q % per_row) * 16;
-            const bool is_a = r < MAX_M;
-            const v4i v = load16(is_a ? rAs : rBs, (uint32_t)((is_a ? r : r - MAX_M) * KB + c));
-            uint32_t *d = reinterpret_cast<uint32_t *>(tab + r * tpitch + c);
-            d[0] = (uint32_t)v[0];
-            d[1] = (uint32_t)v[1];
-            d[2] = (uint32_t)v[2];
-            d[3] = (uint32_t)v[3];
+        if (ps) {
+            // a 16-byte piece is one word (4 blocks) of 4 consecutive rows;
+            // consecutive threads take consecutive row quads of one word
+            constexpr int QUADS = TABLE_ROWS / 4;
+            static_assert(MAX_M % 32 == 0 && TABLE_ROWS % 4 == 0, "quads stay within A or B");
+            for (int q = tid; q < QUADS * 4 * per_row; q += THREADS) {
+                const int r = 4 * (q % QUADS), w = 4 * c_lo + q / QUADS;
+                const bool is_a = r < MAX_M;
+                const v4i v = load16(is_a ? rAs : rBs,
+                                     scale_row((uint32_t)(is_a ? r : r - MAX_M + nsb), KB, 1) + 128u * w);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<uint32_t *>(tab + (r + e) * tpitch + 4 * w) = (uint32_t)v[e];
+            }
+        } else {
+            for (int q = tid; q < TABLE_ROWS * per_row; q += THREADS) {
+                const int r = q / per_row, c = (c_lo + q % per_row) * 16;
+                const bool is_a = r < MAX_M;
+                const v4i v = load16(is_a ? rAs : rBs, (uint32_t)((is_a ? r : r - MAX_M) * KB + c));
+                uint32_t *d = reinterpret_cast<uint32_t *>(tab + r * tpitch + c);
+                d[0] = (uint32_t)v[0];
+                d[1] = (uint32_t)v[1];
+                d[2] = (uint32_t)v[2];
+                d[3] = (uint32_t)v[3];
+            }
         }
         __syncthreads();
     }

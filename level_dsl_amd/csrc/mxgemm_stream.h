@@ -92,10 +92,11 @@ __device__ __forceinline__ uint32_t a_addr(int r, int c) { return r * AROW + ((c
 // SDW selects one aligned dword load, else four byte loads; a dead stage or
 // row reads zeros through an out-of-range offset.
 template <bool SDW>
-__device__ __forceinline__ uint32_t scale_dword(rsrc_t rs, uint32_t r, int KB, int kb0, bool live)
+__device__ __forceinline__ uint32_t scale_dword(rsrc_t rs, uint32_t r, int KB, int kb0, bool live,
+                                                int ps)
 {
-    if constexpr (SDW) {
-        return __builtin_amdgcn_raw_buffer_load_b32(rs, live ? r * KB + kb0 : kOob, 0, 0);
+    if constexpr (SDW) {  // always so with preshuffled scales
+        return __builtin_amdgcn_raw_buffer_load_b32(rs, live ? scale_at(r, kb0, KB, ps) : kOob, 0, 0);
     } else {
         uint32_t v = 0;
 #pragma unroll
@@ -148,8 +149,12 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const rsrc_t rAs = make_rsrc(p.As, (uint32_t)M * KB);
-    const rsrc_t rBs = make_rsrc(p.Bs + (size_t)n0 * KB, (uint32_t)rows_b * KB);
+    // Scale rows: A from row 0; B from row n0, or with preshuffled scales
+    // from the 32-row group that holds it (row n0 is row nsb of the range)
+    const int ps = p.scale_ps;
+    const int nsb = ps ? n0 & 31 : 0;
+    const rsrc_t rAs = make_rsrc(p.As, scale_span(M, KB, ps));
+    const rsrc_t rBs = make_rsrc(p.Bs + (size_t)(n0 - nsb) * KB, scale_span(nsb + rows_b, KB, ps));
     // All waves: the scale dwords of iterations u0 .. u0+SCH-1 into s_lds
     // (row r < 64: A row r; else B row r - 64 of this workgroup), column u - u0.
     // (all loads are issued before the first LDS write, so the chunk costs one
@@ -173,8 +178,8 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
             const int kb0 = (live ? kt_of(u) : 0) * (BK / 32);
             // rows 0..63 are A rows, the rest B rows: pick the descriptor
             const bool is_a = r < MAX_M;
-            v[i] = scale_dword<SDW>(is_a ? rAs : rBs, (uint32_t)(is_a ? r : r - MAX_M), KB, kb0,
-                                    live);
+            v[i] = scale_dword<SDW>(is_a ? rAs : rBs, (uint32_t)(is_a ? r : r - MAX_M + nsb), KB, kb0,
+                                    live, ps);
         }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -326,12 +331,13 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
         const int kb0 = kbeg * (BK / 32), kb1 = min(KB, (kbeg + nk) * (BK / 32));
         constexpr int kNanCode = 4096;  // a B remainder that marks scale byte 255
         const uint32_t bro = (uint32_t)(16 * w + r16);  // this lane's B row in the workgroup
+        const uint32_t bsr = scale_row(bro + nsb, KB, ps);  // its scale row part
 #pragma unroll
         for (int i = 0; i < MT; ++i) acc[i] = v4f{};
         for (int kb = kb0; kb < kb1; ++kb) {
             const v2i xb = __builtin_bit_cast(
                 v2i, __builtin_amdgcn_raw_buffer_load_b64(rB, bro * K + 32 * kb + 8 * g, 0, 0));
-            const uint32_t bb = load1(rBs, bro * KB + kb);
+            const uint32_t bb = load1(rBs, bsr + scale_col(kb, ps));
             float db, nb;
             int eb;
             clamp_scale<FB>(bb, db, eb, nb);
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(threads_for<MT>()) void kernel(GemmArgs p)
                 const uint32_t aro = (uint32_t)(16 * i + r16);  // rows past M read as zero
                 const v2i xa = __builtin_bit_cast(
                     v2i, __builtin_amdgcn_raw_buffer_load_b64(rA, aro * K + 32 * kb + 8 * g, 0, 0));
-                const uint32_t ba = load1(rAs, aro * KB + kb);
+                const uint32_t ba = load1(rAs, scale_at(aro, kb, KB, ps));
                 float da, na;
                 int ea;
                 clamp_scale<FA>(ba, da, ea, na);

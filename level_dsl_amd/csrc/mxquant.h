@@ -26,7 +26,9 @@
 //     values per instruction;
 //   * codes leave as one 4-byte (fp32 input) or 8-byte (bf16 input) store
 //     per lane and chunk -- e2m1: 2 or 4 bytes -- contiguous across the
-//     wave; the first lane of each block stores its scale byte.
+//     wave; the first lane of each block stores its scale byte, at its
+//     place in the row-major or the preshuffled scale layout
+//     (mxgemm_common.h, scale_at).
 // Descriptors are rebased per wave, so every offset stays far below 2^32 and
 // the tail of the stream is masked by the descriptors' range checks.
 #pragma once
@@ -45,6 +47,9 @@ struct QuantArgs {
     uint8_t *codes;
     uint8_t *scales;
     uint64_t n;  // elements (R * K, a multiple of 32)
+    int KB;      // K / 32, scale bytes per row
+    int ps;      // 1: preshuffled scale layout (KB % 4 == 0)
+    uint64_t scale_bytes;  // of the whole scale buffer (preshuffled: rows padded to 32)
 };
 
 template <int FMT>
@@ -84,7 +89,15 @@ __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
     const uint32_t ne = left < (uint64_t)WAVE_ELEMS ? (uint32_t)left : (uint32_t)WAVE_ELEMS;
     const rsrc_t rX = make_rsrc(p.X + e0 * ESZ, ne * ESZ);
     const rsrc_t rQ = FP4 ? make_rsrc(p.codes + e0 / 2, ne / 2) : make_rsrc(p.codes + e0, ne);
-    const rsrc_t rS = make_rsrc(p.scales + e0 / 32, ne / 32);
+    // row-major scales: this wave's bytes from block e0 / 32 on; preshuffled:
+    // from the 32-row group of the wave's first block (row r0 = sr0 + 32 g0,
+    // block kb0 of it) to the end of the buffer
+    const uint64_t b0 = e0 / 32;
+    const uint64_t row0 = b0 / (uint64_t)p.KB;
+    const uint32_t kb0 = (uint32_t)(b0 - row0 * (uint64_t)p.KB), sr0 = (uint32_t)(row0 & 31u);
+    const uint64_t sbase = p.ps ? (row0 - sr0) * (uint64_t)p.KB : b0;
+    const uint64_t sleft = p.ps ? p.scale_bytes - sbase : ne / 32;
+    const rsrc_t rS = make_rsrc(p.scales + sbase, (uint32_t)(sleft < kOob ? sleft : kOob));
 
     v4i x[CHUNKS];
 #pragma unroll
@@ -138,7 +151,17 @@ __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
             else
                 store4(rQ, c * 4, w[0]);
         }
-        if (lane % LPB == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)s, rS, c / LPB, 0, 0);
+        if (lane % LPB == 0) {
+            uint32_t so = c / LPB;
+            if (p.ps) {
+                // block so of the wave: block (kb0 + so) % KB of row sr0 +
+                // (kb0 + so) / KB of the range (a store past the stream's end
+                // is masked)
+                const uint32_t q = kb0 + so, dr = q / (uint32_t)p.KB;
+                so = so < ne / 32 ? scale_at(sr0 + dr, q - dr * (uint32_t)p.KB, p.KB, 1) : kOob;
+            }
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)s, rS, so, 0, 0);
+        }
     }
 }
 

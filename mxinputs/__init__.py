@@ -115,6 +115,21 @@ _TORCH_FP8 = {FMT_E4M3: torch.float8_e4m3fn, FMT_E5M2: torch.float8_e5m2}
 T_A, T_B, T_AS, T_BS, T_CIN = 0, 1, 2, 3, 4
 
 
+def preshuffle_scales(S: np.ndarray) -> np.ndarray:
+    """Row-major scale bytes (R, K/32), K/32 % 4 == 0, in the library's
+    preshuffled layout, as a (ceil(R/32)*32, K/32) array: rows in groups of
+    32, K blocks in groups of 4, each pair of groups one 128-byte unit of
+    the 32 rows' 4-byte words in row order; padding rows are zero.  An index
+    permutation only (the inputs' byte placement, no arithmetic of the
+    multiply)."""
+    R, KB = S.shape
+    assert KB % 4 == 0, "the preshuffled layout needs K % 128 == 0"
+    Rp = (R + 31) // 32 * 32
+    P = np.zeros((Rp, KB), np.uint8)
+    P[:R] = S
+    return np.ascontiguousarray(P.reshape(Rp // 32, 32, KB // 4, 4).transpose(0, 2, 1, 3).reshape(Rp, KB))
+
+
 def rng(workload: int, tensor_id: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(
         np.random.SeedSequence([SEED_ROOT, int(workload), int(tensor_id)])))

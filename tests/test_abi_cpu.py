@@ -156,3 +156,22 @@ def test_large_workspace_size_matches_header():
 ])
 def test_validate_copy(dst, src, n, code):
     assert L.mxgemm_validate_copy(dst, src, n) == L.STATUS_CODE[code]
+
+
+@pytest.mark.parametrize("layout,rows,K,want", [
+    (0, 64, 8192, 64 * 256), (0, 1, 32, 1), (0, 300, 1056, 300 * 33),
+    (1, 64, 8192, 64 * 256), (1, 1, 128, 32 * 4), (1, 33, 256, 64 * 8), (1, 28672, 8192, 28672 * 256),
+    (1, 300, 1056, 0),            # preshuffled needs K % 128 == 0
+    (0, 0, 128, 0), (1, 10, 96, 0), (0, 10, 48, 0), (2, 64, 128, 0), (-1, 64, 128, 0),
+    (0, 1 << 31, 128, 0),         # rows beyond MXGEMM_MAX_M
+])
+def test_scale_bytes(layout, rows, K, want):
+    assert L.mxgemm_scale_bytes(layout, rows, K) == want
+
+
+def test_scale_layout_entry_points_reject_bad_handle_without_gpu_work():
+    for call in (lambda: L.mxgemm_set_scale_layout(None, L.MXGEMM_SCALES_PRESHUFFLED),
+                 lambda: L.mxgemm_preshuffle_scales(None, 0x100000, 0x200000, 64, 256, 0)):
+        with pytest.raises(L.MxgemmError) as e:
+            call()
+        assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_HANDLE"]

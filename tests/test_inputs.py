@@ -117,3 +117,23 @@ def test_fp6_quantize_grid_and_ties():
         c = mi._quantize_fp6(mids.astype(np.float32), fmt)
         assert np.all(c % 2 == 0)  # ties go to the even code
         assert mi._quantize_fp6(np.array([1e9, -1e9], np.float32), fmt).tolist() == [31, 63]
+
+
+def test_preshuffle_layout_formula():
+    """The preshuffled layout against its definition, byte by byte: scale
+    (r, kb) at (r // 32) * 32 * KB + (kb // 4) * 128 + (r % 32) * 4 + kb % 4,
+    padding rows zero; a 32-row group keeps its byte range."""
+    g = np.random.Generator(np.random.PCG64(77))
+    for R, KB in ((1, 4), (31, 8), (32, 4), (33, 12), (70, 16), (64, 256)):
+        S = g.integers(1, 256, size=(R, KB), dtype=np.uint8)
+        P = mi.preshuffle_scales(S).reshape(-1)
+        Rp = (R + 31) // 32 * 32
+        assert P.size == Rp * KB
+        seen = np.zeros(P.size, bool)
+        for r in range(R):
+            for kb in range(KB):
+                o = (r // 32) * 32 * KB + (kb // 4) * 128 + (r % 32) * 4 + kb % 4
+                assert P[o] == S[r, kb]
+                seen[o] = True
+                assert r * KB // (32 * KB) == o // (32 * KB)  # same group, same range
+        assert np.all(P[~seen] == 0) and np.sum(~seen) == (Rp - R) * KB
