@@ -11,15 +11,13 @@ template <int FA, int FB, bool NATIVE, bool SPLIT>
 hipError_t launch_large_s(const mxg::GemmArgs &a, hipStream_t s)
 {
     const int blocks = a.tiles_m * a.tiles_n * a.splits;
-    // 16-byte scale windows need K % 512 == 0 and 16-byte aligned row-major
-    // scale rows (preshuffled scales take one coalesced dword per stage);
-    // the native variant has no registers to spare for them
-    if constexpr (!NATIVE) {
-        if (a.scale_dword == 2 && !a.scale_ps) {
-            hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, true, SPLIT>), dim3(blocks),
-                               dim3(mxg::large::THREADS), 0, s, a);
-            return hipGetLastError();
-        }
+    // 16-byte scale windows (in registers for the exact mode, through LDS for
+    // the scaled-MFMA modes) need K % 512 == 0 and 16-byte aligned row-major
+    // scale rows; preshuffled scales take one coalesced dword per stage
+    if (a.scale_dword == 2 && !a.scale_ps) {
+        hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, true, SPLIT>), dim3(blocks),
+                           dim3(mxg::large::THREADS), 0, s, a);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((mxg::large::kernel<FA, FB, NATIVE, false, SPLIT>), dim3(blocks),
                        dim3(mxg::large::THREADS), 0, s, a);

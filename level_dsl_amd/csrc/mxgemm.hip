@@ -456,8 +456,10 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
         if (tiles <= mxg::stream::MAX_SPLITS_TILES / 2) {
             // stages as the kernel counts them (bytes of a row per stage)
             const int nk = (a.K + stage_bytes - 1) / stage_bytes;
-            const bool scale16 = !native && a.scale_dword == 2 && !ps;  // the kernel's SCALE16
-            const int unit = scale16 ? mxg::large::WINDOW : 1;
+            // the kernel's SCALE16: 16-byte scale windows of 16 / (scale bytes
+            // per stage) stages, whole windows per split
+            const bool scale16 = a.scale_dword == 2 && !ps;
+            const int unit = scale16 ? mxg::large::window_stages(fp4) : 1;
             a.splits = choose_splits_large(h->splits, (int)tiles, nk / unit, unit, ws_bytes);
             if (strict && h->splits >= 2 &&
                 a.splits < choose_splits_large(h->splits, (int)tiles, nk / unit, unit, 0))

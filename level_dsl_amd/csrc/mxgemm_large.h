@@ -18,10 +18,15 @@
 //     barrier (measured 5-8% faster there; the exact mode measured better
 //     with the split, which keeps a 64-load burst from stalling its longer
 //     MFMA stream).
-//   * scales: with K % 512 == 0, each lane fetches 16 scale bytes of each of
-//     its 8 fragment rows at a time (four stages' worth, one dwordx4 load per
-//     row, prefetched a window ahead); otherwise one dword (or four bytes) per
-//     row per stage, prefetched one stage ahead.
+//   * scales: with row-major scales and K % 512 == 0 they come in 16-byte
+//     windows per row (four stages' worth; two for e2m1), prefetched a window
+//     ahead: the exact mode loads each lane's windows of its 8 fragment rows
+//     into registers (one dwordx4 per row); the scaled-MFMA modes load the
+//     windows of all 512 tile rows into LDS once per workgroup (one coalesced
+//     16-byte direct-to-LDS load per row) and read each stage's dwords from
+//     there.  Otherwise (and with preshuffled scales, where a wave's dword
+//     load is one 128-byte line) one dword (or four bytes) per row per stage,
+//     prefetched one stage ahead.
 //   * blocks: a stage is split into blocks (exact mode: the four 32-byte K
 //     blocks; native mode: the two 64-byte MFMA K steps).  While the MFMAs of
 //     block g run, the fragments of block g+1 are read from LDS (ds_read_b128)
@@ -67,7 +72,9 @@ constexpr int SUB_M = WAVE_M / 32, SUB_N = WAVE_N / 32;
 constexpr int TILE_BYTES = BM * BK;           // one operand, one stage (32 KiB)
 constexpr int SEG = 1024;                     // bytes one wave load instruction fills
 constexpr int SEGS_PER_WAVE = TILE_BYTES / SEG / WAVES;  // 8 per operand per stage
-constexpr int WINDOW = 4;                     // stages per 16-byte scale window
+// stages per 16-byte scale window: 128-byte stages of e2m1 (256 codes) hold
+// 8 scale blocks, all other stages 4
+__host__ __device__ constexpr int window_stages(bool fp4) { return fp4 ? 2 : 4; }
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -124,7 +131,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // per row and 128-byte stage and per-stage scale loads
     constexpr bool FP4 = FA == 4;
     static_assert(FP4 == (FB == 4), "e2m1 pairs only with e2m1");
-    static_assert(!FP4 || (NATIVE && !SCALE16), "e2m1 runs on the scaled MFMA");
+    static_assert(!FP4 || NATIVE, "e2m1 runs on the scaled MFMA");
     // e2m3 operands (format 2, four codes per three bytes): every product of
     // a 32-element block fits the scaled MFMA's 8-product window as well, so
     // they too run on it.  A stage is 128 codes, 96 bytes of a row: its four
@@ -135,15 +142,28 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // out as in the fp8 native mode (two 64-code steps per stage).
     constexpr bool FP6 = FA == 2;
     static_assert(FP6 == (FB == 2), "e2m3 pairs only with e2m3");
-    static_assert(!FP6 || (NATIVE && !SCALE16), "e2m3 runs on the scaled MFMA");
+    static_assert(!FP6 || NATIVE, "e2m3 runs on the scaled MFMA");
     constexpr int SB = FP6 ? 96 : BK;                     // bytes of a row per stage
     constexpr int SPS = FP4 ? 8 : 4;                     // scale bytes per row and stage
     constexpr int BLOCKS = NATIVE && !FP4 ? 2 : 4;        // blocks per stage
     constexpr int MF = NATIVE ? SUB_M * SUB_N : 2 * SUB_M * SUB_N;  // MFMAs per block
+    // SCALE16 (row-major scales, K % 512 == 0): the scale bytes of a row come
+    // in 16-byte windows of WIN stages.  Exact mode holds a lane's windows in
+    // registers (SREG).  The scaled-MFMA modes stage them through LDS (SLDS):
+    // the workgroup loads the windows of its 512 tile rows once, one
+    // coalesced 16-byte direct-to-LDS load per row, a window ahead, and each
+    // stage reads its dwords from there.  (Per-row dword loads from global
+    // memory cost each wave instruction 32 cache lines and were what held
+    // these modes back.)
+    constexpr bool SREG = SCALE16 && !NATIVE, SLDS = SCALE16 && NATIVE;
+    constexpr int WIN = SCALE16 ? window_stages(FP4) : 1;  // stages per window
+    static_assert(!SCALE16 || WIN * SPS == 16, "a window is 16 scale bytes");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][TILE_BYTES];  // [stage][A/B]
+    // SLDS: [window buffer][tile row (A rows 0..255, then B rows)][16 bytes]
+    __shared__ __attribute__((aligned(16))) uint8_t slds[SLDS ? 2 : 1][SLDS ? (BM + BN) * 16 : 16];
 
     // workgroup -> (tile, K split); split sp runs stages [ks0, ks0 + nk) of
-    // the nk_all stages (whole 4-stage scale windows when SCALE16)
+    // the nk_all stages (whole scale windows when SCALE16)
     const int ntiles = p.tiles_m * p.tiles_n;
     const int tile = SPLIT ? (int)(blockIdx.x % (unsigned)ntiles) : (int)blockIdx.x;
     const int sp = SPLIT ? (int)(blockIdx.x / (unsigned)ntiles) : 0;
@@ -166,7 +186,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     const int wm = wave & 1, wn = wave >> 1;
     const int lrow = lane & 31, khalf = lane >> 5;
     const int nk_all = (K + SB - 1) / SB;
-    constexpr int SPLIT_UNIT = SCALE16 ? WINDOW : 1;  // stages a split boundary is a multiple of
+    constexpr int SPLIT_UNIT = WIN;                   // stages a split boundary is a multiple of
     const int nu_all = nk_all / SPLIT_UNIT;           // SCALE16 needs K % 512 == 0: no remainder
     const int ks0 = SPLIT ? (int)((int64_t)sp * nu_all / p.splits) * SPLIT_UNIT : 0;
     const int nk = SPLIT ? (int)((int64_t)(sp + 1) * nu_all / p.splits) * SPLIT_UNIT - ks0 : nk_all;
@@ -202,8 +222,9 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     // ---- scales ---------------------------------------------------------
     // Fragment rows of this lane: A rows wm*128 + 32i + lrow, B rows
-    // wn*128 + 32j + lrow.  SCALE16: 16 bytes (4 stages) per row and load;
-    // otherwise one dword (or four bytes) per row and stage.  SCALE16 reads
+    // wn*128 + 32j + lrow.  SREG: 16 bytes (4 stages) per row and load;
+    // SLDS: a stage's dwords from the LDS window; otherwise one dword (or
+    // four bytes) per row and stage.  SCALE16 reads
     // row-major scales only; preshuffled scales take the per-stage dword
     // loads, each one 128-byte line for the wave's 32 rows.
     const uint32_t sra = (uint32_t)(wm * WAVE_M + lrow), srb = (uint32_t)(wn * WAVE_N + lrow);
@@ -236,6 +257,53 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                 xb2[j] = in ? load_scale4(rBs, srb + 32 * j, KB, kb1, p.scale_dword, ps) : 0u;
         }
     };
+    // SLDS: the window starting at local stage kt into LDS buffer (kt / WIN) & 1.
+    // Wave w loads tile rows 128 w .. 128 w + 127 (waves 0, 1: A; 2, 3: B), 64
+    // rows per instruction; rows past the tile and windows past K read zero
+    // or are never used.
+    auto swin = [&](int kt) MXG_INLINE {
+        if constexpr (SLDS) {
+            const int kb0 = (ks0 + kt) * SPS;
+            const bool in = kb0 < KB;
+            const bool isa = wave < 2;
+            const rsrc_t rs = isa ? rAs : rBs;
+            uint8_t *dst = slds[(kt / WIN) & 1];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r0 = 128 * wave + 64 * h;  // first tile row of the instruction
+                const uint32_t row = (uint32_t)((isa ? r0 : r0 - BM) + lane);
+                load16_lds(rs, dst + r0 * 16, in ? row * KB + kb0 : kOob);
+            }
+        }
+    };
+    // SLDS: local stage kt's scale dwords from its window (as scale4)
+    auto scale_lds = [&](int kt, uint32_t *xa, uint32_t *xb, uint32_t *xa2, uint32_t *xb2) MXG_INLINE {
+        if constexpr (SLDS) {
+            const uint8_t *w = slds[(kt / WIN) & 1] + (kt % WIN) * SPS;
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i) {
+                const uint8_t *q = w + srow_a(i) * 16;
+                if constexpr (FP4) {
+                    const v2i v = *reinterpret_cast<const v2i *>(q);
+                    xa[i] = (uint32_t)v[0];
+                    xa2[i] = (uint32_t)v[1];
+                } else {
+                    xa[i] = *reinterpret_cast<const uint32_t *>(q);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) {
+                const uint8_t *q = w + (BM + srow_b(j)) * 16;
+                if constexpr (FP4) {
+                    const v2i v = *reinterpret_cast<const v2i *>(q);
+                    xb[j] = (uint32_t)v[0];
+                    xb2[j] = (uint32_t)v[1];
+                } else {
+                    xb[j] = *reinterpret_cast<const uint32_t *>(q);
+                }
+            }
+        }
+    };
     // Exact mode: every scale byte the fast loop decodes with passes
     // through this check; a byte outside its format's window (where the
     // bf16 decode would round, overflow or misread byte 0 / 255) sends the
@@ -257,7 +325,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) {
                 uint32_t d = chk_b ? xb[i] : xa[i];
-                if constexpr (!SCALE16) d = mask_scale_tail(d, valid);  // SCALE16: KB % 16 == 0
+                if constexpr (!SREG) d = mask_scale_tail(d, valid);  // SREG: KB % 16 == 0
                 rg.add(live[i] ? d : 0x7f7f7f7fu, chk_lo2);
             }
         }
@@ -452,17 +520,23 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     Frags<NATIVE> f0, f1;
     uint32_t csa[SUB_M], csb[SUB_N];  // scale dwords of the stage being decoded
     uint32_t csa2[SUB_M], csb2[SUB_N], sa2_1[SUB_M], sb2_1[SUB_N];  // e2m1: bytes 4..7 of a stage
-    v4i wa[SUB_M], wb[SUB_N], na[SUB_M], nb[SUB_N];  // SCALE16 windows (current, next)
-    uint32_t sa1[SUB_M], sb1[SUB_N];  // !SCALE16: next stage's scale dwords
+    v4i wa[SUB_M], wb[SUB_N], na[SUB_M], nb[SUB_N];  // SREG windows (current, next)
+    uint32_t sa1[SUB_M], sb1[SUB_N];  // !SREG: next stage's scale dwords
 
-    // One stage.  SS: the stage's position in its 4-stage window (SCALE16),
+    // One stage.  SS: the stage's position in its scale window (SREG),
     // CROSS: whether the last block continues into stage kt+1.
     auto stage = [&](int kt, auto SS, auto CROSS) MXG_INLINE {
         constexpr int ss = decltype(SS)::value;
         constexpr bool cross = decltype(CROSS)::value;
         const int st = kt & 1;
-        if constexpr (SCALE16) {
-            if constexpr (ss == 0) scale16(kt + WINDOW, na, nb);  // next window, 4 stages ahead
+        if constexpr (SREG) {
+            if constexpr (ss == 0) scale16(kt + WIN, na, nb);  // next window, 4 stages ahead
+        } else if constexpr (SLDS) {
+            // next window into the other buffer (a wave-uniform test: the
+            // stage loop is not unrolled by windows here, which measured
+            // register spills)
+            if (kt % WIN == 0) swin(kt + WIN);
+            scale_lds(kt + 1, sa1, sb1, sa2_1, sb2_1);     // next stage
         } else {
             scale4(kt + 1, sa1, sb1, sa2_1, sb2_1);               // next stage
         }
@@ -504,14 +578,14 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
                 gload(st, kt + 2, int_c<0>{});  // A tile of stage kt+2
                 if constexpr (NATIVE) gload(st, kt + 2, int_c<1>{});  // and its B tile
                 // scale dwords of stage kt+1
-                if constexpr (SCALE16) {
-                    if constexpr (ss == WINDOW - 1) {
+                if constexpr (SREG) {
+                    if constexpr (ss == WIN - 1) {
 #pragma unroll
                         for (int i = 0; i < SUB_M; ++i) wa[i] = na[i];
 #pragma unroll
                         for (int j = 0; j < SUB_N; ++j) wb[j] = nb[j];
                     }
-                    constexpr int nx = (ss + 1) % WINDOW;
+                    constexpr int nx = (ss + 1) % WIN;
 #pragma unroll
                     for (int i = 0; i < SUB_M; ++i) csa[i] = (uint32_t)wa[i][nx];
 #pragma unroll
@@ -545,8 +619,10 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // ---- prologue ---------------------------------------------------------
     gload(0, 0, int_c<0>{});
     gload(0, 0, int_c<1>{});
-    if constexpr (SCALE16) {
+    if constexpr (SREG) {
         scale16(0, wa, wb);
+    } else if constexpr (SLDS) {
+        swin(0);
     } else {
         scale4(0, sa1, sb1, sa2_1, sb2_1);
     }
@@ -554,7 +630,8 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     __syncthreads();
     gload(1, 1, int_c<0>{});  // exact mode: stage 1's B tile follows in stage 0's first block
     if constexpr (NATIVE) gload(1, 1, int_c<1>{});
-    if constexpr (SCALE16) {
+    if constexpr (SLDS) scale_lds(0, sa1, sb1, sa2_1, sb2_1);
+    if constexpr (SREG) {
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) csa[i] = (uint32_t)wa[i][0];
 #pragma unroll
@@ -579,15 +656,15 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     prep_block(int_c<0>{}, raw, csa, csb, f0);
 
     // ---- main loop --------------------------------------------------------
-    if constexpr (SCALE16) {
+    if constexpr (SREG) {
         // nk is a multiple of the window; the last window's last stage ends
-        const int nw = nk / WINDOW;
+        const int nw = nk / WIN;
         for (int w = 0; w + 1 < nw; ++w)
-            static_for<WINDOW>([&](auto SS) MXG_INLINE { stage(WINDOW * w + decltype(SS)::value, SS, std::true_type{}); });
-        static_for<WINDOW - 1>([&](auto SS) MXG_INLINE {
-            stage(WINDOW * (nw - 1) + decltype(SS)::value, SS, std::true_type{});
+            static_for<WIN>([&](auto SS) MXG_INLINE { stage(WIN * w + decltype(SS)::value, SS, std::true_type{}); });
+        static_for<WIN - 1>([&](auto SS) MXG_INLINE {
+            stage(WIN * (nw - 1) + decltype(SS)::value, SS, std::true_type{});
         });
-        stage(nk - 1, int_c<WINDOW - 1>{}, std::false_type{});
+        stage(nk - 1, int_c<WIN - 1>{}, std::false_type{});
     } else {
         for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, int_c<0>{}, std::true_type{});
         stage(nk - 1, int_c<0>{}, std::false_type{});
