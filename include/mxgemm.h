@@ -203,9 +203,9 @@ int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream)
 
 /* Number of K splits: 0 (default) chooses it from the shape, 1 never
  * splits, S >= 2 forces S splits, reduced to at most the number of 128-byte
- * K stages (of whole 16-byte scale windows -- 4 stages, 2 for e2m1 --
- * where the large kernel reads row-major scales with K % 512 == 0), to 256 / output tiles, and to the partials
- * the workspace holds.  Applies to every kernel.  A forced S >= 2
+ * K stages (of whole 16-byte scale windows -- 4 stages, 2 for e2m1 -- where
+ * the large kernel reads row-major scales with K % 512 == 0), to 256 /
+ * output tiles, and to the partials the workspace holds.  Applies to every kernel.  A forced S >= 2
  * that survives this makes mxgemm_run return MXGEMM_ERR_WORKSPACE when no
  * workspace is attached.  MXGEMM_ERR_SHAPE for S < 0. */
 int mxgemm_set_splits(mxgemm_t h, int splits);
