@@ -14,6 +14,8 @@ Also reported on the same line:
   * native: the same 8192^3 workload on the native scaled-MFMA variant;
   * mxfp4 / mxfp6: the 8192^3 shape with e2m1 / e2m3 operands (exact on the
     scaled MFMA), and the M = 64 decode shape with them;
+  * preshuffled_scales_8192cube: the exact, native and e2m1 8192^3 paths
+    with their scales in the preshuffled layout (mxgemm_set_scale_layout);
   * mx_quantize: MX block quantization of the skinny workload's fp32 weight
     (28672 x 8192 -> e4m3 codes + e8m0 scales) in GB/s of algorithmic bytes
     (X read once, codes and scales written once), inputs rotated over 3
@@ -125,11 +127,13 @@ def time_launches(run_step, steps: int, warmup: int, stream):
     return wall, start.elapsed_time(end) * 1e-3 / steps
 
 
-def upload(p, copies: int, rotate_a: bool = True):
+def upload(p, copies: int, rotate_a: bool = True, preshuffled: bool = False):
     import torch
+    import mxinputs as mi
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    A, As, B, Bs = t(p.A), t(p.As), t(p.B), t(p.Bs)
+    sc = mi.preshuffle_scales if preshuffled else (lambda x: x)
+    A, As, B, Bs = t(p.A), t(sc(p.As)), t(p.B), t(sc(p.Bs))
     sets = [(A, As, B, Bs)]
     for _ in range(copies - 1):
         sets.append((A.clone() if rotate_a else A, As.clone() if rotate_a else As,
@@ -138,9 +142,12 @@ def upload(p, copies: int, rotate_a: bool = True):
 
 
 def bench_gemm(gemm, p, variant, steps, warmup, copies):
+    """Time `steps` launches on `gemm` (whose scale layout decides how the
+    scales are uploaded) over `copies` rotating input sets."""
     import torch
     import level_dsl_amd as L
-    sets = upload(p, copies, rotate_a=p.M > 64)
+    sets = upload(p, copies, rotate_a=p.M > 64,
+                  preshuffled=gemm.scale_layout == L.MXGEMM_SCALES_PRESHUFFLED)
     dt = torch.float32 if p.out_dtype == 0 else torch.bfloat16
     C = [torch.empty((p.M, p.N), dtype=dt, device="cuda:0") for _ in range(copies)]
     stream = torch.cuda.current_stream()
@@ -248,9 +255,9 @@ TRAFFIC_KERNELS = {"large_exact": ("void mxg::large::kernel<0, 0, false, true, f
                                    "MXGEMM_VARIANT_LARGE", 2),
                    "skinny_exact": ("void mxg::stream::kernel<0, 0, true, 4>", 3,
                                     "MXGEMM_VARIANT_SKINNY", 4),
-                   "large_native": ("void mxg::large::kernel<0, 0, true, false, false>", 2,
+                   "large_native": ("void mxg::large::kernel<0, 0, true, true, false>", 2,
                                     "MXGEMM_VARIANT_LARGE_NATIVE", 2),
-                   "mxfp4_large": ("void mxg::large::kernel<4, 4, true, false, false>", "e2m1_8192",
+                   "mxfp4_large": ("void mxg::large::kernel<4, 4, true, true, false>", "e2m1_8192",
                                    "MXGEMM_VARIANT_AUTO", 2)}
 
 
@@ -491,6 +498,7 @@ def main():
         "achieved_per_launch": round(flops / mean_n / 1e12, 2), "peak": PEAK_TFLOPS["fp8"],
         "frac": round(flops / mean_n / 1e12 / PEAK_TFLOPS["fp8"], 4),
         "launch_mean_us": round(mean_n * 1e6, 2),
+        "kernel": "mxg::large::kernel<0,0,true,true,false> (scale windows through LDS)",
         "traffic": traffic_from_profiles("large_native"),
         "note": "v_mfma_scale_f32_32x32x64_f8f6f4; not within 1e-5*sum|ab| (8-product "
                 "groups truncated 13 bits below their largest product)"}
@@ -502,6 +510,20 @@ def main():
     p4 = e2m1_8192()
     log("bench: e2m1 8192^3 generated")
     wall_4, mean_4 = bench_gemm(gemm, p4, L.MXGEMM_VARIANT_AUTO, steps, warmup, 3)
+    # the same three 8192^3 paths with scales in the preshuffled layout
+    # (mxgemm_set_scale_layout): per-stage coalesced scale loads instead of
+    # the 16-byte row windows
+    gps = L.Gemm()
+    gps.set_scale_layout(L.MXGEMM_SCALES_PRESHUFFLED)
+    pre = {}
+    for key, q, v in (("exact", p, L.MXGEMM_VARIANT_LARGE), ("native", p, L.MXGEMM_VARIANT_LARGE_NATIVE),
+                      ("e2m1", p4, L.MXGEMM_VARIANT_AUTO)):
+        _, m = bench_gemm(gps, q, v, steps, warmup, 3)
+        pre[key] = {"launch_mean_us": round(m * 1e6, 2), "unit": "TFLOP/s",
+                    "achieved_per_launch": round(flops / m / 1e12, 2)}
+        log(f"bench: preshuffled scales, {key}: {pre[key]['achieved_per_launch']} TFLOP/s per launch")
+    gps.close()
+    out["preshuffled_scales_8192cube"] = pre
     del p4
     out["mxfp4"] = {
         "value": round(flops * steps / wall_4 / 1e12, 2), "unit": "TFLOP/s",
@@ -511,7 +533,7 @@ def main():
                      "peak": PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
                      "frac": round(flops / mean_4 / 1e12 / PEAK_TFLOPS["fp4"], 4),
                      "traffic": traffic_from_profiles("mxfp4_large"),
-                     "kernel": "mxg::large::kernel<4,4,true,false,false>",
+                     "kernel": "mxg::large::kernel<4,4,true,true,false> (scale windows through LDS)",
                      "launch_mean_us": round(mean_4 * 1e6, 2)}}
     log(f"bench: e2m1 {out['mxfp4']['value']} TFLOP/s")
 
@@ -531,7 +553,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops / mean_6 / 1e12, 2),
                      "peak": PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
                      "frac": round(flops / mean_6 / 1e12 / PEAK_TFLOPS["fp4"], 4),
-                     "kernel": "mxg::large::kernel<2,2,true,false,false>",
+                     "kernel": "mxg::large::kernel<2,2,true,true,false> (scale windows through LDS)",
                      "launch_mean_us": round(mean_6 * 1e6, 2)}}
     log(f"bench: e2m3 {out['mxfp6']['value']} TFLOP/s")
 
