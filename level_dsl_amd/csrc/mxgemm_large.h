@@ -333,12 +333,16 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     // native mode: the upper lane half supplies the odd K blocks (fp8: of
     // each 64-element MFMA step; e2m1: each lane half holds one block)
+    // (a shift by 8 khalf, not a branch on khalf: a lane-divergent branch
+    // would split the MFMA block's scheduling region, and the interleave of
+    // LDS reads with MFMAs would be lost)
     auto native_shift = [&](uint32_t *xa, uint32_t *xb) MXG_INLINE {
-        if (NATIVE && khalf) {
+        if constexpr (NATIVE) {
+            const uint32_t sh = 8u * (uint32_t)khalf;
 #pragma unroll
-            for (int i = 0; i < SUB_M; ++i) xa[i] >>= 8;
+            for (int i = 0; i < SUB_M; ++i) xa[i] >>= sh;
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) xb[j] >>= 8;
+            for (int j = 0; j < SUB_N; ++j) xb[j] >>= sh;
         }
     };
 
@@ -532,11 +536,14 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         if constexpr (SREG) {
             if constexpr (ss == 0) scale16(kt + WIN, na, nb);  // next window, 4 stages ahead
         } else if constexpr (SLDS) {
-            // next window into the other buffer (a wave-uniform test: the
-            // stage loop is not unrolled by windows here, which measured
-            // register spills)
+            // next stage's scale dwords, then the next window into the other
+            // buffer (a wave-uniform test: the stage loop is not unrolled by
+            // windows here, which measured register spills).  The reads come
+            // first: the compiler orders LDS reads of the window buffers
+            // after any direct-to-LDS load into them, with a vmcnt wait that
+            // would also drain the operand loads in flight.
+            scale_lds(kt + 1, sa1, sb1, sa2_1, sb2_1);
             if (kt % WIN == 0) swin(kt + WIN);
-            scale_lds(kt + 1, sa1, sb1, sa2_1, sb2_1);     // next stage
         } else {
             scale4(kt + 1, sa1, sb1, sa2_1, sb2_1);               // next stage
         }
