@@ -106,6 +106,20 @@ __device__ __forceinline__ void load16_lds(rsrc_t r, void *lds_base, uint32_t of
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, off, 0, 0, 0);
 }
 
+// x itself, hidden from the optimizer's reassociation of address arithmetic
+// (an empty asm statement: no instruction is emitted).  v: a per-lane
+// value, s: a wave-uniform one.
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x)
+{
+    asm("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x)
+{
+    asm("" : "+s"(x));
+    return x;
+}
+
 // Wait until every vector-memory operation of this wave has completed,
 // including loads that write LDS directly, which the compiler does not
 // track (s_waitcnt vmcnt(0)).

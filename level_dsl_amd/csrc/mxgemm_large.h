@@ -158,9 +158,16 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     constexpr bool SREG = SCALE16 && !NATIVE, SLDS = SCALE16 && NATIVE;
     constexpr int WIN = SCALE16 ? window_stages(FP4) : 1;  // stages per window
     static_assert(!SCALE16 || WIN * SPS == 16, "a window is 16 scale bytes");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][TILE_BYTES];  // [stage][A/B]
+    static_assert(WIN % 2 == 0 || !SCALE16, "stage parity follows the window position");
+    // The two stage buffers are separate LDS objects ([A/B] each): a read of
+    // one can then be told apart from direct-to-LDS loads into the other, and
+    // the compiler does not drain those loads before it.
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[2][TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[2][TILE_BYTES];
+    auto lbuf = [&](int st, int op) MXG_INLINE -> uint8_t * { return st ? lds1[op] : lds0[op]; };
     // SLDS: [window buffer][tile row (A rows 0..255, then B rows)][16 bytes]
-    __shared__ __attribute__((aligned(16))) uint8_t slds[SLDS ? 2 : 1][SLDS ? (BM + BN) * 16 : 16];
+    constexpr int SWIN_BYTES = (BM + BN) * 16;
+    __shared__ __attribute__((aligned(16))) uint8_t slds[SLDS ? 2 * SWIN_BYTES : 16];
 
     // workgroup -> (tile, K split); split sp runs stages [ks0, ks0 + nk) of
     // the nk_all stages (whole scale windows when SCALE16)
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             const int g = FP6 ? 24 * (c >> 1) + 16 * (c & 1) : 16 * c;
             const bool in = FP6 ? k0 + 24 * (c >> 1) < K : k0 + g < K;
             const uint32_t off = in ? grow + (uint32_t)(8 * j) * K + g + k0 : kOob;
-            load16_lds(op == 0 ? rA : rB, &lds[st][op][s * SEG], off);
+            load16_lds(op == 0 ? rA : rB, lbuf(st, op) + s * SEG, off);
         }
     };
 
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             const bool in = kb0 < KB;
             const bool isa = wave < 2;
             const rsrc_t rs = isa ? rAs : rBs;
-            uint8_t *dst = slds[(kt / WIN) & 1];
+            uint8_t *dst = slds + ((kt / WIN) & 1) * SWIN_BYTES;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int r0 = 128 * wave + 64 * h;  // first tile row of the instruction
@@ -277,12 +284,18 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         }
     };
     // SLDS: local stage kt's scale dwords from its window (as scale4)
+    // Each address is the base plus a stage offset plus a lane offset (plus
+    // a constant), both kept whole: a longer chain of address steps loses
+    // the compiler's record of which LDS object is read, and with it the
+    // knowledge that the direct-to-LDS loads in flight write other objects
+    // (it would wait for them all before the read).
+    const uint32_t soff_a = opaque_v(sra * 16), soff_b = opaque_v((BM + srb) * 16);
     auto scale_lds = [&](int kt, uint32_t *xa, uint32_t *xb, uint32_t *xa2, uint32_t *xb2) MXG_INLINE {
         if constexpr (SLDS) {
-            const uint8_t *w = slds[(kt / WIN) & 1] + (kt % WIN) * SPS;
+            const uint8_t *w = slds + opaque_s((uint32_t)(((kt / WIN) & 1) * SWIN_BYTES + (kt % WIN) * SPS));
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) {
-                const uint8_t *q = w + srow_a(i) * 16;
+                const uint8_t *q = w + soff_a + i * 32 * 16;
                 if constexpr (FP4) {
                     const v2i v = *reinterpret_cast<const v2i *>(q);
                     xa[i] = (uint32_t)v[0];
@@ -293,7 +306,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             }
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j) {
-                const uint8_t *q = w + (BM + srow_b(j)) * 16;
+                const uint8_t *q = w + soff_b + j * 32 * 16;
                 if constexpr (FP4) {
                     const v2i v = *reinterpret_cast<const v2i *>(q);
                     xb[j] = (uint32_t)v[0];
@@ -352,7 +365,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     // read block `blk` of LDS stage `st` (exact: into raw; native: straight
     // into the MFMA operands f)
     auto read_block = [&](int st, int blk, Raw<NATIVE> &r, Frags<NATIVE> &f) MXG_INLINE {
-        const uint8_t *la = lds[st][0] + fa_off, *lb = lds[st][1] + fb_off;
+        const uint8_t *la = lbuf(st, 0) + fa_off, *lb = lbuf(st, 1) + fb_off;
         if constexpr (FP4) {
             // block blk = MFMA step blk: lane half h takes chunk 2 blk + h,
             // the 32 codes of one scale block (the operand layout of the
@@ -529,10 +542,13 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 
     // One stage.  SS: the stage's position in its scale window (SREG),
     // CROSS: whether the last block continues into stage kt+1.
-    auto stage = [&](int kt, auto SS, auto CROSS) MXG_INLINE {
+    auto stage = [&](int kt, auto SS, auto CROSS, auto PAR) MXG_INLINE {
         constexpr int ss = decltype(SS)::value;
         constexpr bool cross = decltype(CROSS)::value;
-        const int st = kt & 1;
+        // stage buffer: a compile-time parity where the loop is unrolled by
+        // two (PAR 0 / 1), else kt & 1 (PAR -1)
+        constexpr int par = decltype(PAR)::value;
+        const int st = par >= 0 ? par : (kt & 1);
         if constexpr (SREG) {
             if constexpr (ss == 0) scale16(kt + WIN, na, nb);  // next window, 4 stages ahead
         } else if constexpr (SLDS) {
@@ -667,15 +683,39 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         // nk is a multiple of the window; the last window's last stage ends
         const int nw = nk / WIN;
         for (int w = 0; w + 1 < nw; ++w)
-            static_for<WIN>([&](auto SS) MXG_INLINE { stage(WIN * w + decltype(SS)::value, SS, std::true_type{}); });
+            static_for<WIN>([&](auto SS) MXG_INLINE {
+                constexpr int ss = decltype(SS)::value;
+                stage(WIN * w + ss, SS, std::true_type{}, int_c<ss & 1>{});
+            });
         static_for<WIN - 1>([&](auto SS) MXG_INLINE {
-            stage(WIN * (nw - 1) + decltype(SS)::value, SS, std::true_type{});
+            constexpr int ss = decltype(SS)::value;
+            stage(WIN * (nw - 1) + ss, SS, std::true_type{}, int_c<ss & 1>{});
         });
-        stage(nk - 1, int_c<WIN - 1>{}, std::false_type{});
+        stage(nk - 1, int_c<WIN - 1>{}, std::false_type{}, int_c<1>{});
+    } else if constexpr (SLDS && !FP6) {
+        // two stages per iteration, so that each copy names its stage buffer
+        // at compile time and the compiler does not drain the direct-to-LDS
+        // loads into one buffer before reading the other (e2m3 fragments
+        // leave too few registers for the larger loop: it spills there); the
+        // last two stages take the parity at run time (nk is even)
+        int kt = 0;
+        for (; kt + 2 < nk; kt += 2) {
+            stage(kt, int_c<0>{}, std::true_type{}, int_c<0>{});
+            stage(kt + 1, int_c<0>{}, std::true_type{}, int_c<1>{});
+        }
+        stage(kt, int_c<0>{}, std::true_type{}, int_c<0>{});
+        stage(kt + 1, int_c<0>{}, std::false_type{}, int_c<1>{});
     } else {
-        for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, int_c<0>{}, std::true_type{});
-        stage(nk - 1, int_c<0>{}, std::false_type{});
+        for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, int_c<0>{}, std::true_type{}, int_c<-1>{});
+        stage(nk - 1, int_c<0>{}, std::false_type{}, int_c<-1>{});
     }
+
+    // every accumulator is complete here (keeps the last stage's MFMAs out
+    // of the epilogue's branches, where their operands would stay live)
+#pragma unroll
+    for (int i = 0; i < SUB_M; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     // ---- epilogue ---------------------------------------------------------
     // acc[i][j] register r of lane l: m = 32 i + (l % 32),
