@@ -122,6 +122,147 @@ struct Raw<true> {};  // native fragments are read straight into the operand reg
 constexpr int SG_VALU = 0x002, SG_SALU = 0x004, SG_MFMA = 0x008, SG_VMEM_RD = 0x020,
               SG_DS_RD = 0x100;
 
+// ---- epilogue ---------------------------------------------------------------
+// Store a wave's 128 x 128 accumulators acc (fp32 or bf16 C, optionally
+// accumulating into it).  Split K (p.splits > 1): the partial goes to the
+// workspace and the last split to arrive adds them up.  slow: the wave
+// recomputes its outputs with slow_tile(i, j) instead (exact mode's
+// fallback for scale bytes outside the decode window).
+template <bool SPLIT, class SlowTile>
+__device__ __forceinline__ void store_tile(const GemmArgs &p, v16f (&acc)[SUB_M][SUB_N], int tile, int sp,
+                                           int ntiles, int m0, int n0, int rows_a, int wm, int wn,
+                                           int lrow, int khalf, bool slow, SlowTile &&slow_tile)
+{
+    // acc[i][j] register r of lane l: m = 32 i + (l % 32),
+    // n = 32 j + 8 (r / 4) + 4 (l / 32) + (r % 4), relative to the wave tile.
+    // Group x = 4 (SUB_N i + j) + g of a lane is registers 4g..4g+3 of acc[i][j].
+    const int esz = p.out_bf16 ? 2 : 4;
+    const rsrc_t rC = make_rsrc((uint8_t *)p.C + ((size_t)m0 * p.N) * esz,
+                                (uint32_t)rows_a * p.N * esz);
+    const int N = p.N;
+    auto store_group = [&](int i, int j, int g, v4f v) MXG_INLINE {
+        const int m = wm * WAVE_M + i * 32 + lrow;                      // tile-local row
+        const int n = n0 + wn * WAVE_N + j * 32 + 8 * g + 4 * khalf;  // global column
+        store_c4(rC, (uint32_t)m * N + n, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
+    };
+    constexpr int GROUPS = SUB_M * SUB_N * 4;  // 16-byte groups per lane
+    // bf16 output with N % 8 == 0: groups g (even) and g + 1 of a sub-tile
+    // are stored as 16-byte rows of 8 bf16.  Lane l holds columns 8g + 4 kh
+    // .. + 3 of both groups (kh = l / 32) and the lane l ^ 32 the other four
+    // of each, so the two lane halves swap one group: the lower half keeps
+    // group g and takes its partner's half of it, the upper half group g + 1.
+    const bool wide_bf16 = p.out_bf16 && p.c_vec == 2;
+    auto store_pair = [&](int i, int j, int g, v4f x, v4f y) MXG_INLINE {  // groups g, g + 1
+        const int kh = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
+        const int lr = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 31);
+        v4f send = kh ? x : y, recv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) recv[e] = __shfl_xor(send[e], 32, 64);
+        const v4f lo = kh ? recv : x, hi = kh ? y : recv;
+        const int m = wm * WAVE_M + i * 32 + lr;                       // tile-local row
+        const int n = n0 + wn * WAVE_N + j * 32 + 8 * (g + kh);      // global column
+        store_bf16x8(rC, (uint32_t)m * N + n, n, N, lo, hi, p.use_acc);
+    };
+
+    if constexpr (SPLIT) {
+        // Split K (p.splits > 1): every split stores its wave's fp32 partial
+        // (the 64 groups of each lane, 1 KiB per store instruction) with
+        // device-coherent (sc1) buffer stores; per (tile, wave) an arrival
+        // counter counts the splits that are done, and the wave that
+        // completes the count adds all partials in split order 0, 1, ...
+        // (deterministic), PER groups at a time, writes them to C and resets
+        // the counter.  The sc1 accesses bypass the per-XCD L2s'
+        // non-coherent copies, so waiting for the stores to complete is the
+        // whole release (no L2 writeback).
+        constexpr int SC1 = 16;
+        constexpr uint32_t WAVE_PART = GROUPS * 64 * 16;  // one wave's partial, bytes
+        // the lane index again (mbcnt), so that nothing lane-dependent has to
+        // stay live across the main loop for this path
+        const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+        const rsrc_t rW = make_rsrc(p.ws, (uint32_t)p.splits * ntiles * WAVES * WAVE_PART);
+        const uint32_t lane_off = (uint32_t)(tile * WAVES + wave) * WAVE_PART + lane * 16;
+        const uint32_t split_pitch = (uint32_t)ntiles * WAVES * WAVE_PART;
+        // group x = 4 (SUB_N i + j) + g of the partial
+        auto put = [&](int i, int j, const v16f &v) MXG_INLINE {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const v4f q = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(v4i, q), rW,
+                    lane_off + sp * split_pitch + (4 * (SUB_N * i + j) + g) * 1024, 0, SC1);
+            }
+        };
+        if (slow) {
+            for (int t = 0; t < SUB_M * SUB_N; ++t) put(t / SUB_N, t % SUB_N, slow_tile(t / SUB_N, t % SUB_N));
+        } else {
+            static_for<SUB_M * SUB_N>([&](auto T) MXG_INLINE {
+                constexpr int t = decltype(T)::value;
+                put(t / SUB_N, t % SUB_N, acc[t / SUB_N][t % SUB_N]);
+            });
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partial has reached the coherent level
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        uint32_t *cnt = p.cnt + tile * WAVES + wave;
+        uint32_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = (uint32_t)__shfl((int)old, 0, 64);
+        if (old != (uint32_t)(p.splits - 1)) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        constexpr int PER = 8;  // groups summed at a time (loads in flight per split)
+        static_for<GROUPS / PER>([&](auto Bt) MXG_INLINE {
+            constexpr int b = decltype(Bt)::value;
+            v4f sum[PER];
+            for (int q = 0; q < p.splits; ++q) {
+                v4f part[PER];
+                static_for<PER>([&](auto Y) MXG_INLINE {
+                    constexpr int y = decltype(Y)::value;
+                    part[y] = __builtin_bit_cast(
+                        v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                 rW, lane_off + q * split_pitch + (b * PER + y) * 1024, 0, SC1));
+                });
+#pragma unroll
+                for (int y = 0; y < PER; ++y) sum[y] = q == 0 ? part[y] : sum[y] + part[y];
+            }
+            if (wide_bf16) {
+                static_for<PER / 2>([&](auto Y) MXG_INLINE {
+                    constexpr int y = 2 * decltype(Y)::value, x = b * PER + y;
+                    store_pair(x / (SUB_N * 4), (x / 4) % SUB_N, x % 4, sum[y], sum[y + 1]);
+                });
+            } else {
+                static_for<PER>([&](auto Y) MXG_INLINE {
+                    constexpr int x = b * PER + decltype(Y)::value;
+                    store_group(x / (SUB_N * 4), (x / 4) % SUB_N, x % 4, sum[decltype(Y)::value]);
+                });
+            }
+        });
+
+    } else {
+        auto put = [&](int i, int j, const v16f &v) MXG_INLINE {
+            if (wide_bf16) {
+#pragma unroll
+                for (int g = 0; g < 4; g += 2)
+                    store_pair(i, j, g, v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]},
+                               v4f{v[4 * g + 4], v[4 * g + 5], v[4 * g + 6], v[4 * g + 7]});
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    store_group(i, j, g, v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]});
+            }
+        };
+        if (slow) {
+            for (int t = 0; t < SUB_M * SUB_N; ++t) put(t / SUB_N, t % SUB_N, slow_tile(t / SUB_N, t % SUB_N));
+        } else {
+            static_for<SUB_M * SUB_N>([&](auto T) MXG_INLINE {
+                constexpr int t = decltype(T)::value;
+                put(t / SUB_N, t % SUB_N, acc[t / SUB_N][t % SUB_N]);
+            });
+        }
+    }
+}
+
 template <int FA, int FB, bool NATIVE, bool SCALE16, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
 {
@@ -159,6 +300,11 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     constexpr int WIN = SCALE16 ? window_stages(FP4) : 1;  // stages per window
     static_assert(!SCALE16 || WIN * SPS == 16, "a window is 16 scale bytes");
     static_assert(WIN % 2 == 0 || !SCALE16, "stage parity follows the window position");
+    // Main loops that run two stages per iteration (compile-time buffer
+    // parity), where they fit in the registers: e2m3 and the fp8 scaled-MFMA
+    // loop with per-stage scale loads spill in them and keep one stage per
+    // iteration.
+    constexpr bool PAIR = !SREG && !FP6 && (SLDS || FP4 || !NATIVE);
     // The two stage buffers are separate LDS objects ([A/B] each): a read of
     // one can then be told apart from direct-to-LDS loads into the other, and
     // the compiler does not drain those loads before it.
@@ -692,19 +838,22 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
             stage(WIN * (nw - 1) + ss, SS, std::true_type{}, int_c<ss & 1>{});
         });
         stage(nk - 1, int_c<WIN - 1>{}, std::false_type{}, int_c<1>{});
-    } else if constexpr (SLDS && !FP6) {
+    } else if constexpr (PAIR) {
         // two stages per iteration, so that each copy names its stage buffer
         // at compile time and the compiler does not drain the direct-to-LDS
-        // loads into one buffer before reading the other (e2m3 fragments
-        // leave too few registers for the larger loop: it spills there); the
-        // last two stages take the parity at run time (nk is even)
+        // loads into one buffer before reading the other
         int kt = 0;
         for (; kt + 2 < nk; kt += 2) {
             stage(kt, int_c<0>{}, std::true_type{}, int_c<0>{});
             stage(kt + 1, int_c<0>{}, std::true_type{}, int_c<1>{});
         }
-        stage(kt, int_c<0>{}, std::true_type{}, int_c<0>{});
-        stage(kt + 1, int_c<0>{}, std::false_type{}, int_c<1>{});
+        if constexpr (SLDS) {  // nk is even
+            stage(kt, int_c<0>{}, std::true_type{}, int_c<0>{});
+            stage(kt + 1, int_c<0>{}, std::false_type{}, int_c<1>{});
+        } else {
+            if (kt + 1 < nk) stage(kt++, int_c<0>{}, std::true_type{}, int_c<-1>{});
+            stage(kt, int_c<0>{}, std::false_type{}, int_c<-1>{});
+        }
     } else {
         for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, int_c<0>{}, std::true_type{}, int_c<-1>{});
         stage(nk - 1, int_c<0>{}, std::false_type{}, int_c<-1>{});
@@ -716,38 +865,6 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     for (int i = 0; i < SUB_M; ++i)
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) asm volatile("" : "+a"(acc[i][j]));
-
-    // ---- epilogue ---------------------------------------------------------
-    // acc[i][j] register r of lane l: m = 32 i + (l % 32),
-    // n = 32 j + 8 (r / 4) + 4 (l / 32) + (r % 4), relative to the wave tile.
-    // Group x = 4 (SUB_N i + j) + g of a lane is registers 4g..4g+3 of acc[i][j].
-    const int esz = p.out_bf16 ? 2 : 4;
-    const rsrc_t rC = make_rsrc((uint8_t *)p.C + ((size_t)m0 * p.N) * esz,
-                                (uint32_t)rows_a * p.N * esz);
-    const int N = p.N;
-    auto store_group = [&](int i, int j, int g, v4f v) MXG_INLINE {
-        const int m = wm * WAVE_M + i * 32 + lrow;                      // tile-local row
-        const int n = n0 + wn * WAVE_N + j * 32 + 8 * g + 4 * khalf;  // global column
-        store_c4(rC, (uint32_t)m * N + n, n, N, v, p.out_bf16, p.use_acc, p.c_vec);
-    };
-    constexpr int GROUPS = SUB_M * SUB_N * 4;  // 16-byte groups per lane
-    // bf16 output with N % 8 == 0: groups g (even) and g + 1 of a sub-tile
-    // are stored as 16-byte rows of 8 bf16.  Lane l holds columns 8g + 4 kh
-    // .. + 3 of both groups (kh = l / 32) and the lane l ^ 32 the other four
-    // of each, so the two lane halves swap one group: the lower half keeps
-    // group g and takes its partner's half of it, the upper half group g + 1.
-    const bool wide_bf16 = p.out_bf16 && p.c_vec == 2;
-    auto store_pair = [&](int i, int j, int g, v4f x, v4f y) MXG_INLINE {  // groups g, g + 1
-        const int kh = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
-        const int lr = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 31);
-        v4f send = kh ? x : y, recv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) recv[e] = __shfl_xor(send[e], 32, 64);
-        const v4f lo = kh ? recv : x, hi = kh ? y : recv;
-        const int m = wm * WAVE_M + i * 32 + lr;                       // tile-local row
-        const int n = n0 + wn * WAVE_N + j * 32 + 8 * (g + kh);      // global column
-        store_bf16x8(rC, (uint32_t)m * N + n, n, N, lo, hi, p.use_acc);
-    };
 
     // ---- fallback for scale bytes outside the window (exact mode) ---------
     // A wave whose A rows or B rows carry a scale byte outside its format's
@@ -799,103 +916,7 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
         return s;
     };
 
-    if constexpr (SPLIT) {
-        // Split K (p.splits > 1): every split stores its wave's fp32 partial
-        // (the 64 groups of each lane, 1 KiB per store instruction) with
-        // device-coherent (sc1) buffer stores; per (tile, wave) an arrival
-        // counter counts the splits that are done, and the wave that
-        // completes the count adds all partials in split order 0, 1, ...
-        // (deterministic), PER groups at a time, writes them to C and resets
-        // the counter.  The sc1 accesses bypass the per-XCD L2s'
-        // non-coherent copies, so waiting for the stores to complete is the
-        // whole release (no L2 writeback).
-        constexpr int SC1 = 16;
-        constexpr uint32_t WAVE_PART = GROUPS * 64 * 16;  // one wave's partial, bytes
-        // the lane index again (mbcnt), so that nothing lane-dependent has to
-        // stay live across the main loop for this path
-        const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-        const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-        const rsrc_t rW = make_rsrc(p.ws, (uint32_t)p.splits * ntiles * WAVES * WAVE_PART);
-        const uint32_t lane_off = (uint32_t)(tile * WAVES + wave) * WAVE_PART + lane * 16;
-        const uint32_t split_pitch = (uint32_t)ntiles * WAVES * WAVE_PART;
-        // group x = 4 (SUB_N i + j) + g of the partial
-        auto put = [&](int i, int j, const v16f &v) MXG_INLINE {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const v4f q = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(v4i, q), rW,
-                    lane_off + sp * split_pitch + (4 * (SUB_N * i + j) + g) * 1024, 0, SC1);
-            }
-        };
-        if (slow) {
-            for (int t = 0; t < SUB_M * SUB_N; ++t) put(t / SUB_N, t % SUB_N, slow_tile(t / SUB_N, t % SUB_N));
-        } else {
-            static_for<SUB_M * SUB_N>([&](auto T) MXG_INLINE {
-                constexpr int t = decltype(T)::value;
-                put(t / SUB_N, t % SUB_N, acc[t / SUB_N][t % SUB_N]);
-            });
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partial has reached the coherent level
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        uint32_t *cnt = p.cnt + tile * WAVES + wave;
-        uint32_t old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = (uint32_t)__shfl((int)old, 0, 64);
-        if (old != (uint32_t)(p.splits - 1)) return;
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        constexpr int PER = 8;  // groups summed at a time (loads in flight per split)
-        static_for<GROUPS / PER>([&](auto Bt) MXG_INLINE {
-            constexpr int b = decltype(Bt)::value;
-            v4f sum[PER];
-            for (int q = 0; q < p.splits; ++q) {
-                v4f part[PER];
-                static_for<PER>([&](auto Y) MXG_INLINE {
-                    constexpr int y = decltype(Y)::value;
-                    part[y] = __builtin_bit_cast(
-                        v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                 rW, lane_off + q * split_pitch + (b * PER + y) * 1024, 0, SC1));
-                });
-#pragma unroll
-                for (int y = 0; y < PER; ++y) sum[y] = q == 0 ? part[y] : sum[y] + part[y];
-            }
-            if (wide_bf16) {
-                static_for<PER / 2>([&](auto Y) MXG_INLINE {
-                    constexpr int y = 2 * decltype(Y)::value, x = b * PER + y;
-                    store_pair(x / (SUB_N * 4), (x / 4) % SUB_N, x % 4, sum[y], sum[y + 1]);
-                });
-            } else {
-                static_for<PER>([&](auto Y) MXG_INLINE {
-                    constexpr int x = b * PER + decltype(Y)::value;
-                    store_group(x / (SUB_N * 4), (x / 4) % SUB_N, x % 4, sum[decltype(Y)::value]);
-                });
-            }
-        });
-
-    } else {
-        auto put = [&](int i, int j, const v16f &v) MXG_INLINE {
-            if (wide_bf16) {
-#pragma unroll
-                for (int g = 0; g < 4; g += 2)
-                    store_pair(i, j, g, v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]},
-                               v4f{v[4 * g + 4], v[4 * g + 5], v[4 * g + 6], v[4 * g + 7]});
-            } else {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    store_group(i, j, g, v4f{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]});
-            }
-        };
-        if (slow) {
-            for (int t = 0; t < SUB_M * SUB_N; ++t) put(t / SUB_N, t % SUB_N, slow_tile(t / SUB_N, t % SUB_N));
-        } else {
-            static_for<SUB_M * SUB_N>([&](auto T) MXG_INLINE {
-                constexpr int t = decltype(T)::value;
-                put(t / SUB_N, t % SUB_N, acc[t / SUB_N][t % SUB_N]);
-            });
-        }
-    }
+    store_tile<SPLIT>(p, acc, tile, sp, ntiles, m0, n0, rows_a, wm, wn, lrow, khalf, slow, slow_tile);
 }
 
 } // namespace large
