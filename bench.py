@@ -6,7 +6,9 @@ B with e8m0 scales, bf16 output), the whole hot path.  The JSON line's
 bracketed by a device synchronisation on both sides, with all inputs
 already resident in HBM.  Inputs rotate over several device copies so that
 no step finds the previous step's operands in L2 or in the 256 MiB
-Infinity Cache.
+Infinity Cache.  `--warmup` untimed launches come first (30 by default:
+the clock takes some milliseconds to settle); every later line also warms
+up for at least SECONDARY_WARM_MS and records its count.
 
 Also reported on the same line:
   * skinny: the M=64, N=28672, K=8192 workload in GB/s of algorithmic bytes
@@ -35,7 +37,7 @@ Also reported on the same line:
   * cpu_baseline: the CPU oracle timed on a bounded sample of outputs of
     the 8192^3 workload on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--protocol-runs 50]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--no-cpu] [--protocol-runs 50]
 
 Counter passes (HBM traffic per launch):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o p -- python bench.py --traffic
@@ -106,14 +108,33 @@ def traffic_from_profiles(kernel_key: str):
     return None if e is None else e.get("bytes_per_launch")
 
 
-def time_launches(run_step, steps: int, warmup: int, stream):
-    """W untimed steps, then exactly `steps` back-to-back launches between a
-    device synchronisation on each side.  Returns the wall time of the timed
-    region and the mean launch duration from one pair of HIP events recorded
-    on the launch stream around it."""
+# Untimed launches of the last time_launches call (the lines record it).
+LAST_WARMUP = {"launches": 0}
+# The lines after the headline also warm up for at least this long: the
+# clock and power state a kernel settles at depends on what ran before it
+# (measured: the M = 64 line right after the e2m3 8192^3 one read 74 us after
+# 2 ms of warm-up, against 62-65 us settled), and a launch count alone does
+# not give every kernel the same time to settle.
+SECONDARY_WARM_MS = 100.0
+
+
+def time_launches(run_step, steps: int, warmup: int, stream, warm_ms: float = 0.0):
+    """W untimed steps (and, with warm_ms, more in rounds of W until that
+    much time has passed), then exactly `steps` back-to-back launches between
+    a device synchronisation on each side.  Returns the wall time of the
+    timed region and the mean launch duration from one pair of HIP events
+    recorded on the launch stream around it."""
     import torch
-    for i in range(warmup):
-        run_step(i)
+    t_w = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(max(warmup, 1) if warm_ms > 0 else warmup):
+            run_step(n)
+            n += 1
+        torch.cuda.synchronize()
+        if warm_ms <= 0 or (time.perf_counter() - t_w) * 1e3 >= warm_ms:
+            break
+    LAST_WARMUP["launches"] = n
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -141,9 +162,10 @@ def upload(p, copies: int, rotate_a: bool = True, preshuffled: bool = False):
     return sets
 
 
-def bench_gemm(gemm, p, variant, steps, warmup, copies):
+def bench_gemm(gemm, p, variant, steps, warmup, copies, warm_ms=SECONDARY_WARM_MS):
     """Time `steps` launches on `gemm` (whose scale layout decides how the
-    scales are uploaded) over `copies` rotating input sets."""
+    scales are uploaded) over `copies` rotating input sets, after at least
+    `warmup` untimed launches and `warm_ms` of them."""
     import torch
     import level_dsl_amd as L
     sets = upload(p, copies, rotate_a=p.M > 64,
@@ -159,7 +181,7 @@ def bench_gemm(gemm, p, variant, steps, warmup, copies):
         L.mxgemm_run(h, A, As, p.fmtA, B, Bs, p.fmtB, C[i % copies], p.M, p.N, p.K,
                      int(p.use_acc), p.out_dtype, stream.cuda_stream)
 
-    wall, mean_s = time_launches(step, steps, warmup, stream)
+    wall, mean_s = time_launches(step, steps, warmup, stream, warm_ms)
     del sets, C
     torch.cuda.empty_cache()
     return wall, mean_s
@@ -289,7 +311,7 @@ def quant_bytes(R, K, esz=4):
     return R * K * esz + R * K + R * K // 32
 
 
-def bench_quantize(gemm, X, steps, warmup, copies):
+def bench_quantize(gemm, X, steps, warmup, copies, warm_ms=SECONDARY_WARM_MS):
     """Time mxgemm_quantize of the (R, K) fp32 host array X, rotated over
     `copies` device copies.  Returns (wall, mean launch seconds)."""
     import torch
@@ -304,7 +326,7 @@ def bench_quantize(gemm, X, steps, warmup, copies):
     def step(i):
         gemm.quantize(xs[i % copies], 0, cs[i % copies], ss[i % copies], stream.cuda_stream)
 
-    wall, mean_s = time_launches(step, steps, warmup, stream)
+    wall, mean_s = time_launches(step, steps, warmup, stream, warm_ms)
     del xs, cs, ss
     torch.cuda.empty_cache()
     return wall, mean_s
@@ -327,9 +349,9 @@ def traffic_launches():
     for key, (_, wid, var, _) in TRAFFIC_KERNELS.items():
         p = traffic_problem(wid)
         log(f"traffic: {key} on {p.name}")
-        bench_gemm(gemm, p, getattr(L, var), 3, 0, 3)
+        bench_gemm(gemm, p, getattr(L, var), 3, 0, 3, warm_ms=0.0)
     log("traffic: mx_quantize")
-    bench_quantize(gemm, mi.skinny_b_raw(), 3, 0, 3)
+    bench_quantize(gemm, mi.skinny_b_raw(), 3, 0, 3, warm_ms=0.0)
     gemm.close()
     torch.cuda.synchronize()
     log("traffic: done")
@@ -429,7 +451,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--protocol-runs", type=int, default=50,
                     help="timed launches per workload in the flushed per-launch protocol (0: skip)")
@@ -464,7 +486,7 @@ def main():
     log(f"bench: {p.name} generated")
     flops = mi.algorithmic_flops(p.M, p.N, p.K)
     steps, warmup = args.steps, args.warmup
-    wall, mean_s = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE, steps, warmup, 3)
+    wall, mean_s = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE, steps, warmup, 3, warm_ms=0.0)
     value = flops * steps / wall / 1e12
     achieved = flops / mean_s / 1e12
     log(f"bench: large exact {value:.1f} TFLOP/s whole-job, {achieved:.1f} per launch "
@@ -493,7 +515,9 @@ def main():
 
     # ---- native scaled-MFMA variant on the same workload ----------------------
     wall_n, mean_n = bench_gemm(gemm, p, L.MXGEMM_VARIANT_LARGE_NATIVE, steps, warmup, 3)
+    warm_n = LAST_WARMUP["launches"]
     out["native_scaled_mfma"] = {
+        "warmup_launches": warm_n,
         "value": round(flops * steps / wall_n / 1e12, 2), "unit": "TFLOP/s",
         "achieved_per_launch": round(flops / mean_n / 1e12, 2), "peak": PEAK_TFLOPS["fp8"],
         "frac": round(flops / mean_n / 1e12 / PEAK_TFLOPS["fp8"], 4),
@@ -510,6 +534,7 @@ def main():
     p4 = e2m1_8192()
     log("bench: e2m1 8192^3 generated")
     wall_4, mean_4 = bench_gemm(gemm, p4, L.MXGEMM_VARIANT_AUTO, steps, warmup, 3)
+    warm_4 = LAST_WARMUP["launches"]
     # the same three 8192^3 paths with scales in the preshuffled layout
     # (mxgemm_set_scale_layout): per-stage coalesced scale loads instead of
     # the 16-byte row windows
@@ -520,12 +545,14 @@ def main():
                       ("e2m1", p4, L.MXGEMM_VARIANT_AUTO)):
         _, m = bench_gemm(gps, q, v, steps, warmup, 3)
         pre[key] = {"launch_mean_us": round(m * 1e6, 2), "unit": "TFLOP/s",
+                    "warmup_launches": LAST_WARMUP["launches"],
                     "achieved_per_launch": round(flops / m / 1e12, 2)}
         log(f"bench: preshuffled scales, {key}: {pre[key]['achieved_per_launch']} TFLOP/s per launch")
     gps.close()
     out["preshuffled_scales_8192cube"] = pre
     del p4
     out["mxfp4"] = {
+        "warmup_launches": warm_4,
         "value": round(flops * steps / wall_4 / 1e12, 2), "unit": "TFLOP/s",
         "config": {"M": 8192, "N": 8192, "K": 8192, "A": "e2m1 (2 per byte)", "B": "e2m1 (2 per byte)",
                    "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1: exact)", "out": "bf16 (RNE)"},
@@ -544,8 +571,10 @@ def main():
                            out_dtype=mi.OUT_BF16)
     log("bench: e2m3 8192^3 generated")
     wall_6, mean_6 = bench_gemm(gemm, p6, L.MXGEMM_VARIANT_AUTO, steps, warmup, 3)
+    warm_6 = LAST_WARMUP["launches"]
     del p6
     out["mxfp6"] = {
+        "warmup_launches": warm_6,
         "value": round(flops * steps / wall_6 / 1e12, 2), "unit": "TFLOP/s",
         "config": {"M": 8192, "N": 8192, "K": 8192, "A": "e2m3 (4 per 3 bytes)",
                    "B": "e2m3 (4 per 3 bytes)",
@@ -564,7 +593,9 @@ def main():
     sbytes = mi.algorithmic_bytes(ps.M, ps.N, ps.K, ps.out_dtype)
     sk_steps = max(steps, 30)
     wall_s, mean_ss = bench_gemm(gemm, ps, L.MXGEMM_VARIANT_SKINNY, sk_steps, warmup, 3)
+    warm_s = LAST_WARMUP["launches"]
     out["skinny_m64"] = {
+        "warmup_launches": warm_s,
         "workload": ps.name, "value": round(sbytes * sk_steps / wall_s / 1e9, 1), "unit": "GB/s",
         "pct_of_hbm_peak": round(100 * sbytes * sk_steps / wall_s / 1e9 / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(sbytes / mean_ss / 1e9, 1),
@@ -584,8 +615,10 @@ def main():
     log("bench: e2m1 decode shape generated")
     b4 = (64 + 28672) * (8192 // 2 + 8192 // 32) + 64 * 28672 * 4
     wall_4s, mean_4s = bench_gemm(gemm, p4s, L.MXGEMM_VARIANT_AUTO, sk_steps, warmup, 3)
+    warm_4s = LAST_WARMUP["launches"]
     del p4s
     out["mxfp4_skinny_m64"] = {
+        "warmup_launches": warm_4s,
         "value": round(b4 * sk_steps / wall_4s / 1e9, 1), "unit": "GB/s",
         "config": {"M": 64, "N": 28672, "K": 8192, "A": "e2m1", "B": "e2m1", "out": "f32"},
         "roofline": {"bound": "hbm", "achieved": round(b4 / mean_4s / 1e9, 1),
@@ -601,8 +634,10 @@ def main():
     log("bench: e2m3 decode shape generated")
     b6 = (64 + 28672) * (3 * 8192 // 4 + 8192 // 32) + 64 * 28672 * 4
     wall_6s, mean_6s = bench_gemm(gemm, p6s, L.MXGEMM_VARIANT_AUTO, sk_steps, warmup, 3)
+    warm_6s = LAST_WARMUP["launches"]
     del p6s
     out["mxfp6_skinny_m64"] = {
+        "warmup_launches": warm_6s,
         "value": round(b6 * sk_steps / wall_6s / 1e9, 1), "unit": "GB/s",
         "config": {"M": 64, "N": 28672, "K": 8192, "A": "e2m3", "B": "e2m3", "out": "f32"},
         "roofline": {"bound": "hbm", "achieved": round(b6 / mean_6s / 1e9, 1),
@@ -619,8 +654,10 @@ def main():
     raw = mi.skinny_b_raw()
     q_steps = max(steps, 30)
     wall_q, mean_q = bench_quantize(gemm, raw, q_steps, warmup, 3)
+    warm_q = LAST_WARMUP["launches"]
     del raw
     out["mx_quantize"] = {
+        "warmup_launches": warm_q,
         "workload": "mxquant_skinny_weight_28672x8192_f32_e4m3", "value":
             round(qbytes * q_steps / wall_q / 1e9, 1), "unit": "GB/s",
         "pct_of_hbm_peak": round(100 * qbytes * q_steps / wall_q / 1e9 / PEAK_HBM_GBS, 2),
