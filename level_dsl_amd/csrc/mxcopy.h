@@ -1,5 +1,5 @@
 // mxcopy.h -- plain streaming copy through raw buffer loads and stores, the
-// measured ceiling ("achievable HBM") that the HBM-bound kernels are judged
+// measured ceiling ("achievable HBM") that the HBM-bound kernels are compared
 // against.  It is the buffer_load / buffer_store pattern of the TLX
 // global-memory page ("Example: buffer load and store"): scalar base plus
 // 32-bit per-lane offsets, the tail masked by the descriptor's range check.
