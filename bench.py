@@ -45,7 +45,8 @@ Counter passes (HBM traffic per launch):
   python bench.py --traffic-report D1/p_counter_collection.csv D2/p_counter_collection.csv
 --traffic launches a plain negating copy of COPY_BYTES (read once, written once)
 and three launches each of the timed GEMM kernels (the 256 x 256 kernel in
-its exact, native and e2m1 modes, the exact small-M kernel) and of the MX
+its exact, native, e2m1 and e2m3 modes, the exact small-M kernel, the small-M
+scaled-MFMA kernel with e2m1 and e2m3) and of the MX
 quantization; --traffic-report scales the
 counters by what they read for that copy and writes profiles/hbm_traffic.json.
 """
@@ -280,7 +281,13 @@ TRAFFIC_KERNELS = {"large_exact": ("void mxg::large::kernel<0, 0, false, true, f
                    "large_native": ("void mxg::large::kernel<0, 0, true, true, false>", 2,
                                     "MXGEMM_VARIANT_LARGE_NATIVE", 2),
                    "mxfp4_large": ("void mxg::large::kernel<4, 4, true, true, false>", "e2m1_8192",
-                                   "MXGEMM_VARIANT_AUTO", 2)}
+                                   "MXGEMM_VARIANT_AUTO", 2),
+                   "mxfp6_large": ("void mxg::large::kernel<2, 2, true, true, false>", "e2m3_8192",
+                                   "MXGEMM_VARIANT_AUTO", 2),
+                   "mxfp4_skinny": ("void mxg::skinny::kernel<4, 4, 2, 4, false>", "e2m1_m64",
+                                    "MXGEMM_VARIANT_AUTO", 4),
+                   "mxfp6_skinny": ("void mxg::skinny::kernel<2, 2, 2, 4, false>", "e2m3_m64",
+                                    "MXGEMM_VARIANT_AUTO", 4)}
 
 
 def e2m1_8192():
@@ -291,9 +298,26 @@ def e2m1_8192():
                              out_dtype=mi.OUT_BF16)
 
 
+def sub_byte_problem(wid):
+    """The bench's sub-byte problems: e2m3 8192^3 (N(0, 1) codes, scales
+    U{120..134}, bf16 out) and the M = 64 decode shape with e2m1 or e2m3
+    operands (f32 out)."""
+    import mxinputs as mi
+    if wid == "e2m3_8192":
+        return mi.random_problem(8192, 8192, 8192, seed=860, fmtA=mi.FMT_E2M3, fmtB=mi.FMT_E2M3,
+                                 out_dtype=mi.OUT_BF16)
+    if wid == "e2m1_m64":
+        return mi.random_problem(64, 28672, 8192, seed=870, fmtA=mi.FMT_E2M1, fmtB=mi.FMT_E2M1)
+    return mi.random_problem(64, 28672, 8192, seed=871, fmtA=mi.FMT_E2M3, fmtB=mi.FMT_E2M3)
+
+
 def traffic_problem(wid):
     import mxinputs as mi
-    return e2m1_8192() if wid == "e2m1_8192" else mi.workload(wid)
+    if wid == "e2m1_8192":
+        return e2m1_8192()
+    if isinstance(wid, str):
+        return sub_byte_problem(wid)
+    return mi.workload(wid)
 
 
 def traffic_shape(wid):
@@ -301,6 +325,12 @@ def traffic_shape(wid):
     import mxinputs as mi
     if wid == "e2m1_8192":
         return "mxfp4_e2m1_8192cube_bf16", 8192, 8192, 8192, 4096
+    if wid == "e2m3_8192":
+        return "mxfp6_e2m3_8192cube_bf16", 8192, 8192, 8192, 6144
+    if wid == "e2m1_m64":
+        return "mxfp4_e2m1_m64_n28672_k8192_f32", 64, 28672, 8192, 4096
+    if wid == "e2m3_m64":
+        return "mxfp6_e2m3_m64_n28672_k8192_f32", 64, 28672, 8192, 6144
     w = mi.WORKLOADS[wid]
     return w["name"], w["M"], w["N"], w["K"], w["K"]
 QUANT_KERNEL = "void mxg::quant::kernel<0, 0>"
@@ -567,8 +597,7 @@ def main():
     # ---- e2m3 (FP6) operands on the same shape --------------------------------
     # N(0, 1) -> e2m3 (RNE, saturating at 7.5), scales U{120..134}, bf16 out;
     # exact on the scaled MFMA like e2m1
-    p6 = mi.random_problem(8192, 8192, 8192, seed=860, fmtA=mi.FMT_E2M3, fmtB=mi.FMT_E2M3,
-                           out_dtype=mi.OUT_BF16)
+    p6 = sub_byte_problem("e2m3_8192")
     log("bench: e2m3 8192^3 generated")
     wall_6, mean_6 = bench_gemm(gemm, p6, L.MXGEMM_VARIANT_AUTO, steps, warmup, 3)
     warm_6 = LAST_WARMUP["launches"]
@@ -582,6 +611,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops / mean_6 / 1e12, 2),
                      "peak": PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
                      "frac": round(flops / mean_6 / 1e12 / PEAK_TFLOPS["fp4"], 4),
+                     "traffic": traffic_from_profiles("mxfp6_large"),
                      "kernel": "mxg::large::kernel<2,2,true,true,false> (scale windows through LDS)",
                      "launch_mean_us": round(mean_6 * 1e6, 2)}}
     log(f"bench: e2m3 {out['mxfp6']['value']} TFLOP/s")
@@ -611,7 +641,7 @@ def main():
     # ---- the same decode shape with e2m1 operands (two codes per byte) ----------
     # N(0, 1) -> e2m1, scales U{120..134}, f32 out; the small-M kernel's scaled
     # MFMA, exact for e2m1.  Bytes: A, B at K/2 per row, K/32 scales, C.
-    p4s = mi.random_problem(64, 28672, 8192, seed=870, fmtA=mi.FMT_E2M1, fmtB=mi.FMT_E2M1)
+    p4s = sub_byte_problem("e2m1_m64")
     log("bench: e2m1 decode shape generated")
     b4 = (64 + 28672) * (8192 // 2 + 8192 // 32) + 64 * 28672 * 4
     wall_4s, mean_4s = bench_gemm(gemm, p4s, L.MXGEMM_VARIANT_AUTO, sk_steps, warmup, 3)
@@ -624,13 +654,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(b4 / mean_4s / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(b4 / mean_4s / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles("mxfp4_skinny"),
                      "kernel": "mxg::skinny::kernel<4,4,2,4,false> (LDS scale table)",
                      "launch_mean_us": round(mean_4s * 1e6, 2)},
         "algorithmic_bytes": b4}
     log(f"bench: e2m1 decode shape {out['mxfp4_skinny_m64']['value']} GB/s")
 
     # ---- and with e2m3 operands (four codes per three bytes) --------------------
-    p6s = mi.random_problem(64, 28672, 8192, seed=871, fmtA=mi.FMT_E2M3, fmtB=mi.FMT_E2M3)
+    p6s = sub_byte_problem("e2m3_m64")
     log("bench: e2m3 decode shape generated")
     b6 = (64 + 28672) * (3 * 8192 // 4 + 8192 // 32) + 64 * 28672 * 4
     wall_6s, mean_6s = bench_gemm(gemm, p6s, L.MXGEMM_VARIANT_AUTO, sk_steps, warmup, 3)
@@ -643,6 +674,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(b6 / mean_6s / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(b6 / mean_6s / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles("mxfp6_skinny"),
                      "kernel": "mxg::skinny::kernel<2,2,2,4,false> (LDS scale table)",
                      "launch_mean_us": round(mean_6s * 1e6, 2)},
         "algorithmic_bytes": b6}
