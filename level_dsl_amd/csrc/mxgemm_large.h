@@ -155,10 +155,20 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, v16f (&acc)[SUB_M]
     auto store_pair = [&](int i, int j, int g, v4f x, v4f y) MXG_INLINE {  // groups g, g + 1
         const int kh = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5);
         const int lr = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 31);
-        v4f send = kh ? x : y, recv;
+        // v_permlane32_swap: the upper lane half of x trades places with
+        // the lower half of y, so the lower half ends with (its x, the upper
+        // lane's x) and the upper half with (the lower lane's y, its y)
+        v4f lo, hi;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) recv[e] = __shfl_xor(send[e], 32, 64);
-        const v4f lo = kh ? recv : x, hi = kh ? y : recv;
+        for (int e = 0; e < 4; ++e) {
+            // (the elements are copied out first: a bit cast of x[e] itself
+            // compiled to a read of element 0 for every e)
+            const float xe = x[e], ye = y[e];
+            const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, xe),
+                                                            __builtin_bit_cast(uint32_t, ye), false, false);
+            lo[e] = __builtin_bit_cast(float, (uint32_t)r[0]);
+            hi[e] = __builtin_bit_cast(float, (uint32_t)r[1]);
+        }
         const int m = wm * WAVE_M + i * 32 + lr;                       // tile-local row
         const int n = n0 + wn * WAVE_N + j * 32 + 8 * (g + kh);      // global column
         store_bf16x8(rC, (uint32_t)m * N + n, n, N, lo, hi, p.use_acc);
