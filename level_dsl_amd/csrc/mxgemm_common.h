@@ -198,6 +198,16 @@ __device__ __forceinline__ uint32_t bf16_bits(float f)
     return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
+// Two floats rounded to bf16 (RNE) and packed, a in the low half: one
+// v_cvt_pk_bf16_f32 (two scalar conversions cost a shift and an OR more).
+typedef float v2f_pack __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_pack __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    const v2bf_pack h = __builtin_convertvector((v2f_pack){a, b}, v2bf_pack);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
 {
     return __builtin_bit_cast(float, bits16 << 16);
@@ -226,8 +236,7 @@ __device__ __forceinline__ void store_c4(rsrc_t rC, uint32_t e0, int n, int N, v
                 v[2] += bf16_to_f32((uint32_t)old[1] & 0xffffu);
                 v[3] += bf16_to_f32((uint32_t)old[1] >> 16);
             }
-            v2i o = {(int)(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16)),
-                     (int)(bf16_bits(v[2]) | (bf16_bits(v[3]) << 16))};
+            v2i o = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
             store8(rC, off, o);
         }
         return;
@@ -268,10 +277,8 @@ __device__ __forceinline__ void store_bf16x8(rsrc_t rC, uint32_t e0, int n, int 
         hi[2] += bf16_to_f32((uint32_t)old[3] & 0xffffu);
         hi[3] += bf16_to_f32((uint32_t)old[3] >> 16);
     }
-    const v4i o = {(int)(bf16_bits(lo[0]) | (bf16_bits(lo[1]) << 16)),
-                   (int)(bf16_bits(lo[2]) | (bf16_bits(lo[3]) << 16)),
-                   (int)(bf16_bits(hi[0]) | (bf16_bits(hi[1]) << 16)),
-                   (int)(bf16_bits(hi[2]) | (bf16_bits(hi[3]) << 16))};
+    const v4i o = {(int)pack_bf16x2(lo[0], lo[1]), (int)pack_bf16x2(lo[2], lo[3]),
+                   (int)pack_bf16x2(hi[0], hi[1]), (int)pack_bf16x2(hi[2], hi[3])};
     __builtin_amdgcn_raw_buffer_store_b128(o, rC, off, 0, 0);
 }
 
