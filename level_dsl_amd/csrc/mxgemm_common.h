@@ -125,6 +125,26 @@ __device__ __forceinline__ uint32_t opaque_s(uint32_t x)
 // track (s_waitcnt vmcnt(0)).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Workgroup barrier without a memory fence (__syncthreads' release fence
+// would also wait for every direct-to-LDS load in flight).  For LDS data
+// that each wave has already waited for itself; the signal fences keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_nofence()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most N of this wave's vector-memory operations are in
+// flight (s_waitcnt vmcnt(N)); they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // ---- scale layouts ---------------------------------------------------------
 // Row-major: scale byte (r, kb) of an operand with KB = K/32 blocks per row
 // at r * KB + kb.  Preshuffled (KB % 4 == 0): rows in groups of 32 and blocks

@@ -796,6 +796,11 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     };
 
     // ---- prologue ---------------------------------------------------------
+    // Stage 0 and its scales, then stage 1's tiles right behind them (buffer
+    // 1 is free; exact mode: stage 1's B tile follows in stage 0's first
+    // block).  The wait lets stage 1's loads stay in flight: direct-to-LDS
+    // loads issue in program order and complete in issue order (the scale
+    // registers the compiler guards itself).
     gload(0, 0, int_c<0>{});
     gload(0, 0, int_c<1>{});
     if constexpr (SREG) {
@@ -805,10 +810,10 @@ __global__ __launch_bounds__(THREADS) void kernel(GemmArgs p)
     } else {
         scale4(0, sa1, sb1, sa2_1, sb2_1);
     }
-    wait_vmem();
-    __syncthreads();
-    gload(1, 1, int_c<0>{});  // exact mode: stage 1's B tile follows in stage 0's first block
+    gload(1, 1, int_c<0>{});
     if constexpr (NATIVE) gload(1, 1, int_c<1>{});
+    wait_vmcnt<(NATIVE ? 2 : 1) * SEGS_PER_WAVE>();
+    barrier_nofence();
     if constexpr (SLDS) scale_lds(0, sa1, sb1, sa2_1, sb2_1);
     if constexpr (SREG) {
 #pragma unroll
