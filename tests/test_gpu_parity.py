@@ -456,3 +456,36 @@ def test_nonfinite_pattern(gemm, fa, fb):
         inf = np.isinf(r)
         assert np.array_equal(got[inf], r[inf]), f"infinities differ ({VNAME[v]})"
         compare(got[fin], {k: a[fin] for k, a in ref.items()}, mi.OUT_F32, f"finite part {VNAME[v]}")
+
+
+BF16_RNE_CASES = [
+    # M, N, K, fmtA, fmtB, variants
+    (300, 520, 1024, 0, 0, (LARGE, LARGE_NATIVE)),          # N % 8 == 0: 16-byte bf16 stores; scale windows
+    (300, 516, 1056, 1, 0, (LARGE, LARGE_NATIVE)),          # N % 8 != 0: 8-byte stores; per-stage scales
+    (48, 520, 1024, 0, 1, (SKINNY, SKINNY_NATIVE, LARGE)),  # the small-M kernels
+    (300, 520, 1024, 4, 4, (AUTO,)),                        # e2m1 on the 256 x 256 kernel
+    (300, 520, 1024, 2, 2, (AUTO,)),                        # e2m3
+]
+
+
+@pytest.mark.parametrize("case", BF16_RNE_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"_f{c[3]}{c[4]}")
+def test_bf16_output_is_rne_of_f32_output(gemm, case):
+    """bf16 output is bit for bit the f32 output of the same call rounded to
+    nearest even (the sums are the same; the bf16 epilogue's lane-half
+    exchange and pairwise packing must leave every value in its place,
+    rounded once)."""
+    M, N, K, fa, fb, variants = case
+    seed = 4400 + M + N + K + fa
+    p32 = mi.random_problem(M, N, K, seed=seed, fmtA=fa, fmtB=fb, out_dtype=mi.OUT_F32)
+    p16 = mi.random_problem(M, N, K, seed=seed, fmtA=fa, fmtB=fb, out_dtype=mi.OUT_BF16)
+    dev = to_dev(p32)
+    for v in variants:
+        log(f"bf16 = RNE(f32) {case[:5]} variant={VNAME[v]}")
+        c32 = run(gemm, p32, v, guard=64, dev_inputs=dev)
+        c16 = run(gemm, p16, v, guard=64, dev_inputs=dev)
+        assert np.isfinite(c32).all()
+        want = torch.from_numpy(c32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        bad = np.flatnonzero(c16 != want)
+        assert bad.size == 0, (f"{case[:5]} variant {VNAME[v]}: {bad.size} bf16 outputs differ from "
+                               f"RNE of the f32 output, e.g. flat index {bad[:5]}")
+    gemm.set_variant(AUTO)
