@@ -72,7 +72,7 @@ KERNEL_SOURCES = ["level_dsl_amd/csrc/" + f for f in (
     "mxgemm.hip", "mxgemm_common.h", "mxgemm_large.h", "mxgemm_skinny.h", "mxgemm_stream.h",
     "mxquant.h", "mxgemm_launch.h", "launch_large.h", "launch_skinny.h", "k_large_exact.hip",
     "k_large_exact_b.hip", "k_large_native.hip", "k_large_e2m1.hip", "k_stream.hip", "k_skinny_fp8.hip",
-    "k_skinny_e2m1.hip", "k_quant.hip", "mxcopy.h")]
+    "k_skinny_e2m1.hip", "k_quant.hip", "mxcopy.h", "mxwiden.h")]
 
 
 def kernel_hash() -> str:

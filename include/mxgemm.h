@@ -22,9 +22,10 @@
  *
  * Memory layout (all dense, no leading-dimension arguments):
  *   A        M x K codes, row-major (byte A[m*K + k]); e2m1: M x K/2 bytes,
- *            e2m3: M x 3K/4 bytes (packed along K, see the formats below).
+ *            e2m3 / e3m2: M x 3K/4 bytes (packed along K, see the formats
+ *            below).
  *   B        N x K codes, K contiguous ("K-major"): byte B[n*K + k] = B[k,n];
- *            e2m1: N x K/2 bytes, e2m3: N x 3K/4 bytes.
+ *            e2m1: N x K/2 bytes, e2m3 / e3m2: N x 3K/4 bytes.
  *   A_scale  M x (K/32) bytes, row-major (or preshuffled, see
  *            mxgemm_set_scale_layout).
  *   B_scale  N x (K/32) bytes, row-major (or preshuffled).
@@ -59,22 +60,37 @@ typedef struct mxgemm_ctx *mxgemm_t;
  * FP4 E2M1 (sign, 2-bit exponent with bias 1, 1-bit mantissa; magnitudes 0,
  * 0.5, 1, 1.5, 2, 3, 4, 6; no inf/NaN), packed two codes per byte along K,
  * the even k in the low nibble (k_pack = True), so an e2m1 operand row is
- * K/2 bytes.  e2m1 pairs only with e2m1 (MXGEMM_ERR_FMT otherwise).  It runs
- * on the gfx950 scaled MFMA, whose 8-product windows hold every e2m1
- * product of a block exactly (measured), so it meets the same
- * 1e-5 * sum|ab| bound as the exact variants at the fp4 MFMA rate. */
+ * K/2 bytes.  e2m1 x e2m1 runs on the gfx950 scaled MFMA, whose 8-product
+ * windows hold every e2m1 product of a block exactly (measured), so it
+ * meets the same 1e-5 * sum|ab| bound as the exact variants at the fp4 MFMA
+ * rate.  e2m1 beside another format runs widened (below). */
 /* e2m3 is the 6-bit member of the same family (a reading as well): OCP FP6
  * E2M3 (sign, 2-bit exponent with bias 1, 3-bit mantissa; magnitudes 0 to
  * 7.5 in steps of 1/8 below 1; no inf/NaN), packed four codes per three
  * bytes along K, code k at bits 6k .. 6k+5 of the row read as one
- * little-endian bit string, so an e2m3 operand row is 3K/4 bytes.  It pairs
- * only with e2m3 and runs on the scaled MFMA, whose 8-product windows hold
- * every e2m3 product of a block exactly (0.125^2 to 7.5^2 spans less than
- * the window), so it too meets the exact variants' bound.  The other FP6
- * member, e3m2 (format 3), is not accepted (MXGEMM_ERR_FMT): its products
- * span about 17 binades, more than the window holds, so the scaled MFMA
- * would not meet the bound, and the exact decode path is fp8-only. */
-enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1, MXGEMM_FMT_E2M3 = 2, MXGEMM_FMT_E2M1 = 4 };
+ * little-endian bit string, so an e2m3 operand row is 3K/4 bytes.  e2m3 x
+ * e2m3 runs on the scaled MFMA, whose 8-product windows hold every e2m3
+ * product of a block exactly (0.125^2 to 7.5^2 spans less than the
+ * window), so it too meets the exact variants' bound.  The other FP6
+ * member, e3m2 (format 3; sign, 3-bit exponent with bias 3, 2-bit
+ * mantissa; magnitudes 0.0625 to 28; no inf/NaN), is packed like e2m3.  Its
+ * products span about 17 binades, more than the window holds, so it always
+ * runs widened.
+ *
+ * Widened pairs: e3m2 with any format, and e2m1 or e2m3 beside any format
+ * but itself.  Every e2m1, e2m3 and e3m2 value is an e4m3 value (2^-4 to
+ * 28, at most three mantissa bits), so the call first rewrites each
+ * sub-byte operand as e4m3 bytes (mxgemm_widen) into the handle's operand
+ * buffer (mxgemm_set_operand_buffer), keeps the scales, and multiplies the
+ * resulting fp8 pair on the variant selected, with that variant's results
+ * and error bound for an fp8 pair. */
+enum {
+    MXGEMM_FMT_E4M3 = 0,
+    MXGEMM_FMT_E5M2 = 1,
+    MXGEMM_FMT_E2M3 = 2,
+    MXGEMM_FMT_E3M2 = 3,
+    MXGEMM_FMT_E2M1 = 4
+};
 
 /* output types of C (out_dtype); bf16 is rounded to nearest even from the
  * fp32 accumulator */
@@ -127,8 +143,7 @@ enum {
 enum {
     MXGEMM_OK = 0,
     MXGEMM_ERR_NULL = 1,    /* a required pointer is NULL */
-    MXGEMM_ERR_FMT = 2,     /* fmtA / fmtB not e4m3, e5m2, e2m3 or e2m1, or a sub-byte
-                               format with another format */
+    MXGEMM_ERR_FMT = 2,     /* fmtA / fmtB not e4m3, e5m2, e2m3, e3m2 or e2m1 */
     MXGEMM_ERR_DTYPE = 3,   /* out_dtype not f32/bf16, or use_acc not 0/1 */
     MXGEMM_ERR_SHAPE = 4,   /* M, N, K out of range or K % 32 != 0 */
     MXGEMM_ERR_ALIGN = 5,   /* A, B or C not 16-byte aligned */
@@ -137,7 +152,9 @@ enum {
     MXGEMM_ERR_HANDLE = 8,  /* NULL or destroyed handle */
     MXGEMM_ERR_ALIAS = 9,   /* C overlaps an input buffer */
     MXGEMM_ERR_VARIANT = 10, /* unknown variant */
-    MXGEMM_ERR_WORKSPACE = 11 /* workspace missing for a forced split, too small or misaligned */
+    MXGEMM_ERR_WORKSPACE = 11 /* workspace missing for a forced split, too small or
+                                 misaligned, or the operand buffer of a widened pair
+                                 missing or too small */
 };
 
 /* Limits of one call. */
@@ -201,6 +218,39 @@ int mxgemm_set_variant(mxgemm_t h, int variant);
  * and workspace).  MXGEMM_ERR_WORKSPACE for a short or misaligned buffer. */
 int mxgemm_set_workspace(mxgemm_t h, void *ws, size_t bytes, hipStream_t stream);
 
+/* Bytes of the operand buffer that a call with this format pair and shape
+ * needs (see "Widened pairs" above): 0 when the pair runs as it is (e4m3 /
+ * e5m2 with each other, e2m1 x e2m1, e2m3 x e2m3); else M * K rounded up to
+ * a multiple of 256 when A is widened, plus N * K when B is.  -1 for an
+ * unknown format or M, N, K out of the ranges of mxgemm_validate_args. */
+int64_t mxgemm_operand_buffer_bytes(int fmtA, int fmtB, int64_t M, int64_t N, int64_t K);
+
+/* Attach a caller-owned device buffer (256-byte aligned) that calls of
+ * widened pairs rewrite their sub-byte operands into, or detach it with buf
+ * = NULL.  A widened call whose buffer is missing or shorter than
+ * mxgemm_operand_buffer_bytes returns MXGEMM_ERR_WORKSPACE, one whose
+ * needed bytes of it overlap an operand, a scale buffer or C returns
+ * MXGEMM_ERR_ALIAS; calls of other pairs never touch it.  Widened A sits
+ * at offset 0 (when A is widened), widened B after it.  The rewrite runs
+ * on the call's stream before the multiply, so widened calls that share one
+ * buffer must not overlap on the GPU (order them on one stream).
+ * mxgemm_run_noalloc uses it too: it is caller memory, so such a call still
+ * allocates nothing.  MXGEMM_ERR_WORKSPACE for a misaligned buffer. */
+int mxgemm_set_operand_buffer(mxgemm_t h, void *buf, size_t bytes);
+
+/* Rewrite rows x K codes of a sub-byte format (fmt e2m1, e2m3 or e3m2,
+ * packed as for mxgemm_run) as rows x K e4m3 bytes, each the code's value
+ * exactly (signed zeros kept), asynchronously on `stream`: the step a
+ * widened call takes, for callers that widen an operand once and reuse it
+ * (the scales stay as they are, and the e4m3 operand multiplies to the same
+ * result).  src and dst are device pointers on the handle's device, both
+ * 16-byte aligned and disjoint; 1 <= rows <= MXGEMM_MAX_M, 32 <= K <=
+ * MXGEMM_MAX_K with K % 32 == 0, rows * K <= MXGEMM_MAX_QELEMS.  Errors:
+ * MXGEMM_ERR_FMT (fmt not sub-byte), _SHAPE, _ALIGN, _ALIAS, _NULL,
+ * _DEVICE, _HANDLE; on an error nothing is launched. */
+int mxgemm_widen(mxgemm_t h, const void *src, int fmt, int64_t rows, int64_t K, uint8_t *dst,
+                 hipStream_t stream);
+
 /* Number of K splits: 0 (default) chooses it from the shape, 1 never
  * splits, S >= 2 forces S splits, reduced to at most the number of 128-byte
  * K stages (of whole 16-byte scale windows -- 4 stages, 2 for e2m1 -- where
@@ -260,10 +310,12 @@ int mxgemm_preshuffle_scales(mxgemm_t h, const uint8_t *src, uint8_t *dst, int64
  * 1 <= N <= MXGEMM_MAX_N, M * N <= MXGEMM_MAX_MN, 32 <= K <= MXGEMM_MAX_K
  * with K % 32 == 0,
  * A, B, C 16-byte aligned, and C not overlapping A, B or the scales
- * (byte ranges A[M*K], B[N*K], A_scale[M*K/32], B_scale[N*K/32],
- * C[M*N*sizeof(out)]).  Scales need no alignment.  These are the checks
- * for row-major scales; a handle set to preshuffled scales adds those of
- * mxgemm_set_scale_layout in mxgemm_run. */
+ * (byte ranges A[M*rowA], B[N*rowB], A_scale[M*K/32], B_scale[N*K/32],
+ * C[M*N*sizeof(out)], with row bytes K for e4m3 / e5m2, K/2 for e2m1, 3K/4
+ * for e2m3 / e3m2).  Scales need no alignment.  These are the checks for
+ * row-major scales; a handle set to preshuffled scales adds those of
+ * mxgemm_set_scale_layout in mxgemm_run, and a widened pair those of
+ * mxgemm_set_operand_buffer. */
 int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA,
                          const void *B, const uint8_t *B_scale, int fmtB,
                          const void *C, int64_t M, int64_t N, int64_t K,

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libmxgemm.so")
 MXGEMM_FMT_E4M3 = 0
 MXGEMM_FMT_E5M2 = 1
 MXGEMM_FMT_E2M3 = 2
+MXGEMM_FMT_E3M2 = 3
 MXGEMM_FMT_E2M1 = 4
 MXGEMM_OUT_F32 = 0
 MXGEMM_OUT_BF16 = 1
@@ -52,6 +53,9 @@ SIGNATURES = {
     "mxgemm_destroy": (_i32, [_vp]),
     "mxgemm_set_variant": (_i32, [_vp, _i32]),
     "mxgemm_set_workspace": (_i32, [_vp, _vp, ctypes.c_size_t, _vp]),
+    "mxgemm_operand_buffer_bytes": (_i64, [_i32, _i32, _i64, _i64, _i64]),
+    "mxgemm_set_operand_buffer": (_i32, [_vp, _vp, ctypes.c_size_t]),
+    "mxgemm_widen": (_i32, [_vp, _vp, _i32, _i64, _i64, _u8p, _vp]),
     "mxgemm_set_splits": (_i32, [_vp, _i32]),
     "mxgemm_set_scale_layout": (_i32, [_vp, _i32]),
     "mxgemm_scale_bytes": (_i64, [_i32, _i64, _i64]),
@@ -136,6 +140,47 @@ def mxgemm_set_workspace(h, ws, nbytes: int, stream=None) -> None:
     _check(load_library().mxgemm_set_workspace(h, _ptr(ws), int(nbytes),
                                                _stream(stream) if ws is not None else None),
            "mxgemm_set_workspace")
+
+
+def mxgemm_operand_buffer_bytes(fmtA: int, fmtB: int, M: int, N: int, K: int) -> int:
+    """Bytes of the operand buffer a widened format pair needs (0: the pair
+    runs as it is, -1: invalid arguments)."""
+    return int(load_library().mxgemm_operand_buffer_bytes(int(fmtA), int(fmtB), int(M), int(N),
+                                                          int(K)))
+
+
+def mxgemm_set_operand_buffer(h, buf, nbytes: int) -> None:
+    """Attach a device buffer (256-byte aligned) for widened operands, or
+    detach with buf=None."""
+    _check(load_library().mxgemm_set_operand_buffer(h, _ptr(buf), int(nbytes) if buf is not None else 0),
+           "mxgemm_set_operand_buffer")
+
+
+def mxgemm_widen(h, src, fmt: int, rows: int, K: int, dst, stream=None) -> None:
+    """rows x K sub-byte codes (e2m1 / e2m3 / e3m2) -> rows x K e4m3 bytes
+    of the same values, on `stream` (default: torch's current stream)."""
+    _check(load_library().mxgemm_widen(h, _ptr(src), int(fmt), int(rows), int(K), _ptr(dst),
+                                       _stream(stream)),
+           "mxgemm_widen")
+
+
+def row_bytes(fmt: int, K: int) -> int:
+    """Bytes of an operand row of K codes: e2m1 K/2, e2m3 and e3m2 3K/4,
+    e4m3 / e5m2 K."""
+    if fmt == MXGEMM_FMT_E2M1:
+        return K // 2
+    if fmt in (MXGEMM_FMT_E2M3, MXGEMM_FMT_E3M2):
+        return 3 * K // 4
+    return K
+
+
+def codes_per_row(fmt: int, nbytes: int) -> int:
+    """K of an operand row of `nbytes` bytes (the inverse of row_bytes)."""
+    if fmt == MXGEMM_FMT_E2M1:
+        return 2 * nbytes
+    if fmt in (MXGEMM_FMT_E2M3, MXGEMM_FMT_E3M2):
+        return 4 * nbytes // 3
+    return nbytes
 
 
 def mxgemm_set_splits(h, splits: int) -> None:
@@ -268,6 +313,19 @@ class Gemm:
     def set_splits(self, splits: int):
         mxgemm_set_splits(self.h, splits)
 
+    def _operand_buffer(self, fmtA, fmtB, M, N, K, device):
+        """Attach an operand buffer large enough for a widened pair (a torch
+        allocation this object keeps, grown as needed); calls through this
+        handle must then be ordered on one stream."""
+        need = mxgemm_operand_buffer_bytes(fmtA, fmtB, M, N, K)
+        if need <= 0:
+            return
+        cur = getattr(self, "opbuf", None)
+        if cur is None or cur.numel() < need or cur.device != device:
+            torch.cuda.synchronize(device)  # a call on any stream may still read the old buffer
+            self.opbuf = torch.empty(need, dtype=torch.uint8, device=device)
+            mxgemm_set_operand_buffer(self.h, self.opbuf, need)
+
     def set_scale_layout(self, layout: int):
         """Scales of later calls are row-major (R, K/32) tensors, or with
         MXGEMM_SCALES_PRESHUFFLED (ceil(R/32)*32, K/32) tensors holding the
@@ -294,21 +352,22 @@ class Gemm:
     def __call__(self, A, A_scale, fmtA, B, B_scale, fmtB, C, use_acc=False,
                  out_dtype=MXGEMM_OUT_F32, stream=None):
         # sub-byte operands are packed along K: e2m1 two codes per byte,
-        # e2m3 four codes per three bytes
+        # e2m3 / e3m2 four codes per three bytes
         M, ka = A.shape
         N = B.shape[0]
-        K = 2 * ka if fmtA == MXGEMM_FMT_E2M1 else (4 * ka // 3 if fmtA == MXGEMM_FMT_E2M3 else ka)
-        kb = K // 2 if fmtB == MXGEMM_FMT_E2M1 else (3 * K // 4 if fmtB == MXGEMM_FMT_E2M3 else K)
-        if B.shape[1] != kb or A_scale.shape != self._scale_shape(M, K) or \
+        K = codes_per_row(fmtA, ka)
+        if B.shape[1] != row_bytes(fmtB, K) or A_scale.shape != self._scale_shape(M, K) or \
                 B_scale.shape != self._scale_shape(N, K):
             raise ValueError("operand shapes do not match (A MxK, B NxK, scales K/32 per row, "
-                             "preshuffled: rows padded to 32; e2m1: K/2 bytes per row, e2m3: 3K/4)")
+                             "preshuffled: rows padded to 32; e2m1: K/2 bytes per row, "
+                             "e2m3 / e3m2: 3K/4)")
         want = torch.float32 if out_dtype == MXGEMM_OUT_F32 else torch.bfloat16
         if C.shape != (M, N) or C.dtype != want:
             raise ValueError(f"C must be ({M}, {N}) {want}")
         for t in (A, A_scale, B, B_scale, C):
             if not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError("all operands must be contiguous device tensors")
+        self._operand_buffer(fmtA, fmtB, M, N, K, A.device)
         mxgemm_run(self.h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, int(bool(use_acc)),
                    out_dtype, stream)
         return C

@@ -1,9 +1,11 @@
-// k_quant.hip -- the MX block quantization kernel, the streaming copy and the
-// conversion of scale bytes to the preshuffled layout.
+// k_quant.hip -- the MX block quantization kernel, the streaming copy, the
+// conversion of scale bytes to the preshuffled layout and the rewrite of
+// sub-byte operand codes as e4m3 bytes.
 #include <algorithm>
 
 #include "mxcopy.h"
 #include "mxgemm_launch.h"
+#include "mxwiden.h"
 
 namespace mxg {
 
@@ -16,6 +18,22 @@ hipError_t launch_quant(int sel, const quant::QuantArgs &a, dim3 grid, dim3 bloc
     case 3: hipLaunchKernelGGL((quant::kernel<1, 1>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((quant::kernel<4, 0>), grid, block, 0, stream, a); break;
     default: hipLaunchKernelGGL((quant::kernel<4, 1>), grid, block, 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_widen(int fmt, const uint8_t *src, uint8_t *dst, uint64_t n, hipStream_t stream)
+{
+    // one thread per 16 codes; at most 8 workgroups per CU, each thread then
+    // loops over its share
+    const uint64_t groups = n / widen::CODES;
+    const uint64_t blocks = std::min<uint64_t>((groups + widen::THREADS - 1) / widen::THREADS, 256 * 8);
+    const dim3 grid((unsigned)std::max<uint64_t>(blocks, 1)), block(widen::THREADS);
+    switch (fmt) {
+    case 4: hipLaunchKernelGGL((widen::kernel<4>), grid, block, 0, stream, src, dst, n); break;
+    case 2: hipLaunchKernelGGL((widen::kernel<2>), grid, block, 0, stream, src, dst, n); break;
+    case 3: hipLaunchKernelGGL((widen::kernel<3>), grid, block, 0, stream, src, dst, n); break;
+    default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

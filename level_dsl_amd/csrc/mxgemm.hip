@@ -30,6 +30,8 @@ struct mxgemm_ctx {
     uint8_t *ws;     // caller's split-K workspace, or NULL
     size_t ws_bytes;
     int scale_layout;  // MXGEMM_SCALES_*
+    uint8_t *opbuf;    // caller's buffer for widened operands, or NULL
+    size_t opbuf_bytes;
 };
 
 // The split-K scratch of mxgemm_run_noalloc: 4 KiB of arrival counters, then
@@ -152,11 +154,40 @@ int choose_splits_large(int forced, int tiles, int units, int unit_stages, size_
 }
 
 // Bytes of an operand row of K codes: e2m1 packs two codes per byte, e2m3
-// four codes per three bytes, e4m3 / e5m2 one per byte.
+// and e3m2 four codes per three bytes, e4m3 / e5m2 one per byte.
 int64_t row_bytes(int fmt, int64_t K)
 {
-    return fmt == MXGEMM_FMT_E2M1 ? K / 2 : fmt == MXGEMM_FMT_E2M3 ? 3 * K / 4 : K;
+    return fmt == MXGEMM_FMT_E2M1                                 ? K / 2
+           : fmt == MXGEMM_FMT_E2M3 || fmt == MXGEMM_FMT_E3M2 ? 3 * K / 4
+                                                                  : K;
 }
+
+bool known_fmt(int f)
+{
+    return f == MXGEMM_FMT_E4M3 || f == MXGEMM_FMT_E5M2 || f == MXGEMM_FMT_E2M3 ||
+           f == MXGEMM_FMT_E3M2 || f == MXGEMM_FMT_E2M1;
+}
+
+bool sub_byte(int f)
+{
+    return f == MXGEMM_FMT_E2M1 || f == MXGEMM_FMT_E2M3 || f == MXGEMM_FMT_E3M2;
+}
+
+// Whether an operand of format f, multiplied with one of format `other`, is
+// rewritten as e4m3 first: e3m2 always (the scaled MFMA's window cannot hold
+// its products' range), e2m1 and e2m3 unless beside themselves.
+bool widened(int f, int other)
+{
+    return sub_byte(f) && (f == MXGEMM_FMT_E3M2 || f != other);
+}
+
+bool shape_ok(int64_t M, int64_t N, int64_t K)
+{
+    return M >= 1 && N >= 1 && K >= 32 && M <= MXGEMM_MAX_M && N <= MXGEMM_MAX_N &&
+           K <= MXGEMM_MAX_K && (K % 32) == 0 && M * N <= MXGEMM_MAX_MN;
+}
+
+constexpr int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // f: 2 fmtA + fmtB for the fp8 pairs (0..3), kF4 for e2m1 x e2m1, kF6 for
 // e2m3 x e2m3 (both always on the scaled MFMA)
@@ -186,7 +217,7 @@ const char *mxgemm_status_string(int code)
     case MXGEMM_OK: return "ok";
     case MXGEMM_ERR_NULL: return "a required pointer is NULL";
     case MXGEMM_ERR_FMT:
-        return "operand format must be e4m3 (0), e5m2 (1), e2m3 (2, with e2m3) or e2m1 (4, with e2m1)";
+        return "operand format must be e4m3 (0), e5m2 (1), e2m3 (2), e3m2 (3) or e2m1 (4)";
     case MXGEMM_ERR_DTYPE: return "out_dtype must be f32 (0) or bf16 (1) and use_acc 0 or 1";
     case MXGEMM_ERR_SHAPE:
         return "M, N, K out of range or K not a multiple of 32 (of 128 with preshuffled scales)";
@@ -196,7 +227,8 @@ const char *mxgemm_status_string(int code)
     case MXGEMM_ERR_HANDLE: return "invalid handle";
     case MXGEMM_ERR_ALIAS: return "C overlaps an input";
     case MXGEMM_ERR_VARIANT: return "unknown kernel variant or scale layout";
-    case MXGEMM_ERR_WORKSPACE: return "split-K workspace missing, too small or misaligned";
+    case MXGEMM_ERR_WORKSPACE:
+        return "split-K workspace or operand buffer missing, too small or misaligned";
     default: return "unknown status";
     }
 }
@@ -221,6 +253,8 @@ int mxgemm_create(mxgemm_t *out)
     h->ws = nullptr;
     h->ws_bytes = 0;
     h->scale_layout = MXGEMM_SCALES_ROW_MAJOR;
+    h->opbuf = nullptr;
+    h->opbuf_bytes = 0;
     *out = h;
     return MXGEMM_OK;
 }
@@ -314,29 +348,54 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA, const 
                          int64_t K, int use_acc, int out_dtype)
 {
     if (!A || !A_scale || !B || !B_scale || !C) return MXGEMM_ERR_NULL;
-    auto known = [](int f) {
-        return f == MXGEMM_FMT_E4M3 || f == MXGEMM_FMT_E5M2 || f == MXGEMM_FMT_E2M3 ||
-               f == MXGEMM_FMT_E2M1;
-    };
-    // the sub-byte formats pair only with themselves; e3m2 is not accepted
-    if (!known(fmtA) || !known(fmtB) || ((fmtA == MXGEMM_FMT_E2M1) != (fmtB == MXGEMM_FMT_E2M1)) ||
-        ((fmtA == MXGEMM_FMT_E2M3) != (fmtB == MXGEMM_FMT_E2M3)))
-        return MXGEMM_ERR_FMT;
+    if (!known_fmt(fmtA) || !known_fmt(fmtB)) return MXGEMM_ERR_FMT;
     if ((out_dtype != MXGEMM_OUT_F32 && out_dtype != MXGEMM_OUT_BF16) ||
         (use_acc != 0 && use_acc != 1))
         return MXGEMM_ERR_DTYPE;
-    if (M < 1 || N < 1 || K < 32 || M > MXGEMM_MAX_M || N > MXGEMM_MAX_N || K > MXGEMM_MAX_K ||
-        (K % 32) != 0 || M * N > MXGEMM_MAX_MN)
-        return MXGEMM_ERR_SHAPE;
+    if (!shape_ok(M, N, K)) return MXGEMM_ERR_SHAPE;
     if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15u) return MXGEMM_ERR_ALIGN;
     const uint64_t csize = (uint64_t)M * (uint64_t)N * (out_dtype == MXGEMM_OUT_F32 ? 4u : 2u);
-    const uint64_t rb = (uint64_t)row_bytes(fmtA, K);
-    if (overlaps(C, csize, A, (uint64_t)M * rb) ||
-        overlaps(C, csize, B, (uint64_t)N * rb) ||
+    if (overlaps(C, csize, A, (uint64_t)M * (uint64_t)row_bytes(fmtA, K)) ||
+        overlaps(C, csize, B, (uint64_t)N * (uint64_t)row_bytes(fmtB, K)) ||
         overlaps(C, csize, A_scale, (uint64_t)M * (K / 32)) ||
         overlaps(C, csize, B_scale, (uint64_t)N * (K / 32)))
         return MXGEMM_ERR_ALIAS;
     return MXGEMM_OK;
+}
+
+int64_t mxgemm_operand_buffer_bytes(int fmtA, int fmtB, int64_t M, int64_t N, int64_t K)
+{
+    if (!known_fmt(fmtA) || !known_fmt(fmtB) || !shape_ok(M, N, K)) return -1;
+    return (widened(fmtA, fmtB) ? round256(M * K) : 0) + (widened(fmtB, fmtA) ? N * K : 0);
+}
+
+int mxgemm_set_operand_buffer(mxgemm_t h, void *buf, size_t bytes)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    if (buf && ((uintptr_t)buf & 255u)) return MXGEMM_ERR_WORKSPACE;
+    h->opbuf = buf ? (uint8_t *)buf : nullptr;
+    h->opbuf_bytes = buf ? bytes : 0;
+    return MXGEMM_OK;
+}
+
+int mxgemm_widen(mxgemm_t h, const void *src, int fmt, int64_t rows, int64_t K, uint8_t *dst,
+                 hipStream_t stream)
+{
+    if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
+    if (!src || !dst) return MXGEMM_ERR_NULL;
+    if (!sub_byte(fmt)) return MXGEMM_ERR_FMT;
+    if (rows < 1 || K < 32 || rows > MXGEMM_MAX_M || K > MXGEMM_MAX_K || K % 32 != 0 ||
+        rows * K > MXGEMM_MAX_QELEMS)
+        return MXGEMM_ERR_SHAPE;
+    if (((uintptr_t)src | (uintptr_t)dst) & 15u) return MXGEMM_ERR_ALIGN;
+    if (overlaps(src, (uint64_t)(rows * row_bytes(fmt, K)), dst, (uint64_t)(rows * K)))
+        return MXGEMM_ERR_ALIAS;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
+    if (dev != h->device) return MXGEMM_ERR_DEVICE;
+    return mxg::launch_widen(fmt, (const uint8_t *)src, dst, (uint64_t)(rows * K), stream) == hipSuccess
+               ? MXGEMM_OK
+               : MXGEMM_ERR_HIP;
 }
 
 } // extern "C"
@@ -346,10 +405,12 @@ namespace {
 // The multiply behind mxgemm_run and mxgemm_run_noalloc: ws / ws_bytes is
 // the split-K workspace (NULL / 0: none), and `strict` turns a forced split
 // count that the workspace cannot hold into MXGEMM_ERR_WORKSPACE instead of
-// fewer splits.
+// fewer splits.  With launch = false it makes every check of the call and
+// launches nothing.
 int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const void *B,
              const uint8_t *B_scale, int fmtB, void *C, int64_t M, int64_t N, int64_t K, int use_acc,
-             int out_dtype, hipStream_t stream, uint8_t *ws, size_t ws_bytes, bool strict)
+             int out_dtype, hipStream_t stream, uint8_t *ws, size_t ws_bytes, bool strict,
+             bool launch)
 {
     if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
     const int rc = mxgemm_validate_args(A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc,
@@ -369,6 +430,39 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
     if (hipGetDevice(&dev) != hipSuccess) return MXGEMM_ERR_HIP;
     if (dev != h->device) return MXGEMM_ERR_DEVICE;
 
+    // A widened pair: each sub-byte operand rewritten as e4m3 into the
+    // operand buffer (A at 0, B after it), then the fp8 pair multiplied.
+    // Every check of that multiply comes first, so that an error launches
+    // nothing.
+    const bool wa = widened(fmtA, fmtB), wb = widened(fmtB, fmtA);
+    if (wa || wb) {
+        const int64_t need = mxgemm_operand_buffer_bytes(fmtA, fmtB, M, N, K);
+        if (!h->opbuf || need <= 0 || (uint64_t)need > h->opbuf_bytes) return MXGEMM_ERR_WORKSPACE;
+        const uint64_t csize = (uint64_t)M * (uint64_t)N * (out_dtype == MXGEMM_OUT_F32 ? 4u : 2u);
+        const int layout = ps ? MXGEMM_SCALES_PRESHUFFLED : MXGEMM_SCALES_ROW_MAJOR;
+        const uint8_t *ob = h->opbuf;
+        if (overlaps(ob, (uint64_t)need, A, (uint64_t)(M * row_bytes(fmtA, K))) ||
+            overlaps(ob, (uint64_t)need, B, (uint64_t)(N * row_bytes(fmtB, K))) ||
+            overlaps(ob, (uint64_t)need, A_scale, (uint64_t)mxgemm_scale_bytes(layout, M, K)) ||
+            overlaps(ob, (uint64_t)need, B_scale, (uint64_t)mxgemm_scale_bytes(layout, N, K)) ||
+            overlaps(ob, (uint64_t)need, C, csize))
+            return MXGEMM_ERR_ALIAS;
+        uint8_t *const wA = h->opbuf;
+        uint8_t *const wB = h->opbuf + (wa ? round256(M * K) : 0);
+        const void *A2 = wa ? (const void *)wA : A;
+        const void *B2 = wb ? (const void *)wB : B;
+        const int fa2 = wa ? (int)MXGEMM_FMT_E4M3 : fmtA, fb2 = wb ? (int)MXGEMM_FMT_E4M3 : fmtB;
+        const int rc2 = run_impl(h, A2, A_scale, fa2, B2, B_scale, fb2, C, M, N, K, use_acc,
+                                 out_dtype, stream, ws, ws_bytes, strict, false);
+        if (rc2 != MXGEMM_OK || !launch) return rc2;
+        if (wa && mxg::launch_widen(fmtA, (const uint8_t *)A, wA, (uint64_t)(M * K), stream) != hipSuccess)
+            return MXGEMM_ERR_HIP;
+        if (wb && mxg::launch_widen(fmtB, (const uint8_t *)B, wB, (uint64_t)(N * K), stream) != hipSuccess)
+            return MXGEMM_ERR_HIP;
+        return run_impl(h, A2, A_scale, fa2, B2, B_scale, fb2, C, M, N, K, use_acc, out_dtype,
+                        stream, ws, ws_bytes, strict, true);
+    }
+
     // 64 < M <= 192 under AUTO: the small-M kernel (exact, or e2m1's) on
     // rows 0..63, 64..127, ..., streaming B once per 64 rows, instead of the
     // 256 x 256 kernel.  Measured at K = 8192: two launches are faster for
@@ -383,13 +477,17 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
         if (M <= 2 * H || (M <= 3 * H && tiles_n <= 64)) {
             const int64_t rb = row_bytes(fmtA, K);
             const size_t esz = out_dtype == MXGEMM_OUT_F32 ? 4 : 2;
-            for (int64_t r = 0; r < M; r += H) {
-                // 64-row steps: whole 32-row groups, the same scale offset in both layouts
-                const int rc_r = run_impl(h, (const uint8_t *)A + r * rb,
-                                          A_scale + r * (K / 32), fmtA, B, B_scale, fmtB,
-                                          (uint8_t *)C + (size_t)r * N * esz, std::min(H, M - r), N,
-                                          K, use_acc, out_dtype, stream, ws, ws_bytes, strict);
-                if (rc_r != MXGEMM_OK) return rc_r;
+            // every chunk checked before the first one launches
+            for (int pass = 0; pass < (launch ? 2 : 1); ++pass) {
+                for (int64_t r = 0; r < M; r += H) {
+                    // 64-row steps: whole 32-row groups, the same scale offset in both layouts
+                    const int rc_r = run_impl(h, (const uint8_t *)A + r * rb,
+                                              A_scale + r * (K / 32), fmtA, B, B_scale, fmtB,
+                                              (uint8_t *)C + (size_t)r * N * esz,
+                                              std::min(H, M - r), N, K, use_acc, out_dtype, stream,
+                                              ws, ws_bytes, strict, pass == 1);
+                    if (rc_r != MXGEMM_OK) return rc_r;
+                }
             }
             return MXGEMM_OK;
         }
@@ -474,6 +572,7 @@ int run_impl(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const 
             }
         }
     }
+    if (!launch) return MXGEMM_OK;
     const int f = fp4 ? kF4 : fp6 ? kF6 : fmtA * 2 + fmtB;
     const hipError_t e = dispatch(native, skinny, f, a, stream);
     return e == hipSuccess ? MXGEMM_OK : MXGEMM_ERR_HIP;
@@ -489,7 +588,7 @@ int mxgemm_run(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, cons
 {
     if (!h || h->magic != kMagic) return MXGEMM_ERR_HANDLE;
     return run_impl(h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc, out_dtype, stream,
-                    h->ws, h->ws_bytes, false);
+                    h->ws, h->ws_bytes, false, true);
 }
 
 int mxgemm_run_noalloc(mxgemm_t h, const void *A, const uint8_t *A_scale, int fmtA, const void *B,
@@ -500,7 +599,7 @@ int mxgemm_run_noalloc(mxgemm_t h, const void *A, const uint8_t *A_scale, int fm
     uint8_t *const sp = h->device >= 0 && h->device < kMaxDevices ? g_scratch[h->device] : nullptr;
     if (!sp) return MXGEMM_ERR_HIP;  // set-up in mxgemm_create did not resolve the array
     return run_impl(h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, use_acc, out_dtype, stream,
-                    sp, kScratchBytes, true);
+                    sp, kScratchBytes, true, true);
 }
 
 

@@ -26,6 +26,8 @@ hipError_t launch_skinny_e2m3(const GemmArgs &a, hipStream_t s);          // k_s
 hipError_t launch_quant(int sel, const quant::QuantArgs &a, dim3 grid, dim3 block,
                         hipStream_t s);                                    // k_quant.hip
 hipError_t launch_copy(const uint8_t *src, uint8_t *dst, uint64_t bytes, hipStream_t s);  // k_quant.hip
+// n codes of format fmt (4 e2m1, 2 e2m3, 3 e3m2; n % 16 == 0) -> n e4m3 bytes
+hipError_t launch_widen(int fmt, const uint8_t *src, uint8_t *dst, uint64_t n, hipStream_t s);  // k_quant.hip
 // row-major scale bytes (rows x KB, KB % 4 == 0) to the preshuffled layout
 hipError_t launch_preshuffle(const uint8_t *src, uint8_t *dst, uint64_t rows, int KB,
                              hipStream_t s);                               // k_quant.hip

@@ -55,8 +55,14 @@ def v(**kw):
 @pytest.mark.parametrize("kw,code", [
     ({}, "MXGEMM_OK"),
     ({"A": 0}, "MXGEMM_ERR_NULL"), ({"B_scale": 0}, "MXGEMM_ERR_NULL"), ({"C": 0}, "MXGEMM_ERR_NULL"),
-    ({"fmtA": 2}, "MXGEMM_ERR_FMT"), ({"fmtB": -1}, "MXGEMM_ERR_FMT"),
-    ({"fmtA": 4}, "MXGEMM_ERR_FMT"), ({"fmtB": 4}, "MXGEMM_ERR_FMT"), ({"fmtA": 3, "fmtB": 3}, "MXGEMM_ERR_FMT"),
+    ({"fmtA": 5}, "MXGEMM_ERR_FMT"), ({"fmtB": -1}, "MXGEMM_ERR_FMT"), ({"fmtB": 7}, "MXGEMM_ERR_FMT"),
+    ({"fmtA": 2}, "MXGEMM_OK"), ({"fmtA": 4}, "MXGEMM_OK"), ({"fmtB": 4}, "MXGEMM_OK"),
+    ({"fmtA": 3, "fmtB": 3}, "MXGEMM_OK"), ({"fmtA": 3, "fmtB": 1}, "MXGEMM_OK"),
+    ({"fmtA": 4, "fmtB": 2}, "MXGEMM_OK"),
+    # B's byte range follows fmtB: C right after a 64 x 128 e2m1 B (4 KiB) is
+    # disjoint from it, and overlaps the same B read as e4m3 (8 KiB)
+    ({"fmtB": 4, "C": 0x31000}, "MXGEMM_OK"), ({"C": 0x31000}, "MXGEMM_ERR_ALIAS"),
+    ({"fmtB": 3, "C": 0x31800}, "MXGEMM_OK"), ({"fmtB": 3, "C": 0x31000}, "MXGEMM_ERR_ALIAS"),
     ({"fmtA": 4, "fmtB": 4}, "MXGEMM_OK"), ({"fmtA": 4, "fmtB": 4, "K": 48}, "MXGEMM_ERR_SHAPE"),
     ({"out_dtype": 2}, "MXGEMM_ERR_DTYPE"), ({"use_acc": 2}, "MXGEMM_ERR_DTYPE"),
     ({"M": 0}, "MXGEMM_ERR_SHAPE"), ({"N": -3}, "MXGEMM_ERR_SHAPE"), ({"K": 0}, "MXGEMM_ERR_SHAPE"),
@@ -70,6 +76,34 @@ def v(**kw):
 ])
 def test_validate_args(kw, code):
     assert v(**kw) == L.STATUS_CODE[code]
+
+
+@pytest.mark.parametrize("fa,fb,M,N,K,want", [
+    (0, 0, 64, 64, 128, 0), (1, 0, 64, 64, 128, 0), (4, 4, 64, 64, 128, 0), (2, 2, 64, 64, 128, 0),
+    (3, 3, 64, 64, 128, 64 * 128 + 64 * 128),            # e3m2: both widened
+    (4, 0, 65, 64, 128, 65 * 128 + 128 + 0),              # A widened: M*K rounded up to 256
+    (0, 2, 65, 64, 128, 64 * 128),                         # B widened only
+    (2, 4, 3, 5, 32, 256 + 5 * 32),                        # both, A padded to 256
+    (5, 0, 64, 64, 128, -1), (0, 3, 64, 64, 48, -1), (0, 3, 0, 64, 128, -1),
+])
+def test_operand_buffer_bytes(fa, fb, M, N, K, want):
+    assert L.mxgemm_operand_buffer_bytes(fa, fb, M, N, K) == want
+
+
+def test_row_bytes_round_trip():
+    for fmt, per in ((0, 1.0), (1, 1.0), (2, 0.75), (3, 0.75), (4, 0.5)):
+        for K in (32, 1056, 1 << 21):
+            assert L.row_bytes(fmt, K) == int(K * per)
+            assert L.codes_per_row(fmt, L.row_bytes(fmt, K)) == K
+
+
+def test_widen_entry_points_reject_bad_handle_without_gpu_work():
+    for call in (lambda: L.mxgemm_widen(None, 0x100000, 3, 4, 128, 0x200000, 0),
+                 lambda: L.mxgemm_set_operand_buffer(None, 0x100000, 4096),
+                 lambda: L.mxgemm_set_operand_buffer(None, None, 0)):
+        with pytest.raises(L.MxgemmError) as e:
+            call()
+        assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_HANDLE"]
 
 
 def test_run_rejects_bad_handle_without_gpu_work():

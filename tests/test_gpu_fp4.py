@@ -291,10 +291,18 @@ def test_fp4_error_paths(gemm):
     p = mi.random_problem(64, 64, 128, seed=860, fmtA=E2M1, fmtB=E2M1)
     A, As, B, Bs = to_dev(p)
     buf, c = alloc_c(p)
-    # e2m1 with e4m3
-    with pytest.raises(L.MxgemmError) as e:
-        L.mxgemm_run(gemm.h, A, As, E2M1, B, Bs, 0, c, 64, 64, 128, 0, 0)
-    assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_FMT"]
+    # e2m1 with e4m3 runs widened: on a handle without an operand buffer it
+    # is rejected before any launch; an unknown format always is
+    w = mi.random_problem(64, 64, 128, seed=862, fmtA=E2M1, fmtB=0)
+    wA, wAs, wB, wBs = to_dev(w)
+    fresh = L.Gemm()
+    try:
+        for fb, name in ((0, "MXGEMM_ERR_WORKSPACE"), (5, "MXGEMM_ERR_FMT")):
+            with pytest.raises(L.MxgemmError) as e:
+                L.mxgemm_run(fresh.h, wA, wAs, E2M1, wB, wBs, fb, c, 64, 64, 128, 0, 0)
+            assert e.value.code == L.STATUS_CODE[name], name
+    finally:
+        fresh.close()
     # a forced small-M variant with M > 64
     q = mi.random_problem(65, 64, 128, seed=861, fmtA=E2M1, fmtB=E2M1)
     qA, qAs, qB, qBs = to_dev(q)

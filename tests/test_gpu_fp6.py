@@ -15,7 +15,8 @@ agreement rule as the exact variants:
     kernels;
   * split-K, forced, on both kernels;
   * the 8192 x 8192 x 8192 shape on sampled outputs;
-  * the error paths (e2m3 with another format, e3m2).
+  * e2m3 beside another format, and e3m2, rejected without an operand
+    buffer (they run widened; tests/test_gpu_widen.py).
 """
 import numpy as np
 import pytest
@@ -157,15 +158,25 @@ def test_fp6_8192cube_sampled(gemm):
             "fp6 8192^3")
 
 
-def test_fp6_rejected_pairs(gemm):
-    """e2m3 with another format, and e3m2 at all, are rejected before any
-    launch."""
+def test_fp6_widened_pairs_need_the_operand_buffer():
+    """e2m3 beside another format, and e3m2, run widened: on a handle
+    without an operand buffer they are rejected before any launch, and an
+    unknown format always is."""
     p = mi.random_problem(64, 64, 128, seed=1600, fmtA=E2M3, fmtB=E2M3)
     A, As, B, Bs = to_dev(p)
     buf, c = alloc_c(p)
-    for fa, fb in ((E2M3, 0), (1, E2M3), (E2M3, 4), (3, 3), (3, 0)):
+    fresh = L.Gemm()
+    try:
+        for fa, fb in ((E2M3, 0), (1, E2M3), (E2M3, 4), (3, 3), (3, 0)):
+            q = mi.random_problem(64, 64, 128, seed=1601 + fa + 8 * fb, fmtA=fa, fmtB=fb)
+            qA, qAs, qB, qBs = to_dev(q)
+            with pytest.raises(L.MxgemmError) as e:
+                L.mxgemm_run(fresh.h, qA, qAs, fa, qB, qBs, fb, c, 64, 64, 128, 0, 0)
+            assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_WORKSPACE"], (fa, fb)
         with pytest.raises(L.MxgemmError) as e:
-            L.mxgemm_run(gemm.h, A, As, fa, B, Bs, fb, c, 64, 64, 128, 0, 0)
-        assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_FMT"], (fa, fb)
+            L.mxgemm_run(fresh.h, A, As, E2M3, B, Bs, 6, c, 64, 64, 128, 0, 0)
+        assert e.value.code == L.STATUS_CODE["MXGEMM_ERR_FMT"]
+    finally:
+        fresh.close()
     torch.cuda.synchronize()
     assert bool(torch.isnan(buf).all()), "a rejected call wrote C"

@@ -405,7 +405,8 @@ def test_invalid_call_launches_nothing(gemm):
     h = gemm.h
     bad = [
         (dict(M=0), "MXGEMM_ERR_SHAPE"), (dict(K=48), "MXGEMM_ERR_SHAPE"),
-        (dict(fmtA=3), "MXGEMM_ERR_FMT"), (dict(out_dtype=7), "MXGEMM_ERR_DTYPE"),
+        (dict(fmtA=5), "MXGEMM_ERR_FMT"), (dict(fmtB=9), "MXGEMM_ERR_FMT"),
+        (dict(out_dtype=7), "MXGEMM_ERR_DTYPE"),
         (dict(C=c.data_ptr() + 4), "MXGEMM_ERR_ALIGN"), (dict(C=A.data_ptr()), "MXGEMM_ERR_ALIAS"),
     ]
     for kw, status in bad:
