@@ -175,6 +175,7 @@ def bench_gemm(gemm, p, variant, steps, warmup, copies, warm_ms=SECONDARY_WARM_M
     C = [torch.empty((p.M, p.N), dtype=dt, device="cuda:0") for _ in range(copies)]
     stream = torch.cuda.current_stream()
     gemm.set_variant(variant)
+    gemm.ensure_operand_buffer(p.fmtA, p.fmtB, p.M, p.N, p.K)  # widened pairs only
     h = gemm.h
 
     def step(i):
@@ -311,6 +312,13 @@ def sub_byte_problem(wid):
     return mi.random_problem(64, 28672, 8192, seed=871, fmtA=mi.FMT_E2M3, fmtB=mi.FMT_E2M3)
 
 
+def widened_problem():
+    """e3m2 x e3m2 at 8192^3: N(0, 1) codes, scales U{120..134}, bf16 out."""
+    import mxinputs as mi
+    return mi.random_problem(8192, 8192, 8192, seed=880, fmtA=mi.FMT_E3M2, fmtB=mi.FMT_E3M2,
+                             out_dtype=mi.OUT_BF16)
+
+
 def traffic_problem(wid):
     import mxinputs as mi
     if wid == "e2m1_8192":
@@ -362,6 +370,45 @@ def bench_quantize(gemm, X, steps, warmup, copies, warm_ms=SECONDARY_WARM_MS):
     return wall, mean_s
 
 
+WIDEN_KERNEL = "void mxg::widen::kernel<3>"
+WIDEN_SHAPE = (28672, 8192)  # the skinny workload's weight, N x K, as e3m2
+
+
+def widen_bytes(R, K):
+    """e3m2 codes read (3/4 byte each), e4m3 bytes written."""
+    return R * K * 3 // 4 + R * K
+
+
+def widen_problem():
+    """N(0, 1) values of the skinny weight's shape quantized to e3m2 (the
+    scales play no part in the rewrite)."""
+    import mxinputs as mi
+    R, K = WIDEN_SHAPE
+    return mi.normal_codes(mi.rng(880, mi.T_B), (R, K), 1.0, mi.FMT_E3M2)
+
+
+def bench_widen(gemm, packed, steps, warmup, copies, warm_ms=SECONDARY_WARM_MS):
+    """Time mxgemm_widen of the packed e3m2 (R, 3K/4) host array, rotated
+    over `copies` device copies.  Returns (wall, mean launch seconds)."""
+    import torch
+    import level_dsl_amd as L
+    dev = torch.device("cuda:0")
+    R, K = WIDEN_SHAPE
+    src = [torch.from_numpy(packed).to(dev)]
+    src += [src[0].clone() for _ in range(copies - 1)]
+    dst = [torch.empty((R, K), dtype=torch.uint8, device=dev) for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        L.mxgemm_widen(gemm.h, src[i % copies], L.MXGEMM_FMT_E3M2, R, K, dst[i % copies],
+                       stream.cuda_stream)
+
+    wall, mean_s = time_launches(step, steps, warmup, stream, warm_ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return wall, mean_s
+
+
 def traffic_launches():
     """Launch the calibration copy and each timed kernel three times (run under
     rocprofv3 --pmc)."""
@@ -382,6 +429,8 @@ def traffic_launches():
         bench_gemm(gemm, p, getattr(L, var), 3, 0, 3, warm_ms=0.0)
     log("traffic: mx_quantize")
     bench_quantize(gemm, mi.skinny_b_raw(), 3, 0, 3, warm_ms=0.0)
+    log("traffic: mx_widen")
+    bench_widen(gemm, widen_problem(), 3, 0, 3, warm_ms=0.0)
     gemm.close()
     torch.cuda.synchronize()
     log("traffic: done")
@@ -418,6 +467,7 @@ def traffic_report(fetch_csv: str, write_csv: str, out_path: str = None):
         out[f"copy_{counter}_kib"] = kib
         names = {k: v[0] for k, v in TRAFFIC_KERNELS.items()}
         names["mx_quantize"] = QUANT_KERNEL
+        names["mx_widen"] = WIDEN_KERNEL
         for key, kname in names.items():
             ks = [tot[d] for d in sorted(tot) if name[d].startswith(kname)]
             if ks:
@@ -443,6 +493,15 @@ def traffic_report(fetch_csv: str, write_csv: str, out_path: str = None):
         alg = quant_bytes(*QUANT_SHAPE)
         out["kernels"]["mx_quantize"] = {
             "kernel": QUANT_KERNEL, "workload": "mxquant_skinny_weight_28672x8192_f32_e4m3",
+            "fetch_bytes": round(v["FETCH_SIZE"]), "write_bytes": round(v["WRITE_SIZE"]),
+            "bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
+            "algorithmic_bytes": alg,
+            "ratio_to_algorithmic": round((v["FETCH_SIZE"] + v["WRITE_SIZE"]) / alg, 3)}
+    v = vals.get("mx_widen", {})
+    if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+        alg = widen_bytes(*WIDEN_SHAPE)
+        out["kernels"]["mx_widen"] = {
+            "kernel": WIDEN_KERNEL, "workload": "mxwiden_skinny_weight_28672x8192_e3m2",
             "fetch_bytes": round(v["FETCH_SIZE"]), "write_bytes": round(v["WRITE_SIZE"]),
             "bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
             "algorithmic_bytes": alg,
@@ -701,6 +760,7 @@ def main():
                      "launch_mean_us": round(mean_q * 1e6, 2)},
         "algorithmic_bytes": qbytes, "steps": q_steps, "x_rotation": 3}
     log(f"bench: mx_quantize {out['mx_quantize']['value']} GB/s")
+
     # ---- the measurement protocol: per-launch events after a cache flush ------
     # C1 256^3 f32, C2 4096^3 f32, C3 8192^3 bf16 (the headline), C4 M = 64,
     # C5 16384^3 e5m2 x e4m3 with use_acc; `runs` launches each after
@@ -729,6 +789,44 @@ def main():
         proto["achievable_hbm"] = achievable_hbm(gemm)
         log(f"bench: streaming copy {proto['achievable_hbm']['rate_at_median']} GB/s")
     out["protocol"] = proto
+
+    # ---- rewrite of e3m2 codes as e4m3 (the widened pairs' first step) --------
+    R, K = WIDEN_SHAPE
+    wbytes = widen_bytes(R, K)
+    packed = widen_problem()
+    wall_w, mean_w = bench_widen(gemm, packed, q_steps, warmup, 3)
+    warm_w = LAST_WARMUP["launches"]
+    del packed
+    out["mx_widen"] = {
+        "warmup_launches": warm_w,
+        "workload": "mxwiden_skinny_weight_28672x8192_e3m2", "value":
+            round(wbytes * q_steps / wall_w / 1e9, 1), "unit": "GB/s",
+        "roofline": {"bound": "hbm", "achieved": round(wbytes / mean_w / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(wbytes / mean_w / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles("mx_widen"),
+                     "kernel": "mxg::widen::kernel<3>",
+                     "launch_mean_us": round(mean_w * 1e6, 2)},
+        "algorithmic_bytes": wbytes, "steps": q_steps, "src_rotation": 3}
+    log(f"bench: mx_widen {out['mx_widen']['value']} GB/s")
+
+    # ---- e3m2 x e3m2 at 8192^3, bf16 out: both operands rewritten as e4m3 -----
+    # into the handle's operand buffer, then the exact 256 x 256 kernel; the
+    # time is the whole call (two rewrites and the multiply)
+    p3 = widened_problem()
+    log("bench: e3m2 8192^3 generated")
+    wall_3, mean_3 = bench_gemm(gemm, p3, L.MXGEMM_VARIANT_AUTO, steps, warmup, 3)
+    warm_3 = LAST_WARMUP["launches"]
+    del p3
+    out["widened_e3m2"] = {
+        "warmup_launches": warm_3,
+        "value": round(flops * steps / wall_3 / 1e12, 2), "unit": "TFLOP/s",
+        "config": {"M": 8192, "N": 8192, "K": 8192, "A": "e3m2 (4 per 3 bytes)",
+                   "B": "e3m2 (4 per 3 bytes)", "out": "bf16 (RNE)",
+                   "path": "mxgemm_widen of A and B, then the exact 256 x 256 kernel"},
+        "call_mean_us": round(mean_3 * 1e6, 2),
+        "pct_of_mxfp8_peak": round(100 * flops / mean_3 / 1e12 / PEAK_TFLOPS["fp8"], 2)}
+    log(f"bench: e3m2 widened {out['widened_e3m2']['value']} TFLOP/s")
     gemm.close()
 
     if not args.no_cpu:

@@ -313,13 +313,14 @@ class Gemm:
     def set_splits(self, splits: int):
         mxgemm_set_splits(self.h, splits)
 
-    def _operand_buffer(self, fmtA, fmtB, M, N, K, device):
+    def ensure_operand_buffer(self, fmtA, fmtB, M, N, K, device="cuda:0"):
         """Attach an operand buffer large enough for a widened pair (a torch
         allocation this object keeps, grown as needed); calls through this
         handle must then be ordered on one stream."""
         need = mxgemm_operand_buffer_bytes(fmtA, fmtB, M, N, K)
         if need <= 0:
             return
+        device = torch.device(device)
         cur = getattr(self, "opbuf", None)
         if cur is None or cur.numel() < need or cur.device != device:
             torch.cuda.synchronize(device)  # a call on any stream may still read the old buffer
@@ -367,7 +368,7 @@ class Gemm:
         for t in (A, A_scale, B, B_scale, C):
             if not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError("all operands must be contiguous device tensors")
-        self._operand_buffer(fmtA, fmtB, M, N, K, A.device)
+        self.ensure_operand_buffer(fmtA, fmtB, M, N, K, A.device)
         mxgemm_run(self.h, A, A_scale, fmtA, B, B_scale, fmtB, C, M, N, K, int(bool(use_acc)),
                    out_dtype, stream)
         return C
