@@ -22,7 +22,9 @@
 // in LDS, filled once per workgroup: a computed conversion costs about 15
 // VALU operations a code, which held the kernel near 3 TB/s on VALU issue;
 // the lookup is one conflict-free LDS byte read (the 64-byte table spans 16
-// distinct banks) between the bit extract and the merge.
+// distinct banks) between the bit extract and the merge.  Loads and stores
+// are non-temporal, as in the streaming copy: every byte is touched once
+// (measured 69.5 against 73.6 us for a 28672 x 8192 e3m2 operand).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,6 +32,9 @@
 #include <cstdint>
 
 namespace mxg::widen {
+
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int THREADS = 256;
 constexpr int CODES = 16;  // per thread
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(THREADS) void kernel(const uint8_t *__restrict__ sr
     for (uint64_t t = (uint64_t)blockIdx.x * THREADS + threadIdx.x; t < groups; t += stride) {
         uint32_t out[4] = {0u, 0u, 0u, 0u};
         if constexpr (FMT == 4) {
-            const uint2 w = *reinterpret_cast<const uint2 *>(src + 8 * t);
+            const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u *>(src + 8 * t));
 #pragma unroll
             for (int j = 0; j < CODES; ++j) {
                 const uint32_t word = j < 8 ? w.x : w.y;
@@ -88,8 +93,9 @@ __global__ __launch_bounds__(THREADS) void kernel(const uint8_t *__restrict__ sr
         } else {
             // 12 bytes at a 4-byte aligned offset: three dwords
             const uint32_t *p = reinterpret_cast<const uint32_t *>(src + 12 * t);
-            const uint64_t lo = (uint64_t)p[0] | ((uint64_t)p[1] << 32);
-            const uint32_t hi = p[2];
+            const uint32_t p0 = __builtin_nontemporal_load(p), p1 = __builtin_nontemporal_load(p + 1);
+            const uint64_t lo = (uint64_t)p0 | ((uint64_t)p1 << 32);
+            const uint32_t hi = __builtin_nontemporal_load(p + 2);
 #pragma unroll
             for (int j = 0; j < CODES; ++j) {
                 const int b = 6 * j;  // first bit of code j
@@ -103,7 +109,8 @@ __global__ __launch_bounds__(THREADS) void kernel(const uint8_t *__restrict__ sr
                 out[j >> 2] |= (uint32_t)lut[c] << (8 * (j & 3));
             }
         }
-        *reinterpret_cast<uint4 *>(dst + 16 * t) = make_uint4(out[0], out[1], out[2], out[3]);
+        const v4u o = {out[0], out[1], out[2], out[3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<v4u *>(dst + 16 * t));
     }
 }
 

@@ -466,6 +466,8 @@ BF16_RNE_CASES = [
     (48, 520, 1024, 0, 1, (SKINNY, SKINNY_NATIVE, LARGE)),  # the small-M kernels
     (300, 520, 1024, 4, 4, (AUTO,)),                        # e2m1 on the 256 x 256 kernel
     (300, 520, 1024, 2, 2, (AUTO,)),                        # e2m3
+    (300, 520, 1024, 3, 0, (AUTO, LARGE_NATIVE)),           # e3m2 x e4m3: widened, then fp8
+    (48, 516, 1024, 0, 4, (SKINNY, SKINNY_NATIVE)),         # e4m3 x e2m1: widened B, small-M kernels
 ]
 
 
