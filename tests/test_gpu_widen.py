@@ -8,7 +8,8 @@ an e4m3 value) and multiplied on the fp8 path.  Checked here:
     e4m3 byte the oracle's decode tables name for each code's value (signed
     zeros included), with a canary past the end of the output;
   * mixed and e3m2 pairs through mxgemm_run on full outputs: both kernels,
-    ragged M, N, K, use_acc, bf16 output, the row-chunked AUTO path;
+    ragged M, N, K, use_acc, bf16 output, the row-chunked AUTO path, and
+    the ABI's limits (the largest K, the largest N, many row tiles);
   * the native variants on a widened pair, to their bound;
   * preshuffled scales, split-K (automatic and forced) and
     mxgemm_run_noalloc on widened pairs;
@@ -261,3 +262,26 @@ def test_widened_error_paths():
         assert bool(torch.isnan(buf).all()), "a rejected call wrote C"
     finally:
         g.close()
+
+
+WIDE_EDGE_CASES = [
+    # M, N, K, fmtA, fmtB, variants
+    (2, 3, 1 << 21, E3M2, E4M3, (AUTO, LARGE)),     # the largest K: a 1.5 MiB packed row of A
+    (3, 1 << 20, 64, E4M3, E2M3, (AUTO, LARGE)),    # the largest N: B rewritten, 64 MiB of e4m3
+    (70000, 40, 64, E2M1, E5M2, (AUTO,)),           # many row tiles, ragged last tile
+]
+
+
+@pytest.mark.parametrize("case", WIDE_EDGE_CASES, ids=lambda c: "x".join(map(str, c[:3])))
+def test_widened_edge_full(gemm, case):
+    """Widened pairs at the limits of the C ABI, full outputs against the
+    oracle, with the guard bands around C intact."""
+    M, N, K, fa, fb, variants = case
+    p = mi.random_problem(M, N, K, seed=(M * 5 + N * 7 + K) % 100019, fmtA=fa, fmtB=fb)
+    ref = oracle_full(p)
+    dev = to_dev(p)
+    for v in variants:
+        log(f"widened edge {case[:5]} variant={v}")
+        got = run(gemm, p, v, guard=64, dev_inputs=dev)
+        compare(got, ref, p.out_dtype, f"widened edge {case[:5]} {v}")
+    gemm.set_variant(AUTO)
