@@ -328,7 +328,9 @@ int mxgemm_validate_args(const void *A, const uint8_t *A_scale, int fmtA,
  * the single rounding to out_dtype.  Buffers must stay valid until the
  * stream reaches this point; the caller synchronises.  Thread-safe: a
  * handle without a workspace may be used from several host threads on
- * different streams (see mxgemm_set_workspace for one with). */
+ * different streams (see mxgemm_set_workspace for one with), except for
+ * widened pairs, whose calls share the handle's operand buffer and must be
+ * ordered (mxgemm_set_operand_buffer). */
 int mxgemm_run(mxgemm_t h,
                const void *A, const uint8_t *A_scale, int fmtA,
                const void *B, const uint8_t *B_scale, int fmtB,
