@@ -18,7 +18,8 @@ exact variants:
   * the 8192 x 8192 x 8192 benchmark shape on sampled outputs;
   * the limits of the C ABI: the largest K and N, many row tiles, and the
     row-chunked small-M launches at the largest N;
-  * the error paths (e2m1 with another format, a small-M variant).
+  * the error paths (e2m1 beside e4m3 on a handle without an operand
+    buffer, an unknown format, a small-M variant with M > 64).
 """
 import numpy as np
 import pytest
