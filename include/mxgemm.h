@@ -364,18 +364,19 @@ int mxgemm_run_noalloc(mxgemm_t h,
  * "TMEM-backed MX Scales"), laid out like the operands of mxgemm_run:
  *   codes   R x K bytes, row-major (an A operand, or B stored K-contiguous);
  *           e2m1: R x K/2 bytes, two codes per byte, the even k in the low
- *           nibble;
+ *           nibble; e2m3 / e3m2: R x 3K/4 bytes, four codes per three bytes;
  *   scales  R x (K/32) bytes, row-major, or in the handle's preshuffled
  *           layout (mxgemm_set_scale_layout).
  * The scale rule (a reading; the pages do not fix it): with MAX = 448
- * (e4m3), 57344 (e5m2) or 6 (e2m1), e is the smallest integer with
+ * (e4m3), 57344 (e5m2), 6 (e2m1), 7.5 (e2m3) or 28 (e3m2), e is the
+ * smallest integer with
  * max|x| <= MAX * 2^e over the block (an all-zero block takes the smallest
  * scale), the scale byte is e + 127 clamped to 0..254, and each code is
  * x * 2^(127 - scale byte) rounded to the nearest value of the format, ties
- * to even, -0 kept as negative zero (0x80; e2m1 0x8).  Inputs must be finite; for a block holding a NaN
+ * to even, -0 kept as negative zero (0x80; e2m1 0x8; e2m3 / e3m2 0x20).  Inputs must be finite; for a block holding a NaN
  * or an infinity the output is unspecified.
  *
- * Checks (pure host): pointers non-NULL, fmt e4m3/e5m2/e2m1, x_dtype, 1 <= R <=
+ * Checks (pure host): pointers non-NULL, fmt e4m3/e5m2/e2m3/e3m2/e2m1, x_dtype, 1 <= R <=
  * MXGEMM_MAX_M, 32 <= K <= MXGEMM_MAX_K with K % 32 == 0, R * K <=
  * MXGEMM_MAX_QELEMS, X and codes 16-byte aligned, and X, codes and scales
  * pairwise disjoint.  Same status codes as mxgemm_validate_args. */

@@ -385,7 +385,7 @@ class Gemm:
         else:
             raise ValueError("X must be float32 or bfloat16")
         R, K = X.shape
-        kc = K // 2 if fmt == MXGEMM_FMT_E2M1 else K  # e2m1: two codes per byte
+        kc = row_bytes(fmt, K)  # e2m1: two codes per byte; e2m3 / e3m2: four per three bytes
         if codes is None:
             codes = torch.empty((R, kc), dtype=torch.uint8, device=X.device)
         if scales is None:
@@ -394,7 +394,7 @@ class Gemm:
             scales = torch.zeros(self._scale_shape(R, K), dtype=torch.uint8, device=X.device)
         if codes.shape != (R, kc) or scales.shape != self._scale_shape(R, K) or \
                 codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
-            raise ValueError("codes must be (R, K) (e2m1: (R, K/2)) and scales (R, K/32) "
-                             "(preshuffled: rows padded to 32), uint8")
+            raise ValueError("codes must be (R, K) (e2m1: (R, K/2), e2m3 / e3m2: (R, 3K/4)) and "
+                             "scales (R, K/32) (preshuffled: rows padded to 32), uint8")
         mxgemm_quantize(self.h, X, xd, R, K, fmt, codes, scales, stream)
         return codes, scales

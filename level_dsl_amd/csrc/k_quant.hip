@@ -16,8 +16,13 @@ hipError_t launch_quant(int sel, const quant::QuantArgs &a, dim3 grid, dim3 bloc
     case 1: hipLaunchKernelGGL((quant::kernel<0, 1>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((quant::kernel<1, 0>), grid, block, 0, stream, a); break;
     case 3: hipLaunchKernelGGL((quant::kernel<1, 1>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((quant::kernel<2, 0>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((quant::kernel<2, 1>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((quant::kernel<3, 0>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((quant::kernel<3, 1>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((quant::kernel<4, 0>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((quant::kernel<4, 1>), grid, block, 0, stream, a); break;
+    case 9: hipLaunchKernelGGL((quant::kernel<4, 1>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

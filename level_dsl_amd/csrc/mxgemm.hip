@@ -607,8 +607,7 @@ int mxgemm_validate_quantize(const void *X, int x_dtype, int64_t R, int64_t K, i
                              const uint8_t *codes, const uint8_t *scales)
 {
     if (!X || !codes || !scales) return MXGEMM_ERR_NULL;
-    if (fmt != MXGEMM_FMT_E4M3 && fmt != MXGEMM_FMT_E5M2 && fmt != MXGEMM_FMT_E2M1)
-        return MXGEMM_ERR_FMT;
+    if (!known_fmt(fmt)) return MXGEMM_ERR_FMT;
     if (x_dtype != MXGEMM_X_F32 && x_dtype != MXGEMM_X_BF16) return MXGEMM_ERR_DTYPE;
     if (R < 1 || K < 32 || R > MXGEMM_MAX_M || K > MXGEMM_MAX_K || (K % 32) != 0 ||
         R * K > MXGEMM_MAX_QELEMS)
@@ -616,7 +615,7 @@ int mxgemm_validate_quantize(const void *X, int x_dtype, int64_t R, int64_t K, i
     if (((uintptr_t)X | (uintptr_t)codes) & 15u) return MXGEMM_ERR_ALIGN;
     const uint64_t n = (uint64_t)R * (uint64_t)K;
     const uint64_t xbytes = n * (x_dtype == MXGEMM_X_F32 ? 4u : 2u);
-    const uint64_t cbytes = fmt == MXGEMM_FMT_E2M1 ? n / 2 : n;  // e2m1: two codes per byte
+    const uint64_t cbytes = (uint64_t)row_bytes(fmt, (int64_t)n);  // packed sub-byte codes
     if (overlaps(X, xbytes, codes, cbytes) || overlaps(X, xbytes, scales, n / 32) ||
         overlaps(codes, cbytes, scales, n / 32))
         return MXGEMM_ERR_ALIAS;
@@ -636,7 +635,7 @@ int mxgemm_quantize(mxgemm_t h, const void *X, int x_dtype, int64_t R, int64_t K
         if (K % 128 != 0) return MXGEMM_ERR_SHAPE;
         const uint64_t n = (uint64_t)R * (uint64_t)K;
         const uint64_t xbytes = n * (x_dtype == MXGEMM_X_F32 ? 4u : 2u);
-        const uint64_t cbytes = fmt == MXGEMM_FMT_E2M1 ? n / 2 : n;
+        const uint64_t cbytes = (uint64_t)row_bytes(fmt, (int64_t)n);
         if (overlaps(X, xbytes, scales, sbytes) || overlaps(codes, cbytes, scales, sbytes))
             return MXGEMM_ERR_ALIAS;
     }

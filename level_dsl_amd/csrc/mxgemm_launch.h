@@ -22,7 +22,7 @@ hipError_t launch_stream_exact(int f, const GemmArgs &a, hipStream_t s);  // k_s
 hipError_t launch_skinny_native(int f, const GemmArgs &a, hipStream_t s); // k_skinny_fp8.hip
 hipError_t launch_skinny_e2m1(const GemmArgs &a, hipStream_t s);          // k_skinny_e2m1.hip
 hipError_t launch_skinny_e2m3(const GemmArgs &a, hipStream_t s);          // k_skinny_e2m1.hip
-// sel = 2 fmt + (x_dtype == bf16), fmt in {0, 1, 4}
+// sel = 2 fmt + (x_dtype == bf16), fmt in {0, 1, 2, 3, 4}
 hipError_t launch_quant(int sel, const quant::QuantArgs &a, dim3 grid, dim3 block,
                         hipStream_t s);                                    // k_quant.hip
 hipError_t launch_copy(const uint8_t *src, uint8_t *dst, uint64_t bytes, hipStream_t s);  // k_quant.hip

@@ -6,8 +6,10 @@
 // max|x| <= MAX * 2^e (MAX = 448 for e4m3, 57344 for e5m2; an all-zero
 // block takes the smallest scale), stored as e + 127 clamped to 0..254, and
 // each code is x * 2^-e rounded to nearest even.  e2m1 (format 4: MAX = 6,
-// codes packed two per byte along K, the even k in the low nibble) follows
-// the same recipe.
+// codes packed two per byte along K, the even k in the low nibble), e2m3
+// (format 2: MAX = 7.5) and e3m2 (format 3: MAX = 28; both packed four codes
+// per three bytes, code k at bits 6k .. 6k+5 of the row's little-endian bit
+// string) follow the same recipe.
 //
 // The work is a flat stream (K % 32 == 0, so blocks never straddle rows):
 //   * a wave owns 4 x 64 consecutive 16-byte chunks of X; lane l loads
@@ -19,13 +21,17 @@
 //     cross-lane shuffles; the scale byte is read off its exponent and
 //     mantissa fields: max|x| = 1.f * 2^(E-127) <= 0.875 * 2^(e+9) for e4m3
 //     gives e + 127 = E - 8 + (f > 0.75), for e5m2 E - 15 + (f > 0.75), for
-//     e2m1 (6 = 1.5 * 2^2) E - 2 + (f > 0.5);
+//     e2m1 (6 = 1.5 * 2^2) E - 2 + (f > 0.5), for e2m3 (7.5 = 1.875 * 2^2)
+//     E - 2 + (f > 0.875), for e3m2 (28 = 1.75 * 2^4) E - 4 + (f > 0.75);
 //   * x * 2^(127 - scale) is exact (a power-of-two product whose magnitude
 //     is at most MAX), and v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 /
 //     v_cvt_scalef32_pk_fp4_f32 (scale 1) round it to nearest even, two
-//     values per instruction;
+//     values per instruction; the 6-bit formats round in software
+//     (fp6_code): the value times a power of two that puts its binade's
+//     grid on the integers, v_rndne_f32, and back;
 //   * codes leave as one 4-byte (fp32 input) or 8-byte (bf16 input) store
-//     per lane and chunk -- e2m1: 2 or 4 bytes -- contiguous across the
+//     per lane and chunk -- e2m1: 2 or 4 bytes, e2m3 / e3m2: 3 or 6 bytes
+//     (4 or 8 codes, whole bytes) -- contiguous across the
 //     wave; the first lane of each block stores its scale byte, at its
 //     place in the row-major or the preshuffled scale layout
 //     (mxgemm_common.h, scale_at).
@@ -70,17 +76,43 @@ __device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t old, float a, float b)
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, B);
 }
 
+// e2m3 (MB = 3, BIAS = 1) / e3m2 (MB = 2, BIAS = 3): the 6-bit code of x *
+// 2^sh rounded to nearest even, for |x| * 2^sh <= the format's largest
+// value.  Below the smallest normal 2^(1-BIAS) the grid is the multiples of
+// 2^(1-BIAS-MB) and the code is the multiple's index (0 .. 2^MB, the last
+// being the smallest normal's code); above it the grid of binade 2^k is the
+// multiples of 2^(k-MB), and the code of a grid value r is its fp32 bits
+// shifted down to MB mantissa bits, rebiased.  Both scalings are exact
+// (powers of two), and rint rounds half to even, i.e. to the even code.
+// The sign is x's (a negative value that rounds to zero gives -0).
+template <int MB, int BIAS>
+__device__ __forceinline__ uint32_t fp6_code(float x, int sh)
+{
+    const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+    const float y = __builtin_ldexpf(__builtin_bit_cast(float, xb & 0x7fffffffu), sh);
+    uint32_t mag;
+    if (y < __builtin_ldexpf(1.0f, 1 - BIAS)) {
+        mag = (uint32_t)__builtin_rintf(__builtin_ldexpf(y, BIAS - 1 + MB));
+    } else {
+        const int k = (int)(__builtin_bit_cast(uint32_t, y) >> 23) - 127;
+        const float r = __builtin_ldexpf(__builtin_rintf(__builtin_ldexpf(y, MB - k)), k - MB);
+        mag = (__builtin_bit_cast(uint32_t, r) >> (23 - MB)) - ((uint32_t)(127 - BIAS) << MB);
+    }
+    return ((xb >> 31) << 5) | mag;
+}
+
 template <int FMT, int XBF16>
 __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
 {
     constexpr bool FP4 = FMT == 4;
+    constexpr bool FP6 = FMT == 2 || FMT == 3;
     constexpr int EPL = XBF16 ? 8 : 4;    // elements per 16-byte chunk
     constexpr int LPB = 32 / EPL;         // lanes per block
     constexpr int ESZ = XBF16 ? 2 : 4;
     constexpr int WAVE_ELEMS = WAVE_BYTES / ESZ;
     // scale byte = E - OFF + (f > THR / 2^23)
-    constexpr uint32_t OFF = FMT == 0 ? 8 : FMT == 1 ? 15 : 2;
-    constexpr uint32_t THR = FP4 ? 0x400000u : 0x600000u;
+    constexpr uint32_t OFF = FMT == 0 ? 8 : FMT == 1 ? 15 : FMT == 3 ? 4 : 2;
+    constexpr uint32_t THR = FP4 ? 0x400000u : FMT == 2 ? 0x700000u : 0x600000u;
 
     const int lane = threadIdx.x & 63;
     const uint64_t e0 = ((uint64_t)blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6)) * WAVE_ELEMS;
@@ -88,7 +120,9 @@ __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
     const uint64_t left = p.n - e0;
     const uint32_t ne = left < (uint64_t)WAVE_ELEMS ? (uint32_t)left : (uint32_t)WAVE_ELEMS;
     const rsrc_t rX = make_rsrc(p.X + e0 * ESZ, ne * ESZ);
-    const rsrc_t rQ = FP4 ? make_rsrc(p.codes + e0 / 2, ne / 2) : make_rsrc(p.codes + e0, ne);
+    const rsrc_t rQ = FP4   ? make_rsrc(p.codes + e0 / 2, ne / 2)
+                      : FP6 ? make_rsrc(p.codes + e0 * 3 / 4, ne * 3 / 4)
+                            : make_rsrc(p.codes + e0, ne);
     // row-major scales: this wave's bytes from block e0 / 32 on; preshuffled:
     // from the 32-row group of the wave's first block (row r0 = sr0 + 32 g0,
     // block kb0 of it) to the end of the buffer
@@ -128,7 +162,31 @@ __global__ __launch_bounds__(THREADS) void kernel(QuantArgs p)
         s = s < 0 ? 0 : (s > 254 ? 254 : s);
         const int sh = 127 - s;
         const uint32_t c = (uint32_t)(64 * j + lane);  // chunk index within the wave
-        if constexpr (FP4) {
+        if constexpr (FP6) {
+            // EPL codes -> 3 EPL / 4 bytes: four codes fill three bytes
+            constexpr int MB = FMT == 2 ? 3 : 2, BIAS = FMT == 2 ? 1 : 3;
+            uint32_t w[EPL / 4];
+#pragma unroll
+            for (int q = 0; q < EPL / 4; ++q) {
+                w[q] = 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[q] |= fp6_code<MB, BIAS>(f[4 * q + i], sh) << (6 * i);
+            }
+            if constexpr (XBF16) {
+                // 48 bits: w[0] in bytes 0..2, w[1] in bytes 3..5, as three
+                // 2-byte stores
+                const uint32_t b = c * 6;
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[0] & 0xffffu), rQ, b, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    (unsigned short)((w[0] >> 16) | ((w[1] & 0xffu) << 8)), rQ, b + 2, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[1] >> 8), rQ, b + 4, 0, 0);
+            } else {
+                const uint32_t b = c * 3;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w[0] >> (8 * i)), rQ, b + i, 0, 0);
+            }
+        } else if constexpr (FP4) {
             // EPL codes -> EPL / 2 bytes, the even element in the low nibble
             uint32_t w = cvt_fp4_pair<0>(0u, __builtin_ldexpf(f[0], sh), __builtin_ldexpf(f[1], sh));
             w = cvt_fp4_pair<1>(w, __builtin_ldexpf(f[2], sh), __builtin_ldexpf(f[3], sh));

@@ -135,7 +135,11 @@ def vq(**kw):
 @pytest.mark.parametrize("kw,code", [
     ({}, "MXGEMM_OK"), ({"x_dtype": 1}, "MXGEMM_OK"), ({"fmt": 1, "R": 1, "K": 32}, "MXGEMM_OK"),
     ({"X": 0}, "MXGEMM_ERR_NULL"), ({"codes": 0}, "MXGEMM_ERR_NULL"), ({"scales": 0}, "MXGEMM_ERR_NULL"),
-    ({"fmt": 2}, "MXGEMM_ERR_FMT"), ({"fmt": 3}, "MXGEMM_ERR_FMT"), ({"fmt": 4}, "MXGEMM_OK"),
+    ({"fmt": 2}, "MXGEMM_OK"), ({"fmt": 3}, "MXGEMM_OK"), ({"fmt": 4}, "MXGEMM_OK"),
+    ({"fmt": 5}, "MXGEMM_ERR_FMT"), ({"fmt": -1}, "MXGEMM_ERR_FMT"),
+    # 6-bit codes take 3/4 of a byte each: 64 x 128 codes end 6 KiB after `codes`
+    ({"fmt": 3, "scales": 0x200000 + 64 * 96}, "MXGEMM_OK"),
+    ({"fmt": 3, "scales": 0x200000 + 64 * 96 - 1}, "MXGEMM_ERR_ALIAS"),
     ({"x_dtype": 2}, "MXGEMM_ERR_DTYPE"),
     ({"R": 0}, "MXGEMM_ERR_SHAPE"), ({"K": 16}, "MXGEMM_ERR_SHAPE"), ({"K": 48}, "MXGEMM_ERR_SHAPE"),
     ({"K": (1 << 21) + 32}, "MXGEMM_ERR_SHAPE"), ({"R": 1 << 20, "K": 1 << 19}, "MXGEMM_ERR_SHAPE"),

@@ -20,7 +20,7 @@ from gpu_helpers import log
 
 pytestmark = pytest.mark.gpu
 
-QMAX = {0: 448.0, 1: 57344.0, 4: 6.0}
+QMAX = {0: 448.0, 1: 57344.0, 2: 7.5, 3: 28.0, 4: 6.0}
 
 
 @pytest.fixture(scope="module")
@@ -38,7 +38,7 @@ def gpu_quantize(gemm, X: np.ndarray, fmt: int):
     else:
         t = torch.from_numpy(X).to("cuda:0")
     R, K = X.shape
-    kc = K // 2 if fmt == 4 else K  # e2m1: two codes per byte
+    kc = L.row_bytes(fmt, K)  # e2m1: two codes per byte; e2m3 / e3m2: four per three bytes
     # guard bytes around both outputs: nothing may be written outside them
     cbuf = torch.full((R * kc + 512,), 0xA5, dtype=torch.uint8, device="cuda:0")
     sbuf = torch.full((R * K // 32 + 512,), 0x5A, dtype=torch.uint8, device="cuda:0")
@@ -68,14 +68,14 @@ def wide_rows(R, K, seed):
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 4])
+@pytest.mark.parametrize("fmt", [0, 1, 4, 2, 3])
 @pytest.mark.parametrize("R,K", [(37, 1120), (1, 32), (3, 96), (129, 4096)])
 def test_random_fp32(gemm, fmt, R, K):
     log(f"quantize fp32 {R}x{K} fmt={fmt}")
     check(gemm, wide_rows(R, K, seed=R * 31 + K + fmt), fmt, f"fp32 {R}x{K}")
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 4])
+@pytest.mark.parametrize("fmt", [0, 1, 4, 2, 3])
 @pytest.mark.parametrize("R,K", [(37, 1120), (5, 64)])
 def test_random_bf16(gemm, fmt, R, K):
     x = wide_rows(R, K, seed=R * 17 + K + fmt)
@@ -84,12 +84,12 @@ def test_random_bf16(gemm, fmt, R, K):
     check(gemm, bits, fmt, f"bf16 {R}x{K}")
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_ties_and_neighbours(gemm, fmt):
     """Blocks whose largest magnitude is exactly MAX (scale 2^0) filled with
     midpoints between neighbouring codes, their fp32 neighbours and the codes'
     own values."""
-    tab = oracle.decode_table(fmt)[:128]
+    tab = oracle.decode_table(fmt)[: 1 << (mi.CODE_BITS[fmt] - 1)]  # the non-negative codes
     fin = np.sort(tab[np.isfinite(tab)])
     mids = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)
     vals = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)),
@@ -105,7 +105,7 @@ def test_ties_and_neighbours(gemm, fmt):
     check(gemm, X, fmt, "ties")
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_extreme_magnitudes_and_zeros(gemm, fmt):
     """Block maxima across the whole fp32 range (subnormals to 3.4e38), all-zero
     and negative-zero blocks."""
