@@ -27,8 +27,9 @@
 //     is at most MAX), and v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 /
 //     v_cvt_scalef32_pk_fp4_f32 (scale 1) round it to nearest even, two
 //     values per instruction; the 6-bit formats round in software
-//     (fp6_code): the value times a power of two that puts its binade's
-//     grid on the integers, v_rndne_f32, and back;
+//     (fp6_code): one fp32 add of a power of two rounds the value to its
+//     binade's grid, half to even, and leaves the grid index in the sum's
+//     mantissa;
 //   * codes leave as one 4-byte (fp32 input) or 8-byte (bf16 input) store
 //     per lane and chunk -- e2m1: 2 or 4 bytes, e2m3 / e3m2: 3 or 6 bytes
 //     (4 or 8 codes, whole bytes) -- contiguous across the
@@ -78,27 +79,24 @@ __device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t old, float a, float b)
 
 // e2m3 (MB = 3, BIAS = 1) / e3m2 (MB = 2, BIAS = 3): the 6-bit code of x *
 // 2^sh rounded to nearest even, for |x| * 2^sh <= the format's largest
-// value.  Below the smallest normal 2^(1-BIAS) the grid is the multiples of
-// 2^(1-BIAS-MB) and the code is the multiple's index (0 .. 2^MB, the last
-// being the smallest normal's code); above it the grid of binade 2^k is the
-// multiples of 2^(k-MB), and the code of a grid value r is its fp32 bits
-// shifted down to MB mantissa bits, rebiased.  Both scalings are exact
-// (powers of two), and rint rounds half to even, i.e. to the even code.
-// The sign is x's (a negative value that rounds to zero gives -0).
+// value.  The grid spacing at magnitude y is q = 2^(k-MB) in binade 2^k,
+// and 2^(1-BIAS-MB) below the smallest normal 2^(1-BIAS).  Adding C = 2^23
+// q to y makes the fp32 adder round y to a multiple of q, half to even (C's
+// ulp is q and y < C), and leaves the multiple's index n in the sum's
+// mantissa field.  Below the smallest normal the code is n; in binade k it
+// is ((k + BIAS - 1) << MB) + n, n running from 2^MB (the binade's first
+// value) to 2^(MB+1) (rounded up into the next binade), which is the same
+// formula with k clamped to 1 - BIAS.  The sign is x's (a negative value
+// that rounds to zero gives -0).
 template <int MB, int BIAS>
 __device__ __forceinline__ uint32_t fp6_code(float x, int sh)
 {
     const uint32_t xb = __builtin_bit_cast(uint32_t, x);
     const float y = __builtin_ldexpf(__builtin_bit_cast(float, xb & 0x7fffffffu), sh);
-    uint32_t mag;
-    if (y < __builtin_ldexpf(1.0f, 1 - BIAS)) {
-        mag = (uint32_t)__builtin_rintf(__builtin_ldexpf(y, BIAS - 1 + MB));
-    } else {
-        const int k = (int)(__builtin_bit_cast(uint32_t, y) >> 23) - 127;
-        const float r = __builtin_ldexpf(__builtin_rintf(__builtin_ldexpf(y, MB - k)), k - MB);
-        mag = (__builtin_bit_cast(uint32_t, r) >> (23 - MB)) - ((uint32_t)(127 - BIAS) << MB);
-    }
-    return ((xb >> 31) << 5) | mag;
+    const uint32_t e = max(__builtin_bit_cast(uint32_t, y) >> 23, (uint32_t)(128 - BIAS));  // biased k, clamped
+    const float c = __builtin_bit_cast(float, (e - MB + 23) << 23);
+    const uint32_t n = __builtin_bit_cast(uint32_t, y + c) & 0x7fffffu;
+    return ((xb >> 31) << 5) | (((e - (128 - BIAS)) << MB) + n);
 }
 
 template <int FMT, int XBF16>
