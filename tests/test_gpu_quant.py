@@ -5,9 +5,10 @@ decision, both taken in the same fp32 arithmetic on both sides).
 
 Cases: random fp32 and bf16 rows spanning many binades, round-to-nearest
 ties and their fp32 neighbours, subnormal and near-overflow magnitudes,
-zeros of both signs, ragged stream tails, both formats, and the full skinny
-workload's weight (its quantized B must equal the workload's stored
-operand).
+zeros of both signs, ragged stream tails, every output format (e4m3,
+e5m2, e2m1, e2m3, e3m2), the full skinny workload's weight (its quantized
+B must equal the workload's stored operand), and GPU-quantized operands
+fed to the multiply (e2m1, and the 6-bit formats alone and beside e4m3).
 """
 import numpy as np
 import pytest
@@ -186,5 +187,31 @@ def test_e2m1_quantize_feeds_the_multiply(gemm):
     gemm(t(qa), t(sa), 4, t(qb), t(sb), 4, C)
     torch.cuda.synchronize()
     ref = oracle.gemm_full(ra, rsa, 4, rb, rsb, 4, M, N, K)
+    err = np.abs(C.cpu().numpy().astype(np.float64) - ref["ref32"])
+    assert np.all(err <= 1e-5 * ref["mag"])
+
+
+@pytest.mark.parametrize("fa,fb", [(2, 2), (3, 3), (3, 0), (0, 2)])
+def test_fp6_quantize_feeds_the_multiply(gemm, fa, fb):
+    """Quantize fp32 A and B on the GPU (6-bit and, where named, e4m3) and
+    multiply them: e2m3 x e2m3 runs on the scaled MFMA, the other pairs
+    widened; the product equals the oracle's product of the oracle's
+    quantization, and the GPU codes equal the oracle's bit for bit."""
+    g = np.random.Generator(np.random.PCG64(73 + fa + 8 * fb))
+    M, N, K = 96, 200, 1024
+    Xa = g.standard_normal((M, K)).astype(np.float32)
+    Xb = (0.02 * g.standard_normal((N, K))).astype(np.float32)
+    qa, sa = gpu_quantize(gemm, Xa, fa)
+    qb, sb = gpu_quantize(gemm, Xb, fb)
+    ra, rsa = oracle.quantize(Xa, fa)
+    rb, rsb = oracle.quantize(Xb, fb)
+    assert np.array_equal(qa, ra) and np.array_equal(sa, rsa)
+    assert np.array_equal(qb, rb) and np.array_equal(sb, rsb)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    log(f"fp6 quantize -> multiply fmtA={fa} fmtB={fb}")
+    gemm(t(qa), t(sa), fa, t(qb), t(sb), fb, C)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_full(ra, rsa, fa, rb, rsb, fb, M, N, K)
     err = np.abs(C.cpu().numpy().astype(np.float64) - ref["ref32"])
     assert np.all(err <= 1e-5 * ref["mag"])
